@@ -1,0 +1,90 @@
+"""ctypes declarations mirroring include/bsc.h."""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_double, c_int32, c_int64, c_size_t, c_void_p
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsc.so")
+
+STATUS = {
+    0: "BSC_OK", -1: "BSC_ERR_ARG", -2: "BSC_ERR_CHARGE", -3: "BSC_ERR_SHAPE", -4: "BSC_ERR_BOUNDS",
+    -5: "BSC_ERR_OVERLAP", -6: "BSC_ERR_MISSING_OUTPUT", -7: "BSC_ERR_UNSUPPORTED", -8: "BSC_ERR_NOT_BOUND",
+    -9: "BSC_ERR_DEVICE_BYTES", -10: "BSC_ERR_HIP",
+}
+
+EXPORTED = ["bsc_options_default", "bsc_plan", "bsc_plan_device_bytes", "bsc_plan_bind", "bsc_contract",
+            "bsc_plan_stats", "bsc_plan_export", "bsc_plan_worklist", "bsc_plan_destroy", "bsc_status_string",
+            "bsc_last_error"]
+
+
+class BscIndex(ctypes.Structure):
+    _fields_ = [("nkeys", c_int32), ("nq", c_int32), ("charge", POINTER(c_int32)),
+                ("dim", POINTER(c_int64)), ("inner", POINTER(c_int64))]
+
+
+class BscOperand(ctypes.Structure):
+    _fields_ = [("nblocks", c_int64), ("row_key", POINTER(c_int32)), ("col_key", POINTER(c_int32)),
+                ("offset", POINTER(c_int64)), ("row_stride", POINTER(c_int64)), ("col_stride", POINTER(c_int64)),
+                ("flux", POINTER(c_int32)), ("buffer_elems", c_int64)]
+
+
+class BscOptions(ctypes.Structure):
+    _fields_ = [("launch_mode", c_int32), ("layout_policy", c_int32), ("accumulate", c_int32),
+                ("grid_limit", c_int32), ("t_launch_us", c_double), ("t_seg_us", c_double),
+                ("pack_gbps", c_double), ("tile_gflops", c_double)]
+
+
+class BscStats(ctypes.Structure):
+    _fields_ = [("triples", c_int64), ("c_blocks", c_int64), ("zero_blocks", c_int64), ("groups", c_int64),
+                ("zero_groups", c_int64), ("axis", c_int32), ("dtype", c_int32),
+                ("mode_count", (c_int64 * 3) * 3), ("runs", c_int64), ("items", c_int64),
+                ("items_by_class", c_int64 * 4), ("launches_per_contract", c_int64),
+                ("launches_per_sector", c_int64), ("useful_flops", c_int64), ("alg_bytes", c_int64),
+                ("pack_bytes", c_int64), ("device_bytes", c_int64), ("tail_triples", c_int64),
+                ("launches_issued", c_int64), ("grid", c_int32), ("reserved", c_int32),
+                ("predicted_us", c_double)]
+
+
+class BscWorklistInfo(ctypes.Structure):
+    _fields_ = [(n, c_int64) for n in ("n_groups", "n_runs", "n_apieces", "n_bpieces", "n_cpieces", "n_tasks",
+                                        "off_groups", "off_runs", "off_apieces", "off_bpieces", "off_cpieces",
+                                        "off_tasks", "bytes", "n_launches")]
+
+
+_lib = None
+
+
+def lib():
+    """Load libbsc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m block_sparse_tensor_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.bsc_options_default.argtypes = [POINTER(BscOptions)]
+        L.bsc_options_default.restype = None
+        L.bsc_plan.argtypes = [POINTER(BscIndex)] * 3 + [POINTER(BscOperand)] * 3 + [c_int32, c_int32,
+                                                                                   POINTER(BscOptions), POINTER(c_void_p)]
+        L.bsc_plan.restype = c_int32
+        L.bsc_plan_device_bytes.argtypes = [c_void_p, POINTER(c_size_t)]
+        L.bsc_plan_device_bytes.restype = c_int32
+        L.bsc_plan_bind.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p]
+        L.bsc_plan_bind.restype = c_int32
+        L.bsc_contract.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.bsc_contract.restype = c_int32
+        L.bsc_plan_stats.argtypes = [c_void_p, POINTER(BscStats)]
+        L.bsc_plan_stats.restype = c_int32
+        L.bsc_plan_export.argtypes = [c_void_p, POINTER(c_int32), POINTER(c_int32), POINTER(c_int32)]
+        L.bsc_plan_export.restype = c_int32
+        L.bsc_plan_worklist.argtypes = [c_void_p, POINTER(BscWorklistInfo), c_void_p, c_size_t]
+        L.bsc_plan_worklist.restype = c_int32
+        L.bsc_plan_destroy.argtypes = [c_void_p]
+        L.bsc_plan_destroy.restype = None
+        L.bsc_status_string.argtypes = [c_int32]
+        L.bsc_status_string.restype = c_char_p
+        L.bsc_last_error.argtypes = []
+        L.bsc_last_error.restype = c_char_p
+        _lib = L
+    return _lib

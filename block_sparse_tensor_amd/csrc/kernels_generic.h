@@ -1,0 +1,169 @@
+// Generic workgroup tile: any strided views, any dtype, vector-ALU FMAs.
+//
+// A 256-thread workgroup computes a 64 x 64 tile of one coalesced group GEMM.
+// For each run of the group it first resolves, once per tile row and column,
+// which piece (member block view) the row or column belongs to and where it
+// starts; the K loop then reads elements through those per-row records
+// (index decoding paid once per tile, not per element).  Operand chunks of
+// 64 x 16 are staged through LDS; each thread owns a 4 x 4 sub-tile with rows
+// and columns strided by 16 so LDS reads are conflict-free.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "bsc_internal.h"
+
+namespace bsc {
+
+struct KArgs {
+    const DTask *tasks;
+    int32_t task0, ntasks;
+    const DGroup *groups;
+    const DRun *runs;
+    const DView *ap, *bp, *cp;
+    const void *A, *B;
+    void *C;
+};
+
+// Address function along the non-piece axis of one row/column of a piece.
+struct Rec {
+    int64_t base;
+    int64_t s0, s1;
+    int32_t in, pad;
+};
+
+template <typename ACC>
+struct Smem {
+    ACC a[16][65];   // [k][row]
+    ACC b[16][65];   // [k][col]
+    Rec ra[64];
+    Rec rb[64];
+};
+
+__device__ __forceinline__ float load_acc(const uint16_t *p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+__device__ __forceinline__ float load_acc(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ double load_acc(const double *p, int64_t i) { return p[i]; }
+
+// last piece whose range starts at or before x (pieces are sorted by begin)
+__device__ __forceinline__ int32_t find_piece(const DView *pc, int32_t n, int32_t x) {
+    int32_t lo = 0, hi = n - 1;
+    while (lo < hi) {
+        int32_t mid = (lo + hi + 1) >> 1;
+        if (pc[mid].begin <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ Rec make_rec(const DView *pc, int32_t n, int32_t x) {
+    const int32_t p = n == 1 ? 0 : find_piece(pc, n, x);
+    const DView v = pc[p];
+    const int32_t xl = x - v.begin;
+    Rec r;
+    r.base = v.off + static_cast<int64_t>(xl / v.ia) * v.sa0 + static_cast<int64_t>(xl % v.ia) * v.sa1;
+    r.s0 = v.sb0;
+    r.s1 = v.sb1;
+    r.in = v.ib;
+    r.pad = 0;
+    return r;
+}
+
+__device__ __forceinline__ int64_t along(const Rec &r, int32_t y) {
+    if (r.in == 1) return r.base + static_cast<int64_t>(y) * r.s0;
+    return r.base + static_cast<int64_t>(y / r.in) * r.s0 + static_cast<int64_t>(y % r.in) * r.s1;
+}
+
+template <typename TA, typename TC, typename ACC>
+__device__ void generic_tile(const KArgs &ka, const DTask &task, Smem<ACC> &sm) {
+    const DGroup g = ka.groups[task.group];
+    const int32_t tid = threadIdx.x;
+    const int32_t m0 = task.m0, n0 = task.n0;
+    const int32_t mlen = min(64, g.M - m0), nlen = min(64, g.N - n0);
+    const int32_t tx = tid & 15, ty = tid >> 4;
+    const TA *A = static_cast<const TA *>(ka.A);
+    const TA *B = static_cast<const TA *>(ka.B);
+
+    ACC acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = ACC(0);
+
+    for (int32_t r = 0; r < g.nrun; ++r) {
+        const DRun run = ka.runs[g.run0 + r];
+        __syncthreads();
+        if (tid < 64) {
+            if (tid < mlen) sm.ra[tid] = make_rec(ka.ap + run.ap0, run.nap, m0 + tid);
+        } else if (tid < 128) {
+            const int32_t j = tid - 64;
+            if (j < nlen) sm.rb[j] = make_rec(ka.bp + run.bp0, run.nbp, n0 + j);
+        }
+        __syncthreads();
+        const bool a_k = (run.flags & R_A_KUNIT) != 0;
+        const bool b_k = (run.flags & R_B_KUNIT) != 0;
+        for (int32_t k0 = 0; k0 < run.K; k0 += 16) {
+            const int32_t kl = min(16, run.K - k0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int32_t e = tid + q * 256;
+                int32_t i, kk;
+                if (a_k) { i = e >> 4; kk = e & 15; }
+                else { i = e & 63; kk = e >> 6; }
+                ACC v = ACC(0);
+                if (i < mlen && kk < kl) v = load_acc(A, along(sm.ra[i], k0 + kk));
+                sm.a[kk][i] = v;
+                int32_t j, kb;
+                if (b_k) { j = e >> 4; kb = e & 15; }
+                else { j = e & 63; kb = e >> 6; }
+                ACC w = ACC(0);
+                if (j < nlen && kb < kl) w = load_acc(B, along(sm.rb[j], k0 + kb));
+                sm.b[kb][j] = w;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                ACC a[4], b[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = sm.a[kk][ty + 16 * i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = sm.b[kk][tx + 16 * j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+            }
+            __syncthreads();
+        }
+    }
+
+    // epilogue: scatter through the C pieces (the per-block views)
+    __syncthreads();
+    const bool cn = (g.flags & G_C_ALONG_N) != 0;
+    if (tid < 64) {
+        if (!cn && tid < mlen) sm.ra[tid] = make_rec(ka.cp + g.cp0, g.ncp, m0 + tid);
+        if (cn && tid < nlen) sm.ra[tid] = make_rec(ka.cp + g.cp0, g.ncp, n0 + tid);
+    }
+    __syncthreads();
+    TC *Cp = static_cast<TC *>(ka.C);
+    const bool accum = (g.flags & G_ACCUMULATE) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int32_t ii = ty + 16 * i;
+        if (ii >= mlen) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int32_t jj = tx + 16 * j;
+            if (jj >= nlen) continue;
+            const int64_t ad = cn ? along(sm.ra[jj], m0 + ii) : along(sm.ra[ii], n0 + jj);
+            ACC v = acc[i][j];
+            if (accum) v += static_cast<ACC>(Cp[ad]);
+            Cp[ad] = static_cast<TC>(v);
+        }
+    }
+}
+
+}  // namespace bsc

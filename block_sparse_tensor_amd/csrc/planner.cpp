@@ -1,0 +1,689 @@
+// Host planner: descriptors -> validated sectors -> sector join -> single-axis
+// groups -> strided pieces and runs -> work list.  Host-only C++17 (no HIP), so
+// it also builds with g++ for sanitizer runs.
+//
+// Follows the uni20 design note "block coalescing":
+//   * sections "Summary" and "Why single-axis coalescing is hole-free": one GEMM
+//     per sector combination (m, k, n), grouped along one axis only;
+//   * section "Expressed as strided views over shared storage": each block
+//     keeps its own (offset, strides) view and the coalesced operand is a wider
+//     view when the members line up;
+//   * section "Interleaved vs contiguous": members that do not line up stay
+//     separate pieces that the kernel walks (no copy);
+//   * section "Coalescing is a plan-time transform": all of this happens here,
+//     once, never inside the kernel.
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <numeric>
+#include <stdexcept>
+#include <unordered_map>
+#include <utility>
+
+#include "bsc_internal.h"
+
+namespace bsc {
+
+namespace {
+
+struct Fail {
+    bsc_status st;
+};
+
+[[noreturn]] void fail(bsc_status st, const std::string &msg) {
+    set_error(msg);
+    throw Fail{st};
+}
+
+struct Idx {
+    int32_t nkeys = 0;
+    std::vector<int32_t> q;      // nkeys * nq
+    std::vector<int64_t> dim, inner;
+};
+
+Idx copy_index(const bsc_index *x, const char *name, int32_t nq) {
+    if (!x) fail(BSC_ERR_ARG, std::string("index ") + name + " is NULL");
+    if (x->nkeys < 0) fail(BSC_ERR_ARG, std::string("index ") + name + ": negative key count");
+    if (x->nq != nq) fail(BSC_ERR_ARG, std::string("index ") + name + ": charge arity differs from index m");
+    Idx r;
+    r.nkeys = x->nkeys;
+    if (r.nkeys > 0 && (!x->charge || !x->dim)) fail(BSC_ERR_ARG, std::string("index ") + name + ": NULL array");
+    r.q.assign(x->charge, x->charge + (size_t)r.nkeys * nq);
+    r.dim.assign(x->dim, x->dim + r.nkeys);
+    r.inner.assign(r.nkeys, 1);
+    if (x->inner) r.inner.assign(x->inner, x->inner + r.nkeys);
+    for (int32_t i = 0; i < r.nkeys; ++i) {
+        if (r.dim[i] < 1 || r.dim[i] > (int64_t(1) << 31) - 1)
+            fail(BSC_ERR_SHAPE, std::string("index ") + name + ": key " + std::to_string(i) + " has dim outside 1..2^31-1");
+        if (r.inner[i] < 1 || r.dim[i] % r.inner[i] != 0)
+            fail(BSC_ERR_SHAPE, std::string("index ") + name + ": key " + std::to_string(i) + " inner extent does not divide dim");
+    }
+    return r;
+}
+
+// Canonical form of one axis of a view: a single leg (inner 1, stride s0, s1 = 0)
+// whenever the two legs collapse, stride 0 for an axis of extent 1.
+void canon_axis(int64_t ext, int64_t inner, int64_t &s0, int64_t &s1, int32_t &in) {
+    int64_t outer = ext / inner;
+    if (ext == 1) { s0 = 0; s1 = 0; in = 1; return; }
+    if (inner == 1) { s1 = 0; in = 1; return; }
+    if (outer == 1) { s0 = s1; s1 = 0; in = 1; return; }
+    if (s0 == inner * s1) { s0 = s1; s1 = 0; in = 1; return; }
+    in = (int32_t)inner;
+}
+
+using u128 = unsigned __int128;
+
+u128 max_addr(int64_t off, int64_t ext_r, int64_t in_r, int64_t rs0, int64_t rs1,
+              int64_t ext_c, int64_t in_c, int64_t cs0, int64_t cs1) {
+    return (u128)off + (u128)(ext_r / in_r - 1) * (u128)rs0 + (u128)(in_r - 1) * (u128)rs1 +
+           (u128)(ext_c / in_c - 1) * (u128)cs0 + (u128)(in_c - 1) * (u128)cs1;
+}
+
+std::vector<Blk> copy_operand(const bsc_operand *X, const char *name, const Idx &R, const Idx &Cc, int32_t nq,
+                              int64_t &elems, std::vector<int32_t> &flux) {
+    if (!X) fail(BSC_ERR_ARG, std::string("operand ") + name + " is NULL");
+    if (X->nblocks < 0) fail(BSC_ERR_ARG, std::string("operand ") + name + ": negative block count");
+    if (X->buffer_elems < 0) fail(BSC_ERR_ARG, std::string("operand ") + name + ": negative buffer size");
+    if (!X->flux) fail(BSC_ERR_ARG, std::string("operand ") + name + ": NULL flux");
+    if (X->nblocks > 0 && (!X->row_key || !X->col_key || !X->offset || !X->row_stride || !X->col_stride))
+        fail(BSC_ERR_ARG, std::string("operand ") + name + ": NULL block array");
+    flux.assign(X->flux, X->flux + nq);
+    elems = X->buffer_elems;
+    std::vector<Blk> out((size_t)X->nblocks);
+    std::unordered_map<uint64_t, int64_t> seen;
+    seen.reserve((size_t)X->nblocks * 2 + 1);
+    for (int64_t b = 0; b < X->nblocks; ++b) {
+        Blk k;
+        k.r = X->row_key[b];
+        k.c = X->col_key[b];
+        std::string where = std::string("operand ") + name + " block " + std::to_string(b);
+        if (k.r < 0 || k.r >= R.nkeys || k.c < 0 || k.c >= Cc.nkeys) fail(BSC_ERR_SHAPE, where + ": key out of range");
+        uint64_t key = ((uint64_t)(uint32_t)k.r << 32) | (uint32_t)k.c;
+        if (!seen.emplace(key, b).second) fail(BSC_ERR_SHAPE, where + ": duplicate (row, col) key pair");
+        for (int32_t j = 0; j < nq; ++j)
+            if ((int64_t)R.q[(size_t)k.r * nq + j] - Cc.q[(size_t)k.c * nq + j] != flux[j])
+                fail(BSC_ERR_CHARGE, where + ": charge rule q_row - q_col == flux broken");
+        k.off = X->offset[b];
+        k.rs0 = X->row_stride[2 * b];
+        k.rs1 = X->row_stride[2 * b + 1];
+        k.cs0 = X->col_stride[2 * b];
+        k.cs1 = X->col_stride[2 * b + 1];
+        int64_t er = R.dim[k.r], ir = R.inner[k.r], ec = Cc.dim[k.c], ic = Cc.inner[k.c];
+        const int64_t legs[4][2] = {{er / ir, k.rs0}, {ir, k.rs1}, {ec / ic, k.cs0}, {ic, k.cs1}};
+        for (auto &lg : legs)
+            if (lg[1] < 0 || (lg[0] > 1 && lg[1] < 1)) fail(BSC_ERR_SHAPE, where + ": a leg of extent > 1 needs a stride >= 1");
+        if (k.off < 0) fail(BSC_ERR_BOUNDS, where + ": negative offset");
+        if (max_addr(k.off, er, ir, k.rs0, k.rs1, ec, ic, k.cs0, k.cs1) >= (u128)elems)
+            fail(BSC_ERR_BOUNDS, where + ": view reaches past the buffer");
+        canon_axis(er, ir, k.rs0, k.rs1, k.ri);
+        canon_axis(ec, ic, k.cs0, k.cs1, k.ci);
+        out[(size_t)b] = k;
+    }
+    return out;
+}
+
+// Element addresses of a canonical block, in row-major element order.
+template <class F>
+void for_each_addr(const Blk &b, int64_t R, int64_t C, F &&f) {
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t rp = b.off + (r / b.ri) * b.rs0 + (r % b.ri) * b.rs1;
+        for (int64_t c = 0; c < C; ++c) f(rp + (c / b.ci) * b.cs0 + (c % b.ci) * b.cs1);
+    }
+}
+
+// C views must be pairwise disjoint and must not alias themselves.  Blocks whose
+// address ranges do not intersect are disjoint; only clusters of intersecting
+// ranges (interleaved views) are checked element by element with a bitmap.
+void check_c_disjoint(const std::vector<Blk> &C, const std::vector<int64_t> &dm, const std::vector<int64_t> &dn) {
+    struct Iv {
+        int64_t lo, hi;
+        size_t i;
+    };
+    std::vector<Iv> iv;
+    iv.reserve(C.size());
+    for (size_t i = 0; i < C.size(); ++i) {
+        const Blk &b = C[i];
+        int64_t R = dm[b.r], Cn = dn[b.c];
+        int64_t hi = (int64_t)max_addr(b.off, R, b.ri, b.rs0, b.rs1, Cn, b.ci, b.cs0, b.cs1);
+        iv.push_back({b.off, hi, i});
+    }
+    std::sort(iv.begin(), iv.end(), [](const Iv &a, const Iv &b) { return a.lo < b.lo || (a.lo == b.lo && a.i < b.i); });
+    auto self_safe = [&](const Blk &b) {
+        int64_t R = dm[b.r], Cn = dn[b.c];
+        std::vector<std::pair<int64_t, int64_t>> legs;  // (stride, extent)
+        int64_t ext[4] = {R / b.ri, b.ri, Cn / b.ci, b.ci};
+        int64_t st[4] = {b.rs0, b.rs1, b.cs0, b.cs1};
+        for (int j = 0; j < 4; ++j)
+            if (ext[j] > 1) legs.push_back({st[j], ext[j]});
+        std::sort(legs.begin(), legs.end());
+        for (size_t j = 1; j < legs.size(); ++j)
+            if ((u128)legs[j].first < (u128)legs[j - 1].first * (u128)legs[j - 1].second) return false;
+        return true;
+    };
+    size_t a = 0;
+    while (a < iv.size()) {
+        size_t e = a + 1;
+        int64_t hi = iv[a].hi;
+        while (e < iv.size() && iv[e].lo <= hi) {
+            hi = std::max(hi, iv[e].hi);
+            ++e;
+        }
+        bool exact = (e - a) > 1 || !self_safe(C[iv[a].i]);
+        if (exact) {
+            int64_t lo = iv[a].lo;
+            std::vector<uint64_t> bits((size_t)((hi - lo) / 64 + 1), 0);
+            for (size_t j = a; j < e; ++j) {
+                const Blk &b = C[iv[j].i];
+                for_each_addr(b, dm[b.r], dn[b.c], [&](int64_t ad) {
+                    uint64_t x = (uint64_t)(ad - lo);
+                    uint64_t &w = bits[x >> 6];
+                    uint64_t m = uint64_t(1) << (x & 63);
+                    if (w & m) fail(BSC_ERR_OVERLAP, "operand C: two C elements share buffer element " + std::to_string(ad));
+                    w |= m;
+                });
+            }
+        }
+        a = e;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// strided pieces
+// ---------------------------------------------------------------------------
+
+// Piece of a canonical block.  along_rows: axis a = block rows, b = block cols.
+DView piece_of(const Blk &b, bool along_rows, int32_t begin, int32_t len) {
+    DView v;
+    v.off = b.off;
+    if (along_rows) {
+        v.sa0 = b.rs0; v.sa1 = b.rs1; v.ia = b.ri;
+        v.sb0 = b.cs0; v.sb1 = b.cs1; v.ib = b.ci;
+    } else {
+        v.sa0 = b.cs0; v.sa1 = b.cs1; v.ia = b.ci;
+        v.sb0 = b.rs0; v.sb1 = b.rs1; v.ib = b.ri;
+    }
+    v.begin = begin;
+    v.len = len;
+    return v;
+}
+
+// Try to extend view `m` (extent m.len along a) by `w` placed right after it
+// along axis a.  Succeeds iff the union is again one strided view.
+bool merge_along_a(DView &m, const DView &w) {
+    if (m.sb0 != w.sb0 || m.sb1 != w.sb1 || m.ib != w.ib) return false;
+    if (m.ia != w.ia) return false;
+    int64_t ia = m.ia;
+    if (ia > 1 && m.sa1 != w.sa1) return false;
+    int64_t mouter = m.len / ia, wouter = w.len / ia;
+    int64_t d = w.off - m.off;
+    if (d <= 0 || d % mouter != 0) return false;
+    int64_t t = d / mouter;                 // outer stride of the union
+    if (mouter > 1 && m.sa0 != t) return false;
+    if (wouter > 1 && w.sa0 != t) return false;
+    m.sa0 = t;
+    m.len += w.len;
+    return true;
+}
+
+// Same along axis b (the contracted axis for A and B pieces): `w` continues `m`
+// along b; both cover the same range along a with identical a-structure.
+bool merge_along_b(DView &m, int64_t m_blen, const DView &w, int64_t w_blen) {
+    if (m.begin != w.begin || m.len != w.len || m.ia != w.ia || m.sa1 != w.sa1) return false;
+    if (m.len > 1 || m.ia > 1) {
+        if (m.sa0 != w.sa0) return false;
+    }
+    if (m.ib != w.ib) return false;
+    int64_t ib = m.ib;
+    if (ib > 1 && m.sb1 != w.sb1) return false;
+    int64_t mouter = m_blen / ib, wouter = w_blen / ib;
+    int64_t d = w.off - m.off;
+    if (d <= 0 || d % mouter != 0) return false;
+    int64_t t = d / mouter;
+    if (mouter > 1 && m.sb0 != t) return false;
+    if (wouter > 1 && w.sb0 != t) return false;
+    m.sb0 = t;
+    return true;
+}
+
+// Stack member views along a: one piece if they interleave into one view.
+std::vector<DView> stack(const std::vector<DView> &mem) {
+    std::vector<DView> out;
+    if (mem.empty()) return out;
+    DView cur = mem[0];
+    bool ok = true;
+    for (size_t i = 1; i < mem.size() && ok; ++i) ok = merge_along_a(cur, mem[i]);
+    if (ok) {
+        out.push_back(cur);
+        return out;
+    }
+    return mem;
+}
+
+int32_t run_flags(const std::vector<DView> &ap, const std::vector<DView> &bp) {
+    auto unit_b = [](const std::vector<DView> &v) {
+        for (auto &p : v)
+            if (p.ib != 1 || (p.sb0 != 1 && p.sb0 != 0)) return false;
+        return true;
+    };
+    auto unit_a = [](const std::vector<DView> &v) {
+        for (auto &p : v)
+            if (p.ia != 1 || (p.sa0 != 1 && p.len > 1)) return false;
+        return true;
+    };
+    int32_t f = 0;
+    if (unit_b(ap)) f |= R_A_KUNIT;
+    if (unit_a(ap)) f |= R_A_FUNIT;
+    if (unit_b(bp)) f |= R_B_KUNIT;
+    if (unit_a(bp)) f |= R_B_FUNIT;
+    return f;
+}
+
+struct Trip {
+    int32_t m, k, n;
+    int32_t ai, bi, ci;
+};
+
+struct GroupSpec {
+    std::vector<int32_t> rows, cols;      // member m keys / n keys
+    std::vector<int32_t> ks;              // contracted keys (ascending)
+    std::vector<int32_t> cblk;            // C block per (row, col) member pair, row-major
+    bool accumulate = false;
+};
+
+}  // namespace
+
+bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc_index *n,
+                      const bsc_operand *A, const bsc_operand *B, const bsc_operand *C) {
+    try {
+        if (!m) fail(BSC_ERR_ARG, "index m is NULL");
+        if (m->nq < 1) fail(BSC_ERR_ARG, "index m: charge arity must be >= 1");
+        const int32_t nq = m->nq;
+        p.nq = nq;
+        Idx im = copy_index(m, "m", nq), ik = copy_index(k, "k", nq), in = copy_index(n, "n", nq);
+        p.dm = im.dim;
+        p.dk = ik.dim;
+        p.dn = in.dim;
+        std::vector<int32_t> fa, fb, fc;
+        p.A = copy_operand(A, "A", im, ik, nq, p.a_elems, fa);
+        p.B = copy_operand(B, "B", ik, in, nq, p.b_elems, fb);
+        p.C = copy_operand(C, "C", im, in, nq, p.c_elems, fc);
+        for (int32_t j = 0; j < nq; ++j)
+            if ((int64_t)fa[j] + fb[j] != fc[j]) fail(BSC_ERR_CHARGE, "flux_C != flux_A + flux_B");
+        check_c_disjoint(p.C, p.dm, p.dn);
+
+        const bool per_sector = p.opt.launch_mode == BSC_LAUNCH_PER_SECTOR;
+        if (!per_sector && p.axis == BSC_AXIS_NONE)
+            fail(BSC_ERR_ARG, "axis NONE needs the per-sector launch mode");
+
+        // ---- sector join on k --------------------------------------------------
+        std::vector<std::vector<int32_t>> b_by_k((size_t)ik.nkeys);
+        for (size_t i = 0; i < p.B.size(); ++i) b_by_k[(size_t)p.B[i].r].push_back((int32_t)i);
+        std::unordered_map<uint64_t, int32_t> cmap;
+        cmap.reserve(p.C.size() * 2 + 1);
+        for (size_t i = 0; i < p.C.size(); ++i)
+            cmap[((uint64_t)(uint32_t)p.C[i].r << 32) | (uint32_t)p.C[i].c] = (int32_t)i;
+        std::vector<Trip> trips;
+        for (size_t ai = 0; ai < p.A.size(); ++ai) {
+            const Blk &a = p.A[ai];
+            for (int32_t bi : b_by_k[(size_t)a.c]) {
+                int32_t nn = p.B[(size_t)bi].c;
+                auto it = cmap.find(((uint64_t)(uint32_t)a.r << 32) | (uint32_t)nn);
+                if (it == cmap.end())
+                    fail(BSC_ERR_MISSING_OUTPUT, "product sector (m=" + std::to_string(a.r) + ", n=" + std::to_string(nn) +
+                                                     ") has no C block");
+                trips.push_back({a.r, a.c, nn, (int32_t)ai, bi, it->second});
+            }
+        }
+        std::sort(trips.begin(), trips.end(), [](const Trip &x, const Trip &y) {
+            if (x.m != y.m) return x.m < y.m;
+            if (x.n != y.n) return x.n < y.n;
+            return x.k < y.k;
+        });
+        p.triples.resize(trips.size());
+        int64_t flops = 0, tail = 0;
+        for (size_t i = 0; i < trips.size(); ++i) {
+            p.triples[i] = {trips[i].m, trips[i].k, trips[i].n};
+            int64_t f = 2 * p.dm[trips[i].m] * p.dk[trips[i].k] * p.dn[trips[i].n];
+            flops += f;
+            if (f <= 1024) ++tail;
+        }
+
+        // C blocks with their k-lists: contiguous stretches of the sorted triples
+        struct CL {
+            int32_t m, n, ci;
+            size_t t0, t1;
+        };
+        std::vector<CL> cls;
+        for (size_t i = 0; i < trips.size();) {
+            size_t j = i;
+            while (j < trips.size() && trips[j].m == trips[i].m && trips[j].n == trips[i].n) ++j;
+            cls.push_back({trips[i].m, trips[i].n, trips[i].ci, i, j});
+            i = j;
+        }
+        std::vector<char> c_has_work(p.C.size(), 0);
+        for (auto &c : cls) c_has_work[(size_t)c.ci] = 1;
+
+        // ---- single-axis grouping ------------------------------------------------
+        int32_t axis = p.axis;
+        auto klist = [&](const CL &c) {
+            std::vector<int32_t> v;
+            for (size_t t = c.t0; t < c.t1; ++t) v.push_back(trips[t].k);
+            return v;
+        };
+        if (per_sector) {
+            axis = BSC_AXIS_NONE;
+        } else if (axis == BSC_AXIS_AUTO) {
+            size_t multi = 0;
+            for (auto &c : cls) multi += (c.t1 - c.t0) > 1;
+            if (!cls.empty() && 4 * multi > cls.size()) {
+                axis = BSC_AXIS_CONTRACT;
+            } else {
+                std::map<std::pair<int32_t, std::vector<int32_t>>, int> gm, gn;
+                for (auto &c : cls) {
+                    auto kl = klist(c);
+                    gm[{c.n, kl}] = 1;
+                    gn[{c.m, kl}] = 1;
+                }
+                axis = gm.size() <= gn.size() ? BSC_AXIS_FREE_M : BSC_AXIS_FREE_N;
+            }
+        }
+        p.axis = axis;
+
+        std::vector<GroupSpec> specs;
+        std::vector<int32_t> gid_of_cl(cls.size(), -1);
+        if (axis == BSC_AXIS_NONE) {
+            for (size_t c = 0; c < cls.size(); ++c)
+                for (size_t t = cls[c].t0; t < cls[c].t1; ++t) {
+                    GroupSpec g;
+                    g.rows = {trips[t].m};
+                    g.cols = {trips[t].n};
+                    g.ks = {trips[t].k};
+                    g.cblk = {trips[t].ci};
+                    g.accumulate = p.opt.accumulate != 0 || t > cls[c].t0;
+                    specs.push_back(std::move(g));
+                }
+        } else if (axis == BSC_AXIS_CONTRACT) {
+            for (size_t c = 0; c < cls.size(); ++c) {
+                GroupSpec g;
+                g.rows = {cls[c].m};
+                g.cols = {cls[c].n};
+                g.ks = klist(cls[c]);
+                g.cblk = {cls[c].ci};
+                g.accumulate = p.opt.accumulate != 0;
+                gid_of_cl[c] = (int32_t)specs.size();
+                specs.push_back(std::move(g));
+            }
+        } else if (axis == BSC_AXIS_FREE_M || axis == BSC_AXIS_FREE_N) {
+            const bool fm = axis == BSC_AXIS_FREE_M;
+            std::map<std::pair<int32_t, std::vector<int32_t>>, std::vector<size_t>> bucket;
+            for (size_t c = 0; c < cls.size(); ++c) bucket[{fm ? cls[c].n : cls[c].m, klist(cls[c])}].push_back(c);
+            struct Tmp {
+                int32_t key, first;
+                std::vector<size_t> members;
+                std::vector<int32_t> ks;
+            };
+            std::vector<Tmp> tmp;
+            for (auto &kv : bucket) {
+                std::vector<size_t> mem = kv.second;
+                std::sort(mem.begin(), mem.end(), [&](size_t x, size_t y) {
+                    return fm ? cls[x].m < cls[y].m : cls[x].n < cls[y].n;
+                });
+                int32_t first = fm ? cls[mem[0]].m : cls[mem[0]].n;
+                tmp.push_back({kv.first.first, first, mem, kv.first.second});
+            }
+            std::sort(tmp.begin(), tmp.end(), [](const Tmp &x, const Tmp &y) {
+                return x.key != y.key ? x.key < y.key : x.first < y.first;
+            });
+            for (auto &t : tmp) {
+                GroupSpec g;
+                g.ks = t.ks;
+                for (size_t c : t.members) {
+                    if (fm) g.rows.push_back(cls[c].m);
+                    else g.cols.push_back(cls[c].n);
+                    g.cblk.push_back(cls[c].ci);
+                    gid_of_cl[c] = (int32_t)specs.size();
+                }
+                if (fm) g.cols = {t.key};
+                else g.rows = {t.key};
+                g.accumulate = p.opt.accumulate != 0;
+                specs.push_back(std::move(g));
+            }
+        } else {
+            fail(BSC_ERR_ARG, "unknown axis");
+        }
+
+        // triple -> group
+        p.group_of_triple.assign(trips.size(), -1);
+        if (axis == BSC_AXIS_NONE) {
+            for (size_t t = 0; t < trips.size(); ++t) p.group_of_triple[t] = (int32_t)t;
+        } else {
+            for (size_t c = 0; c < cls.size(); ++c)
+                for (size_t t = cls[c].t0; t < cls[c].t1; ++t) p.group_of_triple[t] = gid_of_cl[c];
+        }
+
+        // zero-fill groups (overwrite mode): listed C blocks nothing contributes to
+        int64_t zero_blocks = 0;
+        std::vector<int32_t> zero_c;
+        for (size_t i = 0; i < p.C.size(); ++i)
+            if (!c_has_work[i]) {
+                ++zero_blocks;
+                if (!p.opt.accumulate) zero_c.push_back((int32_t)i);
+            }
+
+        // ---- pieces, runs and groups ---------------------------------------------
+        std::unordered_map<uint64_t, int32_t> amap, bmap;
+        amap.reserve(p.A.size() * 2 + 1);
+        bmap.reserve(p.B.size() * 2 + 1);
+        for (size_t i = 0; i < p.A.size(); ++i) amap[((uint64_t)(uint32_t)p.A[i].r << 32) | (uint32_t)p.A[i].c] = (int32_t)i;
+        for (size_t i = 0; i < p.B.size(); ++i) bmap[((uint64_t)(uint32_t)p.B[i].r << 32) | (uint32_t)p.B[i].c] = (int32_t)i;
+        auto akey = [](int32_t r, int32_t c) { return ((uint64_t)(uint32_t)r << 32) | (uint32_t)c; };
+
+        p.groups.clear();
+        p.runs.clear();
+        p.apieces.clear();
+        p.bpieces.clear();
+        p.cpieces.clear();
+        p.group_mode.clear();
+        const int64_t LIM = (int64_t(1) << 31) - 1;
+        for (auto &g : specs) {
+            DGroup dg{};
+            int64_t M = 0, N = 0, K = 0;
+            std::vector<int32_t> rbeg, cbeg;
+            for (int32_t r : g.rows) { rbeg.push_back((int32_t)M); M += p.dm[r]; }
+            for (int32_t c : g.cols) { cbeg.push_back((int32_t)N); N += p.dn[c]; }
+            for (int32_t kk : g.ks) K += p.dk[kk];
+            if (M > LIM || N > LIM || K > LIM) fail(BSC_ERR_UNSUPPORTED, "a coalesced GEMM extent exceeds 2^31-1");
+            dg.M = (int32_t)M;
+            dg.N = (int32_t)N;
+            dg.K = (int32_t)K;
+            dg.flags = g.accumulate ? G_ACCUMULATE : 0;
+            // per-segment pieces
+            std::vector<std::vector<DView>> segA, segB;
+            std::vector<int64_t> segK;
+            for (int32_t kk : g.ks) {
+                std::vector<DView> am, bm;
+                for (size_t i = 0; i < g.rows.size(); ++i) {
+                    const Blk &b = p.A[(size_t)amap.at(akey(g.rows[i], kk))];
+                    am.push_back(piece_of(b, true, rbeg[i], (int32_t)p.dm[g.rows[i]]));
+                }
+                for (size_t j = 0; j < g.cols.size(); ++j) {
+                    const Blk &b = p.B[(size_t)bmap.at(akey(kk, g.cols[j]))];
+                    bm.push_back(piece_of(b, false, cbeg[j], (int32_t)p.dn[g.cols[j]]));
+                }
+                segA.push_back(stack(am));
+                segB.push_back(stack(bm));
+                segK.push_back(p.dk[kk]);
+            }
+            // merge consecutive segments into runs while both operands continue as one view
+            dg.run0 = (int32_t)p.runs.size();
+            bool a_view = true, b_view = true;
+            int64_t kbase = 0;
+            for (size_t s = 0; s < segA.size();) {
+                std::vector<DView> ra = segA[s], rb = segB[s];
+                int64_t rk = segK[s];
+                size_t e = s + 1;
+                while (e < segA.size()) {
+                    if (segA[e].size() != ra.size() || segB[e].size() != rb.size()) break;
+                    std::vector<DView> ta = ra, tb = rb;
+                    bool ok = true;
+                    for (size_t i = 0; i < ta.size() && ok; ++i) ok = merge_along_b(ta[i], rk, segA[e][i], segK[e]);
+                    for (size_t j = 0; j < tb.size() && ok; ++j) ok = merge_along_b(tb[j], rk, segB[e][j], segK[e]);
+                    if (!ok) break;
+                    ra.swap(ta);
+                    rb.swap(tb);
+                    rk += segK[e];
+                    ++e;
+                }
+                DRun r{};
+                r.K = (int32_t)rk;
+                r.kbase = (int32_t)kbase;
+                r.nap = (int32_t)ra.size();
+                r.ap0 = (int32_t)p.apieces.size();
+                r.nbp = (int32_t)rb.size();
+                r.bp0 = (int32_t)p.bpieces.size();
+                r.flags = run_flags(ra, rb);
+                a_view = a_view && ra.size() == 1;
+                b_view = b_view && rb.size() == 1;
+                p.apieces.insert(p.apieces.end(), ra.begin(), ra.end());
+                p.bpieces.insert(p.bpieces.end(), rb.begin(), rb.end());
+                p.runs.push_back(r);
+                kbase += rk;
+                s = e;
+            }
+            dg.nrun = (int32_t)p.runs.size() - dg.run0;
+            // C pieces
+            std::vector<DView> cm;
+            const bool along_n = g.cols.size() > 1;
+            for (size_t i = 0; i < g.rows.size(); ++i)
+                for (size_t j = 0; j < g.cols.size(); ++j) {
+                    const Blk &b = p.C[(size_t)g.cblk[i * g.cols.size() + j]];
+                    if (along_n) cm.push_back(piece_of(b, false, cbeg[j], (int32_t)p.dn[g.cols[j]]));
+                    else cm.push_back(piece_of(b, true, rbeg[i], (int32_t)p.dm[g.rows[i]]));
+                }
+            std::vector<DView> cp = stack(cm);
+            dg.ncp = (int32_t)cp.size();
+            dg.cp0 = (int32_t)p.cpieces.size();
+            if (along_n) dg.flags |= G_C_ALONG_N;
+            p.cpieces.insert(p.cpieces.end(), cp.begin(), cp.end());
+            p.groups.push_back(dg);
+            p.group_mode.push_back({a_view ? BSC_MODE_VIEW : BSC_MODE_SEGMENTS, b_view ? BSC_MODE_VIEW : BSC_MODE_SEGMENTS,
+                                    cp.size() == 1 ? BSC_MODE_VIEW : BSC_MODE_SEGMENTS});
+        }
+        p.n_work_groups = (int32_t)p.groups.size();
+        for (int32_t ci : zero_c) {
+            const Blk &b = p.C[(size_t)ci];
+            DGroup dg{};
+            dg.M = (int32_t)p.dm[b.r];
+            dg.N = (int32_t)p.dn[b.c];
+            dg.K = 0;
+            dg.nrun = 0;
+            dg.run0 = (int32_t)p.runs.size();
+            dg.ncp = 1;
+            dg.cp0 = (int32_t)p.cpieces.size();
+            p.cpieces.push_back(piece_of(b, true, 0, dg.M));
+            p.groups.push_back(dg);
+        }
+
+        // ---- tasks ------------------------------------------------------------------
+        p.tasks.clear();
+        p.launches.clear();
+        const int T = TILE_GENERIC;
+        auto tiles_of = [&](int32_t gi, std::vector<DTask> &out, std::vector<double> *cost) {
+            const DGroup &g = p.groups[(size_t)gi];
+            for (int32_t m0 = 0; m0 < g.M; m0 += T)
+                for (int32_t n0 = 0; n0 < g.N; n0 += T) {
+                    out.push_back({g.nrun ? T_GENERIC : T_ZERO, gi, m0, n0});
+                    if (cost) {
+                        double ml = std::min(T, g.M - m0), nl = std::min(T, g.N - n0);
+                        cost->push_back(2.0 * ml * nl * g.K + 4.0 * ml * nl + 2.0e4 * g.nrun);
+                    }
+                }
+        };
+        if (per_sector) {
+            for (int32_t gi = 0; gi < p.n_work_groups; ++gi) {
+                int32_t t0 = (int32_t)p.tasks.size();
+                tiles_of(gi, p.tasks, nullptr);
+                p.launches.push_back({t0, (int32_t)p.tasks.size()});
+            }
+            if ((int32_t)p.groups.size() > p.n_work_groups) {
+                int32_t t0 = (int32_t)p.tasks.size();
+                for (int32_t gi = p.n_work_groups; gi < (int32_t)p.groups.size(); ++gi) tiles_of(gi, p.tasks, nullptr);
+                p.launches.push_back({t0, (int32_t)p.tasks.size()});
+            }
+        } else {
+            std::vector<DTask> tk;
+            std::vector<double> cost;
+            for (int32_t gi = 0; gi < (int32_t)p.groups.size(); ++gi) tiles_of(gi, tk, &cost);
+            // longest first (stable: ties keep canonical order)
+            std::vector<size_t> ord(tk.size());
+            std::iota(ord.begin(), ord.end(), 0);
+            std::stable_sort(ord.begin(), ord.end(), [&](size_t x, size_t y) { return cost[x] > cost[y]; });
+            for (size_t i : ord) p.tasks.push_back(tk[i]);
+            if (!p.tasks.empty()) p.launches.push_back({0, (int32_t)p.tasks.size()});
+        }
+        if (p.tasks.size() > (size_t)LIM) fail(BSC_ERR_UNSUPPORTED, "too many work items");
+
+        // ---- device image --------------------------------------------------------------
+        auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+        size_t off = 0;
+        p.off_groups = off; off = align(off + p.groups.size() * sizeof(DGroup));
+        p.off_runs = off;   off = align(off + p.runs.size() * sizeof(DRun));
+        p.off_ap = off;     off = align(off + p.apieces.size() * sizeof(DView));
+        p.off_bp = off;     off = align(off + p.bpieces.size() * sizeof(DView));
+        p.off_cp = off;     off = align(off + p.cpieces.size() * sizeof(DView));
+        p.off_tasks = off;  off = align(off + p.tasks.size() * sizeof(DTask));
+        p.dev_bytes = std::max<size_t>(off, 256);
+        p.image.assign(p.dev_bytes, 0);
+        auto put = [&](size_t o, const void *src, size_t nbytes) { if (nbytes) std::memcpy(p.image.data() + o, src, nbytes); };
+        put(p.off_groups, p.groups.data(), p.groups.size() * sizeof(DGroup));
+        put(p.off_runs, p.runs.data(), p.runs.size() * sizeof(DRun));
+        put(p.off_ap, p.apieces.data(), p.apieces.size() * sizeof(DView));
+        put(p.off_bp, p.bpieces.data(), p.bpieces.size() * sizeof(DView));
+        put(p.off_cp, p.cpieces.data(), p.cpieces.size() * sizeof(DView));
+        put(p.off_tasks, p.tasks.data(), p.tasks.size() * sizeof(DTask));
+
+        // ---- statistics ---------------------------------------------------------------
+        bsc_stats &s = p.stats;
+        std::memset(&s, 0, sizeof(s));
+        s.triples = (int64_t)trips.size();
+        s.c_blocks = (int64_t)p.C.size();
+        s.zero_blocks = zero_blocks;
+        s.groups = p.n_work_groups;
+        s.zero_groups = (int64_t)p.groups.size() - p.n_work_groups;
+        s.axis = axis;
+        s.dtype = p.dtype;
+        for (auto &gm : p.group_mode)
+            for (int o = 0; o < 3; ++o) s.mode_count[o][gm[(size_t)o]]++;
+        s.runs = (int64_t)p.runs.size();
+        s.items = (int64_t)p.tasks.size();
+        for (auto &t : p.tasks) s.items_by_class[t.cls]++;
+        s.launches_per_contract = (int64_t)p.launches.size();
+        s.launches_per_sector = s.triples + (zero_c.empty() ? 0 : 1);
+        s.useful_flops = flops;
+        const int64_t ab = p.dtype == BSC_F64 ? 8 : (p.dtype == BSC_F32 ? 4 : 2);
+        const int64_t cb = p.dtype == BSC_F64 ? 8 : 4;
+        int64_t ea = 0, eb = 0, ec = 0;
+        for (auto &b : p.A) ea += p.dm[b.r] * p.dk[b.c];
+        for (auto &b : p.B) eb += p.dk[b.r] * p.dn[b.c];
+        for (auto &b : p.C) ec += p.dm[b.r] * p.dn[b.c];
+        s.alg_bytes = ab * (ea + eb) + cb * ec;
+        s.pack_bytes = 0;
+        s.device_bytes = (int64_t)p.dev_bytes;
+        s.tail_triples = tail;
+        const double rate_gflops = p.dtype == BSC_BF16_F32 ? 2.5e6 : (p.dtype == BSC_F32 ? 157.3e3 : 78.6e3);
+        s.predicted_us = s.launches_per_contract * p.opt.t_launch_us +
+                         std::max((double)flops / (rate_gflops * 1e3), (double)s.alg_bytes / 8.0e6);
+        return BSC_OK;
+    } catch (const Fail &f) {
+        return f.st;
+    } catch (const std::bad_alloc &) {
+        set_error("out of host memory while planning");
+        return BSC_ERR_UNSUPPORTED;
+    } catch (const std::exception &e) {
+        set_error(std::string("planner: ") + e.what());
+        return BSC_ERR_ARG;
+    }
+}
+
+}  // namespace bsc

@@ -1,0 +1,16 @@
+// Device entry points for the host-only planner library used in sanitizer runs
+// on machines without a GPU.  They fail loudly; the shipped library links
+// runtime.hip instead.
+#include "bsc_internal.h"
+
+using namespace bsc;
+
+extern "C" bsc_status bsc_plan_bind(bsc_plan_t, void *, size_t, void *) {
+    set_error("bsc_plan_bind: host-only planner build has no device runtime");
+    return BSC_ERR_UNSUPPORTED;
+}
+
+extern "C" bsc_status bsc_contract(bsc_plan_t, const void *, const void *, void *, void *) {
+    set_error("bsc_contract: host-only planner build has no device runtime");
+    return BSC_ERR_UNSUPPORTED;
+}

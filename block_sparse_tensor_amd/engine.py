@@ -1,0 +1,204 @@
+"""Python binding over the C-ABI (argument marshalling only).
+
+Every step of a contraction runs in libbsc.so: planning in its host planner,
+the contraction in its HIP kernels.  PyTorch supplies device memory and the
+stream; no torch operator touches operand data here.
+"""
+from __future__ import annotations
+
+import ctypes
+from ctypes import byref, c_int32, c_size_t, c_void_p
+
+import numpy as np
+
+from . import _capi
+
+AXES = {"none": 0, "free_m": 1, "free_n": 2, "contract": 3, "auto": 4}
+AXIS_NAMES = {v: k for k, v in AXES.items()}
+DTYPES = {"f64": 0, "f32": 1, "bf16": 2}
+LAUNCH = {"grouped": 0, "per_sector": 1}
+LAYOUT = {"auto": 0, "never_pack": 1, "force_pack": 2}
+MODES = {0: "view", 1: "pack", 2: "segments"}
+
+
+class BscError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = _capi.STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+def _check(st: int):
+    if st != 0:
+        raise BscError(st, _capi.lib().bsc_last_error().decode())
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+class _Keep:
+    """Holds the numpy arrays a ctypes struct points into."""
+
+    def __init__(self):
+        self.arrays = []
+
+    def arr(self, x, dt):
+        a = np.ascontiguousarray(x, dtype=dt)
+        self.arrays.append(a)
+        return a
+
+
+def _index(idx, keep):
+    s = _capi.BscIndex()
+    ch = keep.arr(idx.charge, np.int32)
+    dim = keep.arr(idx.dim, np.int64)
+    s.nkeys = int(dim.shape[0])
+    s.nq = int(ch.shape[1]) if ch.ndim == 2 else 1
+    s.charge = _ptr(ch, ctypes.c_int32)
+    s.dim = _ptr(dim, ctypes.c_int64)
+    s.inner = None if idx.inner is None else _ptr(keep.arr(idx.inner, np.int64), ctypes.c_int64)
+    return s
+
+
+def _operand(op, keep):
+    s = _capi.BscOperand()
+    s.nblocks = int(len(op.row_key))
+    s.row_key = _ptr(keep.arr(op.row_key, np.int32), ctypes.c_int32)
+    s.col_key = _ptr(keep.arr(op.col_key, np.int32), ctypes.c_int32)
+    s.offset = _ptr(keep.arr(op.offset, np.int64), ctypes.c_int64)
+    s.row_stride = _ptr(keep.arr(np.reshape(op.row_stride, (-1, 2)), np.int64), ctypes.c_int64)
+    s.col_stride = _ptr(keep.arr(np.reshape(op.col_stride, (-1, 2)), np.int64), ctypes.c_int64)
+    s.flux = _ptr(keep.arr(op.flux, np.int32), ctypes.c_int32)
+    s.buffer_elems = int(op.buffer_elems)
+    return s
+
+
+def _torch():
+    import torch  # only for device memory and streams
+    return torch
+
+
+def _stream_handle(stream):
+    if stream is None:
+        return c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return c_void_p(stream)
+    return c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """A planned block-sparse contraction C[m,n] = sum_k A[m,k] B[k,n].
+
+    `con` is any object with attributes m, k, n (indices: charge, dim, inner)
+    and A, B, C (operands: row_key, col_key, offset, row_stride, col_stride,
+    flux, buffer_elems), e.g. workloads.Contraction."""
+
+    def __init__(self, con, dtype: str = None, axis: str = "auto", launch_mode: str = "grouped",
+                 layout: str = "auto", accumulate: bool = False, grid_limit: int = 0,
+                 t_launch_us: float = 0.0, t_seg_us: float = 0.0, pack_gbps: float = 0.0, tile_gflops: float = 0.0):
+        L = _capi.lib()
+        self.dtype = dtype or con.dtype
+        keep = _Keep()
+        m, k, n = _index(con.m, keep), _index(con.k, keep), _index(con.n, keep)
+        A, B, C = _operand(con.A, keep), _operand(con.B, keep), _operand(con.C, keep)
+        opt = _capi.BscOptions()
+        L.bsc_options_default(byref(opt))
+        opt.launch_mode = LAUNCH[launch_mode]
+        opt.layout_policy = LAYOUT[layout]
+        opt.accumulate = int(bool(accumulate))
+        opt.grid_limit = int(grid_limit)
+        opt.t_launch_us, opt.t_seg_us, opt.pack_gbps, opt.tile_gflops = t_launch_us, t_seg_us, pack_gbps, tile_gflops
+        h = c_void_p()
+        _check(L.bsc_plan(byref(m), byref(k), byref(n), byref(A), byref(B), byref(C),
+                          DTYPES[self.dtype], AXES[axis], byref(opt), byref(h)))
+        self._h = h
+        self.a_elems, self.b_elems, self.c_elems = int(con.A.buffer_elems), int(con.B.buffer_elems), int(con.C.buffer_elems)
+        self._dev = None
+
+    # -- host-side queries -------------------------------------------------------
+    def device_bytes(self) -> int:
+        n = c_size_t()
+        _check(_capi.lib().bsc_plan_device_bytes(self._h, byref(n)))
+        return int(n.value)
+
+    def stats(self) -> dict:
+        s = _capi.BscStats()
+        _check(_capi.lib().bsc_plan_stats(self._h, byref(s)))
+        out = {}
+        for name, _ in s._fields_:
+            v = getattr(s, name)
+            if name == "mode_count":
+                v = {op: {MODES[j]: int(v[i][j]) for j in range(3)} for i, op in enumerate("ABC")}
+            elif name == "items_by_class":
+                v = dict(zip(("generic", "mfma", "tail", "zero"), (int(x) for x in v)))
+            out[name] = v
+        out["axis_name"] = AXIS_NAMES[out["axis"]]
+        return out
+
+    def export(self):
+        """(triples [T,3] (m,k,n), group_of_triple [T], group_mode [G,3])."""
+        s = self.stats()
+        T, G = s["triples"], s["groups"]
+        t = np.zeros((T, 3), np.int32)
+        g = np.zeros(T, np.int32)
+        md = np.zeros((G, 3), np.int32)
+        _check(_capi.lib().bsc_plan_export(self._h, _ptr(t, ctypes.c_int32), _ptr(g, ctypes.c_int32),
+                                           _ptr(md, ctypes.c_int32)))
+        return t, g, md
+
+    def worklist(self):
+        """(info dict, bytes) of the device work-list image, for inspection."""
+        info = _capi.BscWorklistInfo()
+        _check(_capi.lib().bsc_plan_worklist(self._h, byref(info), None, 0))
+        buf = ctypes.create_string_buffer(int(info.bytes))
+        _check(_capi.lib().bsc_plan_worklist(self._h, byref(info), ctypes.cast(buf, c_void_p), int(info.bytes)))
+        return {n: int(getattr(info, n)) for n, _ in info._fields_}, bytes(buf.raw)
+
+    # -- device ------------------------------------------------------------------
+    def bind(self, device=None, stream=None):
+        """Allocate the plan's device region (torch memory) and upload the work list."""
+        torch = _torch()
+        nbytes = self.device_bytes()
+        dev = torch.empty(nbytes + 256, dtype=torch.uint8, device=device or "cuda")
+        ptr = dev.data_ptr()
+        pad = (-ptr) % 256
+        _check(_capi.lib().bsc_plan_bind(self._h, c_void_p(ptr + pad), c_size_t(nbytes), _stream_handle(stream)))
+        self._dev = dev
+        return self
+
+    def _check_tensor(self, t, name, need, dtypes):
+        torch = _torch()
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA/HIP torch tensor")
+        if t.dtype not in dtypes:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+        if not t.is_contiguous() or t.numel() < need:
+            raise ValueError(f"{name} must be contiguous with at least {need} elements")
+
+    def contract(self, A, B, C, stream=None):
+        """Enqueue C (+)= A B on `stream` (default: torch's current stream)."""
+        if self._dev is None:
+            raise BscError(-8, "plan is not bound (call bind())")
+        torch = _torch()
+        if self.dtype == "f64":
+            ab, cd = (torch.float64,), (torch.float64,)
+        elif self.dtype == "f32":
+            ab, cd = (torch.float32,), (torch.float32,)
+        else:
+            ab, cd = (torch.bfloat16, torch.int16, torch.uint16), (torch.float32,)
+        self._check_tensor(A, "A", self.a_elems, ab)
+        self._check_tensor(B, "B", self.b_elems, ab)
+        self._check_tensor(C, "C", self.c_elems, cd)
+        _check(_capi.lib().bsc_contract(self._h, c_void_p(A.data_ptr()), c_void_p(B.data_ptr()),
+                                        c_void_p(C.data_ptr()), _stream_handle(stream)))
+        return C
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                _capi.lib().bsc_plan_destroy(h)
+            except Exception:
+                pass
+            self._h = None

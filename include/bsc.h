@@ -1,0 +1,227 @@
+/*
+ * bsc.h — block-sparse contraction engine for AMD Instinct MI355X (gfx950).
+ *
+ * Computes the block GEMM over symmetry sectors
+ *
+ *     C[m,n] = sum_k A[m,k] * B[k,n]
+ *
+ * where every index is a list of keys (sectors) and every operand is a list of
+ * blocks, each a strided view into one flat device buffer.  This is the
+ * contraction of the uni20 design note "block coalescing" (section "Why
+ * single-axis coalescing is hole-free").  The planner groups the per-sector
+ * GEMMs along ONE axis only — stacking output blocks that share the other
+ * output key and the contracted-key list (free-axis grouping), or
+ * concatenating the contracted keys of one output block (contraction-axis
+ * grouping) — so the coalesced operands have no structural zeros (same
+ * section).  Each block keeps its sector identity through its own
+ * (offset, stride) view (section "Expressed as strided views over shared
+ * storage"), and grouping happens once, at plan time (section "Coalescing is a
+ * plan-time transform").  A contraction then runs as one persistent
+ * grouped-GEMM launch, plus one gather launch when some group is packed
+ * (section "Interleaved vs contiguous — the real tradeoff is a copy").
+ *
+ * Conventions
+ * -----------
+ * Charges.  Key r of an index carries an integer charge vector of length nq
+ * (1 for U(1), 2 for U(1)xU(1)).  A block (r, c) of operand X may exist only if
+ * q_row(r) - q_col(c) == flux_X componentwise, and flux_C must equal
+ * flux_A + flux_B.
+ *
+ * Views.  A key may be a fused pair of legs: dim = outer * inner.  Element
+ * (r, c) of a block lives at buffer element
+ *     offset + (r / Ri)*rs[0] + (r % Ri)*rs[1] + (c / Ci)*cs[0] + (c % Ci)*cs[1]
+ * with Ri, Ci the inner extents of the row and column keys (1 when `inner` is
+ * NULL).  Strides are in elements; a leg of extent > 1 needs a stride >= 1,
+ * the stride of a unit leg is ignored.  C blocks must not overlap; A and B
+ * blocks may.
+ *
+ * Semantics.  Overwrite mode (default): every listed C block receives
+ * sum over k of A[m,k] B[k,n], or zeros if no k contributes.  Accumulate mode
+ * adds to what C holds.  Elements of C's buffer outside every listed C block
+ * are never written.  A product sector (m, n) absent from C's block list is an
+ * error (BSC_ERR_MISSING_OUTPUT).
+ *
+ * Types.  BSC_F64: A, B, C double.  BSC_F32: A, B, C float.  BSC_BF16_F32:
+ * A, B bfloat16 (16-bit patterns), accumulation and C in float.
+ *
+ * Ownership.  bsc_plan copies every descriptor array; the caller may free them
+ * on return.  A plan owns host memory only.  All device memory — A, B, C and
+ * the plan's device region (work list + pack workspace) — belongs to the
+ * caller and must outlive every contraction enqueued on it.
+ *
+ * Streams.  `stream` arguments are hipStream_t values passed as void*
+ * (NULL = the null stream).  bsc_contract enqueues its launches and returns
+ * without synchronising.  The pack workspace lives in the plan's device
+ * region, so one plan must not run on two streams at once.
+ *
+ * Errors.  Every call returns a bsc_status; nothing throws or aborts across
+ * this interface.  bsc_last_error() gives a thread-local message for the last
+ * failing call.
+ */
+#ifndef BSC_H
+#define BSC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSC_OK = 0,
+    BSC_ERR_ARG = -1,            /* NULL pointer, bad enum, size mismatch, unbound plan buffers */
+    BSC_ERR_CHARGE = -2,         /* a block breaks the charge rule, or flux_C != flux_A + flux_B */
+    BSC_ERR_SHAPE = -3,          /* bad dim / inner extent / stride, duplicate block, key out of range */
+    BSC_ERR_BOUNDS = -4,         /* a block reaches outside its buffer, or a negative offset */
+    BSC_ERR_OVERLAP = -5,        /* two C elements share a buffer element */
+    BSC_ERR_MISSING_OUTPUT = -6, /* a product sector (m,n) has no C block */
+    BSC_ERR_UNSUPPORTED = -7,    /* sizes beyond the engine's 32-bit tile indexing, or no device */
+    BSC_ERR_NOT_BOUND = -8,      /* bsc_contract before bsc_plan_bind */
+    BSC_ERR_DEVICE_BYTES = -9,   /* the device region passed to bind is too small */
+    BSC_ERR_HIP = -10            /* a HIP runtime call failed (detail in bsc_last_error) */
+} bsc_status;
+
+typedef enum { BSC_F64 = 0, BSC_F32 = 1, BSC_BF16_F32 = 2 } bsc_dtype;
+
+/* Coalescing axis.  NONE = one group per sector GEMM (only meaningful with the
+ * per-sector launch mode).  FREE_M: stack output blocks sharing n and the
+ * contracted-key list along M.  FREE_N: the same along N.  CONTRACT: one group
+ * per output block, contracted keys concatenated along K.  AUTO: CONTRACT if
+ * more than a quarter of the non-empty output blocks sum over more than one k,
+ * else whichever free axis yields fewer groups (FREE_M on a tie). */
+typedef enum {
+    BSC_AXIS_NONE = 0, BSC_AXIS_FREE_M = 1, BSC_AXIS_FREE_N = 2,
+    BSC_AXIS_CONTRACT = 3, BSC_AXIS_AUTO = 4
+} bsc_axis;
+
+typedef enum { BSC_LAUNCH_GROUPED = 0, BSC_LAUNCH_PER_SECTOR = 1 } bsc_launch_mode;
+
+/* Operand arrangement policy per group.  AUTO: the cost model decides between
+ * the zero-copy arrangement (VIEW when the members form one strided view,
+ * else SEGMENTS: per-member views walked inside the work item) and PACK (a
+ * gather into contiguous workspace).  NEVER_PACK and FORCE_PACK pin it. */
+typedef enum { BSC_LAYOUT_AUTO = 0, BSC_LAYOUT_NEVER_PACK = 1, BSC_LAYOUT_FORCE_PACK = 2 } bsc_layout_policy;
+
+/* Arrangement of one operand of one group, as reported by bsc_plan_export. */
+typedef enum { BSC_MODE_VIEW = 0, BSC_MODE_PACK = 1, BSC_MODE_SEGMENTS = 2 } bsc_mode;
+
+typedef struct {
+    int32_t nkeys;          /* number of keys (>= 0) */
+    int32_t nq;             /* charge components per key (>= 1, equal for m, k, n) */
+    const int32_t *charge;  /* [nkeys * nq], key-major */
+    const int64_t *dim;     /* [nkeys], >= 1 */
+    const int64_t *inner;   /* [nkeys] inner-leg extents (>= 1, dividing dim), or NULL */
+} bsc_index;
+
+typedef struct {
+    int64_t nblocks;
+    const int32_t *row_key;    /* [nblocks] */
+    const int32_t *col_key;    /* [nblocks] */
+    const int64_t *offset;     /* [nblocks] first element, in elements */
+    const int64_t *row_stride; /* [2 * nblocks]: outer, inner leg of the row key */
+    const int64_t *col_stride; /* [2 * nblocks]: outer, inner leg of the column key */
+    const int32_t *flux;       /* [nq] */
+    int64_t buffer_elems;      /* elements in the operand's flat buffer */
+} bsc_operand;
+
+typedef struct {
+    int32_t launch_mode;    /* bsc_launch_mode */
+    int32_t layout_policy;  /* bsc_layout_policy */
+    int32_t accumulate;     /* 0: C = A B ; 1: C += A B */
+    int32_t grid_limit;     /* cap on workgroups per grouped launch; 0 = engine default */
+    /* cost-model constants; 0 selects the built-in MI355X defaults */
+    double t_launch_us;     /* host-to-kernel launch cost */
+    double t_seg_us;        /* extra cost per contracted segment walked inside a tile */
+    double pack_gbps;       /* gather bandwidth */
+    double tile_gflops;     /* sustained per-workgroup rate of the matrix-core tile */
+} bsc_options;
+
+typedef struct {
+    int64_t triples;                 /* sector GEMMs (m, k, n) */
+    int64_t c_blocks;                /* listed C blocks */
+    int64_t zero_blocks;             /* listed C blocks no k contributes to */
+    int64_t groups;                  /* coalescing groups with work (zero-fill groups excluded) */
+    int64_t zero_groups;             /* zero-fill groups */
+    int32_t axis;                    /* resolved bsc_axis */
+    int32_t dtype;                   /* bsc_dtype */
+    int64_t mode_count[3][3];        /* [operand A,B,C][bsc_mode]: groups per arrangement */
+    int64_t runs;                    /* contiguous K-runs over all groups */
+    int64_t items;                   /* work items per contraction */
+    int64_t items_by_class[4];       /* generic tile, matrix-core tile, wave tail, zero fill */
+    int64_t launches_per_contract;   /* GPU commands bsc_contract enqueues */
+    int64_t launches_per_sector;     /* one launch per sector GEMM (+1 zero fill if needed) */
+    int64_t useful_flops;            /* sum over triples of 2 M N K */
+    int64_t alg_bytes;               /* A and B blocks read once + C blocks written once */
+    int64_t pack_bytes;              /* bytes the gather kernel writes per contraction */
+    int64_t device_bytes;            /* size of the device region bsc_plan_bind needs */
+    int64_t tail_triples;            /* triples with 2 M N K <= 1024 */
+    int64_t launches_issued;         /* launches enqueued by this plan so far */
+    int32_t grid;                    /* workgroups of the grouped launch */
+    int32_t reserved;
+    double predicted_us;             /* cost-model estimate of one contraction */
+} bsc_stats;
+
+typedef struct bsc_plan_s *bsc_plan_t;
+
+/* Fill *opt with defaults (grouped launch, AUTO layout, overwrite, built-in
+ * cost constants). */
+void bsc_options_default(bsc_options *opt);
+
+/* Validate the descriptors, join sectors on k, build single-axis groups along
+ * `axis`, choose each operand's arrangement and build the work list (host
+ * only; no device call).  `opt` may be NULL.  On success *out owns a new plan. */
+bsc_status bsc_plan(const bsc_index *m, const bsc_index *k, const bsc_index *n,
+                    const bsc_operand *A, const bsc_operand *B, const bsc_operand *C,
+                    bsc_dtype dtype, bsc_axis axis, const bsc_options *opt, bsc_plan_t *out);
+
+/* Bytes of device memory bsc_plan_bind needs (work list + pack workspace). */
+bsc_status bsc_plan_device_bytes(bsc_plan_t plan, size_t *bytes);
+
+/* Upload the work list into the caller's device region `dev` (>= device_bytes,
+ * 256-byte aligned) on `stream` and wait for the copy.  Also records the
+ * current device's compute-unit count for the launch grid.  May be called
+ * again with another region. */
+bsc_status bsc_plan_bind(bsc_plan_t plan, void *dev, size_t bytes, void *stream);
+
+/* Enqueue one contraction on `stream`: C (+)= A B.  A, B, C are device
+ * pointers to the flat buffers the descriptors index (element types per
+ * dtype).  Returns without synchronising. */
+bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B, void *C, void *stream);
+
+/* Plan statistics (host only). */
+bsc_status bsc_plan_stats(bsc_plan_t plan, bsc_stats *out);
+
+/* Export the sector map for bit-exact checks: triples [3*T] as (m, k, n) key
+ * ids sorted by (m, n, k); group_of_triple [T] (canonical group order; zero-fill
+ * groups are not numbered); group_mode [3*G] the bsc_mode of A, B, C per group.
+ * Any pointer may be NULL.  Sizes come from bsc_plan_stats (T = triples,
+ * G = groups). */
+bsc_status bsc_plan_export(bsc_plan_t plan, int32_t *triples, int32_t *group_of_triple, int32_t *group_mode);
+
+/* Layout of the device work list (for inspection tools and host-side checks of
+ * the kernels' addressing).  Counts are records; offsets are bytes into the
+ * device region.  The record formats are internal to this library version. */
+typedef struct {
+    int64_t n_groups, n_runs, n_apieces, n_bpieces, n_cpieces, n_tasks;
+    int64_t off_groups, off_runs, off_apieces, off_bpieces, off_cpieces, off_tasks;
+    int64_t bytes;           /* size of the work-list image */
+    int64_t n_launches;      /* launches per contraction */
+} bsc_worklist_info;
+
+/* Fill *info and, if image != NULL and bytes >= info->bytes, copy the host
+ * image of the device work list (what bsc_plan_bind uploads) into image. */
+bsc_status bsc_plan_worklist(bsc_plan_t plan, bsc_worklist_info *info, void *image, size_t bytes);
+
+void bsc_plan_destroy(bsc_plan_t plan);
+
+const char *bsc_status_string(bsc_status s);
+
+/* Thread-local text of the last error raised on this thread ("" if none). */
+const char *bsc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSC_H */

@@ -1,0 +1,223 @@
+"""Host-side tests of the C-ABI library: it loads, exports every symbol the
+header declares, and its planner (no device needed) matches the oracle's
+independent sector join and grouping bit-exactly and rejects malformed input
+with the documented status codes."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.contract import AXIS_AUTO, AXIS_CONTRACT, AXIS_FREE_M, AXIS_FREE_N
+from workloads import configs as C
+
+bst = pytest.importorskip("block_sparse_tensor_amd")
+from block_sparse_tensor_amd import _capi  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_skip():
+    if not os.path.exists(_capi.LIB_PATH):
+        pytest.skip("libbsc.so not built")
+    return _capi.lib()
+
+
+def test_exports_every_declared_symbol():
+    L = _lib_or_skip()
+    hdr = open(os.path.join(ROOT, "include", "bsc.h")).read()
+    declared = set(re.findall(r"\b(bsc_[a-z_]+)\s*\(", hdr))
+    assert declared == set(_capi.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = _lib_or_skip()
+    for code, name in _capi.STATUS.items():
+        assert L.bsc_status_string(code).decode() == name
+
+
+AXES = {"free_m": AXIS_FREE_M, "free_n": AXIS_FREE_N, "contract": AXIS_CONTRACT, "auto": AXIS_AUTO}
+
+
+def _check_against_oracle(con, axis):
+    p = bst.Plan(con, axis=axis)
+    t, g, md = p.export()
+    s = p.stats()
+    assert np.array_equal(t, oracle.triples(con).astype(np.int32))
+    oax, ogid, ogl = oracle.groups(con, AXES[axis])
+    assert s["axis"] == oax
+    assert np.array_equal(g, ogid.astype(np.int32))
+    assert s["groups"] == len(ogl)
+    assert s["useful_flops"] == oracle.useful_flops(con)
+    assert s["alg_bytes"] == oracle.algorithmic_bytes(con)
+    return p, s
+
+
+@pytest.mark.parametrize("axis", list(AXES))
+def test_planner_matches_oracle_configs(axis):
+    _lib_or_skip()
+    for con in [C.cfg1("diag").con, C.cfg1("flux1").con, C.cfg1("flux1_3leg").con, C.cfg2().con,
+                C.cfg5(values=False).con] + [s.con for s in C.cfg3().stages]:
+        _check_against_oracle(con, axis)
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("axis", list(AXES))
+def test_planner_matches_oracle_random(seed, axis):
+    _lib_or_skip()
+    prob = C.random_problem(2000 + seed, nq=1 + seed % 2, nkeys=(7, 6, 7), maxdim=6, qrange=1,
+                            flux=[(0, 0), (1, -1), (1, 0)][seed % 3], density=0.8)
+    _check_against_oracle(prob.con, axis)
+
+
+def test_per_sector_stats():
+    _lib_or_skip()
+    con = C.cfg2().con
+    p = bst.Plan(con, launch_mode="per_sector")
+    s = p.stats()
+    assert s["launches_per_contract"] == 4000 and s["launches_per_sector"] == 4000
+    g = bst.Plan(con, axis="free_m").stats()
+    assert g["launches_per_contract"] == 1
+    assert s["launches_per_sector"] / g["launches_per_contract"] >= 50
+
+
+def test_cfg5_one_launch():
+    _lib_or_skip()
+    s = bst.Plan(C.cfg5(values=False).con).stats()
+    assert s["launches_per_contract"] == 1 and s["launches_per_sector"] == 64
+
+
+def test_zero_blocks_counted():
+    _lib_or_skip()
+    ch = C.cfg4()
+    for st in ch.stages:
+        s = bst.Plan(st.con).stats()
+        t = oracle.triples(st.con)
+        nonempty = len({(int(m), int(n)) for m, k, n in t})
+        assert s["zero_blocks"] == st.con.C.nblocks - nonempty
+        assert s["zero_groups"] == s["zero_blocks"]
+
+
+# ---------------------------------------------------------------------------
+# error codes (every plan-time failure is forced from the host)
+# ---------------------------------------------------------------------------
+
+def _err(con, **kw):
+    with pytest.raises(bst.BscError) as e:
+        bst.Plan(con, **kw)
+    return e.value.name
+
+
+def test_error_charge():
+    _lib_or_skip()
+    p = C.cfg1("diag")
+    p.con.A.col_key[0] = 1
+    assert _err(p.con) == "BSC_ERR_CHARGE"
+
+
+def test_error_flux():
+    _lib_or_skip()
+    p = C.cfg1("diag")
+    p.con.C.flux[:] = 1
+    p.con.C.row_key[:] = p.con.C.row_key  # same blocks now break the rule or the flux sum
+    assert _err(p.con) in ("BSC_ERR_CHARGE",)
+
+
+def test_error_overlap():
+    _lib_or_skip()
+    p = C.cfg1("diag")
+    p.con.C.offset[1] = p.con.C.offset[0]
+    assert _err(p.con) == "BSC_ERR_OVERLAP"
+
+
+def test_error_overlap_interleaved():
+    """Interleaved C views that collide only element-wise are caught."""
+    _lib_or_skip()
+    p = C.cfg1("diag")
+    # block 0 is 8x4 row-major at offset 0: make block 1 (5x2) interleave into its columns
+    p.con.C.offset[1] = 1
+    p.con.C.row_stride[1] = (4, 0)
+    assert _err(p.con) == "BSC_ERR_OVERLAP"
+
+
+def test_interleaved_disjoint_accepted():
+    """Two column-interleaved C views that never collide are legal."""
+    _lib_or_skip()
+    from workloads.model import Contraction, Index, Operand
+    idx = Index([[0], [0]], [3, 3])
+    one = Index([[0]], [2])
+    A = Operand([0, 1], [0, 0], [0, 6], [(2, 0), (2, 0)], [(1, 0), (1, 0)], [0], 12)
+    B = Operand([0], [0], [0], [(2, 0)], [(1, 0)], [0], 4)
+    # C blocks (0,0) and (1,0) are 3x2 each, interleaved: columns of block 0 at even, block 1 at odd addresses
+    Cop = Operand([0, 1], [0, 0], [0, 1], [(4, 0), (4, 0)], [(2, 0), (2, 0)], [0], 12)
+    con = Contraction(idx, one, one, A, B, Cop, "f64")
+    bst.Plan(con, axis="contract")
+
+
+def test_error_missing_output():
+    _lib_or_skip()
+    p = C.cfg1("diag")
+    keep = np.arange(p.con.C.nblocks) != 2
+    for f in ("row_key", "col_key", "offset", "row_stride", "col_stride"):
+        setattr(p.con.C, f, getattr(p.con.C, f)[keep])
+    assert _err(p.con) == "BSC_ERR_MISSING_OUTPUT"
+
+
+def test_error_bounds():
+    _lib_or_skip()
+    p = C.cfg1("diag")
+    p.con.B.buffer_elems = int(p.con.B.offset[-1])
+    assert _err(p.con) == "BSC_ERR_BOUNDS"
+    p = C.cfg1("diag")
+    p.con.A.offset[0] = -1
+    assert _err(p.con) == "BSC_ERR_BOUNDS"
+
+
+def test_error_shape():
+    _lib_or_skip()
+    p = C.cfg1("diag")
+    p.con.A.row_key[1] = p.con.A.row_key[0]
+    p.con.A.col_key[1] = p.con.A.col_key[0]
+    assert _err(p.con) == "BSC_ERR_SHAPE"          # duplicate block
+    p = C.cfg1("diag")
+    p.con.A.row_stride[0] = (0, 0)
+    assert _err(p.con) == "BSC_ERR_SHAPE"          # zero stride on a leg of extent 8
+    p = C.cfg1("diag")
+    p.con.A.row_key[0] = 17
+    assert _err(p.con) == "BSC_ERR_SHAPE"          # key out of range
+    p = C.cfg1("diag")
+    p.con.m.dim[0] = 0
+    assert _err(p.con) == "BSC_ERR_SHAPE"
+
+
+def test_error_axis_none_grouped():
+    _lib_or_skip()
+    assert _err(C.cfg1().con, axis="none") == "BSC_ERR_ARG"
+
+
+def test_contract_before_bind():
+    L = _lib_or_skip()
+    import ctypes
+    p = bst.Plan(C.cfg1().con)
+    st = L.bsc_contract(p._h, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), None)
+    assert _capi.STATUS[st] == "BSC_ERR_NOT_BOUND"
+
+
+def test_bind_too_small():
+    L = _lib_or_skip()
+    import ctypes
+    p = bst.Plan(C.cfg1().con)
+    st = L.bsc_plan_bind(p._h, ctypes.c_void_p(4096), ctypes.c_size_t(1), None)
+    assert _capi.STATUS[st] == "BSC_ERR_DEVICE_BYTES"
+
+
+def test_empty_problem():
+    _lib_or_skip()
+    from workloads.model import Contraction, Index, Operand
+    idx = Index(np.zeros((0, 1)), [])
+    op = Operand([], [], [], np.zeros((0, 2)), np.zeros((0, 2)), [0], 0)
+    s = bst.Plan(Contraction(idx, idx, idx, op, op, op, "f32")).stats()
+    assert s["triples"] == 0 and s["items"] == 0 and s["launches_per_contract"] == 0

@@ -35,8 +35,10 @@ class Index:
     labels: Optional[list] = None      # human-readable key names (not used by the engine)
 
     def __post_init__(self):
-        self.charge = np.ascontiguousarray(np.asarray(self.charge, dtype=np.int32).reshape(len(self.dim), -1))
         self.dim = np.ascontiguousarray(np.asarray(self.dim, dtype=np.int64))
+        ch = np.asarray(self.charge, dtype=np.int32)
+        nq = ch.shape[-1] if ch.ndim == 2 else (ch.size // max(1, len(self.dim)) or 1)
+        self.charge = np.ascontiguousarray(ch.reshape(len(self.dim), nq))
         if self.inner is not None:
             self.inner = np.ascontiguousarray(np.asarray(self.inner, dtype=np.int64))
 

@@ -46,10 +46,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_workload(name):
+def load_workload(name, ld_align=1):
     from workloads import configs as C
     if name == "cfg5":
-        p = C.cfg5()
+        p = C.cfg5(ld_align=ld_align, align=max(1, ld_align))
         stages = [(p.con, "a", "b", "c", "auto")]
         return stages, {"a": p.a, "b": p.b}, {"c": p.con.C.buffer_elems}, "bf16"
     if name == "cfg1":
@@ -72,6 +72,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="cfg5", choices=sorted(WORKLOADS))
     ap.add_argument("--baseline-steps", type=int, default=10)
+    ap.add_argument("--no-baseline", action="store_true", help="skip the per-sector GPU baseline")
+    ap.add_argument("--ld-align", type=int, default=1,
+                    help="cfg5: pad each block's leading dimension to a multiple of this many elements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -88,7 +91,7 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
-    stages, inputs, sizes, dtype = load_workload(args.workload)
+    stages, inputs, sizes, dtype = load_workload(args.workload, args.ld_align)
 
     # inputs resident in HBM before timing
     def dev(x):
@@ -149,8 +152,9 @@ def main():
     peak = MFMA_PEAK[dtype]
 
     # --- uncoalesced GPU baseline: one launch per sector GEMM -----------------------
-    per_sector = plans_for("per_sector")
-    ms_ps = timed(per_sector, args.baseline_steps, 2)
+    if not args.no_baseline:
+        per_sector = plans_for("per_sector")
+        ms_ps = timed(per_sector, args.baseline_steps, 2)
 
     value = flops / (ms * 1e-3) / 1e9
     out = {
@@ -167,6 +171,7 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "stages": len(stages),
+                   "ld_align": args.ld_align,
                    "sector_gemms": sum(s["triples"] for s in st), "useful_flops": flops,
                    "alg_bytes": alg_bytes, "parallelism": "single GPU"},
         "pct_mfma_peak": round(100.0 * value / (peak * 1e3), 3),
@@ -187,7 +192,7 @@ def main():
             "hbm_gbps_on_alg_bytes": round(dom_bytes / (stage_ms[dom] * 1e-3) / 1e9, 2),
             "kernel_source": kernel_source_hash(),
         },
-        "gpu_per_sector_baseline": {
+        "gpu_per_sector_baseline": None if args.no_baseline else {
             "value": round(flops / (ms_ps * 1e-3) / 1e9, 3), "unit": "GFLOP/s", "ms_per_step": round(ms_ps, 6),
             "launches_per_contraction": launches_ps, "steps": args.baseline_steps,
         },

@@ -83,6 +83,10 @@ struct DTask {
 static_assert(sizeof(DTask) == 16, "DTask layout");
 
 constexpr int TILE_GENERIC = 64;   // generic tile edge
+constexpr int TILE_MFMA = 128;     // matrix-core tile edge
+
+inline int32_t tile_m(int32_t cls) { return cls == T_MFMA ? TILE_MFMA : TILE_GENERIC; }
+inline int32_t tile_n(int32_t cls) { return cls == T_MFMA ? TILE_MFMA : TILE_GENERIC; }
 
 struct Blk {
     int32_t r, c;

@@ -9,76 +9,20 @@
 // and columns strided by 16 so LDS reads are conflict-free.
 #pragma once
 
-#include <hip/hip_runtime.h>
-
-#include <cstdint>
-
-#include "bsc_internal.h"
+#include "kernels_common.h"
 
 namespace bsc {
 
-struct KArgs {
-    const DTask *tasks;
-    int32_t task0, ntasks;
-    const DGroup *groups;
-    const DRun *runs;
-    const DView *ap, *bp, *cp;
-    const void *A, *B;
-    void *C;
-};
-
-// Address function along the non-piece axis of one row/column of a piece.
-struct Rec {
-    int64_t base;
-    int64_t s0, s1;
-    int32_t in, pad;
-};
-
 template <typename ACC>
-struct Smem {
+struct GenericSmem {
     ACC a[16][65];   // [k][row]
     ACC b[16][65];   // [k][col]
     Rec ra[64];
     Rec rb[64];
 };
 
-__device__ __forceinline__ float load_acc(const uint16_t *p, int64_t i) {
-    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
-}
-__device__ __forceinline__ float load_acc(const float *p, int64_t i) { return p[i]; }
-__device__ __forceinline__ double load_acc(const double *p, int64_t i) { return p[i]; }
-
-// last piece whose range starts at or before x (pieces are sorted by begin)
-__device__ __forceinline__ int32_t find_piece(const DView *pc, int32_t n, int32_t x) {
-    int32_t lo = 0, hi = n - 1;
-    while (lo < hi) {
-        int32_t mid = (lo + hi + 1) >> 1;
-        if (pc[mid].begin <= x) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
-__device__ __forceinline__ Rec make_rec(const DView *pc, int32_t n, int32_t x) {
-    const int32_t p = n == 1 ? 0 : find_piece(pc, n, x);
-    const DView v = pc[p];
-    const int32_t xl = x - v.begin;
-    Rec r;
-    r.base = v.off + static_cast<int64_t>(xl / v.ia) * v.sa0 + static_cast<int64_t>(xl % v.ia) * v.sa1;
-    r.s0 = v.sb0;
-    r.s1 = v.sb1;
-    r.in = v.ib;
-    r.pad = 0;
-    return r;
-}
-
-__device__ __forceinline__ int64_t along(const Rec &r, int32_t y) {
-    if (r.in == 1) return r.base + static_cast<int64_t>(y) * r.s0;
-    return r.base + static_cast<int64_t>(y / r.in) * r.s0 + static_cast<int64_t>(y % r.in) * r.s1;
-}
-
 template <typename TA, typename TC, typename ACC>
-__device__ void generic_tile(const KArgs &ka, const DTask &task, Smem<ACC> &sm) {
+__device__ void generic_tile(const KArgs &ka, const DTask &task, GenericSmem<ACC> &sm) {
     const DGroup g = ka.groups[task.group];
     const int32_t tid = threadIdx.x;
     const int32_t m0 = task.m0, n0 = task.n0;

@@ -588,15 +588,26 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         // ---- tasks ------------------------------------------------------------------
         p.tasks.clear();
         p.launches.clear();
-        const int T = TILE_GENERIC;
+        // tile class per group: matrix-core tiles where the group is more than a
+        // single instruction's worth of work, vector-ALU tiles for the tiny tail
+        auto class_of = [&](const DGroup &g) -> int32_t {
+            if (g.nrun == 0) return T_ZERO;
+            if (p.dtype == BSC_BF16_F32 && (int64_t)g.M * g.N * g.K >= 32 * 32 * 16 && g.M >= 8 && g.N >= 8)
+                return T_MFMA;
+            return T_GENERIC;
+        };
+        // relative throughput of a tile class (used only to order work longest-first)
+        auto rate_of = [&](int32_t cls) { return cls == T_MFMA ? 16.0 : 1.0; };
         auto tiles_of = [&](int32_t gi, std::vector<DTask> &out, std::vector<double> *cost) {
             const DGroup &g = p.groups[(size_t)gi];
-            for (int32_t m0 = 0; m0 < g.M; m0 += T)
-                for (int32_t n0 = 0; n0 < g.N; n0 += T) {
-                    out.push_back({g.nrun ? T_GENERIC : T_ZERO, gi, m0, n0});
+            const int32_t cls = class_of(g);
+            const int32_t TM = tile_m(cls), TN = tile_n(cls);
+            for (int32_t m0 = 0; m0 < g.M; m0 += TM)
+                for (int32_t n0 = 0; n0 < g.N; n0 += TN) {
+                    out.push_back({cls, gi, m0, n0});
                     if (cost) {
-                        double ml = std::min(T, g.M - m0), nl = std::min(T, g.N - n0);
-                        cost->push_back(2.0 * ml * nl * g.K + 4.0 * ml * nl + 2.0e4 * g.nrun);
+                        double ml = std::min(TM, g.M - m0), nl = std::min(TN, g.N - n0);
+                        cost->push_back((2.0 * ml * nl * g.K) / rate_of(cls) + 4.0 * ml * nl + 2.0e4 * g.nrun);
                     }
                 }
         };

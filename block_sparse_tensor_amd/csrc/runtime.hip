@@ -14,6 +14,7 @@
 
 #include "bsc_internal.h"
 #include "kernels_generic.h"
+#include "kernels_mfma_bf16.h"
 
 namespace bsc {
 
@@ -22,12 +23,31 @@ static bsc_status hip_fail(hipError_t e, const char *what) {
     return BSC_ERR_HIP;
 }
 
+template <typename ACC, bool BF16>
+union TileSmem;
+template <typename ACC>
+union TileSmem<ACC, false> {
+    GenericSmem<ACC> g;
+};
+template <typename ACC>
+union TileSmem<ACC, true> {
+    GenericSmem<ACC> g;
+    MfmaSmemBf16 m;
+};
+
 template <typename TA, typename TC, typename ACC>
 __global__ __launch_bounds__(256) void grouped_contract(KArgs ka) {
-    __shared__ Smem<ACC> sm;
+    constexpr bool kBf16 = sizeof(TA) == 2;
+    __shared__ TileSmem<ACC, kBf16> sm;
     for (int32_t t = blockIdx.x; t < ka.ntasks; t += gridDim.x) {
         const DTask task = ka.tasks[ka.task0 + t];
-        generic_tile<TA, TC, ACC>(ka, task, sm);
+        if constexpr (kBf16) {
+            if (task.cls == T_MFMA) {
+                mfma_tile_bf16<TC>(ka, task, sm.m);
+                continue;
+            }
+        }
+        generic_tile<TA, TC, ACC>(ka, task, sm.g);
     }
 }
 
@@ -100,6 +120,8 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
     ka.A = A;
     ka.B = B;
     ka.C = C;
+    ka.vec_a = (reinterpret_cast<uintptr_t>(A) % 16) == 0;
+    ka.vec_b = (reinterpret_cast<uintptr_t>(B) % 16) == 0;
     for (auto &l : p->launches) {
         ka.task0 = l[0];
         ka.ntasks = l[1] - l[0];

@@ -1,0 +1,67 @@
+"""Single-sector GEMMs through the engine: tile-edge shapes (below, at and past
+the 32/64/128 tile edges, ragged K), every operand orientation, padded and
+unpadded leading dimensions.  Integer-valued inputs make every summation order
+exact, so results must equal the plain product bit-for-bit (one sector is a
+plain GEMM)."""
+import numpy as np
+import pytest
+
+from workloads.layout import write_block
+from workloads.model import Contraction, Index, Operand
+
+from gpuhelp import have_gpu, to_dev, torch
+
+pytestmark = pytest.mark.gpu
+
+if have_gpu():
+    import block_sparse_tensor_amd as bst
+
+SHAPES = [(1, 1, 1), (7, 3, 5), (32, 16, 32), (64, 32, 64), (65, 17, 63), (128, 32, 128), (128, 33, 128),
+          (129, 64, 127), (200, 40, 150), (256, 96, 256), (64, 1024, 64), (300, 7, 300), (17, 300, 9)]
+
+
+def _single(M, K, N, dtype, a_row, b_row, pad, seed):
+    rng = np.random.default_rng(seed)
+    fdt = np.float64 if dtype == "f64" else np.float32
+    A = rng.integers(-2, 3, (M, K)).astype(fdt)
+    B = rng.integers(-2, 3, (K, N)).astype(fdt)
+    if a_row:
+        lda = K + pad
+        ars, acs, na = (lda, 0), (1, 0), M * lda
+    else:
+        lda = M + pad
+        ars, acs, na = (1, 0), (lda, 0), K * lda
+    if b_row:
+        ldb = N + pad
+        brs, bcs, nb = (ldb, 0), (1, 0), K * ldb
+    else:
+        ldb = K + pad
+        brs, bcs, nb = (1, 0), (ldb, 0), N * ldb
+    abuf, bbuf = np.zeros(na + 3, fdt), np.zeros(nb + 3, fdt)
+    write_block(abuf, 3, ars, acs, A)
+    write_block(bbuf, 3, brs, bcs, B)
+    idx = lambda d: Index([[0]], [d])
+    con = Contraction(idx(M), idx(K), idx(N), Operand([0], [0], [3], [ars], [acs], [0], na + 3),
+                      Operand([0], [0], [3], [brs], [bcs], [0], nb + 3),
+                      Operand([0], [0], [0], [(N, 0)], [(1, 0)], [0], M * N), dtype)
+    return con, abuf, bbuf, A @ B
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f64"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_single_sector_exact(dtype, shape):
+    t = torch()
+    M, K, N = shape
+    for a_row in (True, False):
+        for b_row in (True, False):
+            for pad in (0, 8):
+                con, abuf, bbuf, ref = _single(M, K, N, dtype, a_row, b_row, pad, M * 1000 + K * 10 + N)
+                print(f"[tile] {dtype} {M}x{K}x{N} a_row={a_row} b_row={b_row} pad={pad}", flush=True)
+                plan = bst.Plan(con).bind()
+                cdt = t.float64 if dtype == "f64" else t.float32
+                C = t.full((M * N,), float("nan"), dtype=cdt, device="cuda")
+                plan.contract(to_dev(abuf, dtype), to_dev(bbuf, dtype), C)
+                t.cuda.synchronize()
+                got = C.cpu().numpy().reshape(M, N)
+                assert np.array_equal(got, ref.astype(got.dtype)), (
+                    f"{int(np.sum(got != ref))} of {M * N} elements differ")

@@ -18,7 +18,7 @@ DRUN = np.dtype([(n, "<i4") for n in ("K", "nap", "ap0", "nbp", "bp0", "flags", 
 DTASK = np.dtype([(n, "<i4") for n in ("cls", "group", "m0", "n0")])
 G_C_ALONG_N, G_ACCUMULATE = 1, 2
 T_GENERIC, T_MFMA, T_TAIL, T_ZERO = 0, 1, 2, 3
-TILE = {T_GENERIC: (64, 64), T_ZERO: (64, 64)}
+TILE = {T_GENERIC: (64, 64), T_ZERO: (64, 64), T_MFMA: (128, 128)}
 
 assert DVIEW.itemsize == 56 and DGROUP.itemsize == 32 and DRUN.itemsize == 32 and DTASK.itemsize == 16
 

@@ -40,7 +40,7 @@ class BscStats(ctypes.Structure):
     _fields_ = [("triples", c_int64), ("c_blocks", c_int64), ("zero_blocks", c_int64), ("groups", c_int64),
                 ("zero_groups", c_int64), ("axis", c_int32), ("dtype", c_int32),
                 ("mode_count", (c_int64 * 3) * 3), ("runs", c_int64), ("items", c_int64),
-                ("items_by_class", c_int64 * 4), ("launches_per_contract", c_int64),
+                ("items_by_class", c_int64 * 5), ("launches_per_contract", c_int64),
                 ("launches_per_sector", c_int64), ("useful_flops", c_int64), ("alg_bytes", c_int64),
                 ("pack_bytes", c_int64), ("device_bytes", c_int64), ("tail_triples", c_int64),
                 ("launches_issued", c_int64), ("grid", c_int32), ("reserved", c_int32),
@@ -49,8 +49,8 @@ class BscStats(ctypes.Structure):
 
 class BscWorklistInfo(ctypes.Structure):
     _fields_ = [(n, c_int64) for n in ("n_groups", "n_runs", "n_apieces", "n_bpieces", "n_cpieces", "n_tasks",
-                                        "off_groups", "off_runs", "off_apieces", "off_bpieces", "off_cpieces",
-                                        "off_tasks", "bytes", "n_launches")]
+                                        "n_dense", "off_groups", "off_runs", "off_apieces", "off_bpieces",
+                                        "off_cpieces", "off_tasks", "off_dense", "bytes", "n_launches")]
 
 
 _lib = None

@@ -131,12 +131,14 @@ bsc_status bsc_plan_worklist(bsc_plan_t plan, bsc_worklist_info *info, void *ima
     info->n_bpieces = (int64_t)p->bpieces.size();
     info->n_cpieces = (int64_t)p->cpieces.size();
     info->n_tasks = (int64_t)p->tasks.size();
+    info->n_dense = (int64_t)p->fast.size();
     info->off_groups = (int64_t)p->off_groups;
     info->off_runs = (int64_t)p->off_runs;
     info->off_apieces = (int64_t)p->off_ap;
     info->off_bpieces = (int64_t)p->off_bp;
     info->off_cpieces = (int64_t)p->off_cp;
     info->off_tasks = (int64_t)p->off_tasks;
+    info->off_dense = (int64_t)p->off_fast;
     info->bytes = (int64_t)p->image.size();
     info->n_launches = (int64_t)p->launches.size();
     if (image) {

@@ -20,7 +20,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/bsc.h"
+#include "bsc.h"
 
 namespace bsc {
 
@@ -56,6 +56,9 @@ enum : int32_t {
     R_A_FUNIT = 2,       // every A piece: single-leg free axis with stride 1
     R_B_KUNIT = 4,
     R_B_FUNIT = 8,
+    R_A_VEC = 16,        // A: K-unit, every row start 16-byte aligned (16-byte loads along K)
+    R_B_VECK = 32,       // B: K-unit, every column start 16-byte aligned
+    R_B_VECN = 64,       // B: one N-unit piece, K rows 16-byte aligned, rows readable to a multiple of 8
 };
 
 struct DRun {
@@ -73,7 +76,33 @@ enum : int32_t {
     T_MFMA = 1,          // workgroup tile on the matrix cores
     T_TAIL = 2,          // up to four whole small groups, one per wave
     T_ZERO = 3,          // zero fill of a C tile
+    T_MFMA_FAST_N = 4,   // dense matrix-core tile, direct-to-LDS loads, N-contiguous B (group = DFast index)
+    T_MFMA_FAST_K = 5,   // dense matrix-core tile, direct-to-LDS loads, K-contiguous B (group = DFast index)
+    T_NOP = 6,           // placeholder keeping the task -> XCD mapping (no work)
+    T_NCLASS = 7,
 };
+
+// Workgroups of a launch are dispatched round-robin over the chiplets (XCDs),
+// each with its own L2: task t of a grouped launch runs on XCD t % BSC_XCDS
+// when the grid is a multiple of BSC_XCDS.
+constexpr int BSC_XCDS = 8;
+
+// kernel feature sets: which tile bodies a grouped launch contains
+enum : int32_t { FEAT_MFMA = 1, FEAT_FAST_N = 2, FEAT_FAST_K = 4 };
+
+// Per-tile record of a dense matrix-core tile: every operand is a single
+// strided view, so the tile's addressing reduces to bases and strides the
+// planner computes once.  Element addresses (tile-local i, j; run-local k):
+//   A(i, k) = a_base + i * a_rs + k
+//   B(k, j) = b_base + k * b_s + j   (N-contiguous B)   or   b_base + j * b_s + k   (K-contiguous B)
+//   C(i, j) = c_base + i * c_rs + j * c_cs
+struct DFast {
+    int64_t a_base, a_rs;
+    int64_t b_base, b_s;
+    int64_t c_base, c_rs, c_cs;
+    int32_t mlen, nlen, K, flags;   // flags: G_ACCUMULATE
+};
+static_assert(sizeof(DFast) == 72, "DFast layout");
 
 struct DTask {
     int32_t cls;
@@ -85,8 +114,9 @@ static_assert(sizeof(DTask) == 16, "DTask layout");
 constexpr int TILE_GENERIC = 64;   // generic tile edge
 constexpr int TILE_MFMA = 128;     // matrix-core tile edge
 
-inline int32_t tile_m(int32_t cls) { return cls == T_MFMA ? TILE_MFMA : TILE_GENERIC; }
-inline int32_t tile_n(int32_t cls) { return cls == T_MFMA ? TILE_MFMA : TILE_GENERIC; }
+constexpr bool is_mfma(int32_t cls) { return cls == T_MFMA || cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K; }
+constexpr int32_t tile_m(int32_t cls) { return is_mfma(cls) ? TILE_MFMA : TILE_GENERIC; }
+constexpr int32_t tile_n(int32_t cls) { return is_mfma(cls) ? TILE_MFMA : TILE_GENERIC; }
 
 struct Blk {
     int32_t r, c;
@@ -113,15 +143,17 @@ struct Plan {
     std::vector<DRun> runs;
     std::vector<DView> apieces, bpieces, cpieces;
     std::vector<DTask> tasks;
+    std::vector<DFast> fast;      // records of dense matrix-core tiles
     std::vector<std::array<int32_t, 2>> launches;  // per-sector mode: task ranges, one launch each
 
     // device binding
     void *dev = nullptr;
     size_t dev_bytes = 0;
-    size_t off_groups = 0, off_runs = 0, off_ap = 0, off_bp = 0, off_cp = 0, off_tasks = 0;
+    size_t off_groups = 0, off_runs = 0, off_ap = 0, off_bp = 0, off_cp = 0, off_tasks = 0, off_fast = 0;
     std::vector<unsigned char> image;   // host copy of the device tables
     int32_t cu_count = 0;
     int32_t grid = 0;
+    int32_t features = 0;             // FEAT_* bits over all tasks
 
     bsc_stats stats{};
 };

@@ -17,6 +17,7 @@ struct KArgs {
     const DGroup *groups;
     const DRun *runs;
     const DView *ap, *bp, *cp;
+    const DFast *fast;
     const void *A, *B;
     void *C;
 };
@@ -51,7 +52,8 @@ __device__ __forceinline__ Rec make_rec(const DView *pc, int32_t n, int32_t x) {
     const DView v = pc[p];
     const int32_t xl = x - v.begin;
     Rec r;
-    r.base = v.off + static_cast<int64_t>(xl / v.ia) * v.sa0 + static_cast<int64_t>(xl % v.ia) * v.sa1;
+    if (v.ia == 1) r.base = v.off + static_cast<int64_t>(xl) * v.sa0;   // single leg: no division
+    else r.base = v.off + static_cast<int64_t>(xl / v.ia) * v.sa0 + static_cast<int64_t>(xl % v.ia) * v.sa1;
     r.s0 = v.sb0;
     r.s1 = v.sb1;
     r.in = v.ib;

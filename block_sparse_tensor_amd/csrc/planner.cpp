@@ -13,6 +13,7 @@
 //   * section "Coalescing is a plan-time transform": all of this happens here,
 //     once, never inside the kernel.
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <numeric>
@@ -260,7 +261,25 @@ std::vector<DView> stack(const std::vector<DView> &mem) {
     return mem;
 }
 
-int32_t run_flags(const std::vector<DView> &ap, const std::vector<DView> &bp) {
+// 16-byte vector eligibility of a run's operand pieces (bf16: 8 elements).
+bool vec_kcontig(const std::vector<DView> &v, int64_t K) {
+    for (auto &p : v) {
+        if (p.ib != 1 || !(p.sb0 == 1 || K == 1) || p.ia != 1) return false;
+        if (p.off % 8 != 0 || (p.len > 1 && p.sa0 % 8 != 0)) return false;
+    }
+    return true;
+}
+
+bool vec_ncontig(const std::vector<DView> &v, int64_t K, int64_t buffer_elems) {
+    if (v.size() != 1) return false;
+    const DView &p = v[0];
+    if (p.ia != 1 || !(p.sa0 == 1 || p.len == 1) || p.ib != 1) return false;
+    if (p.off % 8 != 0 || (K > 1 && p.sb0 % 8 != 0)) return false;
+    const int64_t padded = (p.len + 7) / 8 * 8;   // the edge granule reads up to a multiple of 8 columns
+    return p.off + (K - 1) * p.sb0 + padded <= buffer_elems;
+}
+
+int32_t run_flags(const std::vector<DView> &ap, const std::vector<DView> &bp, int64_t K, int64_t b_elems) {
     auto unit_b = [](const std::vector<DView> &v) {
         for (auto &p : v)
             if (p.ib != 1 || (p.sb0 != 1 && p.sb0 != 0)) return false;
@@ -276,6 +295,9 @@ int32_t run_flags(const std::vector<DView> &ap, const std::vector<DView> &bp) {
     if (unit_a(ap)) f |= R_A_FUNIT;
     if (unit_b(bp)) f |= R_B_KUNIT;
     if (unit_a(bp)) f |= R_B_FUNIT;
+    if (vec_kcontig(ap, K)) f |= R_A_VEC;
+    if (vec_kcontig(bp, K)) f |= R_B_VECK;
+    if (vec_ncontig(bp, K, b_elems)) f |= R_B_VECN;
     return f;
 }
 
@@ -542,7 +564,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                 r.ap0 = (int32_t)p.apieces.size();
                 r.nbp = (int32_t)rb.size();
                 r.bp0 = (int32_t)p.bpieces.size();
-                r.flags = run_flags(ra, rb);
+                r.flags = run_flags(ra, rb, rk, p.b_elems);
                 a_view = a_view && ra.size() == 1;
                 b_view = b_view && rb.size() == 1;
                 p.apieces.insert(p.apieces.end(), ra.begin(), ra.end());
@@ -587,24 +609,57 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
 
         // ---- tasks ------------------------------------------------------------------
         p.tasks.clear();
+        p.fast.clear();
         p.launches.clear();
         // tile class per group: matrix-core tiles where the group is more than a
         // single instruction's worth of work, vector-ALU tiles for the tiny tail
         auto class_of = [&](const DGroup &g) -> int32_t {
             if (g.nrun == 0) return T_ZERO;
-            if (p.dtype == BSC_BF16_F32 && (int64_t)g.M * g.N * g.K >= 32 * 32 * 16 && g.M >= 8 && g.N >= 8)
+            if (p.dtype == BSC_BF16_F32 && (int64_t)g.M * g.N * g.K >= 32 * 32 * 16 && g.M >= 8 && g.N >= 8) {
+                // dense tile: one run, one piece per operand, single-leg views, 16-byte vectors
+                if (g.nrun == 1 && g.ncp == 1) {
+                    const DRun &r = p.runs[(size_t)g.run0];
+                    const DView &c = p.cpieces[(size_t)g.cp0];
+                    const bool single = r.nap == 1 && r.nbp == 1 && c.ia == 1 && c.ib == 1 &&
+                                        p.apieces[(size_t)r.ap0].ia == 1 && p.bpieces[(size_t)r.bp0].ia == 1;
+                    if (single && (r.flags & R_A_VEC) && (r.flags & R_B_VECN)) return T_MFMA_FAST_N;
+                    if (single && (r.flags & R_A_VEC) && (r.flags & R_B_VECK)) return T_MFMA_FAST_K;
+                }
                 return T_MFMA;
+            }
             return T_GENERIC;
         };
         // relative throughput of a tile class (used only to order work longest-first)
-        auto rate_of = [&](int32_t cls) { return cls == T_MFMA ? 16.0 : 1.0; };
+        auto rate_of = [&](int32_t cls) { return (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) ? 48.0 : (cls == T_MFMA ? 16.0 : 1.0); };
         auto tiles_of = [&](int32_t gi, std::vector<DTask> &out, std::vector<double> *cost) {
             const DGroup &g = p.groups[(size_t)gi];
             const int32_t cls = class_of(g);
             const int32_t TM = tile_m(cls), TN = tile_n(cls);
             for (int32_t m0 = 0; m0 < g.M; m0 += TM)
                 for (int32_t n0 = 0; n0 < g.N; n0 += TN) {
-                    out.push_back({cls, gi, m0, n0});
+                    if (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) {
+                        const DRun &r = p.runs[(size_t)g.run0];
+                        const DView &a = p.apieces[(size_t)r.ap0], &b = p.bpieces[(size_t)r.bp0];
+                        const DView &c = p.cpieces[(size_t)g.cp0];
+                        DFast f{};
+                        f.a_base = a.off + (int64_t)(m0 - a.begin) * a.sa0;
+                        f.a_rs = a.sa0;
+                        f.b_base = b.off + (int64_t)(n0 - b.begin) * b.sa0;
+                        f.b_s = cls == T_MFMA_FAST_N ? b.sb0 : b.sa0;
+                        const bool cn = (g.flags & G_C_ALONG_N) != 0;
+                        // C piece axis a is rows (or columns when cut along N)
+                        f.c_rs = cn ? c.sb0 : c.sa0;
+                        f.c_cs = cn ? c.sa0 : c.sb0;
+                        f.c_base = c.off + (int64_t)(m0 - (cn ? 0 : c.begin)) * f.c_rs + (int64_t)(n0 - (cn ? c.begin : 0)) * f.c_cs;
+                        f.mlen = std::min(TM, g.M - m0);
+                        f.nlen = std::min(TN, g.N - n0);
+                        f.K = r.K;
+                        f.flags = g.flags & G_ACCUMULATE;
+                        out.push_back({cls, (int32_t)p.fast.size(), m0, n0});
+                        p.fast.push_back(f);
+                    } else {
+                        out.push_back({cls, gi, m0, n0});
+                    }
                     if (cost) {
                         double ml = std::min(TM, g.M - m0), nl = std::min(TN, g.N - n0);
                         cost->push_back((2.0 * ml * nl * g.K) / rate_of(cls) + 4.0 * ml * nl + 2.0e4 * g.nrun);
@@ -623,14 +678,55 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                 p.launches.push_back({t0, (int32_t)p.tasks.size()});
             }
         } else {
+            // XCD-aware order: each chiplet gets a queue of tiles balanced by cost;
+            // a group's tiles stay together (small groups whole, large ones in
+            // contiguous row-major slices) so its operand panels are fetched into
+            // few L2s.  Each queue runs longest first; queues are interleaved so
+            // task t lands on XCD t % BSC_XCDS, padded with no-op tasks.
             std::vector<DTask> tk;
             std::vector<double> cost;
-            for (int32_t gi = 0; gi < (int32_t)p.groups.size(); ++gi) tiles_of(gi, tk, &cost);
-            // longest first (stable: ties keep canonical order)
-            std::vector<size_t> ord(tk.size());
-            std::iota(ord.begin(), ord.end(), 0);
-            std::stable_sort(ord.begin(), ord.end(), [&](size_t x, size_t y) { return cost[x] > cost[y]; });
-            for (size_t i : ord) p.tasks.push_back(tk[i]);
+            std::vector<std::pair<size_t, size_t>> span;   // per group: [first, last) task
+            for (int32_t gi = 0; gi < (int32_t)p.groups.size(); ++gi) {
+                size_t a = tk.size();
+                tiles_of(gi, tk, &cost);
+                span.push_back({a, tk.size()});
+            }
+            double total = 0;
+            for (double c : cost) total += c;
+            const double target = total / BSC_XCDS;
+            std::vector<double> gcost(span.size(), 0.0);
+            for (size_t g = 0; g < span.size(); ++g)
+                for (size_t i = span[g].first; i < span[g].second; ++i) gcost[g] += cost[i];
+            std::vector<size_t> gord(span.size());
+            std::iota(gord.begin(), gord.end(), 0);
+            std::stable_sort(gord.begin(), gord.end(), [&](size_t x, size_t y) { return gcost[x] > gcost[y]; });
+            std::vector<std::vector<size_t>> q(BSC_XCDS);
+            std::vector<double> load(BSC_XCDS, 0.0);
+            auto least = [&]() { return (size_t)(std::min_element(load.begin(), load.end()) - load.begin()); };
+            for (size_t g : gord) {
+                const size_t a = span[g].first, b = span[g].second;
+                const size_t ntile = b - a;
+                size_t parts = 1;
+                if (gcost[g] > 0.5 * target) parts = std::min<size_t>({(size_t)BSC_XCDS, ntile, (size_t)std::ceil(gcost[g] / (0.5 * target))});
+                for (size_t part = 0; part < parts; ++part) {
+                    const size_t lo = a + ntile * part / parts, hi = a + ntile * (part + 1) / parts;
+                    const size_t x = least();
+                    for (size_t i = lo; i < hi; ++i) {
+                        q[x].push_back(i);
+                        load[x] += cost[i];
+                    }
+                }
+            }
+            size_t depth = 0;
+            for (auto &v : q) {
+                std::stable_sort(v.begin(), v.end(), [&](size_t x, size_t y) { return cost[x] > cost[y]; });
+                depth = std::max(depth, v.size());
+            }
+            for (size_t d = 0; d < depth; ++d)
+                for (int x = 0; x < BSC_XCDS; ++x)
+                    p.tasks.push_back(d < q[(size_t)x].size() ? tk[q[(size_t)x][d]] : DTask{T_NOP, 0, 0, 0});
+            // trailing no-ops of the last row carry no mapping information
+            while (!p.tasks.empty() && p.tasks.back().cls == T_NOP) p.tasks.pop_back();
             if (!p.tasks.empty()) p.launches.push_back({0, (int32_t)p.tasks.size()});
         }
         if (p.tasks.size() > (size_t)LIM) fail(BSC_ERR_UNSUPPORTED, "too many work items");
@@ -644,6 +740,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         p.off_bp = off;     off = align(off + p.bpieces.size() * sizeof(DView));
         p.off_cp = off;     off = align(off + p.cpieces.size() * sizeof(DView));
         p.off_tasks = off;  off = align(off + p.tasks.size() * sizeof(DTask));
+        p.off_fast = off;   off = align(off + p.fast.size() * sizeof(DFast));
         p.dev_bytes = std::max<size_t>(off, 256);
         p.image.assign(p.dev_bytes, 0);
         auto put = [&](size_t o, const void *src, size_t nbytes) { if (nbytes) std::memcpy(p.image.data() + o, src, nbytes); };
@@ -653,6 +750,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         put(p.off_bp, p.bpieces.data(), p.bpieces.size() * sizeof(DView));
         put(p.off_cp, p.cpieces.data(), p.cpieces.size() * sizeof(DView));
         put(p.off_tasks, p.tasks.data(), p.tasks.size() * sizeof(DTask));
+        put(p.off_fast, p.fast.data(), p.fast.size() * sizeof(DFast));
 
         // ---- statistics ---------------------------------------------------------------
         bsc_stats &s = p.stats;
@@ -667,8 +765,16 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         for (auto &gm : p.group_mode)
             for (int o = 0; o < 3; ++o) s.mode_count[o][gm[(size_t)o]]++;
         s.runs = (int64_t)p.runs.size();
-        s.items = (int64_t)p.tasks.size();
-        for (auto &t : p.tasks) s.items_by_class[t.cls]++;
+        s.items = 0;
+        for (auto &t : p.tasks) s.items += t.cls != T_NOP;
+        p.features = 0;
+        for (auto &t : p.tasks) {
+            if (t.cls == T_NOP) continue;
+            s.items_by_class[t.cls == T_MFMA_FAST_K ? T_MFMA_FAST_N : t.cls]++;
+            if (t.cls == T_MFMA) p.features |= FEAT_MFMA;
+            if (t.cls == T_MFMA_FAST_N) p.features |= FEAT_FAST_N;
+            if (t.cls == T_MFMA_FAST_K) p.features |= FEAT_FAST_K;
+        }
         s.launches_per_contract = (int64_t)p.launches.size();
         s.launches_per_sector = s.triples + (zero_c.empty() ? 0 : 1);
         s.useful_flops = flops;

@@ -11,10 +11,12 @@
 #include <algorithm>
 #include <cstdint>
 #include <string>
+#include <type_traits>
 
 #include "bsc_internal.h"
 #include "kernels_generic.h"
 #include "kernels_mfma_bf16.h"
+#include "kernels_mfma_bf16_fast.h"
 
 namespace bsc {
 
@@ -23,26 +25,36 @@ static bsc_status hip_fail(hipError_t e, const char *what) {
     return BSC_ERR_HIP;
 }
 
-template <typename ACC, bool BF16>
-union TileSmem;
-template <typename ACC>
-union TileSmem<ACC, false> {
+// Shared memory of a grouped launch: the union of the tile bodies it contains.
+template <typename ACC, int32_t FEAT>
+union TileSmem {
     GenericSmem<ACC> g;
-};
-template <typename ACC>
-union TileSmem<ACC, true> {
-    GenericSmem<ACC> g;
-    MfmaSmemBf16 m;
+    typename std::conditional<(FEAT & FEAT_MFMA) != 0, MfmaSmemBf16, char>::type m;
+    typename std::conditional<(FEAT & (FEAT_FAST_N | FEAT_FAST_K)) != 0, FastSmemBf16, char>::type f;
 };
 
-template <typename TA, typename TC, typename ACC>
+extern __shared__ __align__(16) unsigned char bsc_dyn_smem[];
+
+template <typename TA, typename TC, typename ACC, int32_t FEAT>
 __global__ __launch_bounds__(256) void grouped_contract(KArgs ka) {
-    constexpr bool kBf16 = sizeof(TA) == 2;
-    __shared__ TileSmem<ACC, kBf16> sm;
+    TileSmem<ACC, FEAT> &sm = *reinterpret_cast<TileSmem<ACC, FEAT> *>(bsc_dyn_smem);
     for (int32_t t = blockIdx.x; t < ka.ntasks; t += gridDim.x) {
         const DTask task = ka.tasks[ka.task0 + t];
-        if constexpr (kBf16) {
-            if (task.cls == T_MFMA) {
+        if (task.cls == T_NOP) continue;
+        if constexpr ((FEAT & FEAT_FAST_N) != 0) {
+            if (task.cls == T_MFMA_FAST_N) {
+                fast_tile_bf16<TC, true>(ka, task, sm.f);
+                continue;
+            }
+        }
+        if constexpr ((FEAT & FEAT_FAST_K) != 0) {
+            if (task.cls == T_MFMA_FAST_K) {
+                fast_tile_bf16<TC, false>(ka, task, sm.f);
+                continue;
+            }
+        }
+        if constexpr ((FEAT & FEAT_MFMA) != 0) {
+            if (is_mfma(task.cls)) {
                 mfma_tile_bf16<TC>(ka, task, sm.m);
                 continue;
             }
@@ -51,8 +63,49 @@ __global__ __launch_bounds__(256) void grouped_contract(KArgs ka) {
     }
 }
 
+using KernelFn = void (*)(KArgs);
+
+struct KernelRef {
+    KernelFn fn;
+    size_t lds;     // dynamic LDS bytes of the variant
+};
+
+// Opt a kernel variant into more than the default dynamic LDS once per process.
+template <typename TA, typename TC, typename ACC, int32_t FEAT>
+static KernelRef kernel_ref() {
+    KernelFn fn = grouped_contract<TA, TC, ACC, FEAT>;
+    const size_t lds = sizeof(TileSmem<ACC, FEAT>);
+    static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)once;
+    return {fn, lds};
+}
+
+template <int32_t FEAT>
+static KernelRef bf16_kernel() { return kernel_ref<uint16_t, float, float, FEAT>(); }
+
+// bf16 launches pick the variant that holds exactly the tile bodies the plan uses;
+// when an operand base is not 16-byte aligned the direct-to-LDS tiles fall back
+// to the general matrix-core tile (task class T_MFMA_FAST_* is accepted there).
+static KernelRef pick_bf16(int32_t feat, bool vec) {
+    if (!vec && (feat & (FEAT_FAST_N | FEAT_FAST_K))) feat = (feat & ~(FEAT_FAST_N | FEAT_FAST_K)) | FEAT_MFMA;
+    switch (feat) {
+        case 0: return bf16_kernel<0>();
+        case 1: return bf16_kernel<1>();
+        case 2: return bf16_kernel<2>();
+        case 3: return bf16_kernel<3>();
+        case 4: return bf16_kernel<4>();
+        case 5: return bf16_kernel<5>();
+        case 6: return bf16_kernel<6>();
+        default: return bf16_kernel<7>();
+    }
+}
+
+// Grid of a launch: one workgroup per task up to a persistent cap; the cap is
+// a multiple of BSC_XCDS so task t keeps running on XCD t % BSC_XCDS.
 static int32_t grid_for(const Plan &p, int32_t ntasks) {
     int32_t cap = p.opt.grid_limit > 0 ? p.opt.grid_limit : std::max(1, p.cu_count) * 8;
+    if (cap >= BSC_XCDS) cap -= cap % BSC_XCDS;
     return std::max(1, std::min(ntasks, cap));
 }
 
@@ -117,6 +170,7 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
     ka.bp = reinterpret_cast<const DView *>(base + p->off_bp);
     ka.cp = reinterpret_cast<const DView *>(base + p->off_cp);
     ka.tasks = reinterpret_cast<const DTask *>(base + p->off_tasks);
+    ka.fast = reinterpret_cast<const DFast *>(base + p->off_fast);
     ka.A = A;
     ka.B = B;
     ka.C = C;
@@ -127,9 +181,21 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
         ka.ntasks = l[1] - l[0];
         dim3 grid((unsigned)grid_for(*p, ka.ntasks)), block(256);
         switch (p->dtype) {
-            case BSC_F64: hipLaunchKernelGGL((grouped_contract<double, double, double>), grid, block, 0, s, ka); break;
-            case BSC_F32: hipLaunchKernelGGL((grouped_contract<float, float, float>), grid, block, 0, s, ka); break;
-            case BSC_BF16_F32: hipLaunchKernelGGL((grouped_contract<uint16_t, float, float>), grid, block, 0, s, ka); break;
+            case BSC_F64: {
+                const KernelRef k = kernel_ref<double, double, double, 0>();
+                hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
+                break;
+            }
+            case BSC_F32: {
+                const KernelRef k = kernel_ref<float, float, float, 0>();
+                hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
+                break;
+            }
+            case BSC_BF16_F32: {
+                const KernelRef k = pick_bf16(p->features, ka.vec_a && ka.vec_b);
+                hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
+                break;
+            }
         }
         p->stats.launches_issued++;
     }

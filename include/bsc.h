@@ -148,7 +148,8 @@ typedef struct {
     int64_t mode_count[3][3];        /* [operand A,B,C][bsc_mode]: groups per arrangement */
     int64_t runs;                    /* contiguous K-runs over all groups */
     int64_t items;                   /* work items per contraction */
-    int64_t items_by_class[4];       /* generic tile, matrix-core tile, wave tail, zero fill */
+    int64_t items_by_class[5];       /* generic tile, matrix-core tile, wave tail, zero fill,
+                                        matrix-core tile with direct-to-LDS loads */
     int64_t launches_per_contract;   /* GPU commands bsc_contract enqueues */
     int64_t launches_per_sector;     /* one launch per sector GEMM (+1 zero fill if needed) */
     int64_t useful_flops;            /* sum over triples of 2 M N K */
@@ -203,8 +204,8 @@ bsc_status bsc_plan_export(bsc_plan_t plan, int32_t *triples, int32_t *group_of_
  * the kernels' addressing).  Counts are records; offsets are bytes into the
  * device region.  The record formats are internal to this library version. */
 typedef struct {
-    int64_t n_groups, n_runs, n_apieces, n_bpieces, n_cpieces, n_tasks;
-    int64_t off_groups, off_runs, off_apieces, off_bpieces, off_cpieces, off_tasks;
+    int64_t n_groups, n_runs, n_apieces, n_bpieces, n_cpieces, n_tasks, n_dense;
+    int64_t off_groups, off_runs, off_apieces, off_bpieces, off_cpieces, off_tasks, off_dense;
     int64_t bytes;           /* size of the work-list image */
     int64_t n_launches;      /* launches per contraction */
 } bsc_worklist_info;

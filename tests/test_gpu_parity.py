@@ -97,6 +97,14 @@ def test_cfg5_full_size():
     assert s["launches_per_contract"] == 1 and s["launches_per_sector"] == 64
 
 
+def test_cfg5_full_size_aligned():
+    """16-byte aligned, padded layout: the direct-to-LDS tile path."""
+    prob = C.cfg5(ld_align=8, align=8)
+    plan, got = _parity(prob, axis="auto")
+    s = plan.stats()
+    assert s["items_by_class"]["mfma_fast"] > 0 and s["launches_per_contract"] == 1
+
+
 def test_cfg5_small_blocks_ragged():
     """A ragged bf16 block-diagonal case spanning several tiles with odd edges."""
     prob = C.random_problem(4200, nq=1, nkeys=(6, 6, 6), maxdim=150, qrange=2, dtype="bf16", two_leg=False,

@@ -20,7 +20,7 @@ SHAPES = [(1, 1, 1), (7, 3, 5), (32, 16, 32), (64, 32, 64), (65, 17, 63), (128, 
           (129, 64, 127), (200, 40, 150), (256, 96, 256), (64, 1024, 64), (300, 7, 300), (17, 300, 9)]
 
 
-def _single(M, K, N, dtype, a_row, b_row, pad, seed):
+def _single(M, K, N, dtype, a_row, b_row, pad, seed, off=3):
     rng = np.random.default_rng(seed)
     fdt = np.float64 if dtype == "f64" else np.float32
     A = rng.integers(-2, 3, (M, K)).astype(fdt)
@@ -37,12 +37,12 @@ def _single(M, K, N, dtype, a_row, b_row, pad, seed):
     else:
         ldb = K + pad
         brs, bcs, nb = (1, 0), (ldb, 0), N * ldb
-    abuf, bbuf = np.zeros(na + 3, fdt), np.zeros(nb + 3, fdt)
-    write_block(abuf, 3, ars, acs, A)
-    write_block(bbuf, 3, brs, bcs, B)
+    abuf, bbuf = np.zeros(na + off + 8, fdt), np.zeros(nb + off + 8, fdt)
+    write_block(abuf, off, ars, acs, A)
+    write_block(bbuf, off, brs, bcs, B)
     idx = lambda d: Index([[0]], [d])
-    con = Contraction(idx(M), idx(K), idx(N), Operand([0], [0], [3], [ars], [acs], [0], na + 3),
-                      Operand([0], [0], [3], [brs], [bcs], [0], nb + 3),
+    con = Contraction(idx(M), idx(K), idx(N), Operand([0], [0], [off], [ars], [acs], [0], na + off + 8),
+                      Operand([0], [0], [off], [brs], [bcs], [0], nb + off + 8),
                       Operand([0], [0], [0], [(N, 0)], [(1, 0)], [0], M * N), dtype)
     return con, abuf, bbuf, A @ B
 
@@ -54,9 +54,9 @@ def test_single_sector_exact(dtype, shape):
     M, K, N = shape
     for a_row in (True, False):
         for b_row in (True, False):
-            for pad in (0, 8):
-                con, abuf, bbuf, ref = _single(M, K, N, dtype, a_row, b_row, pad, M * 1000 + K * 10 + N)
-                print(f"[tile] {dtype} {M}x{K}x{N} a_row={a_row} b_row={b_row} pad={pad}", flush=True)
+            for pad, off in ((0, 3), (8, 3), (0, 0), (8, 8), ((-K) % 8 if a_row else (-M) % 8, 0)):
+                con, abuf, bbuf, ref = _single(M, K, N, dtype, a_row, b_row, pad, M * 1000 + K * 10 + N, off)
+                print(f"[tile] {dtype} {M}x{K}x{N} a_row={a_row} b_row={b_row} pad={pad} off={off}", flush=True)
                 plan = bst.Plan(con).bind()
                 cdt = t.float64 if dtype == "f64" else t.float32
                 C = t.full((M * N,), float("nan"), dtype=cdt, device="cuda")
@@ -65,3 +65,14 @@ def test_single_sector_exact(dtype, shape):
                 got = C.cpu().numpy().reshape(M, N)
                 assert np.array_equal(got, ref.astype(got.dtype)), (
                     f"{int(np.sum(got != ref))} of {M * N} elements differ")
+
+
+def test_fast_path_selected():
+    """Aligned, padded operands take the direct-to-LDS matrix-core tile."""
+    con, _, _, _ = _single(256, 256, 256, "bf16", True, True, 8, 1, 0)
+    s = bst.Plan(con).stats()
+    assert s["items_by_class"]["mfma_fast"] == 4
+    con, _, _, _ = _single(256, 256, 256, "bf16", True, False, 8, 1, 0)
+    assert bst.Plan(con).stats()["items_by_class"]["mfma_fast"] == 4
+    con, _, _, _ = _single(256, 256, 256, "bf16", True, True, 0, 1, 3)
+    assert bst.Plan(con).stats()["items_by_class"]["mfma"] == 4

@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark: useful GFLOP/s per block-sparse contraction on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload blockdiag_bf16]
 
 A step is one whole contraction (every stage of the workload) over inputs
 already resident in HBM.  Useful flops = sum over sector GEMMs of 2*M*N*K (the
@@ -28,12 +28,12 @@ MFMA_PEAK = {"bf16": 2516.6, "f32": 157.3, "f64": 78.6}
 HBM_PEAK = 8000.0
 
 WORKLOADS = {
-    "cfg5": "block-diagonal bf16 GEMM, 64 U(1) sectors (45 lognormal dims rescaled to a 16384 dense equivalent + "
+    "blockdiag_bf16": "block-diagonal bf16 GEMM, 64 U(1) sectors (45 lognormal dims rescaled to a 16384 dense equivalent + "
             "19 tail dims 1-4), fp32 accumulate",
-    "cfg2": "4000 ragged fp32 sector GEMMs, geometric(0.35) dims capped at 64, stacked 8 per group",
-    "cfg3": "U(1) R/A/B/C environment update, fp64, bond 1024 on 41 sectors, d=4, w=5 (3 chained stages)",
-    "cfg4": "U(1)xU(1) R/A/B/C environment update, fp32, bond 4096 on 177 sectors, d=4, w=6, natural layout",
-    "cfg1": "tiny U(1) block GEMM, fp64, 5 sectors per index",
+    "ragged_batch": "4000 ragged fp32 sector GEMMs, geometric(0.35) dims capped at 64, stacked 8 per group",
+    "rabc_u1": "U(1) R/A/B/C environment update, fp64, bond 1024 on 41 sectors, d=4, w=5 (3 chained stages)",
+    "rabc_u1u1": "U(1)xU(1) R/A/B/C environment update, fp32, bond 4096 on 177 sectors, d=4, w=6, natural layout",
+    "tiny_u1": "tiny U(1) block GEMM, fp64, 5 sectors per index",
 }
 
 
@@ -46,20 +46,42 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_contract_traffic.md")
+
+
+def measured_traffic(workload, ld_align, stage):
+    """HBM bytes per launch of the grouped kernel from committed counter runs
+    (lines starting with TRAFFIC in profiles/grouped_contract_traffic.md), used
+    only while the kernel sources still hash to the value they were taken with."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    src = kernel_source_hash()
+    for ln in lines:
+        if not ln.startswith("TRAFFIC "):
+            continue
+        rec = json.loads(ln[len("TRAFFIC "):])
+        if rec.get("workload") == workload and rec.get("ld_align") == ld_align and rec.get("stage", 0) == stage \
+                and rec.get("kernel_source") == src:
+            return rec["hbm_bytes"]
+    return None
+
+
 def load_workload(name, ld_align=1):
     from workloads import configs as C
-    if name == "cfg5":
-        p = C.cfg5(ld_align=ld_align, align=max(1, ld_align))
+    if name == "blockdiag_bf16":
+        p = C.blockdiag_bf16(ld_align=ld_align, align=max(1, ld_align))
         stages = [(p.con, "a", "b", "c", "auto")]
         return stages, {"a": p.a, "b": p.b}, {"c": p.con.C.buffer_elems}, "bf16"
-    if name == "cfg1":
-        p = C.cfg1()
+    if name == "tiny_u1":
+        p = C.tiny_u1()
         return [(p.con, "a", "b", "c", "auto")], {"a": p.a, "b": p.b}, {"c": p.con.C.buffer_elems}, "f64"
-    if name == "cfg2":
-        p = C.cfg2()
+    if name == "ragged_batch":
+        p = C.ragged_batch()
         return [(p.con, "a", "b", "c", "auto")], {"a": p.a, "b": p.b}, {"c": p.con.C.buffer_elems}, "f32"
-    if name in ("cfg3", "cfg4"):
-        ch = C.cfg3() if name == "cfg3" else C.cfg4()
+    if name in ("rabc_u1", "rabc_u1u1"):
+        ch = C.rabc_u1() if name == "rabc_u1" else C.rabc_u1u1()
         stages = [(st.con, st.a_buf, st.b_buf, st.c_buf, "auto") for st in ch.stages]
         return stages, dict(ch.buffers), dict(ch.sizes), ch.dtype
     raise SystemExit(f"unknown workload {name}")
@@ -70,13 +92,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="cfg5", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="blockdiag_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--baseline-steps", type=int, default=10)
     ap.add_argument("--no-baseline", action="store_true", help="skip the per-sector GPU baseline")
-    ap.add_argument("--ld-align", type=int, default=1,
-                    help="cfg5: pad each block's leading dimension to a multiple of this many elements")
+    ap.add_argument("--ld-align", type=int, default=8,
+                    help="blockdiag_bf16: pad each block's leading dimension (and start) to a multiple of this many "
+                         "elements; 8 = 16-byte aligned rows (default), 1 = unpadded contiguous blocks")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes (counter calibration) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this engine runs on one GPU; --gpus {args.gpus} is not supported "
@@ -91,6 +116,16 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        # a plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for it calibrates the counters
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}), flush=True)
+        return
     stages, inputs, sizes, dtype = load_workload(args.workload, args.ld_align)
 
     # inputs resident in HBM before timing
@@ -130,26 +165,40 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K
 
-    # --- engine: whole-step time -------------------------------------------------
-    ms = timed(grouped, args.steps, args.warmup)
-
-    # --- per-kernel durations: events around each stage's launch on its stream ----
-    per_stage = [[] for _ in stages]
+    # --- engine: timed region ----------------------------------------------------------
+    # K steps between two events on torch's current stream (the stream the engine
+    # launches on).  A one-launch step needs nothing more: the average launch
+    # duration is the region over K.  A step of several launches also records an
+    # event after every launch, so each stage's launches are timed on their own.
+    for _ in range(args.warmup):
+        step(grouped)
     torch.cuda.synchronize()
+    multi = len(stages) > 1
+    marks = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(args.steps):
-        for i, (p, (_, a, b, c, _)) in enumerate(zip(grouped, stages)):
-            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record()
+        for p, (_, a, b, c, _) in zip(grouped, stages):
             p.contract(bufs[a], bufs[b], bufs[c])
-            s1.record()
-            per_stage[i].append((s0, s1))
+            if multi:
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record()
+                marks.append(ev)
+    e1.record()
     torch.cuda.synchronize()
-    stage_ms = [statistics.fmean(x.elapsed_time(y) for x, y in ev) for ev in per_stage]
+    ms = e0.elapsed_time(e1) / args.steps
+    if multi:
+        bounds = [e0] + marks
+        stage_ms = [statistics.fmean(bounds[j].elapsed_time(bounds[j + 1])
+                                     for j in range(i, len(marks), len(stages))) for i in range(len(stages))]
+    else:
+        stage_ms = [ms]
     dom = max(range(len(stages)), key=lambda i: stage_ms[i])
     dom_flops = st[dom]["useful_flops"]
     dom_bytes = st[dom]["alg_bytes"]
     achieved_tflops = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
     peak = MFMA_PEAK[dtype]
+    traffic = measured_traffic(args.workload, args.ld_align, dom)
 
     # --- uncoalesced GPU baseline: one launch per sector GEMM -----------------------
     if not args.no_baseline:
@@ -185,7 +234,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved_tflops / peak, 5),
-            "traffic": None,
+            "traffic": traffic,
             "kernel_ms": round(stage_ms[dom], 6),
             "flops_per_launch": dom_flops,
             "alg_bytes_per_launch": dom_bytes,
@@ -216,7 +265,7 @@ def main():
             for con, a, b, c, _ in stages:
                 hb[c] = oracle.contract(con, hb[a], hb[b], np.zeros(sizes[c]), check=False)
             times.append(time.perf_counter() - t0)
-            if time.perf_counter() - t_start >= args.cpu_seconds or len(times) >= 50:
+            if time.perf_counter() - t_start >= args.cpu_seconds or len(times) >= 1000:
                 break
         med = statistics.median(times)
         out["cpu_baseline"] = {

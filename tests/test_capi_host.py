@@ -59,8 +59,8 @@ def _check_against_oracle(con, axis):
 @pytest.mark.parametrize("axis", list(AXES))
 def test_planner_matches_oracle_configs(axis):
     _lib_or_skip()
-    for con in [C.cfg1("diag").con, C.cfg1("flux1").con, C.cfg1("flux1_3leg").con, C.cfg2().con,
-                C.cfg5(values=False).con] + [s.con for s in C.cfg3().stages]:
+    for con in [C.tiny_u1("diag").con, C.tiny_u1("flux1").con, C.tiny_u1("flux1_3leg").con, C.ragged_batch().con,
+                C.blockdiag_bf16(values=False).con] + [s.con for s in C.rabc_u1().stages]:
         _check_against_oracle(con, axis)
 
 
@@ -75,7 +75,7 @@ def test_planner_matches_oracle_random(seed, axis):
 
 def test_per_sector_stats():
     _lib_or_skip()
-    con = C.cfg2().con
+    con = C.ragged_batch().con
     p = bst.Plan(con, launch_mode="per_sector")
     s = p.stats()
     assert s["launches_per_contract"] == 4000 and s["launches_per_sector"] == 4000
@@ -84,15 +84,15 @@ def test_per_sector_stats():
     assert s["launches_per_sector"] / g["launches_per_contract"] >= 50
 
 
-def test_cfg5_one_launch():
+def test_blockdiag_bf16_one_launch():
     _lib_or_skip()
-    s = bst.Plan(C.cfg5(values=False).con).stats()
+    s = bst.Plan(C.blockdiag_bf16(values=False).con).stats()
     assert s["launches_per_contract"] == 1 and s["launches_per_sector"] == 64
 
 
 def test_zero_blocks_counted():
     _lib_or_skip()
-    ch = C.cfg4()
+    ch = C.rabc_u1u1()
     for st in ch.stages:
         s = bst.Plan(st.con).stats()
         t = oracle.triples(st.con)
@@ -113,14 +113,14 @@ def _err(con, **kw):
 
 def test_error_charge():
     _lib_or_skip()
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     p.con.A.col_key[0] = 1
     assert _err(p.con) == "BSC_ERR_CHARGE"
 
 
 def test_error_flux():
     _lib_or_skip()
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     p.con.C.flux[:] = 1
     p.con.C.row_key[:] = p.con.C.row_key  # same blocks now break the rule or the flux sum
     assert _err(p.con) in ("BSC_ERR_CHARGE",)
@@ -128,7 +128,7 @@ def test_error_flux():
 
 def test_error_overlap():
     _lib_or_skip()
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     p.con.C.offset[1] = p.con.C.offset[0]
     assert _err(p.con) == "BSC_ERR_OVERLAP"
 
@@ -136,7 +136,7 @@ def test_error_overlap():
 def test_error_overlap_interleaved():
     """Interleaved C views that collide only element-wise are caught."""
     _lib_or_skip()
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     # block 0 is 8x4 row-major at offset 0: make block 1 (5x2) interleave into its columns
     p.con.C.offset[1] = 1
     p.con.C.row_stride[1] = (4, 0)
@@ -159,7 +159,7 @@ def test_interleaved_disjoint_accepted():
 
 def test_error_missing_output():
     _lib_or_skip()
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     keep = np.arange(p.con.C.nblocks) != 2
     for f in ("row_key", "col_key", "offset", "row_stride", "col_stride"):
         setattr(p.con.C, f, getattr(p.con.C, f)[keep])
@@ -168,40 +168,40 @@ def test_error_missing_output():
 
 def test_error_bounds():
     _lib_or_skip()
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     p.con.B.buffer_elems = int(p.con.B.offset[-1])
     assert _err(p.con) == "BSC_ERR_BOUNDS"
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     p.con.A.offset[0] = -1
     assert _err(p.con) == "BSC_ERR_BOUNDS"
 
 
 def test_error_shape():
     _lib_or_skip()
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     p.con.A.row_key[1] = p.con.A.row_key[0]
     p.con.A.col_key[1] = p.con.A.col_key[0]
     assert _err(p.con) == "BSC_ERR_SHAPE"          # duplicate block
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     p.con.A.row_stride[0] = (0, 0)
     assert _err(p.con) == "BSC_ERR_SHAPE"          # zero stride on a leg of extent 8
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     p.con.A.row_key[0] = 17
     assert _err(p.con) == "BSC_ERR_SHAPE"          # key out of range
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     p.con.m.dim[0] = 0
     assert _err(p.con) == "BSC_ERR_SHAPE"
 
 
 def test_error_axis_none_grouped():
     _lib_or_skip()
-    assert _err(C.cfg1().con, axis="none") == "BSC_ERR_ARG"
+    assert _err(C.tiny_u1().con, axis="none") == "BSC_ERR_ARG"
 
 
 def test_contract_before_bind():
     L = _lib_or_skip()
     import ctypes
-    p = bst.Plan(C.cfg1().con)
+    p = bst.Plan(C.tiny_u1().con)
     st = L.bsc_contract(p._h, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), None)
     assert _capi.STATUS[st] == "BSC_ERR_NOT_BOUND"
 
@@ -209,7 +209,7 @@ def test_contract_before_bind():
 def test_bind_too_small():
     L = _lib_or_skip()
     import ctypes
-    p = bst.Plan(C.cfg1().con)
+    p = bst.Plan(C.tiny_u1().con)
     st = L.bsc_plan_bind(p._h, ctypes.c_void_p(4096), ctypes.c_size_t(1), None)
     assert _capi.STATUS[st] == "BSC_ERR_DEVICE_BYTES"
 

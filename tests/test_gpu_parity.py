@@ -43,24 +43,24 @@ def _parity(prob, axis="auto", launch_mode="grouped", layout="auto", tol=None, e
 
 @pytest.mark.parametrize("variant", ["diag", "flux1", "flux1_3leg"])
 @pytest.mark.parametrize("axis", AXES)
-def test_cfg1(variant, axis):
-    _parity(C.cfg1(variant), axis=axis)
+def test_tiny_u1(variant, axis):
+    _parity(C.tiny_u1(variant), axis=axis)
 
 
 @pytest.mark.parametrize("variant", ["diag", "flux1"])
-def test_cfg1_per_sector(variant):
-    _parity(C.cfg1(variant), launch_mode="per_sector")
+def test_tiny_u1_per_sector(variant):
+    _parity(C.tiny_u1(variant), launch_mode="per_sector")
 
 
 @pytest.mark.parametrize("axis", AXES)
-def test_cfg2(axis):
-    plan, _ = _parity(C.cfg2(), axis=axis)
+def test_ragged_batch(axis):
+    plan, _ = _parity(C.ragged_batch(), axis=axis)
     if axis in ("auto", "free_m"):
         assert plan.stats()["launches_per_contract"] == 1
 
 
-def test_cfg2_per_sector():
-    plan, _ = _parity(C.cfg2(), launch_mode="per_sector")
+def test_ragged_batch_per_sector():
+    plan, _ = _parity(C.ragged_batch(), launch_mode="per_sector")
     assert plan.stats()["launches_per_contract"] == 4000
 
 
@@ -90,22 +90,22 @@ def test_accumulate(dtype):
     _parity(prob, launch_mode="per_sector", accumulate=True, exact=True)
 
 
-def test_cfg5_full_size():
-    prob = C.cfg5()
+def test_blockdiag_bf16_full_size():
+    prob = C.blockdiag_bf16()
     plan, got = _parity(prob, axis="auto")
     s = plan.stats()
     assert s["launches_per_contract"] == 1 and s["launches_per_sector"] == 64
 
 
-def test_cfg5_full_size_aligned():
+def test_blockdiag_bf16_full_size_aligned():
     """16-byte aligned, padded layout: the direct-to-LDS tile path."""
-    prob = C.cfg5(ld_align=8, align=8)
+    prob = C.blockdiag_bf16(ld_align=8, align=8)
     plan, got = _parity(prob, axis="auto")
     s = plan.stats()
     assert s["items_by_class"]["mfma_fast"] > 0 and s["launches_per_contract"] == 1
 
 
-def test_cfg5_small_blocks_ragged():
+def test_blockdiag_bf16_small_blocks_ragged():
     """A ragged bf16 block-diagonal case spanning several tiles with odd edges."""
     prob = C.random_problem(4200, nq=1, nkeys=(6, 6, 6), maxdim=150, qrange=2, dtype="bf16", two_leg=False,
                             dup_charges=False)
@@ -138,17 +138,17 @@ def test_small_chain(layout):
     _chain_parity(C.small_chain(seed=3, layout=layout), 1e-12)
 
 
-def test_cfg3_chain():
-    _chain_parity(C.cfg3(), 1e-12)
-    _chain_parity(C.cfg3(), 1e-12, axes=("contract", "free_n", "free_m"))
+def test_rabc_u1_chain():
+    _chain_parity(C.rabc_u1(), 1e-12)
+    _chain_parity(C.rabc_u1(), 1e-12, axes=("contract", "free_n", "free_m"))
 
 
-def test_cfg4_chain():
-    _chain_parity(C.cfg4(), 1e-5)
+def test_rabc_u1u1_chain():
+    _chain_parity(C.rabc_u1u1(), 1e-5)
 
 
 def test_determinism():
-    prob = C.cfg2()
+    prob = C.ragged_batch()
     plan = bst.Plan(prob.con).bind()
     t = torch()
     A, B = to_dev(prob.a, "f32"), to_dev(prob.b, "f32")
@@ -174,7 +174,7 @@ def test_coalesced_equals_uncoalesced():
 
 
 def test_launch_counter():
-    prob = C.cfg2()
+    prob = C.ragged_batch()
     plan = bst.Plan(prob.con).bind()
     before = plan.stats()["launches_issued"]
     run_engine(plan, prob.a, prob.b, np.zeros(prob.con.C.buffer_elems, np.float32), "f32", repeats=3)

@@ -157,8 +157,8 @@ def test_p1_scalar_loop_bit_identical(seed):
 
 
 @pytest.mark.parametrize("variant", ["diag", "flux1", "flux1_3leg"])
-def test_p1_cfg1_dense(variant):
-    p = C.cfg1(variant)
+def test_p1_tiny_u1_dense(variant):
+    p = C.tiny_u1(variant)
     out = oracle.contract(p.con, p.a, p.b)
     Cd = oracle.densify(p.con.C, out, p.con.m, p.con.n)
     # dense product formed from the generator's own buffers via independent addresses
@@ -173,9 +173,9 @@ def test_p1_cfg1_dense(variant):
     np.testing.assert_allclose(Cd, Ad @ Bd, rtol=1e-14, atol=1e-14)
 
 
-def test_cfg1_flux_encodings_agree():
-    a = oracle.contract(C.cfg1("flux1").con, C.cfg1("flux1").a, C.cfg1("flux1").b)
-    p3 = C.cfg1("flux1_3leg")
+def test_tiny_u1_flux_encodings_agree():
+    a = oracle.contract(C.tiny_u1("flux1").con, C.tiny_u1("flux1").a, C.tiny_u1("flux1").b)
+    p3 = C.tiny_u1("flux1_3leg")
     b = oracle.contract(p3.con, p3.a, p3.b)
     assert np.array_equal(a, b)
     assert len(oracle.triples(p3.con)) == 4 and oracle.useful_flops(p3.con) == 452
@@ -306,7 +306,7 @@ def test_p6_single_sector_is_plain_gemm(shape, orient):
 
 
 def test_accumulate_adds():
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     first = oracle.contract(p.con, p.a, p.b)
     twice = oracle.contract(p.con, p.a, p.b, first, accumulate=True)
     np.testing.assert_allclose(twice, 2 * first, rtol=1e-15, atol=0)
@@ -388,9 +388,9 @@ def test_p7_groups_invariants(axis, seed):
 
 
 def test_groups_on_configs():
-    ax, gl = _check_groups(C.cfg2().con, AXIS_FREE_M)
+    ax, gl = _check_groups(C.ragged_batch().con, AXIS_FREE_M)
     assert len(gl) == 500 and all(len(r) == 8 for r, c, kl in gl)
-    ch = C.cfg3()
+    ch = C.rabc_u1()
     ax, gl = _check_groups(ch.stages[0].con, AXIS_AUTO)
     assert ax == AXIS_FREE_M
     ax, gl = _check_groups(ch.stages[1].con, AXIS_AUTO)
@@ -415,7 +415,7 @@ def test_auto_rule_threshold():
 # ----------------------------------------------------------------------------
 
 def _tiny():
-    p = C.cfg1("diag")
+    p = C.tiny_u1("diag")
     return p
 
 

@@ -108,14 +108,14 @@ def replay(plan, con, a, b, c0, accumulate=False):
     return c, written
 
 
-CASES = [("cfg1", lambda: C.cfg1().con, lambda: C.cfg1()),
-         ("cfg1-flux1", None, lambda: C.cfg1("flux1")),
-         ("cfg1-3leg", None, lambda: C.cfg1("flux1_3leg")),
-         ("cfg2", None, lambda: C.cfg2())]
+CASES = [("tiny_u1", lambda: C.tiny_u1().con, lambda: C.tiny_u1()),
+         ("tiny_u1-flux1", None, lambda: C.tiny_u1("flux1")),
+         ("tiny_u1-3leg", None, lambda: C.tiny_u1("flux1_3leg")),
+         ("ragged_batch", None, lambda: C.ragged_batch())]
 
 
 @pytest.mark.parametrize("axis", ["auto", "free_m", "free_n", "contract"])
-@pytest.mark.parametrize("name", ["cfg1", "cfg1-flux1", "cfg1-3leg", "cfg2"])
+@pytest.mark.parametrize("name", ["tiny_u1", "tiny_u1-flux1", "tiny_u1-3leg", "ragged_batch"])
 def test_replay_configs(name, axis):
     prob = dict((n, f) for n, _, f in CASES)[name]()
     _check(prob.con, prob.a, prob.b, axis)
@@ -143,8 +143,8 @@ def test_replay_small_chain(layout, axis):
         bufs[st.c_buf] = got
 
 
-def test_replay_cfg3_stages():
-    ch = C.cfg3()
+def test_replay_rabc_u1_stages():
+    ch = C.rabc_u1()
     bufs = {k: np.asarray(v, np.float64) for k, v in ch.buffers.items()}
     ref = oracle.run_chain(ch)
     for st in ch.stages:
@@ -175,7 +175,7 @@ def _check(con, a, b, axis):
 @pytest.mark.parametrize("la", [1, 8])
 def test_replay_bf16_dense_tiles(la):
     """bf16 block-diagonal structures: aligned layouts take the dense tile records."""
-    prob = C.cfg5(ld_align=la, align=la)
+    prob = C.blockdiag_bf16(ld_align=la, align=la)
     # replay a subset of the sectors to keep it quick: rebuild with the first 12 keys
     import copy
     con = prob.con

@@ -82,7 +82,7 @@ def _round_dims(raw, qkeys, total):
 # config 1: tiny U(1) block-sparse GEMM, fp64
 # ----------------------------------------------------------------------------
 
-def cfg1(variant: str = "diag", seed: int = 1001) -> Problem:
+def tiny_u1(variant: str = "diag", seed: int = 1001) -> Problem:
     """Five U(1) sectors q=-2..2 per index, dims uniform in 1..8.
 
     variant 'diag'      : A, B, C diagonal (q_m = q_k = q_n), 5 sector GEMMs;
@@ -117,14 +117,14 @@ def cfg1(variant: str = "diag", seed: int = 1001) -> Problem:
         raise ValueError(variant)
     con = Contraction(m, k, n, _operand(Ab, flux_a, 1, na), _operand(Bb, [0], 1, nb),
                       _operand(Cb, flux_c, 1, nc), "f64")
-    return Problem(f"cfg1-{variant}", con, a, b, {"dims": (dm, dk, dn)})
+    return Problem(f"tiny_u1-{variant}", con, a, b, {"dims": (dm, dk, dn)})
 
 
 # ----------------------------------------------------------------------------
 # config 2: tail-heavy ragged batch, fp32
 # ----------------------------------------------------------------------------
 
-def cfg2(seed: int = 1002, ngroups: int = 500, per_group: int = 8, p: float = 0.35, cap: int = 64) -> Problem:
+def ragged_batch(seed: int = 1002, ngroups: int = 500, per_group: int = 8, p: float = 0.35, cap: int = 64) -> Problem:
     """4000 independent sector GEMMs with geometric(p) dims capped at 64; every
     8 consecutive GEMMs share one (K, N, B) so they stack along M."""
     rng = np.random.default_rng(seed)
@@ -147,14 +147,14 @@ def cfg2(seed: int = 1002, ngroups: int = 500, per_group: int = 8, p: float = 0.
     _fill(b, Bb, K, N, draw)
     con = Contraction(m, k, n, _operand(Ab, [0], 1, na), _operand(Bb, [0], 1, nb),
                       _operand(Cb, [0], 1, nc), "f32")
-    return Problem("cfg2-ragged", con, a, b, {"M": M, "N": N, "K": K})
+    return Problem("ragged_batch-ragged", con, a, b, {"M": M, "N": N, "K": K})
 
 
 # ----------------------------------------------------------------------------
 # config 5: large block-sparse GEMM, bf16 inputs / fp32 accumulate
 # ----------------------------------------------------------------------------
 
-def cfg5_dims(reading: str = "i_scaled", seed: int = 1005):
+def blockdiag_bf16_dims(reading: str = "i_scaled", seed: int = 1005):
     rng = np.random.default_rng(seed)
     if reading == "i_scaled":
         main = np.clip(np.rint(rng.lognormal(5.0, 0.6, 45)), 16, 1024)
@@ -174,7 +174,7 @@ def cfg5_dims(reading: str = "i_scaled", seed: int = 1005):
     return dims[perm], rng
 
 
-def cfg5(reading: str = "i_scaled", seed: int = 1005, ld_align: int = 1, align: int = 1,
+def blockdiag_bf16(reading: str = "i_scaled", seed: int = 1005, ld_align: int = 1, align: int = 1,
          values: bool = True) -> Problem:
     """U(1) sectors q=0..S-1 sharing one dimension list for m, k and n, flux 0, so
     every operand is block diagonal.  Dims are lognormal(5, 0.6) clipped to
@@ -183,7 +183,7 @@ def cfg5(reading: str = "i_scaled", seed: int = 1005, ld_align: int = 1, align: 
 
     ld_align / align pad each block's leading dimension / start offset (in
     elements); 1 gives plain contiguous row-major blocks."""
-    dims, rng = cfg5_dims(reading, seed)
+    dims, rng = blockdiag_bf16_dims(reading, seed)
     S = len(dims)
     q = np.arange(S)
     idx = Index(q[:, None], dims)
@@ -199,7 +199,7 @@ def cfg5(reading: str = "i_scaled", seed: int = 1005, ld_align: int = 1, align: 
         _fill(b, Bb, dims, dims, draw)
     con = Contraction(idx, idx, idx, _operand(Ab, [0], 1, na), _operand(Bb, [0], 1, nb),
                       _operand(Cb, [0], 1, nc), "bf16")
-    return Problem(f"cfg5-{reading}", con, a, b, {"dims": dims})
+    return Problem(f"blockdiag_bf16-{reading}", con, a, b, {"dims": dims})
 
 
 # ----------------------------------------------------------------------------
@@ -470,11 +470,11 @@ def rabc_chain(bond_q, bond_dim, local_q, mpo_q, mpo_pairs, dtype, rng, layout="
     return Chain(name, stages, {"E": Ebuf, "A": Abuf, "W": Wbuf}, sizes, dtype, info)
 
 
-CFG3_MPO_PAIRS = [(0, 0), (0, 1), (0, 2), (0, 3), (0, 4), (1, 4), (2, 4), (3, 4), (4, 4), (1, 1), (2, 2), (3, 3)]
-CFG4_MPO_PAIRS = [(0, j) for j in range(6)] + [(i, 5) for i in range(1, 5)] + [(5, 5)]
+U1_MPO_PAIRS = [(0, 0), (0, 1), (0, 2), (0, 3), (0, 4), (1, 4), (2, 4), (3, 4), (4, 4), (1, 1), (2, 2), (3, 3)]
+U1U1_MPO_PAIRS = [(0, j) for j in range(6)] + [(i, 5) for i in range(1, 5)] + [(5, 5)]
 
 
-def cfg3(seed: int = 1003, layout: str = "coop") -> Chain:
+def rabc_u1(seed: int = 1003, layout: str = "coop") -> Chain:
     """U(1) spin-chain environment update, fp64: bond m=1024 over 41 sectors
     (Gaussian dims, sigma = 6 sectors), LocalSpace d=4 with charges {-1,0,0,+1},
     MPO bond w=5 with 12 nonzero channel pairs."""
@@ -482,10 +482,10 @@ def cfg3(seed: int = 1003, layout: str = "coop") -> Chain:
     bq, bd = _bond_u1(1024, 20, 6.0)
     local = np.array([[-1], [0], [0], [1]])
     mpo = np.array([[0], [-1], [1], [0], [0]])
-    return rabc_chain(bq, bd, local, mpo, CFG3_MPO_PAIRS, "f64", rng, layout, name=f"cfg3-{layout}")
+    return rabc_chain(bq, bd, local, mpo, U1_MPO_PAIRS, "f64", rng, layout, name=f"rabc_u1-{layout}")
 
 
-def cfg4(seed: int = 1004, layout: str = "natural") -> Chain:
+def rabc_u1u1(seed: int = 1004, layout: str = "natural") -> Chain:
     """U(1)xU(1) environment update, fp32: bond m=4096 over the populated part of
     a 15x15 charge grid (Gaussian dims, sigma 2.2 -> 177 sectors), local charges
     (n_up, n_dn), Hubbard-shaped MPO w=6 with 11 nonzero channel pairs."""
@@ -493,7 +493,7 @@ def cfg4(seed: int = 1004, layout: str = "natural") -> Chain:
     bq, bd = _bond_u1u1(4096, 7, 2.2, 0.5)
     local = np.array([[0, 0], [1, 0], [0, 1], [1, 1]])
     mpo = np.array([[0, 0], [-1, 0], [1, 0], [0, -1], [0, 1], [0, 0]])
-    return rabc_chain(bq, bd, local, mpo, CFG4_MPO_PAIRS, "f32", rng, layout, name=f"cfg4-{layout}")
+    return rabc_chain(bq, bd, local, mpo, U1U1_MPO_PAIRS, "f32", rng, layout, name=f"rabc_u1u1-{layout}")
 
 
 def small_chain(seed: int = 7, layout: str = "coop", values: str = "normal", dtype: str = "f64",
@@ -503,7 +503,7 @@ def small_chain(seed: int = 7, layout: str = "coop", values: str = "normal", dty
     bq, bd = _bond_u1(total, qmax, sigma)
     local = np.array([[-1], [0], [0], [1]])
     if w == 5:
-        mpo, pairs = np.array([[0], [-1], [1], [0], [0]]), CFG3_MPO_PAIRS
+        mpo, pairs = np.array([[0], [-1], [1], [0], [0]]), U1_MPO_PAIRS
     elif w == 1:
         mpo, pairs = np.array([[0]]), [(0, 0)]
     else:

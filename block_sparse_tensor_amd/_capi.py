@@ -40,7 +40,7 @@ class BscStats(ctypes.Structure):
     _fields_ = [("triples", c_int64), ("c_blocks", c_int64), ("zero_blocks", c_int64), ("groups", c_int64),
                 ("zero_groups", c_int64), ("axis", c_int32), ("dtype", c_int32),
                 ("mode_count", (c_int64 * 3) * 3), ("runs", c_int64), ("items", c_int64),
-                ("items_by_class", c_int64 * 5), ("launches_per_contract", c_int64),
+                ("items_by_class", c_int64 * 6), ("launches_per_contract", c_int64),
                 ("launches_per_sector", c_int64), ("useful_flops", c_int64), ("alg_bytes", c_int64),
                 ("pack_bytes", c_int64), ("device_bytes", c_int64), ("tail_triples", c_int64),
                 ("launches_issued", c_int64), ("grid", c_int32), ("reserved", c_int32),

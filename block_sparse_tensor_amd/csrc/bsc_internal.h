@@ -79,7 +79,9 @@ enum : int32_t {
     T_MFMA_FAST_N = 4,   // dense matrix-core tile, direct-to-LDS loads, N-contiguous B (group = DFast index)
     T_MFMA_FAST_K = 5,   // dense matrix-core tile, direct-to-LDS loads, K-contiguous B (group = DFast index)
     T_NOP = 6,           // placeholder keeping the task -> XCD mapping (no work)
-    T_NCLASS = 7,
+    T_SKINNY_M = 7,      // at most 16 output columns: 256 rows x all columns, one thread per row
+    T_SKINNY_N = 8,      // at most 16 output rows: all rows x 256 columns, one thread per column
+    T_NCLASS = 9,
 };
 
 // Workgroups of a launch are dispatched round-robin over the chiplets (XCDs),
@@ -112,11 +114,25 @@ struct DTask {
 static_assert(sizeof(DTask) == 16, "DTask layout");
 
 constexpr int TILE_GENERIC = 64;   // generic tile edge
-constexpr int TILE_MFMA = 128;     // matrix-core tile edge
+constexpr int TILE_MFMA = 128;     // bf16 matrix-core tile edge
+constexpr int TILE_MFMA_F = 64;    // fp32 / fp64 matrix-core tile edge
 
 constexpr bool is_mfma(int32_t cls) { return cls == T_MFMA || cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K; }
-constexpr int32_t tile_m(int32_t cls) { return is_mfma(cls) ? TILE_MFMA : TILE_GENERIC; }
-constexpr int32_t tile_n(int32_t cls) { return is_mfma(cls) ? TILE_MFMA : TILE_GENERIC; }
+constexpr int TILE_SKINNY_LONG = 256;   // skinny tile extent along its long axis
+constexpr int TILE_SKINNY_SHORT = 16;   // largest short extent of a skinny group
+
+// output tile extents (rows, columns) of a task class for a plan dtype and group shape
+inline void tile_extents(bsc_dtype dt, int32_t cls, int32_t M, int32_t N, int32_t &tm, int32_t &tn) {
+    if (cls == T_SKINNY_M) {
+        tm = TILE_SKINNY_LONG;
+        tn = N > 0 ? N : 1;
+    } else if (cls == T_SKINNY_N) {
+        tm = M > 0 ? M : 1;
+        tn = TILE_SKINNY_LONG;
+    } else {
+        tm = tn = is_mfma(cls) ? (dt == BSC_BF16_F32 ? TILE_MFMA : TILE_MFMA_F) : TILE_GENERIC;
+    }
+}
 
 struct Blk {
     int32_t r, c;

@@ -1,0 +1,307 @@
+// Matrix-core tile for fp32 and fp64 operands (gfx950).
+//
+// A 256-thread workgroup (4 waves) computes a 64 x 64 output tile of one
+// coalesced group GEMM.  Wave w owns the 32 x 32 quadrant (w & 1, w >> 1) as
+// 2 x 2 tiles of v_mfma_f32_16x16x4_f32 (fp32) or v_mfma_f64_16x16x4_f64
+// (fp64), accumulating in the operand type.
+//
+// Operands are staged through LDS in chunks of KC contracted indices (32 fp32 /
+// 16 fp64 values, 8 KB per operand) with two buffers: the global loads of chunk
+// c+1 are in flight while chunk c feeds the matrix cores.  In LDS both operands
+// are stored k-major, [k][x] with x the free index of the tile, so one MFMA
+// fragment (16 consecutive x for each of 4 k) is a single read per lane.  The
+// x position is XOR-swizzled by k, which keeps both the fragment reads and the
+// transposing stores of k-contiguous rows on distinct banks.
+//
+// Global loads follow the operand's memory order:
+//   k-contiguous rows        -> 16-byte loads along k, transposed while storing;
+//   free-axis-contiguous rows -> 16-byte loads along x, stored as they are;
+//   anything else            -> element loads through the per-row records.
+#pragma once
+
+#include "kernels_common.h"
+
+namespace bsc {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int MF_TILE = 64;
+
+template <typename T>
+struct MfTraits;
+template <>
+struct MfTraits<float> {
+    static constexpr int KC = 32;   // contracted indices per LDS chunk
+    typedef f32x4_t acc_t;
+};
+template <>
+struct MfTraits<double> {
+    static constexpr int KC = 16;
+    typedef f64x4_t acc_t;
+};
+
+// LDS element index of (k, x) inside one operand chunk: 64 values per k, x
+// swizzled by bits of k (the swizzle only flips bits 3..5 of x, so 16-byte
+// groups of consecutive x stay contiguous and aligned).
+__device__ __forceinline__ int32_t mf_idx(int32_t k, int32_t x) {
+    return k * MF_TILE + (x ^ ((16 * (k & 3)) ^ (8 * ((k >> 2) & 7))));
+}
+
+template <typename T>
+struct MfmaSmemF {
+    T a[2][MfTraits<T>::KC * MF_TILE];
+    T b[2][MfTraits<T>::KC * MF_TILE];
+    Rec ra[MF_TILE];
+    Rec rb[MF_TILE];
+};
+
+enum : int32_t { MF_KCONTIG = 0, MF_FCONTIG = 1, MF_GENERIC = 2 };
+
+template <typename T>
+struct MfCtx {
+    int32_t mode;
+    int32_t x0, xlen;     // tile origin along the free axis (group coordinates) and valid extent
+    int32_t K;            // run length
+    int32_t vec;          // base pointer 16-byte aligned
+    const T *P;
+    int64_t off, sk;      // MF_FCONTIG: element (x, k) at off + x + k * sk, x in group coordinates
+    const Rec *rec;       // per-row records (MF_KCONTIG, MF_GENERIC)
+};
+
+// registers carrying one chunk of one operand from global memory to LDS
+template <typename T>
+struct MfStage {
+    T v[2][16 / sizeof(T)];
+};
+
+template <typename T>
+__device__ __forceinline__ MfCtx<T> mf_ctx(const DView *pieces, int32_t np, int32_t flags_k, int32_t flags_f,
+                                           int32_t run_flags, int32_t x0, int32_t xlen, int32_t K, const T *P,
+                                           int32_t vec, const Rec *rec) {
+    MfCtx<T> o;
+    o.x0 = x0;
+    o.xlen = xlen;
+    o.K = K;
+    o.vec = vec;
+    o.P = P;
+    o.rec = rec;
+    o.off = 0;
+    o.sk = 0;
+    if (run_flags & flags_k) {
+        o.mode = MF_KCONTIG;
+    } else if ((run_flags & flags_f) && np == 1 && pieces[0].ib == 1) {
+        o.mode = MF_FCONTIG;
+        o.off = pieces[0].off - pieces[0].begin;
+        o.sk = pieces[0].sb0;
+    } else {
+        o.mode = MF_GENERIC;
+    }
+    return o;
+}
+
+// global -> registers for chunk k0 (the element-wise mode loads in mf_store)
+template <typename T>
+__device__ __forceinline__ void mf_load(const MfCtx<T> &o, int32_t k0, MfStage<T> &st) {
+    constexpr int V = 16 / sizeof(T);
+    const int32_t tid = threadIdx.x;
+    if (o.mode == MF_KCONTIG) {
+        // 8 lanes cover one row's KC values; 32 rows per pass, two passes
+        const int32_t kx = tid & 7, xr = tid >> 3;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int32_t x = xr + 32 * q, k = k0 + V * kx;
+#pragma unroll
+            for (int i = 0; i < V; ++i) st.v[q][i] = T(0);
+            if (x < o.xlen && k < o.K) {
+                const int64_t ad = o.rec[x].base + k;
+                if (o.vec && k + V <= o.K && (ad & (V - 1)) == 0) {
+                    const uint4 u = *reinterpret_cast<const uint4 *>(o.P + ad);
+                    __builtin_memcpy(st.v[q], &u, 16);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < V; ++i)
+                        if (k + i < o.K) st.v[q][i] = o.P[ad + i];
+                }
+            }
+        }
+    } else if (o.mode == MF_FCONTIG) {
+        // 64 / V lanes cover one k row of the tile; two passes cover KC rows
+        constexpr int LPR = MF_TILE / V;
+        constexpr int RPP = 256 / LPR;
+        const int32_t x = V * (tid % LPR), kr = tid / LPR;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int32_t k = k0 + kr + RPP * q;
+#pragma unroll
+            for (int i = 0; i < V; ++i) st.v[q][i] = T(0);
+            if (k < o.K && x < o.xlen) {
+                const int64_t ad = o.off + static_cast<int64_t>(o.x0 + x) + static_cast<int64_t>(k) * o.sk;
+                if (o.vec && x + V <= o.xlen && (ad & (V - 1)) == 0) {
+                    const uint4 u = *reinterpret_cast<const uint4 *>(o.P + ad);
+                    __builtin_memcpy(st.v[q], &u, 16);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < V; ++i)
+                        if (x + i < o.xlen) st.v[q][i] = o.P[ad + i];
+                }
+            }
+        }
+    }
+}
+
+// registers (or, element-wise, global memory) -> LDS chunk
+template <typename T>
+__device__ __forceinline__ void mf_store(const MfCtx<T> &o, const MfStage<T> &st, T *lds, int32_t k0) {
+    constexpr int V = 16 / sizeof(T);
+    constexpr int KC = MfTraits<T>::KC;
+    const int32_t tid = threadIdx.x;
+    if (o.mode == MF_KCONTIG) {
+        const int32_t kx = tid & 7, xr = tid >> 3;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < V; ++i) lds[mf_idx(V * kx + i, xr + 32 * q)] = st.v[q][i];
+    } else if (o.mode == MF_FCONTIG) {
+        constexpr int LPR = MF_TILE / V;
+        constexpr int RPP = 256 / LPR;
+        const int32_t x = V * (tid % LPR), kr = tid / LPR;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            uint4 u;
+            __builtin_memcpy(&u, st.v[q], 16);
+            *reinterpret_cast<uint4 *>(lds + mf_idx(kr + RPP * q, x)) = u;
+        }
+    } else {
+        const int32_t x = tid & 63, kk = tid >> 6;
+        const bool row_ok = x < o.xlen;
+#pragma unroll 4
+        for (int j = 0; j < KC / 4; ++j) {
+            const int32_t k = kk + 4 * j;
+            lds[mf_idx(k, x)] = (row_ok && k0 + k < o.K) ? o.P[along(o.rec[x], k0 + k)] : T(0);
+        }
+    }
+}
+
+__device__ __forceinline__ f32x4_t mf_mma(float a, float b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f64x4_t mf_mma(double a, double b, f64x4_t c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// One chunk through the matrix cores.  MFMA step s covers chunk indices
+// 4s..4s+3; lane l supplies index 4s + (l >> 4) at free position l & 15.
+template <typename T>
+__device__ __forceinline__ void mf_compute(const T *la, const T *lb, typename MfTraits<T>::acc_t (&acc)[2][2]) {
+    constexpr int KC = MfTraits<T>::KC;
+    const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int32_t wm = w & 1, wn = w >> 1;
+    const int32_t j = lane >> 4, xi = lane & 15;
+#pragma unroll
+    for (int s = 0; s < KC / 4; ++s) {
+        const int32_t k = 4 * s + j;
+        T fa[2], fb[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            fa[f] = la[mf_idx(k, wm * 32 + f * 16 + xi)];
+            fb[f] = lb[mf_idx(k, wn * 32 + f * 16 + xi)];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mf_mma(fa[i], fb[jj], acc[i][jj]);
+    }
+}
+
+// tile row of accumulator element r of lane `lane` in a 16 x 16 MFMA tile
+__device__ __forceinline__ int32_t mf_row(float, int32_t lane, int32_t r) { return (lane >> 4) * 4 + r; }
+__device__ __forceinline__ int32_t mf_row(double, int32_t lane, int32_t r) { return (lane >> 4) + 4 * r; }
+
+template <typename T>
+__device__ void mfma_tile_f(const KArgs &ka, const DTask &task, MfmaSmemF<T> &sm) {
+    typedef typename MfTraits<T>::acc_t acc_t;
+    constexpr int KC = MfTraits<T>::KC;
+    const DGroup g = ka.groups[task.group];
+    const int32_t tid = threadIdx.x;
+    const int32_t m0 = task.m0, n0 = task.n0;
+    const int32_t mlen = min(MF_TILE, g.M - m0), nlen = min(MF_TILE, g.N - n0);
+    const T *A = static_cast<const T *>(ka.A);
+    const T *B = static_cast<const T *>(ka.B);
+
+    acc_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = T(0);
+
+    for (int32_t r = 0; r < g.nrun; ++r) {
+        const DRun run = ka.runs[g.run0 + r];
+        __syncthreads();
+        if (tid < MF_TILE) {
+            if (tid < mlen) sm.ra[tid] = make_rec(ka.ap + run.ap0, run.nap, m0 + tid);
+        } else if (tid < 2 * MF_TILE) {
+            const int32_t j = tid - MF_TILE;
+            if (j < nlen) sm.rb[j] = make_rec(ka.bp + run.bp0, run.nbp, n0 + j);
+        }
+        __syncthreads();
+        const MfCtx<T> oa = mf_ctx<T>(ka.ap + run.ap0, run.nap, R_A_KUNIT, R_A_FUNIT, run.flags, m0, mlen, run.K, A,
+                                      ka.vec_a, sm.ra);
+        const MfCtx<T> ob = mf_ctx<T>(ka.bp + run.bp0, run.nbp, R_B_KUNIT, R_B_FUNIT, run.flags, n0, nlen, run.K, B,
+                                      ka.vec_b, sm.rb);
+        const int32_t nchunks = (run.K + KC - 1) / KC;
+        MfStage<T> sa, sb;
+        mf_load(oa, 0, sa);
+        mf_load(ob, 0, sb);
+        mf_store(oa, sa, sm.a[0], 0);
+        mf_store(ob, sb, sm.b[0], 0);
+        __syncthreads();
+        for (int32_t c = 0; c < nchunks; ++c) {
+            const bool more = c + 1 < nchunks;
+            if (more) {
+                mf_load(oa, (c + 1) * KC, sa);
+                mf_load(ob, (c + 1) * KC, sb);
+            }
+            mf_compute<T>(sm.a[c & 1], sm.b[c & 1], acc);
+            if (more) {
+                mf_store(oa, sa, sm.a[(c + 1) & 1], (c + 1) * KC);
+                mf_store(ob, sb, sm.b[(c + 1) & 1], (c + 1) * KC);
+            }
+            __syncthreads();
+        }
+    }
+
+    // epilogue: straight from the accumulators through the C pieces; the 16
+    // lanes of a row write 16 consecutive columns
+    const bool cn = (g.flags & G_C_ALONG_N) != 0;
+    if (tid < MF_TILE) {
+        if (!cn && tid < mlen) sm.ra[tid] = make_rec(ka.cp + g.cp0, g.ncp, m0 + tid);
+        if (cn && tid < nlen) sm.ra[tid] = make_rec(ka.cp + g.cp0, g.ncp, n0 + tid);
+    }
+    __syncthreads();
+    T *Cp = static_cast<T *>(ka.C);
+    const bool accum = (g.flags & G_ACCUMULATE) != 0;
+    const int32_t lane = tid & 63, w = tid >> 6;
+    const int32_t wm = w & 1, wn = w >> 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int32_t col = wn * 32 + j * 16 + (lane & 15);
+            if (col >= nlen) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int32_t row = wm * 32 + i * 16 + mf_row(T(0), lane, r);
+                if (row >= mlen) continue;
+                const int64_t ad = cn ? along(sm.ra[col], m0 + row) : along(sm.ra[row], n0 + col);
+                T v = acc[i][j][r];
+                if (accum) v += Cp[ad];
+                Cp[ad] = v;
+            }
+        }
+    __syncthreads();
+}
+
+}  // namespace bsc

@@ -615,7 +615,13 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         // single instruction's worth of work, vector-ALU tiles for the tiny tail
         auto class_of = [&](const DGroup &g) -> int32_t {
             if (g.nrun == 0) return T_ZERO;
-            if (p.dtype == BSC_BF16_F32 && (int64_t)g.M * g.N * g.K >= 32 * 32 * 16 && g.M >= 8 && g.N >= 8) {
+            // at most 16 output rows or columns: a bandwidth-bound stream over the long operand
+            if (std::min(g.M, g.N) <= TILE_SKINNY_SHORT) return g.M >= g.N ? T_SKINNY_M : T_SKINNY_N;
+            if (p.dtype != BSC_BF16_F32) {
+                // fp32 / fp64: 16 x 16 x 4 matrix-core steps once both free extents reach half a step
+                return ((int64_t)g.M * g.N * g.K >= 16 * 16 * 16 && g.M >= 8 && g.N >= 8) ? T_MFMA : T_GENERIC;
+            }
+            if ((int64_t)g.M * g.N * g.K >= 32 * 32 * 16 && g.M >= 8 && g.N >= 8) {
                 // dense tile: one run, one piece per operand, single-leg views, 16-byte vectors
                 if (g.nrun == 1 && g.ncp == 1) {
                     const DRun &r = p.runs[(size_t)g.run0];
@@ -630,11 +636,16 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             return T_GENERIC;
         };
         // relative throughput of a tile class (used only to order work longest-first)
-        auto rate_of = [&](int32_t cls) { return (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) ? 48.0 : (cls == T_MFMA ? 16.0 : 1.0); };
+        auto rate_of = [&](int32_t cls) {
+            if (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) return 48.0;
+            if (cls == T_MFMA) return p.dtype == BSC_BF16_F32 ? 16.0 : 4.0;
+            return 1.0;
+        };
         auto tiles_of = [&](int32_t gi, std::vector<DTask> &out, std::vector<double> *cost) {
             const DGroup &g = p.groups[(size_t)gi];
             const int32_t cls = class_of(g);
-            const int32_t TM = tile_m(cls), TN = tile_n(cls);
+            int32_t TM = 0, TN = 0;
+            tile_extents(p.dtype, cls, g.M, g.N, TM, TN);
             for (int32_t m0 = 0; m0 < g.M; m0 += TM)
                 for (int32_t n0 = 0; n0 < g.N; n0 += TN) {
                     if (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) {
@@ -770,7 +781,9 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         p.features = 0;
         for (auto &t : p.tasks) {
             if (t.cls == T_NOP) continue;
-            s.items_by_class[t.cls == T_MFMA_FAST_K ? T_MFMA_FAST_N : t.cls]++;
+            const int32_t slot = t.cls == T_MFMA_FAST_K ? T_MFMA_FAST_N
+                                 : (t.cls == T_SKINNY_M || t.cls == T_SKINNY_N) ? 5 : t.cls;
+            s.items_by_class[slot]++;
             if (t.cls == T_MFMA) p.features |= FEAT_MFMA;
             if (t.cls == T_MFMA_FAST_N) p.features |= FEAT_FAST_N;
             if (t.cls == T_MFMA_FAST_K) p.features |= FEAT_FAST_K;

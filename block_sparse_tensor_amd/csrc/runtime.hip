@@ -17,6 +17,8 @@
 #include "kernels_generic.h"
 #include "kernels_mfma_bf16.h"
 #include "kernels_mfma_bf16_fast.h"
+#include "kernels_mfma_f.h"
+#include "kernels_skinny.h"
 
 namespace bsc {
 
@@ -26,21 +28,39 @@ static bsc_status hip_fail(hipError_t e, const char *what) {
 }
 
 // Shared memory of a grouped launch: the union of the tile bodies it contains.
-template <typename ACC, int32_t FEAT>
+template <typename TA>
+struct MfmaSmemOf {
+    typedef MfmaSmemF<TA> type;
+};
+template <>
+struct MfmaSmemOf<uint16_t> {
+    typedef MfmaSmemBf16 type;
+};
+
+template <typename TA, typename ACC, int32_t FEAT>
 union TileSmem {
     GenericSmem<ACC> g;
-    typename std::conditional<(FEAT & FEAT_MFMA) != 0, MfmaSmemBf16, char>::type m;
+    SkinnySmem<ACC> s;
+    typename std::conditional<(FEAT & FEAT_MFMA) != 0, typename MfmaSmemOf<TA>::type, char>::type m;
     typename std::conditional<(FEAT & (FEAT_FAST_N | FEAT_FAST_K)) != 0, FastSmemBf16, char>::type f;
 };
 
 extern __shared__ __align__(16) unsigned char bsc_dyn_smem[];
 
 template <typename TA, typename TC, typename ACC, int32_t FEAT>
-__global__ __launch_bounds__(256) void grouped_contract(KArgs ka) {
-    TileSmem<ACC, FEAT> &sm = *reinterpret_cast<TileSmem<ACC, FEAT> *>(bsc_dyn_smem);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void grouped_contract(KArgs ka) {
+    TileSmem<TA, ACC, FEAT> &sm = *reinterpret_cast<TileSmem<TA, ACC, FEAT> *>(bsc_dyn_smem);
     for (int32_t t = blockIdx.x; t < ka.ntasks; t += gridDim.x) {
         const DTask task = ka.tasks[ka.task0 + t];
         if (task.cls == T_NOP) continue;
+        if (task.cls == T_SKINNY_M) {
+            skinny_tile<TA, TC, ACC, true>(ka, task, sm.s);
+            continue;
+        }
+        if (task.cls == T_SKINNY_N) {
+            skinny_tile<TA, TC, ACC, false>(ka, task, sm.s);
+            continue;
+        }
         if constexpr ((FEAT & FEAT_FAST_N) != 0) {
             if (task.cls == T_MFMA_FAST_N) {
                 fast_tile_bf16<TC, true>(ka, task, sm.f);
@@ -55,7 +75,8 @@ __global__ __launch_bounds__(256) void grouped_contract(KArgs ka) {
         }
         if constexpr ((FEAT & FEAT_MFMA) != 0) {
             if (is_mfma(task.cls)) {
-                mfma_tile_bf16<TC>(ka, task, sm.m);
+                if constexpr (std::is_same<TA, uint16_t>::value) mfma_tile_bf16<TC>(ka, task, sm.m);
+                else mfma_tile_f<TA>(ka, task, sm.m);
                 continue;
             }
         }
@@ -74,7 +95,7 @@ struct KernelRef {
 template <typename TA, typename TC, typename ACC, int32_t FEAT>
 static KernelRef kernel_ref() {
     KernelFn fn = grouped_contract<TA, TC, ACC, FEAT>;
-    const size_t lds = sizeof(TileSmem<ACC, FEAT>);
+    const size_t lds = sizeof(TileSmem<TA, ACC, FEAT>);
     static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)once;
@@ -182,12 +203,14 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
         dim3 grid((unsigned)grid_for(*p, ka.ntasks)), block(256);
         switch (p->dtype) {
             case BSC_F64: {
-                const KernelRef k = kernel_ref<double, double, double, 0>();
+                const KernelRef k = (p->features & FEAT_MFMA) ? kernel_ref<double, double, double, FEAT_MFMA>()
+                                                               : kernel_ref<double, double, double, 0>();
                 hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
                 break;
             }
             case BSC_F32: {
-                const KernelRef k = kernel_ref<float, float, float, 0>();
+                const KernelRef k = (p->features & FEAT_MFMA) ? kernel_ref<float, float, float, FEAT_MFMA>()
+                                                               : kernel_ref<float, float, float, 0>();
                 hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
                 break;
             }

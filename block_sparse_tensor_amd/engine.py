@@ -131,7 +131,7 @@ class Plan:
             if name == "mode_count":
                 v = {op: {MODES[j]: int(v[i][j]) for j in range(3)} for i, op in enumerate("ABC")}
             elif name == "items_by_class":
-                v = dict(zip(("generic", "mfma", "tail", "zero", "mfma_fast"), (int(x) for x in v)))
+                v = dict(zip(("generic", "mfma", "tail", "zero", "mfma_fast", "skinny"), (int(x) for x in v)))
             out[name] = v
         out["axis_name"] = AXIS_NAMES[out["axis"]]
         return out

@@ -148,8 +148,9 @@ typedef struct {
     int64_t mode_count[3][3];        /* [operand A,B,C][bsc_mode]: groups per arrangement */
     int64_t runs;                    /* contiguous K-runs over all groups */
     int64_t items;                   /* work items per contraction */
-    int64_t items_by_class[5];       /* generic tile, matrix-core tile, wave tail, zero fill,
-                                        matrix-core tile with direct-to-LDS loads */
+    int64_t items_by_class[6];       /* generic tile, matrix-core tile, wave tail, zero fill,
+                                        matrix-core tile with direct-to-LDS loads,
+                                        skinny tile (at most 16 output rows or columns) */
     int64_t launches_per_contract;   /* GPU commands bsc_contract enqueues */
     int64_t launches_per_sector;     /* one launch per sector GEMM (+1 zero fill if needed) */
     int64_t useful_flops;            /* sum over triples of 2 M N K */

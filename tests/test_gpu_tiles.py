@@ -17,7 +17,8 @@ if have_gpu():
     import block_sparse_tensor_amd as bst
 
 SHAPES = [(1, 1, 1), (7, 3, 5), (32, 16, 32), (64, 32, 64), (65, 17, 63), (128, 32, 128), (128, 33, 128),
-          (129, 64, 127), (200, 40, 150), (256, 96, 256), (64, 1024, 64), (300, 7, 300), (17, 300, 9)]
+          (129, 64, 127), (200, 40, 150), (256, 96, 256), (64, 1024, 64), (300, 7, 300), (17, 300, 9),
+          (1100, 70, 1), (1100, 3, 16), (5, 130, 1030), (16, 65, 513), (17, 5, 700)]
 
 
 def _single(M, K, N, dtype, a_row, b_row, pad, seed, off=3):
@@ -76,3 +77,24 @@ def test_fast_path_selected():
     assert bst.Plan(con).stats()["items_by_class"]["mfma_fast"] == 4
     con, _, _, _ = _single(256, 256, 256, "bf16", True, True, 0, 1, 3)
     assert bst.Plan(con).stats()["items_by_class"]["mfma"] == 4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_matrix_core_class_for_fp32_fp64(dtype):
+    """fp32 / fp64 groups of more than a few matrix-core steps run on 64 x 64 matrix-core tiles."""
+    con, _, _, _ = _single(130, 20, 70, dtype, True, True, 0, 1, 0)
+    s = bst.Plan(con).stats()
+    assert s["items_by_class"]["mfma"] == 3 * 2 and s["items_by_class"]["generic"] == 0
+    con, _, _, _ = _single(20, 20, 70, dtype, True, True, 0, 1, 0)
+    assert bst.Plan(con).stats()["items_by_class"]["mfma"] == 2
+    con, _, _, _ = _single(24, 4, 24, dtype, True, True, 0, 1, 0)
+    assert bst.Plan(con).stats()["items_by_class"]["generic"] == 1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f64"])
+def test_skinny_class(dtype):
+    """Groups with at most 16 output rows or columns stream through the skinny tile."""
+    con, _, _, _ = _single(1300, 20, 16, dtype, True, True, 0, 1, 0)
+    assert bst.Plan(con).stats()["items_by_class"]["skinny"] == 6      # 256 rows per tile
+    con, _, _, _ = _single(7, 20, 600, dtype, True, True, 0, 1, 0)
+    assert bst.Plan(con).stats()["items_by_class"]["skinny"] == 3

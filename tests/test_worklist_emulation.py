@@ -21,10 +21,12 @@ DFAST = np.dtype([(n, "<i8") for n in ("a_base", "a_rs", "b_base", "b_s", "c_bas
 G_C_ALONG_N, G_ACCUMULATE = 1, 2
 T_GENERIC, T_MFMA, T_TAIL, T_ZERO = 0, 1, 2, 3
 TILE = {T_GENERIC: (64, 64), T_ZERO: (64, 64), T_MFMA: (128, 128), 4: (128, 128), 5: (128, 128)}
+TILE_MFMA_F = (64, 64)   # fp32 / fp64 matrix-core tile
 
 assert DVIEW.itemsize == 56 and DGROUP.itemsize == 32 and DRUN.itemsize == 32 and DTASK.itemsize == 16
 assert DFAST.itemsize == 72
 T_DENSE_N, T_DENSE_K = 4, 5
+T_SKINNY_M, T_SKINNY_N = 7, 8    # long axis M (at most 16 columns) / long axis N (at most 16 rows)
 
 
 def decode(plan):
@@ -77,7 +79,12 @@ def replay(plan, con, a, b, c0, accumulate=False):
             np.add.at(written, cad.ravel(), 1)
             continue
         g = groups[t["group"]]
-        TM, TN = TILE[int(t["cls"])]
+        if t["cls"] == T_SKINNY_M:
+            TM, TN = 256, max(1, int(g["N"]))
+        elif t["cls"] == T_SKINNY_N:
+            TM, TN = max(1, int(g["M"])), 256
+        else:
+            TM, TN = TILE_MFMA_F if (t["cls"] == T_MFMA and con.dtype != "bf16") else TILE[int(t["cls"])]
         m0, n0 = int(t["m0"]), int(t["n0"])
         assert 0 <= m0 < g["M"] and 0 <= n0 < g["N"]
         rows = np.arange(m0, min(m0 + TM, g["M"]))

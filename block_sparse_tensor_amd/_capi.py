@@ -50,7 +50,9 @@ class BscStats(ctypes.Structure):
 class BscWorklistInfo(ctypes.Structure):
     _fields_ = [(n, c_int64) for n in ("n_groups", "n_runs", "n_apieces", "n_bpieces", "n_cpieces", "n_tasks",
                                         "n_dense", "off_groups", "off_runs", "off_apieces", "off_bpieces",
-                                        "off_cpieces", "off_tasks", "off_dense", "bytes", "n_launches")]
+                                        "off_cpieces", "off_tasks", "off_dense", "n_packs", "n_pack_tasks",
+                                        "off_packs", "off_pack_tasks", "off_workspace", "workspace_elems",
+                                        "bytes", "n_launches")]
 
 
 _lib = None

@@ -139,8 +139,14 @@ bsc_status bsc_plan_worklist(bsc_plan_t plan, bsc_worklist_info *info, void *ima
     info->off_cpieces = (int64_t)p->off_cp;
     info->off_tasks = (int64_t)p->off_tasks;
     info->off_dense = (int64_t)p->off_fast;
+    info->n_packs = (int64_t)p->packs.size();
+    info->n_pack_tasks = (int64_t)p->pack_tasks.size();
+    info->off_packs = (int64_t)p->off_packs;
+    info->off_pack_tasks = (int64_t)p->off_ptasks;
+    info->off_workspace = (int64_t)p->off_ws;
+    info->workspace_elems = p->ws_elems;
     info->bytes = (int64_t)p->image.size();
-    info->n_launches = (int64_t)p->launches.size();
+    info->n_launches = (int64_t)p->launches.size() + (p->packs.empty() ? 0 : 1);
     if (image) {
         if (bytes < p->image.size()) {
             set_error("bsc_plan_worklist: image buffer too small");

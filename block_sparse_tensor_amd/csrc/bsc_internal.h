@@ -59,6 +59,8 @@ enum : int32_t {
     R_A_VEC = 16,        // A: K-unit, every row start 16-byte aligned (16-byte loads along K)
     R_B_VECK = 32,       // B: K-unit, every column start 16-byte aligned
     R_B_VECN = 64,       // B: one N-unit piece, K rows 16-byte aligned, rows readable to a multiple of 8
+    R_A_WS = 128,        // A pieces address the pack workspace (a gathered copy), not A
+    R_B_WS = 256,        // B pieces address the pack workspace, not B
 };
 
 struct DRun {
@@ -102,9 +104,31 @@ struct DFast {
     int64_t a_base, a_rs;
     int64_t b_base, b_s;
     int64_t c_base, c_rs, c_cs;
-    int32_t mlen, nlen, K, flags;   // flags: G_ACCUMULATE
+    int32_t mlen, nlen, K, flags;   // flags: G_ACCUMULATE, F_A_WS, F_B_WS
+    int32_t group, pad;             // the tile's group (for the general tile when this one is not compiled in)
 };
-static_assert(sizeof(DFast) == 72, "DFast layout");
+enum : int32_t { F_A_WS = 4, F_B_WS = 8 };   // DFast operand read from the pack workspace
+static_assert(sizeof(DFast) == 80, "DFast layout");
+
+// One gather of the pack kernel (uni20 "block coalescing", section
+// "Interleaved vs contiguous — the real tradeoff is a copy": members that do not
+// line up are copied once into a contiguous operand).  `rows` x `cols` elements
+// of a strided source view — axis a = the group's free axis, axis b = k —
+// land in the workspace at dst + x * ld + y, so every packed operand is
+// k-contiguous with a constant leading dimension.
+struct DPack {
+    int64_t off, sa0, sa1, sb0, sb1;   // source view, element (x, y) as in DView
+    int64_t dst;                        // workspace element of (0, 0)
+    int32_t ia, ib;
+    int32_t rows, cols;                 // extents along a and b
+    int32_t ld;                         // workspace leading dimension (elements)
+    int32_t src;                        // 0: the A buffer, 1: the B buffer
+};
+static_assert(sizeof(DPack) == 72, "DPack layout");
+constexpr int TILE_PACK = 64;           // a pack task copies up to 64 x 64 elements
+// Output tiles in flight at once on MI355X (256 CUs x two resident 256-thread
+// workgroups); the planner's cost model divides per-tile costs by it.
+constexpr double CONCURRENT_TILES = 512.0;
 
 struct DTask {
     int32_t cls;
@@ -160,12 +184,16 @@ struct Plan {
     std::vector<DView> apieces, bpieces, cpieces;
     std::vector<DTask> tasks;
     std::vector<DFast> fast;      // records of dense matrix-core tiles
+    std::vector<DPack> packs;     // gathers into the pack workspace
+    std::vector<DTask> pack_tasks;   // 64 x 64 pieces of the gathers (group = gather index)
+    int64_t ws_elems = 0;         // pack workspace size (operand elements)
     std::vector<std::array<int32_t, 2>> launches;  // per-sector mode: task ranges, one launch each
 
     // device binding
     void *dev = nullptr;
     size_t dev_bytes = 0;
     size_t off_groups = 0, off_runs = 0, off_ap = 0, off_bp = 0, off_cp = 0, off_tasks = 0, off_fast = 0;
+    size_t off_packs = 0, off_ptasks = 0, off_ws = 0;   // gathers, their tasks, the workspace
     std::vector<unsigned char> image;   // host copy of the device tables
     int32_t cu_count = 0;
     int32_t grid = 0;

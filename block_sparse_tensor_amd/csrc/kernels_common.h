@@ -20,7 +20,18 @@ struct KArgs {
     const DFast *fast;
     const void *A, *B;
     void *C;
+    const void *W;          // pack workspace (operands of runs flagged R_A_WS / R_B_WS)
 };
+
+// Buffer a run's A (B) pieces address: the caller's operand or the workspace.
+template <typename T>
+__device__ __forceinline__ const T *run_a(const KArgs &ka, int32_t run_flags) {
+    return static_cast<const T *>((run_flags & R_A_WS) ? ka.W : ka.A);
+}
+template <typename T>
+__device__ __forceinline__ const T *run_b(const KArgs &ka, int32_t run_flags) {
+    return static_cast<const T *>((run_flags & R_B_WS) ? ka.W : ka.B);
+}
 
 // Address function along the non-piece axis of one row/column of a piece.
 struct Rec {

@@ -28,8 +28,6 @@ __device__ void generic_tile(const KArgs &ka, const DTask &task, GenericSmem<ACC
     const int32_t m0 = task.m0, n0 = task.n0;
     const int32_t mlen = min(64, g.M - m0), nlen = min(64, g.N - n0);
     const int32_t tx = tid & 15, ty = tid >> 4;
-    const TA *A = static_cast<const TA *>(ka.A);
-    const TA *B = static_cast<const TA *>(ka.B);
 
     ACC acc[4][4];
 #pragma unroll
@@ -47,6 +45,8 @@ __device__ void generic_tile(const KArgs &ka, const DTask &task, GenericSmem<ACC
             if (j < nlen) sm.rb[j] = make_rec(ka.bp + run.bp0, run.nbp, n0 + j);
         }
         __syncthreads();
+        const TA *A = run_a<TA>(ka, run.flags);
+        const TA *B = run_b<TA>(ka, run.flags);
         const bool a_k = (run.flags & R_A_KUNIT) != 0;
         const bool b_k = (run.flags & R_B_KUNIT) != 0;
         for (int32_t k0 = 0; k0 < run.K; k0 += 16) {

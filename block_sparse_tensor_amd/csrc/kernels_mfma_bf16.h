@@ -196,12 +196,11 @@ __device__ __forceinline__ OpCtx mb_ctx(const DView *pieces, int32_t np, int32_t
 
 template <typename TC>
 __device__ void mfma_tile_bf16(const KArgs &ka, const DTask &task, MfmaSmemBf16 &sm) {
-    const DGroup g = ka.groups[task.group];
+    // a dense-tile task (its direct-to-LDS body not compiled into this launch) names its group through its record
+    const DGroup g = ka.groups[task.cls == T_MFMA ? task.group : ka.fast[task.group].group];
     const int32_t tid = threadIdx.x;
     const int32_t m0 = task.m0, n0 = task.n0;
     const int32_t mlen = min(MB_BM, g.M - m0), nlen = min(MB_BN, g.N - n0);
-    const uint16_t *A = static_cast<const uint16_t *>(ka.A);
-    const uint16_t *B = static_cast<const uint16_t *>(ka.B);
 
     f32x16_t acc[2][2];
 #pragma unroll
@@ -221,8 +220,11 @@ __device__ void mfma_tile_bf16(const KArgs &ka, const DTask &task, MfmaSmemBf16 
             if (j < nlen) sm.rb[j] = make_rec(ka.bp + run.bp0, run.nbp, n0 + j);
         }
         __syncthreads();
-        const OpCtx oa = mb_ctx(ka.ap + run.ap0, run.nap, R_A_KUNIT, R_A_FUNIT, run.flags, m0, mlen, run.K, A, ka.vec_a, sm.ra);
-        const OpCtx ob = mb_ctx(ka.bp + run.bp0, run.nbp, R_B_KUNIT, R_B_FUNIT, run.flags, n0, nlen, run.K, B, ka.vec_b, sm.rb);
+        const int32_t va = (run.flags & R_A_WS) ? 1 : ka.vec_a, vb = (run.flags & R_B_WS) ? 1 : ka.vec_b;
+        const OpCtx oa = mb_ctx(ka.ap + run.ap0, run.nap, R_A_KUNIT, R_A_FUNIT, run.flags, m0, mlen, run.K,
+                                run_a<uint16_t>(ka, run.flags), va, sm.ra);
+        const OpCtx ob = mb_ctx(ka.bp + run.bp0, run.nbp, R_B_KUNIT, R_B_FUNIT, run.flags, n0, nlen, run.K,
+                                run_b<uint16_t>(ka, run.flags), vb, sm.rb);
         const int32_t nchunks = (run.K + MB_BK - 1) / MB_BK;
         MbStage sa, sb;
         mb_load(oa, 0, sa);

@@ -226,8 +226,6 @@ __device__ void mfma_tile_f(const KArgs &ka, const DTask &task, MfmaSmemF<T> &sm
     const int32_t tid = threadIdx.x;
     const int32_t m0 = task.m0, n0 = task.n0;
     const int32_t mlen = min(MF_TILE, g.M - m0), nlen = min(MF_TILE, g.N - n0);
-    const T *A = static_cast<const T *>(ka.A);
-    const T *B = static_cast<const T *>(ka.B);
 
     acc_t acc[2][2];
 #pragma unroll
@@ -247,10 +245,11 @@ __device__ void mfma_tile_f(const KArgs &ka, const DTask &task, MfmaSmemF<T> &sm
             if (j < nlen) sm.rb[j] = make_rec(ka.bp + run.bp0, run.nbp, n0 + j);
         }
         __syncthreads();
-        const MfCtx<T> oa = mf_ctx<T>(ka.ap + run.ap0, run.nap, R_A_KUNIT, R_A_FUNIT, run.flags, m0, mlen, run.K, A,
-                                      ka.vec_a, sm.ra);
-        const MfCtx<T> ob = mf_ctx<T>(ka.bp + run.bp0, run.nbp, R_B_KUNIT, R_B_FUNIT, run.flags, n0, nlen, run.K, B,
-                                      ka.vec_b, sm.rb);
+        const int32_t va = (run.flags & R_A_WS) ? 1 : ka.vec_a, vb = (run.flags & R_B_WS) ? 1 : ka.vec_b;
+        const MfCtx<T> oa = mf_ctx<T>(ka.ap + run.ap0, run.nap, R_A_KUNIT, R_A_FUNIT, run.flags, m0, mlen, run.K,
+                                      run_a<T>(ka, run.flags), va, sm.ra);
+        const MfCtx<T> ob = mf_ctx<T>(ka.bp + run.bp0, run.nbp, R_B_KUNIT, R_B_FUNIT, run.flags, n0, nlen, run.K,
+                                      run_b<T>(ka, run.flags), vb, sm.rb);
         const int32_t nchunks = (run.K + KC - 1) / KC;
         MfStage<T> sa, sb;
         mf_load(oa, 0, sa);

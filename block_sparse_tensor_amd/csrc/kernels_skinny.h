@@ -38,8 +38,6 @@ __device__ void skinny_tile(const KArgs &ka, const DTask &task, SkinnySmem<ACC> 
     const int32_t X = LONG_M ? g.M : g.N;
     const int32_t Y = LONG_M ? g.N : g.M;
     const int32_t xlen = min(SK_LONG, X - x0);
-    const TA *Pl = static_cast<const TA *>(LONG_M ? ka.A : ka.B);
-    const TA *Ps = static_cast<const TA *>(LONG_M ? ka.B : ka.A);
 
     ACC acc[SK_PER][SK_SHORT];
 #pragma unroll
@@ -53,6 +51,8 @@ __device__ void skinny_tile(const KArgs &ka, const DTask &task, SkinnySmem<ACC> 
         const DView *sp = LONG_M ? ka.bp + run.bp0 : ka.ap + run.ap0;
         const int32_t nl = LONG_M ? run.nap : run.nbp;
         const int32_t ns = LONG_M ? run.nbp : run.nap;
+        const TA *Pl = LONG_M ? run_a<TA>(ka, run.flags) : run_b<TA>(ka, run.flags);
+        const TA *Ps = LONG_M ? run_b<TA>(ka, run.flags) : run_a<TA>(ka, run.flags);
         Rec rl[SK_PER];
 #pragma unroll
         for (int q = 0; q < SK_PER; ++q) {

@@ -508,6 +508,102 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         p.cpieces.clear();
         p.group_mode.clear();
         const int64_t LIM = (int64_t(1) << 31) - 1;
+        p.packs.clear();
+        p.pack_tasks.clear();
+        p.ws_elems = 0;
+
+        // Whether an operand of a group, as per-k-segment piece lists, is one
+        // strided view over the group's whole free x contracted extent.
+        auto one_view = [&](const std::vector<std::vector<DView>> &seg, const std::vector<int64_t> &segK) {
+            DView v{};
+            int64_t kk = 0;
+            for (size_t s = 0; s < seg.size(); ++s) {
+                if (seg[s].size() != 1) return false;
+                if (s == 0) v = seg[s][0];
+                else if (!merge_along_b(v, kk, seg[s][0], segK[s])) return false;
+                kk += segK[s];
+            }
+            return true;
+        };
+        // Pack-cost-versus-savings model (uni20 "block coalescing", section
+        // "Interleaved vs contiguous — the real tradeoff is a copy", and the
+        // launch-cost crossover of its open questions).  All times are whole-GPU
+        // microseconds.  Gathering operand X of a group costs its traffic,
+        // 2 * bytes / pack_gbps (read once, written once).  It saves, on each of
+        // the group's output tiles, the set-up of every piece beyond one per
+        // k-segment (t_seg_us each; tiles run CONCURRENT_TILES at a time), and
+        // the matrix-core K-step padding of the k-segments it fuses
+        // (pad flops / tile_gflops).  The one extra launch a plan with gathers
+        // needs is charged afterwards, against the sum over all packed operands.
+        const double concurrent = CONCURRENT_TILES;
+        const int64_t esz = p.dtype == BSC_F64 ? 8 : (p.dtype == BSC_F32 ? 4 : 2);
+        const int64_t kq = p.dtype == BSC_BF16_F32 ? 16 : 4;     // matrix-core K step
+        double pack_net_us = 0;                                   // sum of savings - gather costs
+        auto decide_pack = [&](const DGroup &dg, const std::vector<std::vector<DView>> &seg,
+                               const std::vector<int64_t> &segK, bool is_a) -> bool {
+            if (p.opt.layout_policy == BSC_LAYOUT_NEVER_PACK) return false;
+            if (one_view(seg, segK)) return false;   // already zero-copy and single-view
+            if (p.opt.layout_policy == BSC_LAYOUT_FORCE_PACK) return true;
+            const int64_t free = is_a ? dg.M : dg.N;
+            const int64_t other = is_a ? dg.N : dg.M;
+            const int64_t T = p.dtype == BSC_BF16_F32 ? TILE_MFMA : TILE_MFMA_F;
+            const int64_t tiles = ((dg.M + T - 1) / T) * ((dg.N + T - 1) / T);
+            int64_t pieces = 0, pad = 0;
+            for (size_t s = 0; s < seg.size(); ++s) {
+                pieces += (int64_t)seg[s].size();
+                pad += (segK[s] + kq - 1) / kq * kq - segK[s];
+            }
+            const int64_t pad_after = ((int64_t)dg.K + kq - 1) / kq * kq - dg.K;
+            const double extra = (double)(pieces - 1);
+            const double gain = (double)tiles * extra * p.opt.t_seg_us / concurrent +
+                                2.0 * (double)free * (double)other * (double)std::max<int64_t>(0, pad - pad_after) /
+                                    (p.opt.tile_gflops * 1e3);
+            const double cost = 2.0 * (double)(free * dg.K * esz) / (p.opt.pack_gbps * 1e3);
+            if (gain <= cost) return false;
+            pack_net_us += gain - cost;
+            return true;
+        };
+        // Gather an operand into a fresh workspace region: [free][ld] with
+        // ld = K rounded up to 8 elements (16-byte rows for every dtype), so the
+        // packed operand is one k-contiguous view.  Returns the new per-segment
+        // pieces (one workspace piece per k-segment).
+        auto pack_operand = [&](const std::vector<std::vector<DView>> &seg, const std::vector<int64_t> &segK,
+                                int64_t free, int64_t K, int32_t src) {
+            const int64_t ld = (K + 7) / 8 * 8;
+            if (ld > LIM) fail(BSC_ERR_UNSUPPORTED, "a packed operand's leading dimension exceeds 2^31-1");
+            const int64_t base = (p.ws_elems + 63) / 64 * 64;
+            p.ws_elems = base + free * ld;
+            std::vector<std::vector<DView>> out(seg.size());
+            int64_t kb = 0;
+            for (size_t s = 0; s < seg.size(); ++s) {
+                for (const DView &v : seg[s]) {
+                    DPack d{};
+                    d.off = v.off;
+                    d.sa0 = v.sa0; d.sa1 = v.sa1; d.ia = v.ia;
+                    d.sb0 = v.sb0; d.sb1 = v.sb1; d.ib = v.ib;
+                    d.rows = v.len;
+                    d.cols = (int32_t)segK[s];
+                    d.dst = base + (int64_t)v.begin * ld + kb;
+                    d.ld = (int32_t)ld;
+                    d.src = src;
+                    const int32_t gi = (int32_t)p.packs.size();
+                    p.packs.push_back(d);
+                    for (int32_t x0 = 0; x0 < d.rows; x0 += TILE_PACK)
+                        for (int32_t y0 = 0; y0 < d.cols; y0 += TILE_PACK) p.pack_tasks.push_back({0, gi, x0, y0});
+                }
+                DView w{};
+                w.off = base + kb;
+                w.sa0 = free > 1 ? ld : 0;
+                w.sb0 = segK[s] > 1 ? 1 : 0;
+                w.ia = w.ib = 1;
+                w.begin = 0;
+                w.len = (int32_t)free;
+                out[s].push_back(w);
+                kb += segK[s];
+            }
+            return out;
+        };
+
         for (auto &g : specs) {
             DGroup dg{};
             int64_t M = 0, N = 0, K = 0;
@@ -537,6 +633,11 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                 segB.push_back(stack(bm));
                 segK.push_back(p.dk[kk]);
             }
+            // operand arrangement: the zero-copy pieces, or one gather into the workspace
+            const bool pack_a = !per_sector && decide_pack(dg, segA, segK, true);
+            const bool pack_b = !per_sector && decide_pack(dg, segB, segK, false);
+            if (pack_a) segA = pack_operand(segA, segK, dg.M, dg.K, 0);
+            if (pack_b) segB = pack_operand(segB, segK, dg.N, dg.K, 1);
             // merge consecutive segments into runs while both operands continue as one view
             dg.run0 = (int32_t)p.runs.size();
             bool a_view = true, b_view = true;
@@ -564,7 +665,9 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                 r.ap0 = (int32_t)p.apieces.size();
                 r.nbp = (int32_t)rb.size();
                 r.bp0 = (int32_t)p.bpieces.size();
-                r.flags = run_flags(ra, rb, rk, p.b_elems);
+                r.flags = run_flags(ra, rb, rk, pack_b ? p.ws_elems : p.b_elems);
+                if (pack_a) r.flags |= R_A_WS;
+                if (pack_b) r.flags |= R_B_WS;
                 a_view = a_view && ra.size() == 1;
                 b_view = b_view && rb.size() == 1;
                 p.apieces.insert(p.apieces.end(), ra.begin(), ra.end());
@@ -589,7 +692,8 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             if (along_n) dg.flags |= G_C_ALONG_N;
             p.cpieces.insert(p.cpieces.end(), cp.begin(), cp.end());
             p.groups.push_back(dg);
-            p.group_mode.push_back({a_view ? BSC_MODE_VIEW : BSC_MODE_SEGMENTS, b_view ? BSC_MODE_VIEW : BSC_MODE_SEGMENTS,
+            p.group_mode.push_back({pack_a ? BSC_MODE_PACK : a_view ? BSC_MODE_VIEW : BSC_MODE_SEGMENTS,
+                                    pack_b ? BSC_MODE_PACK : b_view ? BSC_MODE_VIEW : BSC_MODE_SEGMENTS,
                                     cp.size() == 1 ? BSC_MODE_VIEW : BSC_MODE_SEGMENTS});
         }
         p.n_work_groups = (int32_t)p.groups.size();
@@ -665,7 +769,9 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                         f.mlen = std::min(TM, g.M - m0);
                         f.nlen = std::min(TN, g.N - n0);
                         f.K = r.K;
-                        f.flags = g.flags & G_ACCUMULATE;
+                        f.group = gi;
+                        f.flags = (g.flags & G_ACCUMULATE) | ((r.flags & R_A_WS) ? F_A_WS : 0) |
+                                  ((r.flags & R_B_WS) ? F_B_WS : 0);
                         out.push_back({cls, (int32_t)p.fast.size(), m0, n0});
                         p.fast.push_back(f);
                     } else {
@@ -740,7 +846,13 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             while (!p.tasks.empty() && p.tasks.back().cls == T_NOP) p.tasks.pop_back();
             if (!p.tasks.empty()) p.launches.push_back({0, (int32_t)p.tasks.size()});
         }
-        if (p.tasks.size() > (size_t)LIM) fail(BSC_ERR_UNSUPPORTED, "too many work items");
+        if (p.tasks.size() > (size_t)LIM || p.pack_tasks.size() > (size_t)LIM)
+            fail(BSC_ERR_UNSUPPORTED, "too many work items");
+        // a plan with gathers needs one more launch: keep them only if they pay for it
+        if (!p.packs.empty() && p.opt.layout_policy == BSC_LAYOUT_AUTO && pack_net_us <= p.opt.t_launch_us) {
+            p.opt.layout_policy = BSC_LAYOUT_NEVER_PACK;
+            return build_plan(p, m, k, n, A, B, C);
+        }
 
         // ---- device image --------------------------------------------------------------
         auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -752,8 +864,11 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         p.off_cp = off;     off = align(off + p.cpieces.size() * sizeof(DView));
         p.off_tasks = off;  off = align(off + p.tasks.size() * sizeof(DTask));
         p.off_fast = off;   off = align(off + p.fast.size() * sizeof(DFast));
-        p.dev_bytes = std::max<size_t>(off, 256);
-        p.image.assign(p.dev_bytes, 0);
+        p.off_packs = off;  off = align(off + p.packs.size() * sizeof(DPack));
+        p.off_ptasks = off; off = align(off + p.pack_tasks.size() * sizeof(DTask));
+        p.image.assign(std::max<size_t>(off, 256), 0);
+        p.off_ws = p.image.size();
+        p.dev_bytes = p.off_ws + (size_t)(p.ws_elems * esz);
         auto put = [&](size_t o, const void *src, size_t nbytes) { if (nbytes) std::memcpy(p.image.data() + o, src, nbytes); };
         put(p.off_groups, p.groups.data(), p.groups.size() * sizeof(DGroup));
         put(p.off_runs, p.runs.data(), p.runs.size() * sizeof(DRun));
@@ -762,6 +877,8 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         put(p.off_cp, p.cpieces.data(), p.cpieces.size() * sizeof(DView));
         put(p.off_tasks, p.tasks.data(), p.tasks.size() * sizeof(DTask));
         put(p.off_fast, p.fast.data(), p.fast.size() * sizeof(DFast));
+        put(p.off_packs, p.packs.data(), p.packs.size() * sizeof(DPack));
+        put(p.off_ptasks, p.pack_tasks.data(), p.pack_tasks.size() * sizeof(DTask));
 
         // ---- statistics ---------------------------------------------------------------
         bsc_stats &s = p.stats;
@@ -788,7 +905,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             if (t.cls == T_MFMA_FAST_N) p.features |= FEAT_FAST_N;
             if (t.cls == T_MFMA_FAST_K) p.features |= FEAT_FAST_K;
         }
-        s.launches_per_contract = (int64_t)p.launches.size();
+        s.launches_per_contract = (int64_t)p.launches.size() + (p.packs.empty() ? 0 : 1);
         s.launches_per_sector = s.triples + (zero_c.empty() ? 0 : 1);
         s.useful_flops = flops;
         const int64_t ab = p.dtype == BSC_F64 ? 8 : (p.dtype == BSC_F32 ? 4 : 2);
@@ -799,11 +916,13 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         for (auto &b : p.C) ec += p.dm[b.r] * p.dn[b.c];
         s.alg_bytes = ab * (ea + eb) + cb * ec;
         s.pack_bytes = 0;
+        for (auto &d : p.packs) s.pack_bytes += (int64_t)d.rows * d.cols * ab;
         s.device_bytes = (int64_t)p.dev_bytes;
         s.tail_triples = tail;
         const double rate_gflops = p.dtype == BSC_BF16_F32 ? 2.5e6 : (p.dtype == BSC_F32 ? 157.3e3 : 78.6e3);
         s.predicted_us = s.launches_per_contract * p.opt.t_launch_us +
-                         std::max((double)flops / (rate_gflops * 1e3), (double)s.alg_bytes / 8.0e6);
+                         std::max((double)flops / (rate_gflops * 1e3), (double)s.alg_bytes / 8.0e6) +
+                         2.0 * (double)s.pack_bytes / (p.opt.pack_gbps * 1e3);
         return BSC_OK;
     } catch (const Fail &f) {
         return f.st;

@@ -18,6 +18,7 @@
 #include "kernels_mfma_bf16.h"
 #include "kernels_mfma_bf16_fast.h"
 #include "kernels_mfma_f.h"
+#include "kernels_pack.h"
 #include "kernels_skinny.h"
 
 namespace bsc {
@@ -156,7 +157,7 @@ extern "C" bsc_status bsc_plan_bind(bsc_plan_t plan, void *dev, size_t bytes, vo
     int cus = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev_id);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    e = hipMemcpyAsync(dev, p->image.data(), p->dev_bytes, hipMemcpyHostToDevice, s);
+    e = hipMemcpyAsync(dev, p->image.data(), p->image.size(), hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (work list upload)");
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (work list upload)");
@@ -195,6 +196,26 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
     ka.A = A;
     ka.B = B;
     ka.C = C;
+    ka.W = base + p->off_ws;
+    if (!p->pack_tasks.empty()) {
+        // gathers first, on the same stream: the grouped launch reads the workspace after them
+        PArgs pa;
+        pa.packs = reinterpret_cast<const DPack *>(base + p->off_packs);
+        pa.tasks = reinterpret_cast<const DTask *>(base + p->off_ptasks);
+        pa.ntasks = (int32_t)p->pack_tasks.size();
+        pa.pad = 0;
+        pa.A = A;
+        pa.B = B;
+        pa.W = const_cast<unsigned char *>(base) + p->off_ws;
+        const int32_t cap = std::max(1, p->cu_count) * 8;
+        dim3 grid((unsigned)std::max(1, std::min(pa.ntasks, cap))), block(256);
+        switch (p->dtype) {
+            case BSC_F64: hipLaunchKernelGGL(pack_gather<double>, grid, block, 0, s, pa); break;
+            case BSC_F32: hipLaunchKernelGGL(pack_gather<float>, grid, block, 0, s, pa); break;
+            case BSC_BF16_F32: hipLaunchKernelGGL(pack_gather<uint16_t>, grid, block, 0, s, pa); break;
+        }
+        p->stats.launches_issued++;
+    }
     ka.vec_a = (reinterpret_cast<uintptr_t>(A) % 16) == 0;
     ka.vec_b = (reinterpret_cast<uintptr_t>(B) % 16) == 0;
     for (auto &l : p->launches) {

@@ -207,6 +207,10 @@ bsc_status bsc_plan_export(bsc_plan_t plan, int32_t *triples, int32_t *group_of_
 typedef struct {
     int64_t n_groups, n_runs, n_apieces, n_bpieces, n_cpieces, n_tasks, n_dense;
     int64_t off_groups, off_runs, off_apieces, off_bpieces, off_cpieces, off_tasks, off_dense;
+    int64_t n_packs, n_pack_tasks;   /* gathers into the pack workspace and their work items */
+    int64_t off_packs, off_pack_tasks;
+    int64_t off_workspace;   /* byte offset of the pack workspace in the device region (after the image) */
+    int64_t workspace_elems; /* pack workspace size in operand elements */
     int64_t bytes;           /* size of the work-list image */
     int64_t n_launches;      /* launches per contraction */
 } bsc_worklist_info;

@@ -17,14 +17,18 @@ DGROUP = np.dtype([(n, "<i4") for n in ("M", "N", "K", "nrun", "run0", "ncp", "c
 DRUN = np.dtype([(n, "<i4") for n in ("K", "nap", "ap0", "nbp", "bp0", "flags", "kbase", "pad")])
 DTASK = np.dtype([(n, "<i4") for n in ("cls", "group", "m0", "n0")])
 DFAST = np.dtype([(n, "<i8") for n in ("a_base", "a_rs", "b_base", "b_s", "c_base", "c_rs", "c_cs")] +
-                 [(n, "<i4") for n in ("mlen", "nlen", "K", "flags")])
+                 [(n, "<i4") for n in ("mlen", "nlen", "K", "flags", "group", "pad")])
+DPACK = np.dtype([(n, "<i8") for n in ("off", "sa0", "sa1", "sb0", "sb1", "dst")] +
+                 [(n, "<i4") for n in ("ia", "ib", "rows", "cols", "ld", "src")])
+R_A_WS, R_B_WS = 128, 256          # run reads A / B from the pack workspace
+F_A_WS, F_B_WS = 4, 8              # dense record reads A / B from the pack workspace
 G_C_ALONG_N, G_ACCUMULATE = 1, 2
 T_GENERIC, T_MFMA, T_TAIL, T_ZERO = 0, 1, 2, 3
 TILE = {T_GENERIC: (64, 64), T_ZERO: (64, 64), T_MFMA: (128, 128), 4: (128, 128), 5: (128, 128)}
 TILE_MFMA_F = (64, 64)   # fp32 / fp64 matrix-core tile
 
 assert DVIEW.itemsize == 56 and DGROUP.itemsize == 32 and DRUN.itemsize == 32 and DTASK.itemsize == 16
-assert DFAST.itemsize == 72
+assert DFAST.itemsize == 80 and DPACK.itemsize == 72
 T_DENSE_N, T_DENSE_K = 4, 5
 T_SKINNY_M, T_SKINNY_N = 7, 8    # long axis M (at most 16 columns) / long axis N (at most 16 rows)
 
@@ -36,6 +40,36 @@ def decode(plan):
             tab(DVIEW, info["n_apieces"], info["off_apieces"]), tab(DVIEW, info["n_bpieces"], info["off_bpieces"]),
             tab(DVIEW, info["n_cpieces"], info["off_cpieces"]), tab(DTASK, info["n_tasks"], info["off_tasks"]),
             tab(DFAST, info["n_dense"], info["off_dense"]))
+
+
+def decode_packs(plan):
+    info, img = plan.worklist()
+    tab = lambda dt, n, off: np.frombuffer(img, dtype=dt, count=n, offset=off)
+    return info, tab(DPACK, info["n_packs"], info["off_packs"]), tab(DTASK, info["n_pack_tasks"], info["off_pack_tasks"])
+
+
+def replay_packs(plan, con, a64, b64):
+    """The gather launch: every pack task copies its 64 x 64 piece of a gather
+    from A or B into the workspace.  Every workspace element is written at most
+    once; returns the workspace and the mask of written elements."""
+    info, packs, ptasks = decode_packs(plan)
+    ws = np.full(info["workspace_elems"], np.nan)
+    hit = np.zeros(info["workspace_elems"], np.int64)
+    for t in ptasks:
+        d = packs[t["group"]]
+        x = np.arange(t["m0"], min(t["m0"] + 64, d["rows"]))
+        y = np.arange(t["n0"], min(t["n0"] + 64, d["cols"]))
+        assert len(x) and len(y)
+        src = d["off"] + (x[:, None] // d["ia"]) * d["sa0"] + (x[:, None] % d["ia"]) * d["sa1"] + \
+            (y[None, :] // d["ib"]) * d["sb0"] + (y[None, :] % d["ib"]) * d["sb1"]
+        buf = a64 if d["src"] == 0 else b64
+        assert src.min() >= 0 and src.max() < buf.size
+        dst = d["dst"] + x[:, None] * d["ld"] + y[None, :]
+        assert dst.min() >= 0 and dst.max() < ws.size
+        ws[dst] = buf[src]
+        np.add.at(hit, dst.ravel(), 1)
+    assert hit.max(initial=0) <= 1, "a workspace element is gathered twice"
+    return ws, hit > 0
 
 
 def rec_addr(pieces, x, y):
@@ -55,6 +89,7 @@ def replay(plan, con, a, b, c0, accumulate=False):
     c = np.array(c0, dtype=np.float64)
     written = np.zeros(c.size, np.int64)
     a64, b64 = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    ws, ws_written = replay_packs(plan, con, a64, b64)
     for t in tasks:
         if t["cls"] == 6:      # no-op placeholder
             continue
@@ -70,9 +105,14 @@ def replay(plan, con, a, b, c0, accumulate=False):
             else:
                 bad = f["b_base"] + j * f["b_s"] + k[:, None]
             cad = f["c_base"] + i * f["c_rs"] + j * f["c_cs"]
-            for ad, n in ((aad, con.A.buffer_elems), (bad, con.B.buffer_elems), (cad, con.C.buffer_elems)):
+            abuf = ws if f["flags"] & F_A_WS else a64
+            bbuf = ws if f["flags"] & F_B_WS else b64
+            for ad, n in ((aad, abuf.size), (bad, bbuf.size), (cad, con.C.buffer_elems)):
                 assert ad.min() >= 0 and ad.max() < n
-            acc = a64[aad] @ b64[bad]
+            for ad, flag in ((aad, F_A_WS), (bad, F_B_WS)):
+                if f["flags"] & flag:
+                    assert ws_written[ad].all(), "a tile reads a workspace element no gather wrote"
+            acc = abuf[aad] @ bbuf[bad]
             if f["flags"] & G_ACCUMULATE:
                 acc = acc + c[cad]
             c[cad] = acc
@@ -98,9 +138,14 @@ def replay(plan, con, a, b, c0, accumulate=False):
             ks = np.arange(run["K"])
             aad = rec_addr(ap[run["ap0"]:run["ap0"] + run["nap"]], rows, ks)
             bad = rec_addr(bp[run["bp0"]:run["bp0"] + run["nbp"]], cols, ks)
-            assert aad.min(initial=0) >= 0 and aad.max(initial=-1) < con.A.buffer_elems
-            assert bad.min(initial=0) >= 0 and bad.max(initial=-1) < con.B.buffer_elems
-            acc += a64[aad] @ b64[bad].T
+            abuf = ws if run["flags"] & R_A_WS else a64
+            bbuf = ws if run["flags"] & R_B_WS else b64
+            assert aad.min(initial=0) >= 0 and aad.max(initial=-1) < abuf.size
+            assert bad.min(initial=0) >= 0 and bad.max(initial=-1) < bbuf.size
+            for ad, flag in ((aad, R_A_WS), (bad, R_B_WS)):
+                if run["flags"] & flag:
+                    assert ws_written[ad].all(), "a tile reads a workspace element no gather wrote"
+            acc += abuf[aad] @ bbuf[bad].T
         assert kseen == g["K"]
         cps = cp[g["cp0"]:g["cp0"] + g["ncp"]]
         if g["flags"] & G_C_ALONG_N:
@@ -223,3 +268,35 @@ def test_replay_dense_random(seed):
         got, written = replay(plan, con, abuf, bbuf, c0)
         ref = oracle.contract(con, abuf, bbuf, c0, accumulate=acc)
         np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("axis", ["free_m", "free_n", "contract"])
+def test_replay_force_pack_random(seed, axis):
+    """Every scattered operand gathered into the workspace: the gathers cover
+    exactly what the tiles read, and the result is the oracle's."""
+    prob = C.random_problem(7000 + seed, nq=1 + seed % 2, nkeys=(6, 6, 6), maxdim=12, qrange=1,
+                            flux=[(0, 0), (1, -1), (1, 0)][seed % 3], density=0.8)
+    plan = bst.Plan(prob.con, axis=axis, layout="force_pack")
+    c0 = np.full(prob.con.C.buffer_elems, -3.5)
+    got, written = replay(plan, prob.con, prob.a, prob.b, c0)
+    ref = oracle.contract(prob.con, prob.a, prob.b, c0)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    s = plan.stats()
+    modes = s["mode_count"]
+    assert modes["A"]["segments"] == 0 and modes["B"]["segments"] == 0
+    if modes["A"]["pack"] + modes["B"]["pack"]:
+        assert s["launches_per_contract"] == 2 and s["pack_bytes"] > 0
+
+
+@pytest.mark.parametrize("layout", ["force_pack", "auto"])
+def test_replay_pack_natural_chain(layout):
+    """The natural-layout environment update with gathers, stage by stage."""
+    ch = C.small_chain(seed=4, layout="natural")
+    bufs = {k: np.asarray(v, np.float64) for k, v in ch.buffers.items()}
+    ref = oracle.run_chain(ch)
+    for st in ch.stages:
+        plan = bst.Plan(st.con, layout=layout)
+        got, written = replay(plan, st.con, bufs[st.a_buf], bufs[st.b_buf], np.zeros(ch.sizes[st.c_buf]))
+        np.testing.assert_allclose(got, ref[st.c_buf], rtol=1e-12, atol=1e-12)
+        bufs[st.c_buf] = got

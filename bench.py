@@ -100,6 +100,8 @@ def main():
                          "elements; 8 = 16-byte aligned rows (default), 1 = unpadded contiguous blocks")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (counter calibration) and exit")
+    ap.add_argument("--layout", default="auto", choices=["auto", "never_pack", "force_pack"],
+                    help="operand arrangement policy of the grouped plans (auto = the planner's pack-cost model)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -140,7 +142,8 @@ def main():
             bufs[k] = torch.zeros(n, dtype=cdt, device="cuda")
 
     def plans_for(mode):
-        return [bst.Plan(con, axis=ax, launch_mode=mode).bind() for con, _, _, _, ax in stages]
+        layout = args.layout if mode == "grouped" else "never_pack"
+        return [bst.Plan(con, axis=ax, launch_mode=mode, layout=layout).bind() for con, _, _, _, ax in stages]
 
     def step(plans):
         for p, (_, a, b, c, _) in zip(plans, stages):
@@ -220,7 +223,8 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "stages": len(stages),
-                   "ld_align": args.ld_align,
+                   "ld_align": args.ld_align, "layout": args.layout,
+                   "pack_bytes": sum(s["pack_bytes"] for s in st),
                    "sector_gemms": sum(s["triples"] for s in st), "useful_flops": flops,
                    "alg_bytes": alg_bytes, "parallelism": "single GPU"},
         "pct_mfma_peak": round(100.0 * value / (peak * 1e3), 3),

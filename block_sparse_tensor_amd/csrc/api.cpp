@@ -28,12 +28,21 @@ void bsc_options_default(bsc_options *opt) {
     opt->grid_limit = 0;
 }
 
-static void fill_cost_defaults(bsc_options &o) {
-    // MI355X defaults; calibrated constants may be passed in instead
+static void fill_cost_defaults(bsc_options &o, bsc_dtype dt) {
+    // MI355X defaults, measured on one MI355X with this library (calibrated
+    // constants may be passed in instead):
+    //   t_launch_us  back-to-back launches of small grouped kernels, 3.6-6 us each;
+    //   pack_gbps    the gather kernel moved 2 x 29.6 MB in 23.5 us (2.5 TB/s)
+    //                on the natural-layout environment update;
+    //   tile_gflops  sustained whole-GPU rate of the matrix-core tiles on
+    //                mid-sized sector GEMMs (bf16 ~ 250 TFLOP/s, fp32 and fp64
+    //                ~ 10 TFLOP/s);
+    //   t_seg_us     per extra piece walked by one tile (record set-up and a
+    //                pipeline restart), an estimate.
     if (o.t_launch_us <= 0) o.t_launch_us = 4.0;
     if (o.t_seg_us <= 0) o.t_seg_us = 0.05;
-    if (o.pack_gbps <= 0) o.pack_gbps = 4000.0;
-    if (o.tile_gflops <= 0) o.tile_gflops = 2000.0;
+    if (o.pack_gbps <= 0) o.pack_gbps = 2500.0;
+    if (o.tile_gflops <= 0) o.tile_gflops = dt == BSC_BF16_F32 ? 250000.0 : 10000.0;
 }
 
 bsc_status bsc_plan(const bsc_index *m, const bsc_index *k, const bsc_index *n, const bsc_operand *A,
@@ -70,7 +79,7 @@ bsc_status bsc_plan(const bsc_index *m, const bsc_index *k, const bsc_index *n, 
         set_error("bsc_plan: bad layout policy or grid limit");
         return BSC_ERR_ARG;
     }
-    fill_cost_defaults(p->opt);
+    fill_cost_defaults(p->opt, dtype);
     p->dtype = dtype;
     p->axis = axis;
     bsc_status st = build_plan(*p, m, k, n, A, B, C);

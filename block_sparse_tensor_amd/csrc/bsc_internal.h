@@ -112,10 +112,11 @@ static_assert(sizeof(DFast) == 80, "DFast layout");
 
 // One gather of the pack kernel (uni20 "block coalescing", section
 // "Interleaved vs contiguous — the real tradeoff is a copy": members that do not
-// line up are copied once into a contiguous operand).  `rows` x `cols` elements
-// of a strided source view — axis a = the group's free axis, axis b = k —
-// land in the workspace at dst + x * ld + y, so every packed operand is
-// k-contiguous with a constant leading dimension.
+// line up are copied once into a contiguous operand with a constant leading
+// dimension).  `rows` x `cols` elements of a strided source view — axis a = the
+// group's free axis, axis b = k — land in the workspace at
+//   dst + x * ld + y   (k-major destination, dmode 0)  or
+//   dst + y * ld + x   (free-major destination, dmode 1).
 struct DPack {
     int64_t off, sa0, sa1, sb0, sb1;   // source view, element (x, y) as in DView
     int64_t dst;                        // workspace element of (0, 0)
@@ -123,9 +124,22 @@ struct DPack {
     int32_t rows, cols;                 // extents along a and b
     int32_t ld;                         // workspace leading dimension (elements)
     int32_t src;                        // 0: the A buffer, 1: the B buffer
+    int32_t dmode;                      // 0: k-major, 1: free-major destination
+    int32_t pad;
 };
-static_assert(sizeof(DPack) == 72, "DPack layout");
-constexpr int TILE_PACK = 64;           // a pack task copies up to 64 x 64 elements
+static_assert(sizeof(DPack) == 80, "DPack layout");
+
+// Piece of a gather one pack task copies: up to 4096 elements, tc (a power of
+// two, at most 64) columns by tr rows, so thin gathers (a few k) still move
+// whole runs of rows per task.
+constexpr int PACK_TILE_ELEMS = 4096;
+constexpr int PACK_TILE_MAXROWS = 1024;
+constexpr int PACK_LDS_ELEMS = 5120;    // max over tc of tr * (tc + 1)
+constexpr void pack_tile(int32_t cols, int32_t &tr, int32_t &tc) {
+    tc = 1;
+    while (tc < cols && tc < 64) tc *= 2;
+    tr = PACK_TILE_ELEMS / tc < PACK_TILE_MAXROWS ? PACK_TILE_ELEMS / tc : PACK_TILE_MAXROWS;
+}
 // Output tiles in flight at once on MI355X (256 CUs x two resident 256-thread
 // workgroups); the planner's cost model divides per-tile costs by it.
 constexpr double CONCURRENT_TILES = 512.0;

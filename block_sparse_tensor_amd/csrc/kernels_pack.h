@@ -3,12 +3,13 @@
 // section "Interleaved vs contiguous — the real tradeoff is a copy": one pack
 // kernel is far cheaper than one launch per sector GEMM).
 //
-// A task moves a 64 x 64 piece of one gather (rows along the group's free axis,
-// columns along k).  The destination is always k-contiguous, so the writes run
-// along k.  The reads follow the source's own unit-stride axis: a
-// k-contiguous source is read along k, a free-axis-contiguous source along the
-// rows; the piece passes through LDS so both sides stay coalesced.  The copy
-// is HBM-bound: its roofline is 2 * bytes / 8 TB/s.
+// A task moves one tr x tc piece of one gather (rows along the group's free
+// axis, columns along k; pack_tile picks the shape from the gather's width).
+// When the source and the destination have the same unit-stride axis the piece
+// is copied straight, element i of a wave's sweep to element i, both sides
+// coalesced.  Otherwise it passes through LDS: read along the source's unit
+// axis, written along the destination's.  The copy is HBM-bound: its roofline
+// is 2 * bytes / 8 TB/s.
 #pragma once
 
 #include "kernels_common.h"
@@ -23,11 +24,6 @@ struct PArgs {
     void *W;
 };
 
-template <typename T>
-struct PackSmem {
-    T t[TILE_PACK][TILE_PACK + 1];   // [row][k]; odd pitch keeps both access orders on distinct banks
-};
-
 // source element (x, y) of a gather
 __device__ __forceinline__ int64_t pack_src(const DPack &d, int32_t x, int32_t y) {
     const int64_t ax = d.ia == 1 ? static_cast<int64_t>(x) * d.sa0
@@ -37,34 +33,50 @@ __device__ __forceinline__ int64_t pack_src(const DPack &d, int32_t x, int32_t y
     return d.off + ax + by;
 }
 
+__device__ __forceinline__ int64_t pack_dst(const DPack &d, int32_t x, int32_t y) {
+    return d.dmode == 0 ? d.dst + static_cast<int64_t>(x) * d.ld + y : d.dst + static_cast<int64_t>(y) * d.ld + x;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void pack_gather(PArgs pa) {
-    __shared__ PackSmem<T> sm;
+    __shared__ T lds[PACK_LDS_ELEMS];
     const int32_t tid = threadIdx.x;
     T *W = static_cast<T *>(pa.W);
     for (int32_t t = blockIdx.x; t < pa.ntasks; t += gridDim.x) {
         const DTask task = pa.tasks[t];
         const DPack d = pa.packs[task.group];
         const T *S = static_cast<const T *>(d.src == 0 ? pa.A : pa.B);
+        int32_t tr = 0, tc = 0;
+        pack_tile(d.cols, tr, tc);
         const int32_t x0 = task.m0, y0 = task.n0;
-        const int32_t rows = min(TILE_PACK, d.rows - x0), cols = min(TILE_PACK, d.cols - y0);
-        // a k-contiguous source (single k leg, unit stride) is read along k
-        const bool along_k = d.ib == 1 && (d.sb0 == 1 || d.cols == 1);
-        __syncthreads();   // the previous task's reads of the LDS piece are done
-#pragma unroll 4
-        for (int32_t i = 0; i < TILE_PACK * TILE_PACK / 256; ++i) {
-            const int32_t e = tid + 256 * i;
-            const int32_t x = along_k ? e / TILE_PACK : e % TILE_PACK;
-            const int32_t y = along_k ? e % TILE_PACK : e / TILE_PACK;
-            if (x < rows && y < cols) sm.t[x][y] = S[pack_src(d, x0 + x, y0 + y)];
+        const int32_t rows = min(tr, d.rows - x0), cols = min(tc, d.cols - y0);
+        const int32_t n = rows * cols;
+        // unit-stride axes: of the source view, and of the destination
+        const bool s_k = d.ib == 1 && (d.sb0 == 1 || d.cols == 1);
+        const bool s_f = d.ia == 1 && (d.sa0 == 1 || d.rows == 1);
+        const bool d_k = d.dmode == 0;
+        if ((d_k && s_k) || (!d_k && s_f)) {
+            // same unit axis on both sides: straight copy along it
+            for (int32_t e = tid; e < n; e += 256) {
+                const int32_t x = d_k ? e / cols : e % rows;
+                const int32_t y = d_k ? e % cols : e / rows;
+                W[pack_dst(d, x0 + x, y0 + y)] = S[pack_src(d, x0 + x, y0 + y)];
+            }
+            continue;
+        }
+        // through LDS: [x][y] with pitch cols + 1
+        const bool read_k = s_k || !s_f;
+        __syncthreads();   // the previous task's LDS reads are done
+        for (int32_t e = tid; e < n; e += 256) {
+            const int32_t x = read_k ? e / cols : e % rows;
+            const int32_t y = read_k ? e % cols : e / rows;
+            lds[x * (cols + 1) + y] = S[pack_src(d, x0 + x, y0 + y)];
         }
         __syncthreads();
-#pragma unroll 4
-        for (int32_t i = 0; i < TILE_PACK * TILE_PACK / 256; ++i) {
-            const int32_t e = tid + 256 * i;
-            const int32_t x = e / TILE_PACK, y = e % TILE_PACK;
-            if (x < rows && y < cols)
-                W[d.dst + static_cast<int64_t>(x0 + x) * d.ld + (y0 + y)] = sm.t[x][y];
+        for (int32_t e = tid; e < n; e += 256) {
+            const int32_t x = d_k ? e / cols : e % rows;
+            const int32_t y = d_k ? e % cols : e / rows;
+            W[pack_dst(d, x0 + x, y0 + y)] = lds[x * (cols + 1) + y];
         }
     }
 }

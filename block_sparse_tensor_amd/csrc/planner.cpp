@@ -563,16 +563,26 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             pack_net_us += gain - cost;
             return true;
         };
-        // Gather an operand into a fresh workspace region: [free][ld] with
-        // ld = K rounded up to 8 elements (16-byte rows for every dtype), so the
-        // packed operand is one k-contiguous view.  Returns the new per-segment
-        // pieces (one workspace piece per k-segment).
+        // Gather an operand into a fresh workspace region with a constant
+        // leading dimension (rounded up to 8 elements: 16-byte rows for every
+        // dtype).  The destination keeps the unit-stride axis most source bytes
+        // have, so the copy stays coalesced on both sides: k-major
+        // [free][ld >= K] or free-major [K][ld >= free].  bf16 A is always
+        // k-major, the layout of the direct-to-LDS matrix-core tile.  Returns the
+        // new per-segment pieces (one workspace piece per k-segment).
         auto pack_operand = [&](const std::vector<std::vector<DView>> &seg, const std::vector<int64_t> &segK,
                                 int64_t free, int64_t K, int32_t src) {
-            const int64_t ld = (K + 7) / 8 * 8;
+            int64_t kbytes = 0, fbytes = 0;
+            for (size_t s = 0; s < seg.size(); ++s)
+                for (const DView &v : seg[s]) {
+                    if (v.ib == 1 && v.sb0 == 1 && segK[s] > 1) kbytes += (int64_t)v.len * segK[s];
+                    if (v.ia == 1 && v.sa0 == 1 && v.len > 1) fbytes += (int64_t)v.len * segK[s];
+                }
+            const bool kmajor = (p.dtype == BSC_BF16_F32 && src == 0) || kbytes >= fbytes;
+            const int64_t ld = kmajor ? (K + 7) / 8 * 8 : (free + 7) / 8 * 8;
             if (ld > LIM) fail(BSC_ERR_UNSUPPORTED, "a packed operand's leading dimension exceeds 2^31-1");
             const int64_t base = (p.ws_elems + 63) / 64 * 64;
-            p.ws_elems = base + free * ld;
+            p.ws_elems = base + (kmajor ? free : K) * ld;
             std::vector<std::vector<DView>> out(seg.size());
             int64_t kb = 0;
             for (size_t s = 0; s < seg.size(); ++s) {
@@ -583,21 +593,30 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                     d.sb0 = v.sb0; d.sb1 = v.sb1; d.ib = v.ib;
                     d.rows = v.len;
                     d.cols = (int32_t)segK[s];
-                    d.dst = base + (int64_t)v.begin * ld + kb;
+                    d.dst = kmajor ? base + (int64_t)v.begin * ld + kb : base + kb * ld + v.begin;
                     d.ld = (int32_t)ld;
                     d.src = src;
+                    d.dmode = kmajor ? 0 : 1;
                     const int32_t gi = (int32_t)p.packs.size();
                     p.packs.push_back(d);
-                    for (int32_t x0 = 0; x0 < d.rows; x0 += TILE_PACK)
-                        for (int32_t y0 = 0; y0 < d.cols; y0 += TILE_PACK) p.pack_tasks.push_back({0, gi, x0, y0});
+                    int32_t tr = 0, tc = 0;
+                    pack_tile(d.cols, tr, tc);
+                    for (int32_t x0 = 0; x0 < d.rows; x0 += tr)
+                        for (int32_t y0 = 0; y0 < d.cols; y0 += tc) p.pack_tasks.push_back({0, gi, x0, y0});
                 }
                 DView w{};
-                w.off = base + kb;
-                w.sa0 = free > 1 ? ld : 0;
-                w.sb0 = segK[s] > 1 ? 1 : 0;
                 w.ia = w.ib = 1;
                 w.begin = 0;
                 w.len = (int32_t)free;
+                if (kmajor) {
+                    w.off = base + kb;
+                    w.sa0 = free > 1 ? ld : 0;
+                    w.sb0 = segK[s] > 1 ? 1 : 0;
+                } else {
+                    w.off = base + kb * ld;
+                    w.sa0 = free > 1 ? 1 : 0;
+                    w.sb0 = segK[s] > 1 ? ld : 0;
+                }
                 out[s].push_back(w);
                 kb += segK[s];
             }

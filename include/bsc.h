@@ -130,11 +130,17 @@ typedef struct {
     int32_t layout_policy;  /* bsc_layout_policy */
     int32_t accumulate;     /* 0: C = A B ; 1: C += A B */
     int32_t grid_limit;     /* cap on workgroups per grouped launch; 0 = engine default */
-    /* cost-model constants; 0 selects the built-in MI355X defaults */
-    double t_launch_us;     /* host-to-kernel launch cost */
-    double t_seg_us;        /* extra cost per contracted segment walked inside a tile */
-    double pack_gbps;       /* gather bandwidth */
-    double tile_gflops;     /* sustained per-workgroup rate of the matrix-core tile */
+    /* Pack-cost model (uni20 "block coalescing", section "Interleaved vs
+     * contiguous"): operand X of a group is gathered when
+     *   2 * bytes(X) / pack_gbps  <  tiles * (pieces(X) - 1) * t_seg_us / 512
+     *                                + padding flops saved / tile_gflops,
+     * and the plan keeps its gathers only if their summed net saving exceeds
+     * t_launch_us (the extra launch).  Times in microseconds; 512 tiles run
+     * at once on MI355X.  0 selects the built-in MI355X defaults. */
+    double t_launch_us;     /* cost of one more launch per contraction */
+    double t_seg_us;        /* extra cost per piece one tile walks beyond one per k-segment */
+    double pack_gbps;       /* gather bandwidth, counting read + write bytes */
+    double tile_gflops;     /* sustained whole-GPU rate of the matrix-core tiles */
 } bsc_options;
 
 typedef struct {

@@ -221,3 +221,47 @@ def test_empty_problem():
     op = Operand([], [], [], np.zeros((0, 2)), np.zeros((0, 2)), [0], 0)
     s = bst.Plan(Contraction(idx, idx, idx, op, op, op, "f32")).stats()
     assert s["triples"] == 0 and s["items"] == 0 and s["launches_per_contract"] == 0
+
+
+def _packed_operands(plan):
+    m = plan.stats()["mode_count"]
+    return m["A"]["pack"] + m["B"]["pack"]
+
+
+def test_pack_cost_model_responds_to_constants():
+    """AUTO packs a scattered operand when the gather is cheap against the
+    set-up it saves, and never when the gather (or the extra launch) costs more."""
+    from workloads import configs as C
+    ch = C.small_chain(seed=4, layout="natural")
+    con = ch.stages[0].con
+    base = _packed_operands(bst.Plan(con, layout="force_pack"))
+    assert base > 0
+    cheap = bst.Plan(con, layout="auto", pack_gbps=1e12, t_seg_us=10.0, t_launch_us=1e-6)
+    assert _packed_operands(cheap) == base
+    assert cheap.stats()["launches_per_contract"] == 2
+    dear = bst.Plan(con, layout="auto", pack_gbps=1e-3, t_seg_us=10.0, t_launch_us=1e-6)
+    assert _packed_operands(dear) == 0 and dear.stats()["pack_bytes"] == 0
+    no_launch = bst.Plan(con, layout="auto", pack_gbps=1e12, t_seg_us=10.0, t_launch_us=1e9)
+    assert _packed_operands(no_launch) == 0 and no_launch.stats()["launches_per_contract"] == 1
+    assert _packed_operands(bst.Plan(con, layout="never_pack", pack_gbps=1e12, t_seg_us=10.0)) == 0
+
+
+def test_pack_never_applies_to_single_view_operands():
+    """An operand that already is one strided view over the group is never copied."""
+    from workloads import configs as C
+    prob = C.blockdiag_bf16(ld_align=8, align=8, values=False)
+    plan = bst.Plan(prob.con, layout="force_pack")
+    assert _packed_operands(plan) == 0 and plan.stats()["launches_per_contract"] == 1
+
+
+def test_pack_workspace_in_device_bytes():
+    from workloads import configs as C
+    ch = C.small_chain(seed=4, layout="natural")
+    con = ch.stages[0].con
+    never = bst.Plan(con, layout="never_pack")
+    forced = bst.Plan(con, layout="force_pack")
+    info, _ = forced.worklist()
+    esz = 8 if con.dtype == "f64" else 4
+    assert forced.device_bytes() >= info["off_workspace"] + info["workspace_elems"] * esz
+    assert info["workspace_elems"] * esz >= forced.stats()["pack_bytes"]
+    assert forced.device_bytes() > never.device_bytes()

@@ -19,7 +19,7 @@ DTASK = np.dtype([(n, "<i4") for n in ("cls", "group", "m0", "n0")])
 DFAST = np.dtype([(n, "<i8") for n in ("a_base", "a_rs", "b_base", "b_s", "c_base", "c_rs", "c_cs")] +
                  [(n, "<i4") for n in ("mlen", "nlen", "K", "flags", "group", "pad")])
 DPACK = np.dtype([(n, "<i8") for n in ("off", "sa0", "sa1", "sb0", "sb1", "dst")] +
-                 [(n, "<i4") for n in ("ia", "ib", "rows", "cols", "ld", "src")])
+                 [(n, "<i4") for n in ("ia", "ib", "rows", "cols", "ld", "src", "dmode", "pad")])
 R_A_WS, R_B_WS = 128, 256          # run reads A / B from the pack workspace
 F_A_WS, F_B_WS = 4, 8              # dense record reads A / B from the pack workspace
 G_C_ALONG_N, G_ACCUMULATE = 1, 2
@@ -28,7 +28,7 @@ TILE = {T_GENERIC: (64, 64), T_ZERO: (64, 64), T_MFMA: (128, 128), 4: (128, 128)
 TILE_MFMA_F = (64, 64)   # fp32 / fp64 matrix-core tile
 
 assert DVIEW.itemsize == 56 and DGROUP.itemsize == 32 and DRUN.itemsize == 32 and DTASK.itemsize == 16
-assert DFAST.itemsize == 80 and DPACK.itemsize == 72
+assert DFAST.itemsize == 80 and DPACK.itemsize == 80
 T_DENSE_N, T_DENSE_K = 4, 5
 T_SKINNY_M, T_SKINNY_N = 7, 8    # long axis M (at most 16 columns) / long axis N (at most 16 rows)
 
@@ -57,14 +57,22 @@ def replay_packs(plan, con, a64, b64):
     hit = np.zeros(info["workspace_elems"], np.int64)
     for t in ptasks:
         d = packs[t["group"]]
-        x = np.arange(t["m0"], min(t["m0"] + 64, d["rows"]))
-        y = np.arange(t["n0"], min(t["n0"] + 64, d["cols"]))
+        tc = 1
+        while tc < d["cols"] and tc < 64:
+            tc *= 2
+        tr = min(4096 // tc, 1024)                      # the kernel's piece shape
+        assert t["m0"] % tr == 0 and t["n0"] % tc == 0
+        x = np.arange(t["m0"], min(t["m0"] + tr, d["rows"]))
+        y = np.arange(t["n0"], min(t["n0"] + tc, d["cols"]))
         assert len(x) and len(y)
         src = d["off"] + (x[:, None] // d["ia"]) * d["sa0"] + (x[:, None] % d["ia"]) * d["sa1"] + \
             (y[None, :] // d["ib"]) * d["sb0"] + (y[None, :] % d["ib"]) * d["sb1"]
         buf = a64 if d["src"] == 0 else b64
         assert src.min() >= 0 and src.max() < buf.size
-        dst = d["dst"] + x[:, None] * d["ld"] + y[None, :]
+        if d["dmode"] == 0:
+            dst = d["dst"] + x[:, None] * d["ld"] + y[None, :]
+        else:
+            dst = d["dst"] + y[None, :] * d["ld"] + x[:, None]
         assert dst.min() >= 0 and dst.max() < ws.size
         ws[dst] = buf[src]
         np.add.at(hit, dst.ravel(), 1)

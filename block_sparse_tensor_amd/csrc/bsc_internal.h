@@ -107,7 +107,10 @@ struct DFast {
     int32_t mlen, nlen, K, flags;   // flags: G_ACCUMULATE, F_A_WS, F_B_WS
     int32_t group, pad;             // the tile's group (for the general tile when this one is not compiled in)
 };
-enum : int32_t { F_A_WS = 4, F_B_WS = 8 };   // DFast operand read from the pack workspace
+enum : int32_t {
+    F_A_WS = 4,          // DFast: A read from the pack workspace
+    F_B_WS = 8,          // DFast: B read from the pack workspace
+};
 static_assert(sizeof(DFast) == 80, "DFast layout");
 
 // One gather of the pack kernel (uni20 "block coalescing", section
@@ -153,6 +156,7 @@ static_assert(sizeof(DTask) == 16, "DTask layout");
 
 constexpr int TILE_GENERIC = 64;   // generic tile edge
 constexpr int TILE_MFMA = 128;     // bf16 matrix-core tile edge
+constexpr int TILE_MFMA_DENSE_M = 128;   // rows of the dense (direct-to-LDS) bf16 tile; 128 columns
 constexpr int TILE_MFMA_F = 64;    // fp32 / fp64 matrix-core tile edge
 
 constexpr bool is_mfma(int32_t cls) { return cls == T_MFMA || cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K; }
@@ -167,6 +171,9 @@ inline void tile_extents(bsc_dtype dt, int32_t cls, int32_t M, int32_t N, int32_
     } else if (cls == T_SKINNY_N) {
         tm = M > 0 ? M : 1;
         tn = TILE_SKINNY_LONG;
+    } else if (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) {
+        tm = TILE_MFMA_DENSE_M;
+        tn = TILE_MFMA;
     } else {
         tm = tn = is_mfma(cls) ? (dt == BSC_BF16_F32 ? TILE_MFMA : TILE_MFMA_F) : TILE_GENERIC;
     }

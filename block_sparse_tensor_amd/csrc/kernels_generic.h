@@ -22,7 +22,7 @@ struct GenericSmem {
 };
 
 template <typename TA, typename TC, typename ACC>
-__device__ void generic_tile(const KArgs &ka, const DTask &task, GenericSmem<ACC> &sm) {
+__device__ __forceinline__ void generic_tile(const KArgs &ka, const DTask &task, GenericSmem<ACC> &sm) {
     const DGroup g = ka.groups[task.group];
     const int32_t tid = threadIdx.x;
     const int32_t m0 = task.m0, n0 = task.n0;

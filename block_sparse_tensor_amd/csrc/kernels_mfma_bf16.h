@@ -195,7 +195,7 @@ __device__ __forceinline__ OpCtx mb_ctx(const DView *pieces, int32_t np, int32_t
 }
 
 template <typename TC>
-__device__ void mfma_tile_bf16(const KArgs &ka, const DTask &task, MfmaSmemBf16 &sm) {
+__device__ __forceinline__ void mfma_tile_bf16(const KArgs &ka, const DTask &task, MfmaSmemBf16 &sm) {
     // a dense-tile task (its direct-to-LDS body not compiled into this launch) names its group through its record
     const DGroup g = ka.groups[task.cls == T_MFMA ? task.group : ka.fast[task.group].group];
     const int32_t tid = threadIdx.x;

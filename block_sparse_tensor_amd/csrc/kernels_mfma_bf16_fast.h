@@ -280,7 +280,7 @@ __device__ __forceinline__ void fast_chunk(const uint16_t *la, const uint16_t *l
 }
 
 template <typename TC, bool BN>
-__device__ void fast_tile_bf16(const KArgs &ka, const DTask &task, FastSmemBf16 &sm) {
+__device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DTask &task, FastSmemBf16 &sm) {
     const DFast fd = ka.fast[task.group];
     const uint16_t *A = static_cast<const uint16_t *>((fd.flags & F_A_WS) ? ka.W : ka.A);
     const uint16_t *B = static_cast<const uint16_t *>((fd.flags & F_B_WS) ? ka.W : ka.B);

@@ -219,7 +219,7 @@ __device__ __forceinline__ int32_t mf_row(float, int32_t lane, int32_t r) { retu
 __device__ __forceinline__ int32_t mf_row(double, int32_t lane, int32_t r) { return (lane >> 4) + 4 * r; }
 
 template <typename T>
-__device__ void mfma_tile_f(const KArgs &ka, const DTask &task, MfmaSmemF<T> &sm) {
+__device__ __forceinline__ void mfma_tile_f(const KArgs &ka, const DTask &task, MfmaSmemF<T> &sm) {
     typedef typename MfTraits<T>::acc_t acc_t;
     constexpr int KC = MfTraits<T>::KC;
     const DGroup g = ka.groups[task.group];

@@ -31,7 +31,7 @@ struct SkinnySmem {
 // LONG_M: the long axis is M (A is the long operand, B the short one);
 // otherwise the long axis is N (B long, A short).
 template <typename TA, typename TC, typename ACC, bool LONG_M>
-__device__ void skinny_tile(const KArgs &ka, const DTask &task, SkinnySmem<ACC> &sm) {
+__device__ __forceinline__ void skinny_tile(const KArgs &ka, const DTask &task, SkinnySmem<ACC> &sm) {
     const DGroup g = ka.groups[task.group];
     const int32_t tid = threadIdx.x;
     const int32_t x0 = LONG_M ? task.m0 : task.n0;

@@ -49,7 +49,7 @@ union TileSmem {
 extern __shared__ __align__(16) unsigned char bsc_dyn_smem[];
 
 template <typename TA, typename TC, typename ACC, int32_t FEAT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void grouped_contract(KArgs ka) {
+__device__ __forceinline__ void grouped_body(const KArgs &ka) {
     TileSmem<TA, ACC, FEAT> &sm = *reinterpret_cast<TileSmem<TA, ACC, FEAT> *>(bsc_dyn_smem);
     for (int32_t t = blockIdx.x; t < ka.ntasks; t += gridDim.x) {
         const DTask task = ka.tasks[ka.task0 + t];
@@ -76,13 +76,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
         }
         if constexpr ((FEAT & FEAT_MFMA) != 0) {
             if (is_mfma(task.cls)) {
-                if constexpr (std::is_same<TA, uint16_t>::value) mfma_tile_bf16<TC>(ka, task, sm.m);
-                else mfma_tile_f<TA>(ka, task, sm.m);
+                if constexpr (std::is_same<TA, uint16_t>::value) {
+                    static_assert(TILE_MFMA_DENSE_M == TILE_MFMA, "a dense task must fit one general tile");
+                    mfma_tile_bf16<TC>(ka, task, sm.m);
+                } else {
+                    mfma_tile_f<TA>(ka, task, sm.m);
+                }
                 continue;
             }
         }
         generic_tile<TA, TC, ACC>(ka, task, sm.g);
     }
+}
+
+// A launch whose LDS allows only one workgroup per CU gets the whole register
+// file (one wave per SIMD); the others keep two workgroups per CU.
+template <typename TA, typename ACC, int32_t FEAT>
+constexpr bool one_per_cu() { return sizeof(TileSmem<TA, ACC, FEAT>) > 80 * 1024; }
+
+template <typename TA, typename TC, typename ACC, int32_t FEAT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void grouped_contract(KArgs ka) {
+    grouped_body<TA, TC, ACC, FEAT>(ka);
+}
+
+template <typename TA, typename TC, typename ACC, int32_t FEAT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void grouped_contract_wide(KArgs ka) {
+    grouped_body<TA, TC, ACC, FEAT>(ka);
 }
 
 using KernelFn = void (*)(KArgs);
@@ -95,7 +114,9 @@ struct KernelRef {
 // Opt a kernel variant into more than the default dynamic LDS once per process.
 template <typename TA, typename TC, typename ACC, int32_t FEAT>
 static KernelRef kernel_ref() {
-    KernelFn fn = grouped_contract<TA, TC, ACC, FEAT>;
+    KernelFn fn;
+    if constexpr (one_per_cu<TA, ACC, FEAT>()) fn = grouped_contract_wide<TA, TC, ACC, FEAT>;
+    else fn = grouped_contract<TA, TC, ACC, FEAT>;
     const size_t lds = sizeof(TileSmem<TA, ACC, FEAT>);
     static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

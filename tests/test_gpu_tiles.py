@@ -69,7 +69,7 @@ def test_single_sector_exact(dtype, shape):
 
 
 def test_fast_path_selected():
-    """Aligned, padded operands take the direct-to-LDS matrix-core tile."""
+    """Aligned, padded operands take the direct-to-LDS matrix-core tile (128 x 128)."""
     con, _, _, _ = _single(256, 256, 256, "bf16", True, True, 8, 1, 0)
     s = bst.Plan(con).stats()
     assert s["items_by_class"]["mfma_fast"] == 4

@@ -81,9 +81,12 @@ enum : int32_t {
     T_MFMA_FAST_N = 4,   // dense matrix-core tile, direct-to-LDS loads, N-contiguous B (group = DFast index)
     T_MFMA_FAST_K = 5,   // dense matrix-core tile, direct-to-LDS loads, K-contiguous B (group = DFast index)
     T_NOP = 6,           // placeholder keeping the task -> XCD mapping (no work)
-    T_SKINNY_M = 7,      // at most 16 output columns: 256 rows x all columns, one thread per row
-    T_SKINNY_N = 8,      // at most 16 output rows: all rows x 256 columns, one thread per column
-    T_NCLASS = 9,
+    T_SKINNY_M = 7,      // at most 16 output columns: 256 R rows x all columns, R rows per thread
+    T_SKINNY_N = 8,      // at most 16 output rows: all rows x 256 R columns, R columns per thread
+    T_MFMA_DENSE = 9,    // fp32 / fp64 matrix-core tile addressed through a DFast record (group = DFast index)
+    T_SKINNY_DENSE_M = 10,   // skinny tile, long axis M, addressed through a DFast record
+    T_SKINNY_DENSE_N = 11,   // skinny tile, long axis N, addressed through a DFast record
+    T_NCLASS = 12,
 };
 
 // Workgroups of a launch are dispatched round-robin over the chiplets (XCDs),
@@ -94,24 +97,26 @@ constexpr int BSC_XCDS = 8;
 // kernel feature sets: which tile bodies a grouped launch contains
 enum : int32_t { FEAT_MFMA = 1, FEAT_FAST_N = 2, FEAT_FAST_K = 4 };
 
-// Per-tile record of a dense matrix-core tile: every operand is a single
-// strided view, so the tile's addressing reduces to bases and strides the
-// planner computes once.  Element addresses (tile-local i, j; run-local k):
-//   A(i, k) = a_base + i * a_rs + k
-//   B(k, j) = b_base + k * b_s + j   (N-contiguous B)   or   b_base + j * b_s + k   (K-contiguous B)
+// Per-tile record of a dense matrix-core tile: the tile's rows of A, columns of
+// B and block of C each lie inside one single-leg strided view, so the tile's
+// addressing reduces to bases and strides the planner computes once (the
+// per-element decode is paid at plan time, not per element or per tile).
+// Element addresses (tile-local i, j; run-local k):
+//   A(i, k) = a_base + i * a_rs + k * a_ks
+//   B(k, j) = b_base + k * b_ks + j * b_ns
 //   C(i, j) = c_base + i * c_rs + j * c_cs
 struct DFast {
-    int64_t a_base, a_rs;
-    int64_t b_base, b_s;
+    int64_t a_base, a_rs, a_ks;
+    int64_t b_base, b_ks, b_ns;
     int64_t c_base, c_rs, c_cs;
     int32_t mlen, nlen, K, flags;   // flags: G_ACCUMULATE, F_A_WS, F_B_WS
     int32_t group, pad;             // the tile's group (for the general tile when this one is not compiled in)
 };
+static_assert(sizeof(DFast) == 96, "DFast layout");
 enum : int32_t {
     F_A_WS = 4,          // DFast: A read from the pack workspace
     F_B_WS = 8,          // DFast: B read from the pack workspace
 };
-static_assert(sizeof(DFast) == 80, "DFast layout");
 
 // One gather of the pack kernel (uni20 "block coalescing", section
 // "Interleaved vs contiguous — the real tradeoff is a copy": members that do not
@@ -159,18 +164,32 @@ constexpr int TILE_MFMA = 128;     // bf16 matrix-core tile edge
 constexpr int TILE_MFMA_DENSE_M = 128;   // rows of the dense (direct-to-LDS) bf16 tile; 128 columns
 constexpr int TILE_MFMA_F = 64;    // fp32 / fp64 matrix-core tile edge
 
-constexpr bool is_mfma(int32_t cls) { return cls == T_MFMA || cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K; }
-constexpr int TILE_SKINNY_LONG = 256;   // skinny tile extent along its long axis
+// task classes addressed through a DFast record (task t's record is record t)
+constexpr bool has_record(int32_t cls) {
+    return cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K || cls == T_MFMA_DENSE || cls == T_SKINNY_DENSE_M ||
+           cls == T_SKINNY_DENSE_N;
+}
+constexpr bool is_mfma(int32_t cls) {
+    return cls == T_MFMA || cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K || cls == T_MFMA_DENSE;
+}
 constexpr int TILE_SKINNY_SHORT = 16;   // largest short extent of a skinny group
+
+// Skinny tile extent along its long axis: 256 threads x R lines, where R times
+// the short extent rounded up to 4, 8 or 16 is the accumulator budget per
+// thread (32).
+inline int32_t skinny_long(bsc_dtype, int32_t short_ext) {
+    const int32_t yb = short_ext <= 4 ? 4 : (short_ext <= 8 ? 8 : 16);
+    return 256 * (32 / yb);
+}
 
 // output tile extents (rows, columns) of a task class for a plan dtype and group shape
 inline void tile_extents(bsc_dtype dt, int32_t cls, int32_t M, int32_t N, int32_t &tm, int32_t &tn) {
     if (cls == T_SKINNY_M) {
-        tm = TILE_SKINNY_LONG;
+        tm = skinny_long(dt, N);
         tn = N > 0 ? N : 1;
     } else if (cls == T_SKINNY_N) {
         tm = M > 0 ? M : 1;
-        tn = TILE_SKINNY_LONG;
+        tn = skinny_long(dt, M);
     } else if (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) {
         tm = TILE_MFMA_DENSE_M;
         tn = TILE_MFMA;

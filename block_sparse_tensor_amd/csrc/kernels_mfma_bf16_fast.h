@@ -280,8 +280,8 @@ __device__ __forceinline__ void fast_chunk(const uint16_t *la, const uint16_t *l
 }
 
 template <typename TC, bool BN>
-__device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DTask &task, FastSmemBf16 &sm) {
-    const DFast fd = ka.fast[task.group];
+__device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_ref, FastSmemBf16 &sm) {
+    const DFast fd = fd_ref;   // one read of the record
     const uint16_t *A = static_cast<const uint16_t *>((fd.flags & F_A_WS) ? ka.W : ka.A);
     const uint16_t *B = static_cast<const uint16_t *>((fd.flags & F_B_WS) ? ka.W : ka.B);
     const int32_t mlen = fd.mlen, nlen = fd.nlen, K = fd.K;
@@ -295,13 +295,14 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DTask &tas
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const FastOp fa = dense_setup_kcontig(fd.a_base, fd.a_rs, mlen, A);
-    const FastOp fb = BN ? dense_setup_ncontig(fd.b_base, fd.b_s, nlen, B) : dense_setup_kcontig(fd.b_base, fd.b_s, nlen, B);
+    const int64_t b_s = BN ? fd.b_ks : fd.b_ns;   // stride of B's non-contiguous axis
+    const FastOp fb = BN ? dense_setup_ncontig(fd.b_base, b_s, nlen, B) : dense_setup_kcontig(fd.b_base, b_s, nlen, B);
     const int32_t nfull = K / FB_BK;
     const int32_t ntot = (K + FB_BK - 1) / FB_BK;
     auto fill_partial = [&](int32_t stage) {
         dense_fill_kcontig(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, sm.op[stage][0]);
-        if (BN) dense_fill_ncontig(fd.b_base, fd.b_s, nlen, nfull * FB_BK, K, B, sm.op[stage][1]);
-        else dense_fill_kcontig(fd.b_base, fd.b_s, nlen, nfull * FB_BK, K, B, sm.op[stage][1]);
+        if (BN) dense_fill_ncontig(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, sm.op[stage][1]);
+        else dense_fill_kcontig(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, sm.op[stage][1]);
     };
     wait_vm<0>();      // nothing else outstanding: the counted waits below see only this tile's copies
     __syncthreads();   // previous users of the LDS ring are done

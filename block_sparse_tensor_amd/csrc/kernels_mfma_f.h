@@ -218,14 +218,64 @@ __device__ __forceinline__ void mf_compute(const T *la, const T *lb, typename Mf
 __device__ __forceinline__ int32_t mf_row(float, int32_t lane, int32_t r) { return (lane >> 4) * 4 + r; }
 __device__ __forceinline__ int32_t mf_row(double, int32_t lane, int32_t r) { return (lane >> 4) + 4 * r; }
 
+// The K loop of one operand pair over K contracted indices.  Chunk c + 2 is
+// loaded into registers while chunk c runs on the matrix cores and chunk c + 1
+// (loaded one iteration earlier) waits in registers to be stored: two chunks of
+// global loads are always in flight, against the ~1 us latency of a miss.
 template <typename T>
-__device__ __forceinline__ void mfma_tile_f(const KArgs &ka, const DTask &task, MfmaSmemF<T> &sm) {
-    typedef typename MfTraits<T>::acc_t acc_t;
+__device__ __forceinline__ void mf_kloop(const MfCtx<T> &oa, const MfCtx<T> &ob, int32_t K, MfmaSmemF<T> &sm,
+                                         typename MfTraits<T>::acc_t (&acc)[2][2]) {
     constexpr int KC = MfTraits<T>::KC;
-    const DGroup g = ka.groups[task.group];
+    const int32_t nchunks = (K + KC - 1) / KC;
+    MfStage<T> sa, sb, na, nb;
+    mf_load(oa, 0, sa);
+    mf_load(ob, 0, sb);
+    if (nchunks > 1) {
+        mf_load(oa, KC, na);
+        mf_load(ob, KC, nb);
+    }
+    mf_store(oa, sa, sm.a[0], 0);
+    mf_store(ob, sb, sm.b[0], 0);
+    __syncthreads();
+    for (int32_t c = 0; c < nchunks; ++c) {
+        // registers: na/nb hold chunk c + 1; chunk c + 2 goes into sa/sb
+        if (c + 2 < nchunks) {
+            mf_load(oa, (c + 2) * KC, sa);
+            mf_load(ob, (c + 2) * KC, sb);
+        }
+        mf_compute<T>(sm.a[c & 1], sm.b[c & 1], acc);
+        if (c + 1 < nchunks) {
+            mf_store(oa, na, sm.a[(c + 1) & 1], (c + 1) * KC);
+            mf_store(ob, nb, sm.b[(c + 1) & 1], (c + 1) * KC);
+        }
+        __syncthreads();
+        na = sa;
+        nb = sb;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void mfma_tile_f(const KArgs &ka, const DTask &task, const DFast &fd_ref, MfmaSmemF<T> &sm) {
+    typedef typename MfTraits<T>::acc_t acc_t;
     const int32_t tid = threadIdx.x;
-    const int32_t m0 = task.m0, n0 = task.n0;
-    const int32_t mlen = min(MF_TILE, g.M - m0), nlen = min(MF_TILE, g.N - n0);
+    const bool dense = task.cls == T_MFMA_DENSE;
+    // dense tiles carry their own record: no group, run or piece lookups
+    DGroup g;
+    DFast fd;
+    int32_t m0, n0, mlen, nlen;
+    if (dense) {
+        fd = fd_ref;
+        m0 = 0;
+        n0 = 0;
+        mlen = fd.mlen;
+        nlen = fd.nlen;
+    } else {
+        g = ka.groups[task.group];
+        m0 = task.m0;
+        n0 = task.n0;
+        mlen = min(MF_TILE, g.M - m0);
+        nlen = min(MF_TILE, g.N - n0);
+    }
 
     acc_t acc[2][2];
 #pragma unroll
@@ -235,53 +285,58 @@ __device__ __forceinline__ void mfma_tile_f(const KArgs &ka, const DTask &task, 
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[i][j][r] = T(0);
 
-    for (int32_t r = 0; r < g.nrun; ++r) {
-        const DRun run = ka.runs[g.run0 + r];
+    if (dense) {
         __syncthreads();
         if (tid < MF_TILE) {
-            if (tid < mlen) sm.ra[tid] = make_rec(ka.ap + run.ap0, run.nap, m0 + tid);
+            sm.ra[tid] = Rec{fd.a_base + static_cast<int64_t>(tid) * fd.a_rs, fd.a_ks, 0, 1, 0};
         } else if (tid < 2 * MF_TILE) {
             const int32_t j = tid - MF_TILE;
-            if (j < nlen) sm.rb[j] = make_rec(ka.bp + run.bp0, run.nbp, n0 + j);
+            sm.rb[j] = Rec{fd.b_base + static_cast<int64_t>(j) * fd.b_ns, fd.b_ks, 0, 1, 0};
         }
         __syncthreads();
-        const int32_t va = (run.flags & R_A_WS) ? 1 : ka.vec_a, vb = (run.flags & R_B_WS) ? 1 : ka.vec_b;
-        const MfCtx<T> oa = mf_ctx<T>(ka.ap + run.ap0, run.nap, R_A_KUNIT, R_A_FUNIT, run.flags, m0, mlen, run.K,
-                                      run_a<T>(ka, run.flags), va, sm.ra);
-        const MfCtx<T> ob = mf_ctx<T>(ka.bp + run.bp0, run.nbp, R_B_KUNIT, R_B_FUNIT, run.flags, n0, nlen, run.K,
-                                      run_b<T>(ka, run.flags), vb, sm.rb);
-        const int32_t nchunks = (run.K + KC - 1) / KC;
-        MfStage<T> sa, sb;
-        mf_load(oa, 0, sa);
-        mf_load(ob, 0, sb);
-        mf_store(oa, sa, sm.a[0], 0);
-        mf_store(ob, sb, sm.b[0], 0);
-        __syncthreads();
-        for (int32_t c = 0; c < nchunks; ++c) {
-            const bool more = c + 1 < nchunks;
-            if (more) {
-                mf_load(oa, (c + 1) * KC, sa);
-                mf_load(ob, (c + 1) * KC, sb);
-            }
-            mf_compute<T>(sm.a[c & 1], sm.b[c & 1], acc);
-            if (more) {
-                mf_store(oa, sa, sm.a[(c + 1) & 1], (c + 1) * KC);
-                mf_store(ob, sb, sm.b[(c + 1) & 1], (c + 1) * KC);
+        // element loads by mode: k-contiguous rows, free-axis-contiguous lines, or per-row records
+        const T *A = static_cast<const T *>((fd.flags & F_A_WS) ? ka.W : ka.A);
+        const T *B = static_cast<const T *>((fd.flags & F_B_WS) ? ka.W : ka.B);
+        MfCtx<T> oa, ob;
+        oa.x0 = 0; oa.xlen = mlen; oa.K = fd.K; oa.vec = (fd.flags & F_A_WS) ? 1 : ka.vec_a; oa.P = A; oa.rec = sm.ra;
+        ob.x0 = 0; ob.xlen = nlen; ob.K = fd.K; ob.vec = (fd.flags & F_B_WS) ? 1 : ka.vec_b; ob.P = B; ob.rec = sm.rb;
+        oa.mode = (fd.a_ks == 1 || fd.K == 1) ? MF_KCONTIG : (fd.a_rs == 1 ? MF_FCONTIG : MF_GENERIC);
+        ob.mode = (fd.b_ks == 1 || fd.K == 1) ? MF_KCONTIG : (fd.b_ns == 1 ? MF_FCONTIG : MF_GENERIC);
+        oa.off = fd.a_base; oa.sk = fd.a_ks;
+        ob.off = fd.b_base; ob.sk = fd.b_ks;
+        mf_kloop<T>(oa, ob, fd.K, sm, acc);
+    } else {
+        for (int32_t r = 0; r < g.nrun; ++r) {
+            const DRun run = ka.runs[g.run0 + r];
+            __syncthreads();
+            if (tid < MF_TILE) {
+                if (tid < mlen) sm.ra[tid] = make_rec(ka.ap + run.ap0, run.nap, m0 + tid);
+            } else if (tid < 2 * MF_TILE) {
+                const int32_t j = tid - MF_TILE;
+                if (j < nlen) sm.rb[j] = make_rec(ka.bp + run.bp0, run.nbp, n0 + j);
             }
             __syncthreads();
+            const int32_t va = (run.flags & R_A_WS) ? 1 : ka.vec_a, vb = (run.flags & R_B_WS) ? 1 : ka.vec_b;
+            const MfCtx<T> oa = mf_ctx<T>(ka.ap + run.ap0, run.nap, R_A_KUNIT, R_A_FUNIT, run.flags, m0, mlen, run.K,
+                                          run_a<T>(ka, run.flags), va, sm.ra);
+            const MfCtx<T> ob = mf_ctx<T>(ka.bp + run.bp0, run.nbp, R_B_KUNIT, R_B_FUNIT, run.flags, n0, nlen, run.K,
+                                          run_b<T>(ka, run.flags), vb, sm.rb);
+            mf_kloop<T>(oa, ob, run.K, sm, acc);
         }
     }
 
-    // epilogue: straight from the accumulators through the C pieces; the 16
-    // lanes of a row write 16 consecutive columns
-    const bool cn = (g.flags & G_C_ALONG_N) != 0;
-    if (tid < MF_TILE) {
-        if (!cn && tid < mlen) sm.ra[tid] = make_rec(ka.cp + g.cp0, g.ncp, m0 + tid);
-        if (cn && tid < nlen) sm.ra[tid] = make_rec(ka.cp + g.cp0, g.ncp, n0 + tid);
+    // epilogue: straight from the accumulators through the C pieces (or the
+    // record); the 16 lanes of a row write 16 consecutive columns
+    const bool cn = !dense && (g.flags & G_C_ALONG_N) != 0;
+    if (!dense) {
+        if (tid < MF_TILE) {
+            if (!cn && tid < mlen) sm.ra[tid] = make_rec(ka.cp + g.cp0, g.ncp, m0 + tid);
+            if (cn && tid < nlen) sm.ra[tid] = make_rec(ka.cp + g.cp0, g.ncp, n0 + tid);
+        }
+        __syncthreads();
     }
-    __syncthreads();
     T *Cp = static_cast<T *>(ka.C);
-    const bool accum = (g.flags & G_ACCUMULATE) != 0;
+    const bool accum = ((dense ? fd.flags : g.flags) & G_ACCUMULATE) != 0;
     const int32_t lane = tid & 63, w = tid >> 6;
     const int32_t wm = w & 1, wn = w >> 1;
 #pragma unroll
@@ -294,7 +349,8 @@ __device__ __forceinline__ void mfma_tile_f(const KArgs &ka, const DTask &task, 
             for (int r = 0; r < 4; ++r) {
                 const int32_t row = wm * 32 + i * 16 + mf_row(T(0), lane, r);
                 if (row >= mlen) continue;
-                const int64_t ad = cn ? along(sm.ra[col], m0 + row) : along(sm.ra[row], n0 + col);
+                const int64_t ad = dense ? fd.c_base + static_cast<int64_t>(row) * fd.c_rs + static_cast<int64_t>(col) * fd.c_cs
+                                         : (cn ? along(sm.ra[col], m0 + row) : along(sm.ra[row], n0 + col));
                 T v = acc[i][j][r];
                 if (accum) v += Cp[ad];
                 Cp[ad] = v;

@@ -739,7 +739,18 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         auto class_of = [&](const DGroup &g) -> int32_t {
             if (g.nrun == 0) return T_ZERO;
             // at most 16 output rows or columns: a bandwidth-bound stream over the long operand
-            if (std::min(g.M, g.N) <= TILE_SKINNY_SHORT) return g.M >= g.N ? T_SKINNY_M : T_SKINNY_N;
+            // (the long operand's pieces must have a single contracted leg)
+            if (std::min(g.M, g.N) <= TILE_SKINNY_SHORT) {
+                const bool long_m = g.M >= g.N;
+                bool single_k = true;
+                for (int32_t r = 0; r < g.nrun && single_k; ++r) {
+                    const DRun &run = p.runs[(size_t)(g.run0 + r)];
+                    const std::vector<DView> &pcs = long_m ? p.apieces : p.bpieces;
+                    const int32_t first = long_m ? run.ap0 : run.bp0, cnt = long_m ? run.nap : run.nbp;
+                    for (int32_t i = 0; i < cnt && single_k; ++i) single_k = pcs[(size_t)(first + i)].ib == 1;
+                }
+                if (single_k) return long_m ? T_SKINNY_M : T_SKINNY_N;
+            }
             if (p.dtype != BSC_BF16_F32) {
                 // fp32 / fp64: 16 x 16 x 4 matrix-core steps once both free extents reach half a step
                 return ((int64_t)g.M * g.N * g.K >= 16 * 16 * 16 && g.M >= 8 && g.N >= 8) ? T_MFMA : T_GENERIC;
@@ -758,10 +769,121 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             }
             return T_GENERIC;
         };
+        // The record of a tile whose A rows, B columns and C block each lie in one
+        // single-leg view of a one-run group (false otherwise).
+        auto dense_record = [&](const DGroup &g, int32_t gi, int32_t m0, int32_t ml, int32_t n0, int32_t nl,
+                                DFast &f) -> bool {
+            if (g.nrun != 1) return false;
+            const DRun &r = p.runs[(size_t)g.run0];
+            auto piece_at = [](const std::vector<DView> &pc, int32_t first, int32_t n, int32_t x0, int32_t len,
+                               const DView *&out) {
+                for (int32_t i = 0; i < n; ++i) {
+                    const DView &v = pc[(size_t)(first + i)];
+                    if (v.begin <= x0 && x0 + len <= v.begin + v.len) {
+                        if (v.ia != 1 || v.ib != 1) return false;
+                        out = &v;
+                        return true;
+                    }
+                }
+                return false;
+            };
+            const bool cn = (g.flags & G_C_ALONG_N) != 0;
+            const DView *a = nullptr, *b = nullptr, *c = nullptr;
+            if (!piece_at(p.apieces, r.ap0, r.nap, m0, ml, a)) return false;
+            if (!piece_at(p.bpieces, r.bp0, r.nbp, n0, nl, b)) return false;
+            if (!piece_at(p.cpieces, g.cp0, g.ncp, cn ? n0 : m0, cn ? nl : ml, c)) return false;
+            f.a_base = a->off + (int64_t)(m0 - a->begin) * a->sa0;
+            f.a_rs = a->sa0;
+            f.a_ks = a->sb0;
+            f.b_base = b->off + (int64_t)(n0 - b->begin) * b->sa0;
+            f.b_ns = b->sa0;
+            f.b_ks = b->sb0;
+            // C piece axis a is rows (or columns when cut along N)
+            f.c_rs = cn ? c->sb0 : c->sa0;
+            f.c_cs = cn ? c->sa0 : c->sb0;
+            f.c_base = c->off + (int64_t)(m0 - (cn ? 0 : c->begin)) * f.c_rs + (int64_t)(n0 - (cn ? c->begin : 0)) * f.c_cs;
+            f.mlen = ml;
+            f.nlen = nl;
+            f.K = r.K;
+            f.group = gi;
+            f.flags = (g.flags & G_ACCUMULATE) | ((r.flags & R_A_WS) ? F_A_WS : 0) | ((r.flags & R_B_WS) ? F_B_WS : 0);
+            return true;
+        };
+        // Skinny groups of one run whose views are all single-leg become items
+        // addressed through records: the long axis is cut at every piece boundary
+        // of the long operand and of C (and every skinny_long lines), so each item
+        // lies in one view of each operand.  Returns false (nothing emitted) when
+        // the group does not qualify.
+        auto skinny_records = [&](const DGroup &g, int32_t gi, bool long_m, std::vector<DTask> &out,
+                                  std::vector<double> *cost) -> bool {
+            if (g.nrun != 1) return false;
+            const DRun &r = p.runs[(size_t)g.run0];
+            const bool cn = (g.flags & G_C_ALONG_N) != 0;
+            const bool c_long = long_m ? !cn : cn;
+            const int32_t lfirst = long_m ? r.ap0 : r.bp0, lcnt = long_m ? r.nap : r.nbp;
+            const int32_t sfirst = long_m ? r.bp0 : r.ap0, scnt = long_m ? r.nbp : r.nap;
+            const std::vector<DView> &lp = long_m ? p.apieces : p.bpieces;
+            const std::vector<DView> &sp = long_m ? p.bpieces : p.apieces;
+            auto single = [](const DView &v) { return v.ia == 1 && v.ib == 1; };
+            if (scnt != 1 || !single(sp[(size_t)sfirst])) return false;
+            if (!c_long && g.ncp != 1) return false;
+            std::vector<int32_t> cuts;
+            for (int32_t i = 0; i < lcnt; ++i) {
+                if (!single(lp[(size_t)(lfirst + i)])) return false;
+                cuts.push_back(lp[(size_t)(lfirst + i)].begin);
+            }
+            for (int32_t i = 0; i < g.ncp; ++i) {
+                const DView &c = p.cpieces[(size_t)(g.cp0 + i)];
+                if (!single(c)) return false;
+                if (c_long) cuts.push_back(c.begin);
+            }
+            const int32_t X = long_m ? g.M : g.N, Y = long_m ? g.N : g.M;
+            cuts.push_back(X);
+            std::sort(cuts.begin(), cuts.end());
+            cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+            const int32_t ext = skinny_long(p.dtype, Y);
+            const DView &s = sp[(size_t)sfirst];
+            int32_t li = 0, ci = 0;
+            for (size_t q = 0; q + 1 < cuts.size(); ++q) {
+                for (int32_t x0 = cuts[q]; x0 < cuts[q + 1]; x0 += ext) {
+                    const int32_t xl = std::min(ext, cuts[q + 1] - x0);
+                    while (li + 1 < lcnt && lp[(size_t)(lfirst + li + 1)].begin <= x0) ++li;
+                    const DView &l = lp[(size_t)(lfirst + li)];
+                    const DView *c = &p.cpieces[(size_t)g.cp0];
+                    if (c_long) {
+                        while (ci + 1 < g.ncp && p.cpieces[(size_t)(g.cp0 + ci + 1)].begin <= x0) ++ci;
+                        c = &p.cpieces[(size_t)(g.cp0 + ci)];
+                    }
+                    DFast f{};
+                    const int64_t lbase = l.off + (int64_t)(x0 - l.begin) * l.sa0;
+                    // (tile-local i, j as in every record: i along M, j along N)
+                    if (long_m) {
+                        f.a_base = lbase; f.a_rs = l.sa0; f.a_ks = l.sb0;
+                        f.b_base = s.off; f.b_ns = s.sa0; f.b_ks = s.sb0;
+                        f.mlen = xl; f.nlen = Y;
+                    } else {
+                        f.b_base = lbase; f.b_ns = l.sa0; f.b_ks = l.sb0;
+                        f.a_base = s.off; f.a_rs = s.sa0; f.a_ks = s.sb0;
+                        f.mlen = Y; f.nlen = xl;
+                    }
+                    const int32_t cm0 = long_m ? x0 : 0, cn0 = long_m ? 0 : x0;
+                    f.c_rs = cn ? c->sb0 : c->sa0;
+                    f.c_cs = cn ? c->sa0 : c->sb0;
+                    f.c_base = c->off + (int64_t)(cm0 - (cn ? 0 : c->begin)) * f.c_rs + (int64_t)(cn0 - (cn ? c->begin : 0)) * f.c_cs;
+                    f.K = r.K;
+                    f.group = gi;
+                    f.flags = (g.flags & G_ACCUMULATE) | ((r.flags & R_A_WS) ? F_A_WS : 0) | ((r.flags & R_B_WS) ? F_B_WS : 0);
+                    out.push_back({long_m ? T_SKINNY_DENSE_M : T_SKINNY_DENSE_N, (int32_t)p.fast.size(), cm0, cn0});
+                    p.fast.push_back(f);
+                    if (cost) cost->push_back(4.0 * (double)xl * (double)(r.K + Y) + 2.0e4);
+                }
+            }
+            return true;
+        };
         // relative throughput of a tile class (used only to order work longest-first)
         auto rate_of = [&](int32_t cls) {
             if (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) return 48.0;
-            if (cls == T_MFMA) return p.dtype == BSC_BF16_F32 ? 16.0 : 4.0;
+            if (cls == T_MFMA || cls == T_MFMA_DENSE) return p.dtype == BSC_BF16_F32 ? 16.0 : 4.0;
             return 1.0;
         };
         auto tiles_of = [&](int32_t gi, std::vector<DTask> &out, std::vector<double> *cost) {
@@ -769,32 +891,26 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             const int32_t cls = class_of(g);
             int32_t TM = 0, TN = 0;
             tile_extents(p.dtype, cls, g.M, g.N, TM, TN);
+            if ((cls == T_SKINNY_M || cls == T_SKINNY_N) && skinny_records(g, gi, cls == T_SKINNY_M, out, cost)) return;
             for (int32_t m0 = 0; m0 < g.M; m0 += TM)
                 for (int32_t n0 = 0; n0 < g.N; n0 += TN) {
-                    if (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) {
-                        const DRun &r = p.runs[(size_t)g.run0];
-                        const DView &a = p.apieces[(size_t)r.ap0], &b = p.bpieces[(size_t)r.bp0];
-                        const DView &c = p.cpieces[(size_t)g.cp0];
-                        DFast f{};
-                        f.a_base = a.off + (int64_t)(m0 - a.begin) * a.sa0;
-                        f.a_rs = a.sa0;
-                        f.b_base = b.off + (int64_t)(n0 - b.begin) * b.sa0;
-                        f.b_s = cls == T_MFMA_FAST_N ? b.sb0 : b.sa0;
-                        const bool cn = (g.flags & G_C_ALONG_N) != 0;
-                        // C piece axis a is rows (or columns when cut along N)
-                        f.c_rs = cn ? c.sb0 : c.sa0;
-                        f.c_cs = cn ? c.sa0 : c.sb0;
-                        f.c_base = c.off + (int64_t)(m0 - (cn ? 0 : c.begin)) * f.c_rs + (int64_t)(n0 - (cn ? c.begin : 0)) * f.c_cs;
-                        f.mlen = std::min(TM, g.M - m0);
-                        f.nlen = std::min(TN, g.N - n0);
-                        f.K = r.K;
-                        f.group = gi;
-                        f.flags = (g.flags & G_ACCUMULATE) | ((r.flags & R_A_WS) ? F_A_WS : 0) |
-                                  ((r.flags & R_B_WS) ? F_B_WS : 0);
-                        out.push_back({cls, (int32_t)p.fast.size(), m0, n0});
-                        p.fast.push_back(f);
+                    const int32_t ml = std::min(TM, g.M - m0), nl = std::min(TN, g.N - n0);
+                    DFast f{};
+                    if ((cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K || cls == T_MFMA) &&
+                        dense_record(g, gi, m0, ml, n0, nl, f)) {
+                        // bf16 direct-to-LDS tiles always qualify; fp32 / fp64 tiles that do
+                        // become record-addressed dense tiles
+                        const int32_t c2 = cls == T_MFMA ? (p.dtype == BSC_BF16_F32 ? T_MFMA : T_MFMA_DENSE) : cls;
+                        if (c2 != T_MFMA) {
+                            out.push_back({c2, (int32_t)p.fast.size(), m0, n0});
+                            p.fast.push_back(f);
+                        } else {
+                            out.push_back({cls, gi, m0, n0});
+                        }
                     } else {
-                        out.push_back({cls, gi, m0, n0});
+                        // (a direct-to-LDS class always has its record; the general tile is the fallback)
+                        const bool fastc = cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K;
+                        out.push_back({fastc ? T_MFMA : cls, gi, m0, n0});
                     }
                     if (cost) {
                         double ml = std::min(TM, g.M - m0), nl = std::min(TN, g.N - n0);
@@ -865,6 +981,20 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             while (!p.tasks.empty() && p.tasks.back().cls == T_NOP) p.tasks.pop_back();
             if (!p.tasks.empty()) p.launches.push_back({0, (int32_t)p.tasks.size()});
         }
+        // Records in task order (record t belongs to task t), so a workgroup
+        // reads its task and its record at once instead of one after the other;
+        // tasks without a record leave their slot empty.
+        {
+            std::vector<DFast> by_task(p.tasks.size(), DFast{});
+            for (size_t t = 0; t < p.tasks.size(); ++t) {
+                DTask &tk = p.tasks[t];
+                if (has_record(tk.cls)) {
+                    by_task[t] = p.fast[(size_t)tk.group];
+                    tk.group = (int32_t)t;
+                }
+            }
+            p.fast.swap(by_task);
+        }
         if (p.tasks.size() > (size_t)LIM || p.pack_tasks.size() > (size_t)LIM)
             fail(BSC_ERR_UNSUPPORTED, "too many work items");
         // a plan with gathers needs one more launch: keep them only if they pay for it
@@ -918,9 +1048,11 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         for (auto &t : p.tasks) {
             if (t.cls == T_NOP) continue;
             const int32_t slot = t.cls == T_MFMA_FAST_K ? T_MFMA_FAST_N
-                                 : (t.cls == T_SKINNY_M || t.cls == T_SKINNY_N) ? 5 : t.cls;
+                                 : (t.cls == T_SKINNY_M || t.cls == T_SKINNY_N || t.cls == T_SKINNY_DENSE_M ||
+                                    t.cls == T_SKINNY_DENSE_N) ? 5
+                                 : t.cls == T_MFMA_DENSE ? T_MFMA : t.cls;
             s.items_by_class[slot]++;
-            if (t.cls == T_MFMA) p.features |= FEAT_MFMA;
+            if (t.cls == T_MFMA || t.cls == T_MFMA_DENSE) p.features |= FEAT_MFMA;
             if (t.cls == T_MFMA_FAST_N) p.features |= FEAT_FAST_N;
             if (t.cls == T_MFMA_FAST_K) p.features |= FEAT_FAST_K;
         }

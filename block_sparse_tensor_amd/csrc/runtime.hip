@@ -51,9 +51,19 @@ extern __shared__ __align__(16) unsigned char bsc_dyn_smem[];
 template <typename TA, typename TC, typename ACC, int32_t FEAT>
 __device__ __forceinline__ void grouped_body(const KArgs &ka) {
     TileSmem<TA, ACC, FEAT> &sm = *reinterpret_cast<TileSmem<TA, ACC, FEAT> *>(bsc_dyn_smem);
+    // a task with a record finds it at its own index (record t belongs to task t)
     for (int32_t t = blockIdx.x; t < ka.ntasks; t += gridDim.x) {
-        const DTask task = ka.tasks[ka.task0 + t];
+        const int32_t ti = ka.task0 + t;
+        const DTask task = ka.tasks[ti];
         if (task.cls == T_NOP) continue;
+        if (task.cls == T_SKINNY_DENSE_M) {
+            skinny_dense<TA, TC, ACC, true>(ka, ka.fast[ti], sm.s);
+            continue;
+        }
+        if (task.cls == T_SKINNY_DENSE_N) {
+            skinny_dense<TA, TC, ACC, false>(ka, ka.fast[ti], sm.s);
+            continue;
+        }
         if (task.cls == T_SKINNY_M) {
             skinny_tile<TA, TC, ACC, true>(ka, task, sm.s);
             continue;
@@ -64,13 +74,13 @@ __device__ __forceinline__ void grouped_body(const KArgs &ka) {
         }
         if constexpr ((FEAT & FEAT_FAST_N) != 0) {
             if (task.cls == T_MFMA_FAST_N) {
-                fast_tile_bf16<TC, true>(ka, task, sm.f);
+                fast_tile_bf16<TC, true>(ka, ka.fast[ti], sm.f);
                 continue;
             }
         }
         if constexpr ((FEAT & FEAT_FAST_K) != 0) {
             if (task.cls == T_MFMA_FAST_K) {
-                fast_tile_bf16<TC, false>(ka, task, sm.f);
+                fast_tile_bf16<TC, false>(ka, ka.fast[ti], sm.f);
                 continue;
             }
         }
@@ -80,7 +90,7 @@ __device__ __forceinline__ void grouped_body(const KArgs &ka) {
                     static_assert(TILE_MFMA_DENSE_M == TILE_MFMA, "a dense task must fit one general tile");
                     mfma_tile_bf16<TC>(ka, task, sm.m);
                 } else {
-                    mfma_tile_f<TA>(ka, task, sm.m);
+                    mfma_tile_f<TA>(ka, task, ka.fast[ti], sm.m);
                 }
                 continue;
             }

@@ -94,7 +94,11 @@ def test_matrix_core_class_for_fp32_fp64(dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "f64"])
 def test_skinny_class(dtype):
     """Groups with at most 16 output rows or columns stream through the skinny tile."""
+    # 256 threads x R lines per tile, R x (short extent rounded to 4/8/16) = 32
+    budget = 32
     con, _, _, _ = _single(1300, 20, 16, dtype, True, True, 0, 1, 0)
-    assert bst.Plan(con).stats()["items_by_class"]["skinny"] == 6      # 256 rows per tile
+    assert bst.Plan(con).stats()["items_by_class"]["skinny"] == -(-1300 // (256 * (budget // 16)))
     con, _, _, _ = _single(7, 20, 600, dtype, True, True, 0, 1, 0)
-    assert bst.Plan(con).stats()["items_by_class"]["skinny"] == 3
+    assert bst.Plan(con).stats()["items_by_class"]["skinny"] == -(-600 // (256 * (budget // 8)))
+    con, _, _, _ = _single(5000, 9, 1, dtype, True, True, 0, 1, 0)
+    assert bst.Plan(con).stats()["items_by_class"]["skinny"] == -(-5000 // (256 * (budget // 4)))

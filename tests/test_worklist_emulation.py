@@ -16,7 +16,7 @@ DVIEW = np.dtype([("off", "<i8"), ("sa0", "<i8"), ("sa1", "<i8"), ("sb0", "<i8")
 DGROUP = np.dtype([(n, "<i4") for n in ("M", "N", "K", "nrun", "run0", "ncp", "cp0", "flags")])
 DRUN = np.dtype([(n, "<i4") for n in ("K", "nap", "ap0", "nbp", "bp0", "flags", "kbase", "pad")])
 DTASK = np.dtype([(n, "<i4") for n in ("cls", "group", "m0", "n0")])
-DFAST = np.dtype([(n, "<i8") for n in ("a_base", "a_rs", "b_base", "b_s", "c_base", "c_rs", "c_cs")] +
+DFAST = np.dtype([(n, "<i8") for n in ("a_base", "a_rs", "a_ks", "b_base", "b_ks", "b_ns", "c_base", "c_rs", "c_cs")] +
                  [(n, "<i4") for n in ("mlen", "nlen", "K", "flags", "group", "pad")])
 DPACK = np.dtype([(n, "<i8") for n in ("off", "sa0", "sa1", "sb0", "sb1", "dst")] +
                  [(n, "<i4") for n in ("ia", "ib", "rows", "cols", "ld", "src", "dmode", "pad")])
@@ -28,9 +28,18 @@ TILE = {T_GENERIC: (64, 64), T_ZERO: (64, 64), T_MFMA: (128, 128), 4: (128, 128)
 TILE_MFMA_F = (64, 64)   # fp32 / fp64 matrix-core tile
 
 assert DVIEW.itemsize == 56 and DGROUP.itemsize == 32 and DRUN.itemsize == 32 and DTASK.itemsize == 16
-assert DFAST.itemsize == 80 and DPACK.itemsize == 80
+assert DFAST.itemsize == 96 and DPACK.itemsize == 80
 T_DENSE_N, T_DENSE_K = 4, 5
+T_MFMA_DENSE = 9                  # fp32 / fp64 record-addressed matrix-core tile
+T_SKINNY_DENSE = (10, 11)         # record-addressed skinny items (long axis M / N)
 T_SKINNY_M, T_SKINNY_N = 7, 8    # long axis M (at most 16 columns) / long axis N (at most 16 rows)
+
+
+def skinny_long(dtype, short):
+    """Long-axis extent of a skinny tile: 256 threads x R lines, R x (short
+    extent rounded up to 4, 8 or 16) = 32 accumulators."""
+    yb = 4 if short <= 4 else (8 if short <= 8 else 16)
+    return 256 * (32 // yb)
 
 
 def decode(plan):
@@ -101,17 +110,20 @@ def replay(plan, con, a, b, c0, accumulate=False):
     for t in tasks:
         if t["cls"] == 6:      # no-op placeholder
             continue
-        if t["cls"] in (T_DENSE_N, T_DENSE_K):
+        if t["cls"] in (T_DENSE_N, T_DENSE_K, T_MFMA_DENSE) + T_SKINNY_DENSE:
             # dense tile: bases and strides only (the kernel's addressing)
             f = dense[t["group"]]
             i = np.arange(f["mlen"])[:, None]
             j = np.arange(f["nlen"])[None, :]
             k = np.arange(f["K"])
-            aad = f["a_base"] + i * f["a_rs"] + k[None, :]
             if t["cls"] == T_DENSE_N:
-                bad = f["b_base"] + k[:, None] * f["b_s"] + j
-            else:
-                bad = f["b_base"] + j * f["b_s"] + k[:, None]
+                assert f["b_ns"] == 1 or f["nlen"] == 1
+            if t["cls"] in (T_DENSE_N, T_DENSE_K):
+                assert f["a_ks"] == 1 or f["K"] == 1
+            if t["cls"] == T_DENSE_K:
+                assert f["b_ks"] == 1 or f["K"] == 1
+            aad = f["a_base"] + i * f["a_rs"] + k[None, :] * f["a_ks"]
+            bad = f["b_base"] + k[:, None] * f["b_ks"] + j * f["b_ns"]
             cad = f["c_base"] + i * f["c_rs"] + j * f["c_cs"]
             abuf = ws if f["flags"] & F_A_WS else a64
             bbuf = ws if f["flags"] & F_B_WS else b64
@@ -128,9 +140,9 @@ def replay(plan, con, a, b, c0, accumulate=False):
             continue
         g = groups[t["group"]]
         if t["cls"] == T_SKINNY_M:
-            TM, TN = 256, max(1, int(g["N"]))
+            TM, TN = skinny_long(con.dtype, int(g["N"])), max(1, int(g["N"]))
         elif t["cls"] == T_SKINNY_N:
-            TM, TN = max(1, int(g["M"])), 256
+            TM, TN = max(1, int(g["M"])), skinny_long(con.dtype, int(g["M"]))
         else:
             TM, TN = TILE_MFMA_F if (t["cls"] == T_MFMA and con.dtype != "bf16") else TILE[int(t["cls"])]
         m0, n0 = int(t["m0"]), int(t["n0"])

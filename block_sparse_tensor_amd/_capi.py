@@ -33,7 +33,7 @@ class BscOperand(ctypes.Structure):
 class BscOptions(ctypes.Structure):
     _fields_ = [("launch_mode", c_int32), ("layout_policy", c_int32), ("accumulate", c_int32),
                 ("grid_limit", c_int32), ("t_launch_us", c_double), ("t_seg_us", c_double),
-                ("pack_gbps", c_double), ("tile_gflops", c_double)]
+                ("pack_gbps", c_double), ("tile_gflops", c_double), ("split_k", c_int32), ("reserved", c_int32)]
 
 
 class BscStats(ctypes.Structure):
@@ -43,7 +43,7 @@ class BscStats(ctypes.Structure):
                 ("items_by_class", c_int64 * 6), ("launches_per_contract", c_int64),
                 ("launches_per_sector", c_int64), ("useful_flops", c_int64), ("alg_bytes", c_int64),
                 ("pack_bytes", c_int64), ("device_bytes", c_int64), ("tail_triples", c_int64),
-                ("launches_issued", c_int64), ("grid", c_int32), ("reserved", c_int32),
+                ("launches_issued", c_int64), ("grid", c_int32), ("split_tiles", c_int32),
                 ("predicted_us", c_double)]
 
 
@@ -52,7 +52,8 @@ class BscWorklistInfo(ctypes.Structure):
                                         "n_dense", "off_groups", "off_runs", "off_apieces", "off_bpieces",
                                         "off_cpieces", "off_tasks", "off_dense", "n_packs", "n_pack_tasks",
                                         "off_packs", "off_pack_tasks", "off_workspace", "workspace_elems",
-                                        "bytes", "n_launches")]
+                                        "bytes", "n_launches", "n_counters", "off_counters",
+                                        "off_partials", "partial_elems")]
 
 
 _lib = None

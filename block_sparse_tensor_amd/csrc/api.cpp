@@ -74,9 +74,10 @@ bsc_status bsc_plan(const bsc_index *m, const bsc_index *k, const bsc_index *n, 
         set_error("bsc_plan: unknown launch mode");
         return BSC_ERR_ARG;
     }
-    if (p->opt.layout_policy < BSC_LAYOUT_AUTO || p->opt.layout_policy > BSC_LAYOUT_FORCE_PACK || p->opt.grid_limit < 0) {
+    if (p->opt.layout_policy < BSC_LAYOUT_AUTO || p->opt.layout_policy > BSC_LAYOUT_FORCE_PACK || p->opt.grid_limit < 0 ||
+        p->opt.split_k < -1) {
         delete p;
-        set_error("bsc_plan: bad layout policy or grid limit");
+        set_error("bsc_plan: bad layout policy, grid limit or split_k");
         return BSC_ERR_ARG;
     }
     fill_cost_defaults(p->opt, dtype);
@@ -156,6 +157,10 @@ bsc_status bsc_plan_worklist(bsc_plan_t plan, bsc_worklist_info *info, void *ima
     info->workspace_elems = p->ws_elems;
     info->bytes = (int64_t)p->image.size();
     info->n_launches = (int64_t)p->launches.size() + (p->packs.empty() ? 0 : 1);
+    info->n_counters = p->n_counters;
+    info->off_counters = (int64_t)p->off_cnt;
+    info->off_partials = (int64_t)p->off_part;
+    info->partial_elems = p->part_elems;
     if (image) {
         if (bytes < p->image.size()) {
             set_error("bsc_plan_worklist: image buffer too small");

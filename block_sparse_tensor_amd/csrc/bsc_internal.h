@@ -110,9 +110,17 @@ struct DFast {
     int64_t b_base, b_ks, b_ns;
     int64_t c_base, c_rs, c_cs;
     int32_t mlen, nlen, K, flags;   // flags: G_ACCUMULATE, F_A_WS, F_B_WS
-    int32_t group, pad;             // the tile's group (for the general tile when this one is not compiled in)
+    int32_t group;                  // the tile's group (for the general tile when this one is not compiled in)
+    // K split (bf16 direct-to-LDS tile only): the output tile is summed over
+    // `nsplit` K-slices, each a task of its own; this record covers slice
+    // `split` (its bases and K are the slice's).  Every slice stores its fp32
+    // partial tile at part + split * TILE_MFMA_DENSE_M * TILE_MFMA and counts
+    // itself in counter `counter`; the last to arrive adds the partials in
+    // slice order and writes C.  nsplit = 1: no split.
+    int32_t split, nsplit, counter;
+    int64_t part;
 };
-static_assert(sizeof(DFast) == 96, "DFast layout");
+static_assert(sizeof(DFast) == 112, "DFast layout");
 enum : int32_t {
     F_A_WS = 4,          // DFast: A read from the pack workspace
     F_B_WS = 8,          // DFast: B read from the pack workspace
@@ -161,7 +169,7 @@ static_assert(sizeof(DTask) == 16, "DTask layout");
 
 constexpr int TILE_GENERIC = 64;   // generic tile edge
 constexpr int TILE_MFMA = 128;     // bf16 matrix-core tile edge
-constexpr int TILE_MFMA_DENSE_M = 128;   // rows of the dense (direct-to-LDS) bf16 tile; 128 columns
+constexpr int TILE_MFMA_DENSE_M = 256;   // rows of the dense (direct-to-LDS) bf16 tile; 128 columns
 constexpr int TILE_MFMA_F = 64;    // fp32 / fp64 matrix-core tile edge
 
 // task classes addressed through a DFast record (task t's record is record t)
@@ -227,6 +235,9 @@ struct Plan {
     std::vector<DPack> packs;     // gathers into the pack workspace
     std::vector<DTask> pack_tasks;   // 64 x 64 pieces of the gathers (group = gather index)
     int64_t ws_elems = 0;         // pack workspace size (operand elements)
+    int32_t n_counters = 0;       // K-split arrival counters (one per split tile, zero between launches)
+    int64_t part_elems = 0;       // K-split partial tiles (fp32 elements)
+    int32_t split_tiles = 0;      // output tiles cut along K
     std::vector<std::array<int32_t, 2>> launches;  // per-sector mode: task ranges, one launch each
 
     // device binding
@@ -234,6 +245,7 @@ struct Plan {
     size_t dev_bytes = 0;
     size_t off_groups = 0, off_runs = 0, off_ap = 0, off_bp = 0, off_cp = 0, off_tasks = 0, off_fast = 0;
     size_t off_packs = 0, off_ptasks = 0, off_ws = 0;   // gathers, their tasks, the workspace
+    size_t off_cnt = 0, off_part = 0;                    // K-split counters (in the image), partials
     std::vector<unsigned char> image;   // host copy of the device tables
     int32_t cu_count = 0;
     int32_t grid = 0;

@@ -21,6 +21,8 @@ struct KArgs {
     const void *A, *B;
     void *C;
     const void *W;          // pack workspace (operands of runs flagged R_A_WS / R_B_WS)
+    float *P;               // K-split partial tiles
+    int32_t *cnt;           // K-split arrival counters (zero between launches)
 };
 
 // Buffer a run's A (B) pieces address: the caller's operand or the workspace.

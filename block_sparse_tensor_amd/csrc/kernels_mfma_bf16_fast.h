@@ -3,22 +3,33 @@
 // For a coalesced group that is one run of single strided views with
 // 16-byte aligned rows (the planner's R_A_VEC and R_B_VECN / R_B_VECK
 // conditions), the whole tile is described by a host-computed record (DFast):
-// operand bases and strides, extents, K.  On top of the wave layout of the
-// general tile (128 x 128 output, four 64 x 64 quadrants of
-// v_mfma_f32_32x32x16_bf16):
+// operand bases and strides, extents, K.  The tile is 256 x 128, computed by
+// four waves in a 2 x 2 arrangement; each wave owns 128 x 64 as 4 x 2 tiles
+// of v_mfma_f32_32x32x16_bf16.  Two workgroups share a CU, so every SIMD holds
+// two waves and one wave's LDS fragment reads overlap the other's MFMAs.
 //
-//  * K chunks of 64 are copied global -> LDS with 16-byte direct-to-LDS loads
-//    (no register staging); each wave instruction fills 1 KB of LDS in lane
-//    order and the lane -> global mapping applies an XOR swizzle so the
-//    fragment reads hit distinct banks;
-//  * A (and B when it is K-contiguous) lives in LDS as [row][k] (128 B rows,
-//    16-byte granules swizzled by row); fragments are single 16-byte reads;
+// Why this shape: with a 64 x 64 wave tile the LDS fragment reads (1 KB per
+// MFMA) take as long as the MFMAs themselves; a 128 x 64 wave tile reads
+// 0.75 KB per MFMA, which two waves per SIMD hide behind the matrix cores.  A
+// 256 x 128 tile also fetches 25 % fewer operand bytes per flop than 128 x 128.
+//
+//  * K is cut into chunks of 32 (24 KB per stage: A 256 x 32, B 32 x 128)
+//    held in a ring of FB_STAGES stages (72 KB per workgroup, two per CU);
+//    FB_STAGES - 1 chunks are in flight while one feeds the matrix cores;
+//  * chunks are copied global -> LDS with 16-byte direct-to-LDS loads (no
+//    register staging); each wave instruction fills 1 KB of LDS in lane order
+//    and the lane -> global mapping applies an XOR swizzle so the fragment
+//    reads hit distinct banks;
+//  * A (and B when it is K-contiguous) lives in LDS as [row][k], 64-byte rows
+//    of four 16-byte granules, granule g of row r in slot g ^ fa_perm(r): the
+//    eight rows one LDS cycle serves sit in distinct 16-byte bank groups;
 //  * B that is N-contiguous (row-major B) lives in LDS as [k][n] (256 B rows,
 //    64-byte granules swizzled by k) and each MFMA B fragment comes from two
 //    transposing LDS reads (ds_read_b64_tr_b16), so no ALU transpose;
-//  * STAGES LDS stages in a ring: while chunk c feeds the matrix cores the
-//    copies of the next STAGES - 1 chunks are in flight; each wave waits
-//    (vmcnt) only for its own copies of chunk c, then one barrier per chunk;
+//  * each wave waits (vmcnt) only for its own copies of chunk c, then one
+//    barrier per chunk hands the stage over; a wave whose A rows all lie past
+//    the tile edge copies no A (the rows it would fill only feed results that
+//    are dropped);
 //  * the last, partial K chunk goes through masked register loads so every
 //    element with k >= K is an exact zero in both operands; rows (columns)
 //    past the tile edge are clamped to a valid row and their results dropped;
@@ -30,15 +41,25 @@
 namespace bsc {
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int FB_BK = 64;
-constexpr int FB_STAGE = 128 * 64;       // bf16 elements per operand per stage (16 KB)
-constexpr int FB_STAGES = 2;             // LDS ring depth (FB_STAGES * 32 KB of LDS)
+constexpr int FB_BM = 256;                      // tile rows
+constexpr int FB_BN = 128;                      // tile columns
+constexpr int FB_BK = 32;                       // contracted indices per chunk
+constexpr int FB_STAGES = 3;                    // LDS ring depth
+constexpr int FB_A_STAGE = FB_BM * FB_BK;       // bf16 elements of A per stage (16 KB)
+constexpr int FB_B_STAGE = FB_BN * FB_BK;       // bf16 elements of B per stage (8 KB)
+constexpr int FB_STAGE = FB_A_STAGE + FB_B_STAGE;
+constexpr int FB_NIA = FB_A_STAGE * 2 / 1024 / 4;   // 1 KB copies of A per wave and chunk (4)
+constexpr int FB_NIB = FB_B_STAGE * 2 / 1024 / 4;   // 1 KB copies of B per wave and chunk (2)
+constexpr int FB_FM = FB_BM / 2 / 32;               // row fragments per wave (4)
+static_assert(FB_BM == TILE_MFMA_DENSE_M && FB_BN == TILE_MFMA, "tile shape the planner cuts");
 
 #define BSC_LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 
 struct FastSmemBf16 {
-    uint16_t op[FB_STAGES][2][FB_STAGE];   // [stage][A=0,B=1][...]
+    uint16_t op[FB_STAGES][FB_STAGE];   // [stage][A (256 x 32), then B (128 x 32)]
+    int32_t last;                       // K split: this workgroup finishes the tile
 };
 
 // Wait until at most N vector-memory operations of this wave are outstanding
@@ -49,19 +70,17 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until this wave's copies of the chunk that has `chunks_after` newer
+// chunks in flight have landed (PER copies per chunk and wave).
+template <int PER>
 __device__ __forceinline__ void wait_vm_chunks(int32_t chunks_after) {
-    // each chunk is 8 copies per wave (4 for A, 4 for B)
     switch (chunks_after) {
         case 0: wait_vm<0>(); break;
-        case 1: wait_vm<8>(); break;
-        case 2: wait_vm<16>(); break;
-        case 3: wait_vm<24>(); break;
-        case 4: wait_vm<32>(); break;
-        case 5: wait_vm<40>(); break;
-        default: wait_vm<48>(); break;
+        case 1: wait_vm<PER>(); break;
+        default: wait_vm<2 * PER>(); break;
     }
 }
-static_assert(FB_STAGES - 1 <= 6, "vmcnt table covers at most 6 chunks ahead");
+static_assert(FB_STAGES - 1 <= 2, "the wait table covers at most two chunks in flight");
 
 // Workgroup barrier for handing LDS stages between waves.  Each wave first
 // waits for its own LDS writes (lgkmcnt) — its direct-to-LDS copies were
@@ -75,40 +94,48 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// 16-byte granule (of 8) holding k-granule g in A-layout row r
-__device__ __forceinline__ int32_t fa_slot(int32_t r, int32_t g) { return g ^ ((r ^ (r >> 3)) & 7); }
+// Row permutation of the A-layout swizzle (values 0..3, period 16): the four
+// rows of one parity among any eight consecutive rows get distinct values.
+__device__ __forceinline__ int32_t fa_perm(int32_t r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
+// 16-byte slot (of 4) holding k-granule g in A-layout row r
+__device__ __forceinline__ int32_t fa_slot(int32_t r, int32_t g) { return g ^ fa_perm(r); }
 // 64-byte granule (of 4) holding n-granule G in B-layout row k
 __device__ __forceinline__ int32_t fb_pos(int32_t k, int32_t G) { return G ^ (k & 3); }
 
+template <int NI>
 struct FastOp {
-    const uint16_t *p[4];   // per-instruction global pointers at chunk 0
-    int64_t step;           // elements to advance per chunk
+    const uint16_t *p[NI];   // per-instruction global pointers at chunk 0
+    int64_t step;            // elements to advance per chunk
 };
 
 // K-contiguous operand ([x][k] layout), element (x, k) at base + x * xs + k:
-// wave w instruction j covers rows 32w + 8j .. +8, lane l row 8j + l/8, slot l%8.
-__device__ __forceinline__ FastOp dense_setup_kcontig(int64_t base, int64_t xs, int32_t xlen, const uint16_t *P) {
-    FastOp f;
+// wave w instruction j fills rows 16 (NI w + j) .. +16 (1 KB); lane l fills
+// row l / 4, slot l % 4, so it copies k-granule (l % 4) ^ fa_perm(row).
+template <int NI>
+__device__ __forceinline__ FastOp<NI> dense_setup_kcontig(int64_t base, int64_t xs, int32_t xlen, const uint16_t *P) {
+    FastOp<NI> f;
     const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int32_t r = 32 * w + 8 * j + (lane >> 3);
+    for (int j = 0; j < NI; ++j) {
+        const int32_t r = 16 * (NI * w + j) + (lane >> 2);
         const int32_t rr = r < xlen ? r : 0;                      // rows past the edge: a valid row
-        f.p[j] = P + base + static_cast<int64_t>(rr) * xs + 8 * fa_slot(r, lane & 7);
+        f.p[j] = P + base + static_cast<int64_t>(rr) * xs + 8 * ((lane & 3) ^ fa_perm(r));
     }
     f.step = FB_BK;
     return f;
 }
 
 // N-contiguous operand ([k][n] layout), element (k, n) at base + k * ks + n:
-// instruction j covers k rows 16w + 4j .. +4, lane l row 4j + l/16, 16-byte slot l%16.
-__device__ __forceinline__ FastOp dense_setup_ncontig(int64_t base, int64_t ks, int32_t nlen, const uint16_t *P) {
-    FastOp f;
+// instruction j fills k rows 4 (NI w + j) .. +4; lane l fills row l / 16,
+// 16-byte slot l % 16.
+template <int NI>
+__device__ __forceinline__ FastOp<NI> dense_setup_ncontig(int64_t base, int64_t ks, int32_t nlen, const uint16_t *P) {
+    FastOp<NI> f;
     const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int32_t s = lane & 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int32_t kr = 16 * w + 4 * j + (lane >> 4);
+    for (int j = 0; j < NI; ++j) {
+        const int32_t kr = 4 * (NI * w + j) + (lane >> 4);
         const int32_t G = fb_pos(kr, s >> 2);                     // global n-granule for this LDS position
         int32_t n = 32 * G + 8 * (s & 3);
         if (n >= nlen) n = 0;                                      // columns past the edge: a valid column
@@ -118,30 +145,33 @@ __device__ __forceinline__ FastOp dense_setup_ncontig(int64_t base, int64_t ks, 
     return f;
 }
 
-__device__ __forceinline__ void fast_issue(const FastOp &f, int32_t c, uint16_t *lds_stage) {
+template <int NI>
+__device__ __forceinline__ void fast_issue(const FastOp<NI> &f, int32_t c, uint16_t *lds_op) {
     const int32_t w = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NI; ++j) {
         const uint16_t *src = f.p[j] + static_cast<int64_t>(c) * f.step;
-        uint16_t *dst = lds_stage + (4 * w + j) * 512;               // 1 KB per wave instruction
+        uint16_t *dst = lds_op + (NI * w + j) * 512;                 // 1 KB per wave instruction
         __builtin_amdgcn_global_load_lds(src, BSC_LDS_PTR(void, dst), 16, 0, 0);
     }
 }
 
-// Masked fills of a partial chunk (k0 .. K-1 valid) through registers.
+// Masked fill of a partial chunk (k0 .. K-1 valid) of a K-contiguous operand
+// through registers: ROWS rows of four 16-byte granules.
+template <int ROWS>
 __device__ __forceinline__ void dense_fill_kcontig(int64_t base, int64_t xs, int32_t xlen, int32_t k0, int32_t K,
                                                    const uint16_t *P, uint16_t *lds) {
     const int32_t tid = threadIdx.x;
 #pragma unroll 1
-    for (int q = 0; q < 4; ++q) {
-        const int32_t u = tid + 256 * q;         // 1024 granules: row u >> 3, k-granule u & 7
-        const int32_t r = u >> 3, g = u & 7;
+    for (int q = 0; q < ROWS * 4 / 256; ++q) {
+        const int32_t u = tid + 256 * q;         // row u / 4, k-granule u % 4
+        const int32_t r = u >> 2, g = u & 3;
         const int32_t k = k0 + 8 * g;
         uint16_t e[8];
         const uint16_t *row = P + base + static_cast<int64_t>(r) * xs;
 #pragma unroll
         for (int t = 0; t < 8; ++t) e[t] = (r < xlen && k + t < K) ? row[k + t] : uint16_t(0);
-        *reinterpret_cast<uint4 *>(lds + r * 64 + 8 * fa_slot(r, g)) = u4_from(e);
+        *reinterpret_cast<uint4 *>(lds + r * FB_BK + 8 * fa_slot(r, g)) = u4_from(e);
     }
 }
 
@@ -149,15 +179,15 @@ __device__ __forceinline__ void dense_fill_ncontig(int64_t base, int64_t ks, int
                                                    const uint16_t *P, uint16_t *lds) {
     const int32_t tid = threadIdx.x;
 #pragma unroll 1
-    for (int q = 0; q < 4; ++q) {
-        const int32_t u = tid + 256 * q;         // 1024 granules: k row u >> 4, 8-column piece u & 15
+    for (int q = 0; q < FB_BK * 16 / 256; ++q) {
+        const int32_t u = tid + 256 * q;         // k row u / 16, 8-column piece u % 16
         const int32_t kr = u >> 4, s = u & 15;
         const int32_t n = 8 * s, k = k0 + kr;
         uint16_t e[8];
         const uint16_t *row = P + base + static_cast<int64_t>(k) * ks;
 #pragma unroll
         for (int t = 0; t < 8; ++t) e[t] = (k < K && n + t < nlen) ? row[n + t] : uint16_t(0);
-        *reinterpret_cast<uint4 *>(lds + kr * 128 + 32 * fb_pos(kr, n >> 5) + 8 * ((n >> 3) & 3)) = u4_from(e);
+        *reinterpret_cast<uint4 *>(lds + kr * FB_BN + 32 * fb_pos(kr, n >> 5) + 8 * ((n >> 3) & 3)) = u4_from(e);
     }
 }
 
@@ -170,81 +200,109 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // for that copy first), and, with scheduling barriers around the MFMAs, keeps
 // the reads of K-step s+1 in flight while step s runs on the matrix cores.
 // frag_wait waits for all LDS reads; naming the fragments as its outputs keeps
-// every use after it.
+// every use after it.  Every read is a per-chunk base address plus an
+// immediate offset, so the addresses cost a few registers per wave.
 typedef int v4i32_t __attribute__((ext_vector_type(4)));
 
+template <int OFF>
 __device__ __forceinline__ void lds_read_b128(uint32_t ad, v4i32_t &r) {
-    asm volatile("ds_read_b128 %0, %1" : "=&v"(r) : "v"(ad) : "memory");
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(r) : "v"(ad), "i"(OFF) : "memory");
 }
 
-__device__ __forceinline__ void lds_read_tr4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, v4i16_t &r0,
-                                             v4i16_t &r1, v4i16_t &r2, v4i16_t &r3) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4\n\t"
-        "ds_read_b64_tr_b16 %1, %5\n\t"
-        "ds_read_b64_tr_b16 %2, %6\n\t"
-        "ds_read_b64_tr_b16 %3, %7"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-        : "memory");
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr(uint32_t ad, v4i16_t &r) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=&v"(r) : "v"(ad), "i"(OFF) : "memory");
 }
 
-// Operand fragments of one K-step (16) for the 2 x 2 MFMA tiles.
+// Per-lane byte offsets of a wave's fragment reads within a stage, fixed for
+// the whole tile.  A rows wm*128 + f*32 + (lane % 32) read k-granule
+// 2 ks + lane / 32; the row swizzle has period 16, so f moves the address by
+// f * 2 KB and ks flips bit 5 of it.  N-contiguous B: lane (gk, half, p) reads
+// k rows 16 ks + 8 gk + 4 h2 + p / 4 (h2 and ks move the address by 1 KB and
+// 4 KB), columns wn*64 + f*32 + 16 half + 4 (p % 4); f flips bit 6.
+struct FragOff {
+    uint32_t a[2];   // A, by K-step
+    uint32_t b[2];   // K-contiguous B by K-step; N-contiguous B by column fragment
+};
+
+template <bool BN>
+__device__ __forceinline__ FragOff frag_offsets() {
+    const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int32_t wm = w & 1, wn = w >> 1;
+    FragOff o;
+    const int32_t ra = wm * (FB_BM / 2) + (lane & 31);
+    o.a[0] = 2 * (ra * FB_BK + 8 * fa_slot(ra, lane >> 5));
+    o.a[1] = o.a[0] ^ 32;
+    if constexpr (BN) {
+        const int32_t hh = lane >> 4, p = lane & 15;
+        const int32_t k = 8 * (hh >> 1) + (p >> 2);
+        const int32_t n = wn * 64 + 16 * (hh & 1) + 4 * (p & 3);
+        o.b[0] = 2 * (FB_A_STAGE + k * FB_BN + 32 * fb_pos(k, n >> 5) + (n & 31));
+        o.b[1] = o.b[0] ^ 64;
+    } else {
+        const int32_t rb = wn * 64 + (lane & 31);
+        o.b[0] = 2 * (FB_A_STAGE + rb * FB_BK + 8 * fa_slot(rb, lane >> 5));
+        o.b[1] = o.b[0] ^ 32;
+    }
+    return o;
+}
+
+// Operand fragments of one K-step (16) of one wave: four row fragments of A,
+// two column fragments of B.
 struct Frags {
-    v4i32_t a[2];
+    v4i32_t a[FB_FM];
     v4i32_t b[2];     // K-contiguous B
     v4i16_t t[4];     // N-contiguous B: transposed halves
 };
 
-template <bool BN>
-__device__ __forceinline__ void frag_issue(const uint16_t *la, const uint16_t *lb, int32_t ks, Frags &fr) {
-    const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int32_t wm = w & 1, wn = w >> 1;
+// stage: LDS byte address of the stage; va / vb: its per-lane read bases
+template <bool BN, int KS>
+__device__ __forceinline__ void frag_issue(uint32_t va, uint32_t vb0, uint32_t vb1, Frags &fr) {
     if constexpr (BN) {
-        const int32_t hh = lane >> 4, p = lane & 15;
-        const int32_t gk = hh >> 1, noff = 16 * (hh & 1);
-        uint32_t ad[4];
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            const int32_t n = wn * 64 + f * 32 + noff + 4 * (p & 3);
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int32_t k = ks * 16 + 8 * gk + 4 * h2 + (p >> 2);
-                ad[2 * f + h2] = lds_addr(lb + k * 128 + 32 * fb_pos(k, n >> 5) + (n & 31));
-            }
-        }
-        lds_read_tr4(ad[0], ad[1], ad[2], ad[3], fr.t[0], fr.t[1], fr.t[2], fr.t[3]);
+        constexpr int KO = 2 * 16 * KS * FB_BN;   // 16 k rows per step
+        constexpr int HO = 2 * 4 * FB_BN;         // 4 k rows per half
+        lds_read_tr<KO>(vb0, fr.t[0]);
+        lds_read_tr<KO + HO>(vb0, fr.t[1]);
+        lds_read_tr<KO>(vb1, fr.t[2]);
+        lds_read_tr<KO + HO>(vb1, fr.t[3]);
     } else {
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            const int32_t r = wn * 64 + f * 32 + (lane & 31);
-            lds_read_b128(lds_addr(lb + r * 64 + 8 * fa_slot(r, 2 * ks + (lane >> 5))), fr.b[f]);
-        }
+        lds_read_b128<0>(vb0, fr.b[0]);
+        lds_read_b128<2 * 32 * FB_BK>(vb0, fr.b[1]);
     }
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        const int32_t r = wm * 64 + f * 32 + (lane & 31);
-        lds_read_b128(lds_addr(la + r * 64 + 8 * fa_slot(r, 2 * ks + (lane >> 5))), fr.a[f]);
-    }
+    lds_read_b128<0>(va, fr.a[0]);
+    lds_read_b128<1 * 2 * 32 * FB_BK>(va, fr.a[1]);
+    lds_read_b128<2 * 2 * 32 * FB_BK>(va, fr.a[2]);
+    lds_read_b128<3 * 2 * 32 * FB_BK>(va, fr.a[3]);
 }
 
 template <bool BN>
 __device__ __forceinline__ void frag_wait(Frags &fr) {
+    static_assert(FB_FM == 4, "four row fragments per wave");
     if constexpr (BN)
         asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(fr.a[0]), "+v"(fr.a[1]), "+v"(fr.t[0]), "+v"(fr.t[1]), "+v"(fr.t[2]), "+v"(fr.t[3])
+                     : "+v"(fr.a[0]), "+v"(fr.a[1]), "+v"(fr.a[2]), "+v"(fr.a[3]), "+v"(fr.t[0]), "+v"(fr.t[1]),
+                       "+v"(fr.t[2]), "+v"(fr.t[3])
                      :
                      : "memory");
     else
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fr.a[0]), "+v"(fr.a[1]), "+v"(fr.b[0]), "+v"(fr.b[1]) : : "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(fr.a[0]), "+v"(fr.a[1]), "+v"(fr.a[2]), "+v"(fr.a[3]), "+v"(fr.b[0]), "+v"(fr.b[1])
+                     :
+                     : "memory");
 }
 
+// The MFMAs of one K-step.  Fragments past the tile edge are computed too
+// (their rows were loaded clamped to a valid row): conditional MFMAs would make
+// the accumulators merge across branches, which costs far more than the work.
 template <bool BN>
-__device__ __forceinline__ void frag_mfma(const Frags &fr, f32x16_t (&acc)[2][2]) {
-    bf16x8_t fa[2], fb[2];
+__device__ __forceinline__ void frag_mfma(const Frags &fr, f32x16_t (&acc)[FB_FM][2]) {
+    bf16x8_t fa[FB_FM], fb[2];
+#pragma unroll
+    for (int f = 0; f < FB_FM; ++f) fa[f] = __builtin_bit_cast(bf16x8_t, fr.a[f]);
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-        fa[f] = __builtin_bit_cast(bf16x8_t, fr.a[f]);
         if constexpr (BN) {
             const v4i16_t lo = fr.t[2 * f], hi = fr.t[2 * f + 1];
             short e8 __attribute__((ext_vector_type(8))) = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -254,29 +312,85 @@ __device__ __forceinline__ void frag_mfma(const Frags &fr, f32x16_t (&acc)[2][2]
         }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FB_FM; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
-// One K chunk (4 steps of 16) with the fragment reads of step s+1 in flight
-// while the matrix cores run step s.
-template <bool BN>
-__device__ __forceinline__ void fast_chunk(const uint16_t *la, const uint16_t *lb, f32x16_t (&acc)[2][2]) {
-    Frags cur, nxt;
-    frag_issue<BN>(la, lb, 0, cur);
-    frag_wait<BN>(cur);
+// Fragment reads of one K-step (0 or 1) of the chunk whose stage starts at
+// LDS byte address `stage`.
+template <bool BN, int KS>
+__device__ __forceinline__ void frag_step(uint32_t stage, const FragOff &o, Frags &fr) {
+    static_assert(FB_BK == 32, "two K-steps per chunk");
+    // K-contiguous B: one base per K-step; N-contiguous B: one per column fragment
+    const uint32_t vb0 = stage + o.b[0], vb1 = stage + o.b[1];
+    if constexpr (BN) frag_issue<BN, KS>(stage + o.a[KS], vb0, vb1, fr);
+    else frag_issue<BN, KS>(stage + o.a[KS], KS ? vb1 : vb0, vb1, fr);
+}
+
+// K split: one slice of the tile is done.  The slice stores its partial tile
+// (lane-contiguous: 16-byte group q of lane l at q * 64 + l within the wave's
+// block), waits until the stores are complete, then counts itself in the
+// tile's counter.  Returns false for every slice but the last; the last resets
+// the counter for the next launch and reloads its accumulators as the sum of
+// all partials taken in slice order, so the result does not depend on which
+// slice finishes last.
+//
+// Slices run on different CUs, possibly on different chiplets, whose L2
+// caches are not kept coherent with each other.  The partials are therefore
+// written and read with device-coherent buffer accesses (the sc1 cache policy
+// that device-scope atomic loads and stores use, here without their
+// one-at-a-time waits), and the counter is a device-scope atomic; no
+// device-scope fence, whose whole-cache write-back and invalidation would
+// stall every other workgroup on the chiplet.  The buffer descriptor covers
+// exactly the tile's partials, so the hardware drops any access outside them.
+constexpr int32_t BUF_DWORD3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
+constexpr int32_t CPOL_SC1 = 16;             // device-coherent cache policy
+
+__device__ __forceinline__ bool split_arrive(const KArgs &ka, const DFast &fd, f32x16_t (&acc)[FB_FM][2], int32_t w,
+                                             int32_t lane, int32_t &last) {
+    constexpr int SPLIT_BYTES = FB_BM * FB_BN * 4;   // one partial tile
+    constexpr int NQ = FB_FM * 2 * 4;                 // 16-byte groups per lane (32)
+    // the record is wave-uniform: build the descriptor in scalar registers
+    const uint64_t base = reinterpret_cast<uint64_t>(ka.P + fd.part);
+    const uint64_t ubase = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(base >> 32))) << 32) |
+                           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(base)));
+    const int32_t nsplit = __builtin_amdgcn_readfirstlane(fd.nsplit);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ubase), 0, nsplit * SPLIT_BYTES, BUF_DWORD3);
+    const int32_t lane_off = (w * NQ * 64 + lane) * 16;
+    const int32_t mine = fd.split * SPLIT_BYTES + lane_off;
 #pragma unroll
-    for (int32_t ks = 0; ks < 4; ++ks) {
-        if (ks < 3) frag_issue<BN>(la, lb, ks + 1, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-        frag_mfma<BN>(cur, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks < 3) {
-            frag_wait<BN>(nxt);
-            cur = nxt;
+    for (int q = 0; q < NQ; ++q) {
+        const f32x16_t &a = acc[q / 8][(q / 4) & 1];
+        const int r = 4 * (q & 3);
+        const f32x4_t v = {a[r], a[r + 1], a[r + 2], a[r + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i32_t, v), rs, mine + q * 1024, 0, CPOL_SC1);
+    }
+    wait_vm<0>();   // this wave's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int32_t before = __hip_atomic_fetch_add(ka.cnt + fd.counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = before == fd.nsplit - 1;
+        if (last) __hip_atomic_store(ka.cnt + fd.counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return false;
+    for (int32_t s = 0; s < nsplit; ++s) {
+        const int32_t src = s * SPLIT_BYTES + lane_off;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            f32x16_t &a = acc[q / 8][(q / 4) & 1];
+            const int r = 4 * (q & 3);
+            // (the whole vector is reinterpreted at once: extracting single lanes of
+            // the loaded integer vector through bit casts is narrowed to a
+            // one-dword load by this compiler)
+            const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, src + q * 1024, 0, CPOL_SC1));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[r + e] = s == 0 ? x[e] : a[r + e] + x[e];
         }
     }
+    return true;
 }
 
 template <typename TC, bool BN>
@@ -285,24 +399,34 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
     const uint16_t *A = static_cast<const uint16_t *>((fd.flags & F_A_WS) ? ka.W : ka.A);
     const uint16_t *B = static_cast<const uint16_t *>((fd.flags & F_B_WS) ? ka.W : ka.B);
     const int32_t mlen = fd.mlen, nlen = fd.nlen, K = fd.K;
+    // the wave index through a scalar register, so tests on it are scalar branches
+    const int32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[FB_FM][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FB_FM; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const FastOp fa = dense_setup_kcontig(fd.a_base, fd.a_rs, mlen, A);
+    const FastOp<FB_NIA> fa = dense_setup_kcontig<FB_NIA>(fd.a_base, fd.a_rs, mlen, A);
     const int64_t b_s = BN ? fd.b_ks : fd.b_ns;   // stride of B's non-contiguous axis
-    const FastOp fb = BN ? dense_setup_ncontig(fd.b_base, b_s, nlen, B) : dense_setup_kcontig(fd.b_base, b_s, nlen, B);
+    FastOp<FB_NIB> fb;
+    if constexpr (BN) fb = dense_setup_ncontig<FB_NIB>(fd.b_base, b_s, nlen, B);
+    else fb = dense_setup_kcontig<FB_NIB>(fd.b_base, b_s, nlen, B);
     const int32_t nfull = K / FB_BK;
     const int32_t ntot = (K + FB_BK - 1) / FB_BK;
+    const bool a_live = 16 * FB_NIA * w < mlen;   // this wave's A copies reach a row inside the tile
+    const FragOff fo = frag_offsets<BN>();
     auto fill_partial = [&](int32_t stage) {
-        dense_fill_kcontig(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, sm.op[stage][0]);
-        if (BN) dense_fill_ncontig(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, sm.op[stage][1]);
-        else dense_fill_kcontig(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, sm.op[stage][1]);
+        dense_fill_kcontig<FB_BM>(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, sm.op[stage]);
+        if constexpr (BN) dense_fill_ncontig(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, sm.op[stage] + FB_A_STAGE);
+        else dense_fill_kcontig<FB_BN>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, sm.op[stage] + FB_A_STAGE);
+    };
+    auto issue = [&](int32_t c, int32_t stage) {
+        if (a_live) fast_issue<FB_NIA>(fa, c, sm.op[stage]);
+        fast_issue<FB_NIB>(fb, c, sm.op[stage] + FB_A_STAGE);
     };
     wait_vm<0>();      // nothing else outstanding: the counted waits below see only this tile's copies
     __syncthreads();   // previous users of the LDS ring are done
@@ -310,32 +434,60 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
 #pragma unroll
     for (int32_t p = 0; p < FB_STAGES - 1; ++p) {
         if (p < nfull) {
-            fast_issue(fa, p, sm.op[p][0]);
-            fast_issue(fb, p, sm.op[p][1]);
+            issue(p, p);
             ++issued;
         }
     }
     if (nfull < ntot && nfull <= FB_STAGES - 2) fill_partial(nfull);
-    for (int32_t c = 0; c < ntot; ++c) {
-        if (c < nfull) wait_vm_chunks(issued - c - 1);   // this wave's copies of chunk c have landed
-        lds_barrier();                                  // ... and every other wave's
-        const int32_t nx = c + FB_STAGES - 1;           // refill the stage chunk c-1 used
+    // Make chunk cn readable: this wave's copies of it have landed, then the
+    // barrier (every wave's have, and every wave is done reading chunk cn - 1,
+    // whose stage is refilled with chunk cn + FB_STAGES - 1).
+    auto advance = [&](int32_t cn) {
+        if (cn < nfull) {
+            if (a_live) wait_vm_chunks<FB_NIA + FB_NIB>(issued - cn - 1);
+            else wait_vm_chunks<FB_NIB>(issued - cn - 1);
+        }
+        lds_barrier();
+        const int32_t nx = cn + FB_STAGES - 1;
         const int32_t st = nx % FB_STAGES;
         if (nx < nfull) {
-            fast_issue(fa, nx, sm.op[st][0]);
-            fast_issue(fb, nx, sm.op[st][1]);
+            issue(nx, st);
             ++issued;
         } else if (nx == nfull && nfull < ntot) {
             fill_partial(st);
         }
-        const int32_t cs = c % FB_STAGES;
-        fast_chunk<BN>(sm.op[cs][0], sm.op[cs][1], acc);
+    };
+    auto stage_addr = [&](int32_t c) { return lds_addr(sm.op[c % FB_STAGES]); };
+    // K loop, software-pipelined across chunks: the reads of step 1 of chunk c
+    // overlap the MFMAs of step 0, and the reads of step 0 of chunk c + 1 (after
+    // the hand-over barrier) overlap the MFMAs of step 1.
+    Frags s0, s1;
+    advance(0);
+    frag_step<BN, 0>(stage_addr(0), fo, s0);
+    frag_wait<BN>(s0);
+    for (int32_t c = 0; c < ntot; ++c) {
+        frag_step<BN, 1>(stage_addr(c), fo, s1);
+        __builtin_amdgcn_sched_barrier(0);
+        frag_mfma<BN>(s0, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        frag_wait<BN>(s1);
+        const bool more = c + 1 < ntot;
+        if (more) {
+            advance(c + 1);
+            frag_step<BN, 0>(stage_addr(c + 1), fo, s0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        frag_mfma<BN>(s1, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) frag_wait<BN>(s0);
     }
+
+    const int32_t lane = threadIdx.x & 63;
+    if (fd.nsplit > 1 && !split_arrive(ka, fd, acc, w, lane, sm.last)) return;
 
     // epilogue: straight from the accumulators, 32 consecutive columns per row
     TC *Cp = static_cast<TC *>(ka.C);
     const bool accum = (fd.flags & G_ACCUMULATE) != 0;
-    const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int32_t wm = w & 1, wn = w >> 1;
 #pragma unroll
     for (int fj = 0; fj < 2; ++fj) {
@@ -343,10 +495,10 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
         if (j >= nlen) continue;
         TC *col = Cp + fd.c_base + static_cast<int64_t>(j) * fd.c_cs;
 #pragma unroll
-        for (int fi = 0; fi < 2; ++fi)
+        for (int fi = 0; fi < FB_FM; ++fi)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int32_t i = wm * 64 + fi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int32_t i = wm * (FB_BM / 2) + fi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 if (i >= mlen) continue;
                 TC *dst = col + static_cast<int64_t>(i) * fd.c_rs;
                 float v = acc[fi][fj][r];

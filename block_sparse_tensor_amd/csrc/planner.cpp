@@ -734,6 +734,9 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         p.tasks.clear();
         p.fast.clear();
         p.launches.clear();
+        p.n_counters = 0;
+        p.part_elems = 0;
+        p.split_tiles = 0;
         // tile class per group: matrix-core tiles where the group is more than a
         // single instruction's worth of work, vector-ALU tiles for the tiny tail
         auto class_of = [&](const DGroup &g) -> int32_t {
@@ -807,6 +810,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             f.K = r.K;
             f.group = gi;
             f.flags = (g.flags & G_ACCUMULATE) | ((r.flags & R_A_WS) ? F_A_WS : 0) | ((r.flags & R_B_WS) ? F_B_WS : 0);
+            f.nsplit = 1;
             return true;
         };
         // Skinny groups of one run whose views are all single-leg become items
@@ -886,6 +890,41 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             if (cls == T_MFMA || cls == T_MFMA_DENSE) return p.dtype == BSC_BF16_F32 ? 16.0 : 4.0;
             return 1.0;
         };
+        // K split of the bf16 direct-to-LDS tiles (grouped launches only): a tile
+        // whose K chain is much longer than one slot's share of the plan's work
+        // would alone set the launch's duration, so it is cut into K-slices of
+        // about that share.  Every slice moves a 128 KB partial tile through
+        // device-coherent memory and the last one reads them all back, which on
+        // MI355X costs more than the shorter chain saves unless the slices stay
+        // long: automatic slices are at least SPLIT_MIN_CHUNKS chunks of 32
+        // (K >= 2048), so only very long K chains are cut.
+        constexpr int32_t SPLIT_CHUNK = 32, SPLIT_MIN_CHUNKS = 64, SPLIT_MAX = 32;
+        int64_t split_target = 0;   // most chunks per slice; 0: no split
+        if (!per_sector && p.dtype == BSC_BF16_F32 && p.opt.split_k >= 0) {
+            if (p.opt.split_k > 0) {
+                split_target = p.opt.split_k;
+            } else {
+                double total = 0;
+                for (int32_t gi = 0; gi < p.n_work_groups; ++gi) {
+                    const DGroup &g = p.groups[(size_t)gi];
+                    const int32_t cls = class_of(g);
+                    if (cls != T_MFMA_FAST_N && cls != T_MFMA_FAST_K) continue;
+                    total += (double)((g.M + TILE_MFMA_DENSE_M - 1) / TILE_MFMA_DENSE_M) *
+                             (double)((g.N + TILE_MFMA - 1) / TILE_MFMA) * (double)((g.K + SPLIT_CHUNK - 1) / SPLIT_CHUNK);
+                }
+                split_target = std::max<int64_t>(SPLIT_MIN_CHUNKS, (int64_t)std::ceil(total / CONCURRENT_TILES));
+            }
+        }
+        // slices of a tile with K contracted indices (1: no split)
+        auto slices_of = [&](int32_t K) -> int32_t {
+            if (split_target <= 0) return 1;
+            const int64_t chunks = (K + SPLIT_CHUNK - 1) / SPLIT_CHUNK;
+            if (p.opt.split_k == 0 && chunks <= 2 * split_target) return 1;   // automatic: only clear wins
+            int64_t S = std::min<int64_t>(SPLIT_MAX, (chunks + split_target - 1) / split_target);
+            if (S <= 1) return 1;
+            const int64_t per = (chunks + S - 1) / S;   // chunks per slice; the last slice takes the rest
+            return (int32_t)((chunks + per - 1) / per);
+        };
         auto tiles_of = [&](int32_t gi, std::vector<DTask> &out, std::vector<double> *cost) {
             const DGroup &g = p.groups[(size_t)gi];
             const int32_t cls = class_of(g);
@@ -901,6 +940,35 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                         // bf16 direct-to-LDS tiles always qualify; fp32 / fp64 tiles that do
                         // become record-addressed dense tiles
                         const int32_t c2 = cls == T_MFMA ? (p.dtype == BSC_BF16_F32 ? T_MFMA : T_MFMA_DENSE) : cls;
+                        const int32_t S = (c2 == T_MFMA_FAST_N || c2 == T_MFMA_FAST_K) ? slices_of(f.K) : 1;
+                        if (S > 1) {
+                            // K-slices of SPLIT_CHUNK multiples (only the last may end in a partial chunk)
+                            const int32_t chunks = (f.K + SPLIT_CHUNK - 1) / SPLIT_CHUNK;
+                            const int32_t per = (chunks + S - 1) / S;
+                            const int32_t counter = p.n_counters++;
+                            const int64_t part = p.part_elems;
+                            p.part_elems += (int64_t)S * TILE_MFMA_DENSE_M * TILE_MFMA;
+                            p.split_tiles++;
+                            for (int32_t sl = 0; sl < S; ++sl) {
+                                DFast fs = f;
+                                const int32_t k0 = sl * per * SPLIT_CHUNK;
+                                fs.K = std::min(f.K, k0 + per * SPLIT_CHUNK) - k0;
+                                fs.a_base += (int64_t)k0 * f.a_ks;
+                                fs.b_base += (int64_t)k0 * f.b_ks;
+                                fs.split = sl;
+                                fs.nsplit = S;
+                                fs.counter = counter;
+                                fs.part = part;
+                                out.push_back({c2, (int32_t)p.fast.size(), m0, n0});
+                                p.fast.push_back(fs);
+                                if (cost) {
+                                    const double mlf = ml, nlf = nl;
+                                    // the slice's flops, its partial tile out, and the last slice's reads
+                                    cost->push_back((2.0 * mlf * nlf * fs.K) / rate_of(cls) + 8.0 * mlf * nlf + 2.0e4);
+                                }
+                            }
+                            continue;
+                        }
                         if (c2 != T_MFMA) {
                             out.push_back({c2, (int32_t)p.fast.size(), m0, n0});
                             p.fast.push_back(f);
@@ -1015,9 +1083,11 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         p.off_fast = off;   off = align(off + p.fast.size() * sizeof(DFast));
         p.off_packs = off;  off = align(off + p.packs.size() * sizeof(DPack));
         p.off_ptasks = off; off = align(off + p.pack_tasks.size() * sizeof(DTask));
+        p.off_cnt = off;    off = align(off + (size_t)p.n_counters * sizeof(int32_t));   // zero in the image
         p.image.assign(std::max<size_t>(off, 256), 0);
         p.off_ws = p.image.size();
-        p.dev_bytes = p.off_ws + (size_t)(p.ws_elems * esz);
+        p.off_part = align(p.off_ws + (size_t)(p.ws_elems * esz));
+        p.dev_bytes = p.off_part + (size_t)p.part_elems * sizeof(float);
         auto put = [&](size_t o, const void *src, size_t nbytes) { if (nbytes) std::memcpy(p.image.data() + o, src, nbytes); };
         put(p.off_groups, p.groups.data(), p.groups.size() * sizeof(DGroup));
         put(p.off_runs, p.runs.data(), p.runs.size() * sizeof(DRun));
@@ -1070,6 +1140,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         for (auto &d : p.packs) s.pack_bytes += (int64_t)d.rows * d.cols * ab;
         s.device_bytes = (int64_t)p.dev_bytes;
         s.tail_triples = tail;
+        s.split_tiles = p.split_tiles;
         const double rate_gflops = p.dtype == BSC_BF16_F32 ? 2.5e6 : (p.dtype == BSC_F32 ? 157.3e3 : 78.6e3);
         s.predicted_us = s.launches_per_contract * p.opt.t_launch_us +
                          std::max((double)flops / (rate_gflops * 1e3), (double)s.alg_bytes / 8.0e6) +

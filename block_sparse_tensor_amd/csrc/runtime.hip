@@ -87,8 +87,17 @@ __device__ __forceinline__ void grouped_body(const KArgs &ka) {
         if constexpr ((FEAT & FEAT_MFMA) != 0) {
             if (is_mfma(task.cls)) {
                 if constexpr (std::is_same<TA, uint16_t>::value) {
-                    static_assert(TILE_MFMA_DENSE_M == TILE_MFMA, "a dense task must fit one general tile");
+                    // a direct-to-LDS task run on the general tile (a launch whose operand
+                    // bases are not 16-byte aligned) covers its rows in two halves; of the
+                    // K-slices of a split tile, the first computes the whole tile
+                    static_assert(TILE_MFMA_DENSE_M <= 2 * TILE_MFMA, "a dense task fits two general tiles");
+                    if (task.cls != T_MFMA && ka.fast[ti].nsplit > 1 && ka.fast[ti].split != 0) continue;
                     mfma_tile_bf16<TC>(ka, task, sm.m);
+                    if (task.cls != T_MFMA && ka.fast[ti].mlen > TILE_MFMA) {
+                        DTask lower = task;
+                        lower.m0 += TILE_MFMA;
+                        mfma_tile_bf16<TC>(ka, lower, sm.m);
+                    }
                 } else {
                     mfma_tile_f<TA>(ka, task, ka.fast[ti], sm.m);
                 }
@@ -228,6 +237,8 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
     ka.B = B;
     ka.C = C;
     ka.W = base + p->off_ws;
+    ka.P = reinterpret_cast<float *>(const_cast<unsigned char *>(base) + p->off_part);
+    ka.cnt = reinterpret_cast<int32_t *>(const_cast<unsigned char *>(base) + p->off_cnt);
     if (!p->pack_tasks.empty()) {
         // gathers first, on the same stream: the grouped launch reads the workspace after them
         PArgs pa;

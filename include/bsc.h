@@ -141,6 +141,18 @@ typedef struct {
     double t_seg_us;        /* extra cost per piece one tile walks beyond one per k-segment */
     double pack_gbps;       /* gather bandwidth, counting read + write bytes */
     double tile_gflops;     /* sustained whole-GPU rate of the matrix-core tiles */
+    /* K split of the bf16 direct-to-LDS tiles (uni20 "block coalescing":
+     * enough independent work to fill the machine).  A 256 x 128 output tile
+     * whose K chain is much longer than the plan's work per concurrent tile
+     * slot is cut into K-slices that run as separate work items; the last
+     * slice to finish adds the fp32 partial tiles in slice order (so results
+     * do not depend on timing) and writes C.  The partials travel through
+     * device-coherent memory, so splitting pays only for very long K chains.
+     * 0: automatic (a tile is cut when its K exceeds twice the larger of
+     * 64 x 32 and one slot's share of the plan's work, into slices of about
+     * that length); -1: never split; n > 0: slices of at most n x 32 K. */
+    int32_t split_k;
+    int32_t reserved;
 } bsc_options;
 
 typedef struct {
@@ -166,7 +178,7 @@ typedef struct {
     int64_t tail_triples;            /* triples with 2 M N K <= 1024 */
     int64_t launches_issued;         /* launches enqueued by this plan so far */
     int32_t grid;                    /* workgroups of the grouped launch */
-    int32_t reserved;
+    int32_t split_tiles;             /* output tiles whose K is cut into slices (see split_k) */
     double predicted_us;             /* cost-model estimate of one contraction */
 } bsc_stats;
 
@@ -183,7 +195,8 @@ bsc_status bsc_plan(const bsc_index *m, const bsc_index *k, const bsc_index *n,
                     const bsc_operand *A, const bsc_operand *B, const bsc_operand *C,
                     bsc_dtype dtype, bsc_axis axis, const bsc_options *opt, bsc_plan_t *out);
 
-/* Bytes of device memory bsc_plan_bind needs (work list + pack workspace). */
+/* Bytes of device memory bsc_plan_bind needs (work list + pack workspace +
+ * K-split partial tiles). */
 bsc_status bsc_plan_device_bytes(bsc_plan_t plan, size_t *bytes);
 
 /* Upload the work list into the caller's device region `dev` (>= device_bytes,
@@ -219,6 +232,8 @@ typedef struct {
     int64_t workspace_elems; /* pack workspace size in operand elements */
     int64_t bytes;           /* size of the work-list image */
     int64_t n_launches;      /* launches per contraction */
+    int64_t n_counters, off_counters;   /* K-split arrival counters (int32, in the image, zero) */
+    int64_t off_partials, partial_elems; /* K-split partial tiles (fp32, after the workspace) */
 } bsc_worklist_info;
 
 /* Fill *info and, if image != NULL and bytes >= info->bytes, copy the host

@@ -17,18 +17,20 @@ DGROUP = np.dtype([(n, "<i4") for n in ("M", "N", "K", "nrun", "run0", "ncp", "c
 DRUN = np.dtype([(n, "<i4") for n in ("K", "nap", "ap0", "nbp", "bp0", "flags", "kbase", "pad")])
 DTASK = np.dtype([(n, "<i4") for n in ("cls", "group", "m0", "n0")])
 DFAST = np.dtype([(n, "<i8") for n in ("a_base", "a_rs", "a_ks", "b_base", "b_ks", "b_ns", "c_base", "c_rs", "c_cs")] +
-                 [(n, "<i4") for n in ("mlen", "nlen", "K", "flags", "group", "pad")])
+                 [(n, "<i4") for n in ("mlen", "nlen", "K", "flags", "group", "split", "nsplit", "counter")] +
+                 [("part", "<i8")])
 DPACK = np.dtype([(n, "<i8") for n in ("off", "sa0", "sa1", "sb0", "sb1", "dst")] +
                  [(n, "<i4") for n in ("ia", "ib", "rows", "cols", "ld", "src", "dmode", "pad")])
 R_A_WS, R_B_WS = 128, 256          # run reads A / B from the pack workspace
 F_A_WS, F_B_WS = 4, 8              # dense record reads A / B from the pack workspace
 G_C_ALONG_N, G_ACCUMULATE = 1, 2
 T_GENERIC, T_MFMA, T_TAIL, T_ZERO = 0, 1, 2, 3
-TILE = {T_GENERIC: (64, 64), T_ZERO: (64, 64), T_MFMA: (128, 128), 4: (128, 128), 5: (128, 128)}
+TILE = {T_GENERIC: (64, 64), T_ZERO: (64, 64), T_MFMA: (128, 128), 4: (256, 128), 5: (256, 128)}
 TILE_MFMA_F = (64, 64)   # fp32 / fp64 matrix-core tile
 
 assert DVIEW.itemsize == 56 and DGROUP.itemsize == 32 and DRUN.itemsize == 32 and DTASK.itemsize == 16
-assert DFAST.itemsize == 96 and DPACK.itemsize == 80
+assert DFAST.itemsize == 112 and DPACK.itemsize == 80
+SPLIT_TILE = 256 * 128   # fp32 elements of one K-slice partial tile
 T_DENSE_N, T_DENSE_K = 4, 5
 T_MFMA_DENSE = 9                  # fp32 / fp64 record-addressed matrix-core tile
 T_SKINNY_DENSE = (10, 11)         # record-addressed skinny items (long axis M / N)
@@ -107,6 +109,7 @@ def replay(plan, con, a, b, c0, accumulate=False):
     written = np.zeros(c.size, np.int64)
     a64, b64 = np.asarray(a, np.float64), np.asarray(b, np.float64)
     ws, ws_written = replay_packs(plan, con, a64, b64)
+    splits = {}   # K-split tiles by counter: the partials of their slices
     for t in tasks:
         if t["cls"] == 6:      # no-op placeholder
             continue
@@ -133,6 +136,17 @@ def replay(plan, con, a, b, c0, accumulate=False):
                 if f["flags"] & flag:
                     assert ws_written[ad].all(), "a tile reads a workspace element no gather wrote"
             acc = abuf[aad] @ bbuf[bad]
+            if f["nsplit"] > 1:
+                # K-slice of a split tile: its partial waits for the other slices
+                assert t["cls"] in (T_DENSE_N, T_DENSE_K) and 0 <= f["split"] < f["nsplit"]
+                assert 0 <= f["counter"] < info["n_counters"]
+                assert 0 <= f["part"] and f["part"] + f["nsplit"] * SPLIT_TILE <= info["partial_elems"]
+                slot = splits.setdefault(int(f["counter"]), {"n": int(f["nsplit"]), "part": int(f["part"]),
+                                                             "cad": cad, "f": f, "p": {}})
+                assert slot["n"] == f["nsplit"] and slot["part"] == f["part"] and np.array_equal(slot["cad"], cad)
+                assert int(f["split"]) not in slot["p"], "a K-slice appears twice"
+                slot["p"][int(f["split"])] = (acc, aad[0, :], int(f["K"]))
+                continue
             if f["flags"] & G_ACCUMULATE:
                 acc = acc + c[cad]
             c[cad] = acc
@@ -177,6 +191,25 @@ def replay(plan, con, a, b, c0, accumulate=False):
             acc = acc + c[cad]
         c[cad] = acc
         np.add.at(written, cad.ravel(), 1)
+    # K-split tiles: every slice once, slices cover consecutive K ranges, the
+    # partials summed in slice order
+    parts_used = np.zeros(info["partial_elems"], np.int64)
+    for slot in splits.values():
+        n, f = slot["n"], slot["f"]
+        assert sorted(slot["p"]) == list(range(n)), "a K-slice is missing"
+        krow = np.concatenate([slot["p"][s][1] for s in range(n)])   # A addresses along k of the first row
+        assert len(krow) == len(np.unique(krow)) and np.all(np.diff(krow) == f["a_ks"])
+        assert all(slot["p"][s][2] % 32 == 0 for s in range(n - 1)), "only the last slice may end in a partial chunk"
+        parts_used[slot["part"]:slot["part"] + n * SPLIT_TILE] += 1
+        acc = slot["p"][0][0]
+        for s in range(1, n):
+            acc = acc + slot["p"][s][0]
+        cad = slot["cad"]
+        if f["flags"] & G_ACCUMULATE:
+            acc = acc + c[cad]
+        c[cad] = acc
+        np.add.at(written, cad.ravel(), 1)
+    assert parts_used.max(initial=0) <= 1, "two split tiles share partial storage"
     return c, written
 
 
@@ -288,6 +321,75 @@ def test_replay_dense_random(seed):
         got, written = replay(plan, con, abuf, bbuf, c0)
         ref = oracle.contract(con, abuf, bbuf, c0, accumulate=acc)
         np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def _dense_con(M, K, N, brow):
+    """One aligned bf16 GEMM block: A row-major, B row- or column-major."""
+    from workloads.model import Contraction, Index, Operand
+    lda, ldb, ldk = (K + 7) // 8 * 8, (N + 7) // 8 * 8, (K + 7) // 8 * 8
+    brs, bcs = ((ldb, 0), (1, 0)) if brow else ((1, 0), (ldk, 0))
+    na, nb = M * lda + 16, K * ldb + N * ldb + 16
+    idx = lambda d: Index([[0]], [d])
+    return Contraction(idx(M), idx(K), idx(N), Operand([0], [0], [8], [(lda, 0)], [(1, 0)], [0], na),
+                       Operand([0], [0], [8], [brs], [bcs], [0], nb),
+                       Operand([0], [0], [5], [(N + 3, 0)], [(1, 0)], [0], 5 + M * (N + 3)), "bf16")
+
+
+def _dense_single(seed, M, K, N, brow):
+    from workloads.layout import write_block
+    rng = np.random.default_rng(seed)
+    con = _dense_con(M, K, N, brow)
+    A = rng.standard_normal((M, K)); B = rng.standard_normal((K, N))
+    abuf, bbuf = np.zeros(con.A.buffer_elems), np.zeros(con.B.buffer_elems)
+    write_block(abuf, 8, con.A.row_stride[0], con.A.col_stride[0], A)
+    write_block(bbuf, 8, con.B.row_stride[0], con.B.col_stride[0], B)
+    return con, abuf, bbuf
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 3, 5])
+@pytest.mark.parametrize("brow", [True, False])
+def test_replay_split_k(split_k, brow):
+    """K-split tiles: slices cover K in order, every slice once, partial
+    storage disjoint, and the summed partials give the oracle's result (also
+    when accumulating)."""
+    con, abuf, bbuf = _dense_single(40 + split_k, 300, 333, 150, brow)
+    for acc in (False, True):
+        plan = bst.Plan(con, accumulate=acc, split_k=split_k)
+        s = plan.stats()
+        tiles = 2 * 2   # 256 x 128 tiles over 300 x 150
+        assert s["split_tiles"] == tiles and s["items_by_class"]["mfma_fast"] == tiles * -(-11 // split_k)
+        info, *_ = decode(plan)
+        assert info["n_counters"] == tiles and info["partial_elems"] == tiles * -(-11 // split_k) * SPLIT_TILE
+        assert plan.device_bytes() >= info["off_partials"] + 4 * info["partial_elems"]
+        c0 = np.full(con.C.buffer_elems, 0.5)
+        got, written = replay(plan, con, abuf, bbuf, c0, accumulate=acc)
+        ref = oracle.contract(con, abuf, bbuf, c0, accumulate=acc)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+        assert written.max() == 1
+
+
+def test_split_k_policy():
+    """Automatic K split: only tiles whose K chain is far above both 64 chunks
+    and one slot's share of the plan's work; never in per-sector mode, with
+    split_k=-1, or for fp32."""
+    prob = C.blockdiag_bf16(ld_align=8, align=8, values=False)
+    assert bst.Plan(prob.con).stats()["split_tiles"] == 0          # K <= 1024
+    assert bst.Plan(prob.con, split_k=8).stats()["split_tiles"] > 0
+    assert bst.Plan(prob.con, split_k=8, launch_mode="per_sector").stats()["split_tiles"] == 0
+    for shape in ((4096, 4096, 4096), (2048, 2048, 2048), (1024, 1024, 1024)):
+        assert bst.Plan(_dense_con(*shape, True)).stats()["split_tiles"] == 0
+    # one tile with K = 32768 (1024 chunks): slices of 64 chunks
+    con = _dense_con(256, 32768, 128, True)
+    s = bst.Plan(con).stats()
+    assert s["split_tiles"] == 1 and s["items_by_class"]["mfma_fast"] == 16
+    assert bst.Plan(con, split_k=-1).stats()["split_tiles"] == 0
+    assert bst.Plan(con, split_k=100).stats()["items_by_class"]["mfma_fast"] == 11
+    # fp32 tiles are never split
+    con32 = _dense_con(256, 32768, 128, True)
+    con32.dtype = "f32"
+    assert bst.Plan(con32, split_k=4).stats()["split_tiles"] == 0
+    with pytest.raises(bst.BscError):
+        bst.Plan(con, split_k=-2)
 
 
 @pytest.mark.parametrize("seed", range(12))

@@ -36,6 +36,8 @@
 //  * results go straight from the accumulators to C (no staging).
 #pragma once
 
+#include <type_traits>
+
 #include "kernels_mfma_bf16.h"
 
 namespace bsc {
@@ -102,26 +104,43 @@ __device__ __forceinline__ int32_t fa_slot(int32_t r, int32_t g) { return g ^ fa
 // 64-byte granule (of 4) holding n-granule G in B-layout row k
 __device__ __forceinline__ int32_t fb_pos(int32_t k, int32_t G) { return G ^ (k & 3); }
 
+// Copies go through buffer descriptors: the tile's range of the operand in
+// scalar registers, one 32-bit lane offset per copy instruction, and the chunk
+// advance as the scalar offset (the planner keeps every tile range below
+// 2 GiB).  The descriptor's range also bounds every copy in hardware.
+constexpr int32_t BUF_DWORD3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t ua = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(a >> 32))) << 32) |
+                        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(a)));
+    const int32_t n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(bytes));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ua), 0, n, BUF_DWORD3);
+}
+
 template <int NI>
 struct FastOp {
-    const uint16_t *p[NI];   // per-instruction global pointers at chunk 0
-    int64_t step;            // elements to advance per chunk
+    __amdgpu_buffer_rsrc_t rs;   // the operand's range for this tile
+    uint32_t off[NI];            // per-instruction lane byte offsets at chunk 0
+    uint32_t step;               // bytes to advance per chunk
 };
 
 // K-contiguous operand ([x][k] layout), element (x, k) at base + x * xs + k:
 // wave w instruction j fills rows 16 (NI w + j) .. +16 (1 KB); lane l fills
 // row l / 4, slot l % 4, so it copies k-granule (l % 4) ^ fa_perm(row).
 template <int NI>
-__device__ __forceinline__ FastOp<NI> dense_setup_kcontig(int64_t base, int64_t xs, int32_t xlen, const uint16_t *P) {
+__device__ __forceinline__ FastOp<NI> dense_setup_kcontig(int64_t base, int64_t xs, int32_t xlen, int32_t K,
+                                                          const uint16_t *P) {
     FastOp<NI> f;
     const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    f.rs = wave_rsrc(P + base, 2 * (static_cast<int64_t>(xlen - 1) * xs + K) + 16);
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
         const int32_t r = 16 * (NI * w + j) + (lane >> 2);
         const int32_t rr = r < xlen ? r : 0;                      // rows past the edge: a valid row
-        f.p[j] = P + base + static_cast<int64_t>(rr) * xs + 8 * ((lane & 3) ^ fa_perm(r));
+        f.off[j] = static_cast<uint32_t>(2 * (static_cast<int64_t>(rr) * xs + 8 * ((lane & 3) ^ fa_perm(r))));
     }
-    f.step = FB_BK;
+    f.step = 2 * FB_BK;
     return f;
 }
 
@@ -129,30 +148,42 @@ __device__ __forceinline__ FastOp<NI> dense_setup_kcontig(int64_t base, int64_t 
 // instruction j fills k rows 4 (NI w + j) .. +4; lane l fills row l / 16,
 // 16-byte slot l % 16.
 template <int NI>
-__device__ __forceinline__ FastOp<NI> dense_setup_ncontig(int64_t base, int64_t ks, int32_t nlen, const uint16_t *P) {
+__device__ __forceinline__ FastOp<NI> dense_setup_ncontig(int64_t base, int64_t ks, int32_t nlen, int32_t K,
+                                                          const uint16_t *P) {
     FastOp<NI> f;
     const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int32_t s = lane & 15;
+    f.rs = wave_rsrc(P + base, 2 * (static_cast<int64_t>(K - 1) * ks + FB_BN) + 16);
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
         const int32_t kr = 4 * (NI * w + j) + (lane >> 4);
         const int32_t G = fb_pos(kr, s >> 2);                     // global n-granule for this LDS position
         int32_t n = 32 * G + 8 * (s & 3);
         if (n >= nlen) n = 0;                                      // columns past the edge: a valid column
-        f.p[j] = P + base + n + static_cast<int64_t>(kr) * ks;
+        f.off[j] = static_cast<uint32_t>(2 * (n + static_cast<int64_t>(kr) * ks));
     }
-    f.step = static_cast<int64_t>(FB_BK) * ks;
+    f.step = static_cast<uint32_t>(2 * FB_BK * ks);
     return f;
 }
 
+template <bool BN>
+__device__ __forceinline__ FastOp<FB_NIB> dense_setup_b(int64_t base, int64_t s, int32_t nlen, int32_t K,
+                                                        const uint16_t *P) {
+    if constexpr (BN) return dense_setup_ncontig<FB_NIB>(base, s, nlen, K, P);
+    else return dense_setup_kcontig<FB_NIB>(base, s, nlen, K, P);
+}
+
+// w: the wave index, wave-uniform (the LDS destination goes through M0)
 template <int NI>
-__device__ __forceinline__ void fast_issue(const FastOp<NI> &f, int32_t c, uint16_t *lds_op) {
-    const int32_t w = threadIdx.x >> 6;
+__device__ __forceinline__ void fast_issue(const FastOp<NI> &f, int32_t c, uint16_t *lds_op, int32_t w) {
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-        const uint16_t *src = f.p[j] + static_cast<int64_t>(c) * f.step;
         uint16_t *dst = lds_op + (NI * w + j) * 512;                 // 1 KB per wave instruction
-        __builtin_amdgcn_global_load_lds(src, BSC_LDS_PTR(void, dst), 16, 0, 0);
+        // (a non-const descriptor and int offsets: the form this compiler's host
+        // pass accepts when the kernel template is instantiated from host code)
+        __amdgpu_buffer_rsrc_t rs = f.rs;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, BSC_LDS_PTR(void, dst), 16, static_cast<int>(f.off[j]),
+                                                 static_cast<int>(static_cast<uint32_t>(c) * f.step), 0, 0);
     }
 }
 
@@ -344,7 +375,6 @@ __device__ __forceinline__ void frag_step(uint32_t stage, const FragOff &o, Frag
 // device-scope fence, whose whole-cache write-back and invalidation would
 // stall every other workgroup on the chiplet.  The buffer descriptor covers
 // exactly the tile's partials, so the hardware drops any access outside them.
-constexpr int32_t BUF_DWORD3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
 constexpr int32_t CPOL_SC1 = 16;             // device-coherent cache policy
 
 __device__ __forceinline__ bool split_arrive(const KArgs &ka, const DFast &fd, f32x16_t (&acc)[FB_FM][2], int32_t w,
@@ -410,23 +440,23 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const FastOp<FB_NIA> fa = dense_setup_kcontig<FB_NIA>(fd.a_base, fd.a_rs, mlen, A);
+    const FastOp<FB_NIA> fa = dense_setup_kcontig<FB_NIA>(fd.a_base, fd.a_rs, mlen, K, A);
     const int64_t b_s = BN ? fd.b_ks : fd.b_ns;   // stride of B's non-contiguous axis
-    FastOp<FB_NIB> fb;
-    if constexpr (BN) fb = dense_setup_ncontig<FB_NIB>(fd.b_base, b_s, nlen, B);
-    else fb = dense_setup_kcontig<FB_NIB>(fd.b_base, b_s, nlen, B);
+    const FastOp<FB_NIB> fb = dense_setup_b<BN>(fd.b_base, b_s, nlen, K, B);
     const int32_t nfull = K / FB_BK;
     const int32_t ntot = (K + FB_BK - 1) / FB_BK;
-    const bool a_live = 16 * FB_NIA * w < mlen;   // this wave's A copies reach a row inside the tile
     const FragOff fo = frag_offsets<BN>();
     auto fill_partial = [&](int32_t stage) {
         dense_fill_kcontig<FB_BM>(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, sm.op[stage]);
         if constexpr (BN) dense_fill_ncontig(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, sm.op[stage] + FB_A_STAGE);
         else dense_fill_kcontig<FB_BN>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, sm.op[stage] + FB_A_STAGE);
     };
+    // every wave copies its share of every chunk (rows past the edge repeat a
+    // valid row), so each chunk is FB_NIA + FB_NIB copies per wave
+    constexpr int PER = FB_NIA + FB_NIB;
     auto issue = [&](int32_t c, int32_t stage) {
-        if (a_live) fast_issue<FB_NIA>(fa, c, sm.op[stage]);
-        fast_issue<FB_NIB>(fb, c, sm.op[stage] + FB_A_STAGE);
+        fast_issue<FB_NIA>(fa, c, sm.op[stage], w);
+        fast_issue<FB_NIB>(fb, c, sm.op[stage] + FB_A_STAGE, w);
     };
     wait_vm<0>();      // nothing else outstanding: the counted waits below see only this tile's copies
     __syncthreads();   // previous users of the LDS ring are done
@@ -443,10 +473,7 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
     // barrier (every wave's have, and every wave is done reading chunk cn - 1,
     // whose stage is refilled with chunk cn + FB_STAGES - 1).
     auto advance = [&](int32_t cn) {
-        if (cn < nfull) {
-            if (a_live) wait_vm_chunks<FB_NIA + FB_NIB>(issued - cn - 1);
-            else wait_vm_chunks<FB_NIB>(issued - cn - 1);
-        }
+        if (cn < nfull) wait_vm_chunks<PER>(issued - cn - 1);
         lds_barrier();
         const int32_t nx = cn + FB_STAGES - 1;
         const int32_t st = nx % FB_STAGES;
@@ -465,7 +492,33 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
     advance(0);
     frag_step<BN, 0>(stage_addr(0), fo, s0);
     frag_wait<BN>(s0);
-    for (int32_t c = 0; c < ntot; ++c) {
+    // Steady state, without branches: while chunk c + FB_STAGES is a full
+    // chunk, iteration c waits for chunk c + 1 with FB_STAGES - 2 newer chunks
+    // still in flight and refills chunk c's stage with chunk c + FB_STAGES.
+    // The stage rotates through scalar selects.
+    const uint32_t ring = lds_addr(sm.op[0]);
+    constexpr uint32_t STAGE_BYTES = FB_STAGE * 2;
+    int32_t c = 0, st = 0;
+    const int32_t nsteady = nfull - FB_STAGES;   // iterations whose refill is a full chunk
+    for (; c < nsteady; ++c) {
+        const int32_t sn = st == FB_STAGES - 1 ? 0 : st + 1;
+        frag_step<BN, 1>(ring + st * STAGE_BYTES, fo, s1);
+        __builtin_amdgcn_sched_barrier(0);
+        frag_mfma<BN>(s0, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        frag_wait<BN>(s1);
+        wait_vm<PER * (FB_STAGES - 2)>();
+        lds_barrier();
+        issue(c + FB_STAGES, st);
+        frag_step<BN, 0>(ring + sn * STAGE_BYTES, fo, s0);
+        __builtin_amdgcn_sched_barrier(0);
+        frag_mfma<BN>(s1, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        frag_wait<BN>(s0);
+        st = sn;
+    }
+    issued = c + FB_STAGES < nfull ? c + FB_STAGES : nfull;   // chunks 0 .. c + FB_STAGES - 1 are issued
+    for (; c < ntot; ++c) {
         frag_step<BN, 1>(stage_addr(c), fo, s1);
         __builtin_amdgcn_sched_barrier(0);
         frag_mfma<BN>(s0, acc);

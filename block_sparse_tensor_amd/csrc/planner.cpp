@@ -884,6 +884,17 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             }
             return true;
         };
+        // The direct-to-LDS tile addresses each operand of a tile through a buffer
+        // descriptor with 32-bit byte offsets: its range must stay below 2 GiB
+        // (else the tile runs on the general matrix-core tile).
+        auto fast_in_range = [&](int32_t cls, const DFast &f) -> bool {
+            if (cls != T_MFMA_FAST_N && cls != T_MFMA_FAST_K) return true;
+            const double lim = 2147483647.0;
+            const double a = 2.0 * ((double)(f.mlen - 1) * (double)f.a_rs + f.K) + 16;
+            const double b = cls == T_MFMA_FAST_N ? 2.0 * ((double)(f.K - 1) * (double)f.b_ks + TILE_MFMA) + 16
+                                                  : 2.0 * ((double)(f.nlen - 1) * (double)f.b_ns + f.K) + 16;
+            return f.a_rs >= 0 && f.b_ks >= 0 && f.b_ns >= 0 && a < lim && b < lim;
+        };
         // relative throughput of a tile class (used only to order work longest-first)
         auto rate_of = [&](int32_t cls) {
             if (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) return 48.0;
@@ -936,7 +947,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                     const int32_t ml = std::min(TM, g.M - m0), nl = std::min(TN, g.N - n0);
                     DFast f{};
                     if ((cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K || cls == T_MFMA) &&
-                        dense_record(g, gi, m0, ml, n0, nl, f)) {
+                        dense_record(g, gi, m0, ml, n0, nl, f) && fast_in_range(cls, f)) {
                         // bf16 direct-to-LDS tiles always qualify; fp32 / fp64 tiles that do
                         // become record-addressed dense tiles
                         const int32_t c2 = cls == T_MFMA ? (p.dtype == BSC_BF16_F32 ? T_MFMA : T_MFMA_DENSE) : cls;
@@ -976,7 +987,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                             out.push_back({cls, gi, m0, n0});
                         }
                     } else {
-                        // (a direct-to-LDS class always has its record; the general tile is the fallback)
+                        // a direct-to-LDS tile without a record or beyond the descriptor range runs on the general tile
                         const bool fastc = cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K;
                         out.push_back({fastc ? T_MFMA : cls, gi, m0, n0});
                     }
@@ -1037,14 +1048,35 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                     }
                 }
             }
+            // Each queue runs longest first.  Its first BSC_CUS_PER_XCD tiles take a
+            // CU each; the next ones become the second residents of those CUs:
+            // two tiles on one CU each run slower than one alone, so the longest
+            // tiles get no partner (a no-op in that slot) and the remaining
+            // partners go to the shortest first residents, longest partner first.
+            const size_t CUX = BSC_CUS_PER_XCD;
+            constexpr size_t NONE = ~size_t(0);
+            std::vector<std::vector<size_t>> slots(BSC_XCDS);
             size_t depth = 0;
-            for (auto &v : q) {
-                std::stable_sort(v.begin(), v.end(), [&](size_t x, size_t y) { return cost[x] > cost[y]; });
-                depth = std::max(depth, v.size());
+            for (int x = 0; x < BSC_XCDS; ++x) {
+                std::vector<size_t> &v = q[(size_t)x];
+                std::stable_sort(v.begin(), v.end(), [&](size_t a, size_t b) { return cost[a] > cost[b]; });
+                std::vector<size_t> &s = slots[(size_t)x];
+                if (v.size() <= CUX) {
+                    s = v;
+                } else {
+                    s.assign(v.begin(), v.begin() + CUX);
+                    s.resize(2 * CUX, NONE);
+                    const size_t m = std::min(CUX, v.size() - CUX);   // partners
+                    for (size_t i = 0; i < m; ++i) s[CUX + (CUX - 1 - i)] = v[CUX + i];
+                    s.insert(s.end(), v.begin() + CUX + m, v.end());
+                }
+                depth = std::max(depth, s.size());
             }
             for (size_t d = 0; d < depth; ++d)
-                for (int x = 0; x < BSC_XCDS; ++x)
-                    p.tasks.push_back(d < q[(size_t)x].size() ? tk[q[(size_t)x][d]] : DTask{T_NOP, 0, 0, 0});
+                for (int x = 0; x < BSC_XCDS; ++x) {
+                    const std::vector<size_t> &s = slots[(size_t)x];
+                    p.tasks.push_back(d < s.size() && s[d] != NONE ? tk[s[d]] : DTask{T_NOP, 0, 0, 0});
+                }
             // trailing no-ops of the last row carry no mapping information
             while (!p.tasks.empty() && p.tasks.back().cls == T_NOP) p.tasks.pop_back();
             if (!p.tasks.empty()) p.launches.push_back({0, (int32_t)p.tasks.size()});

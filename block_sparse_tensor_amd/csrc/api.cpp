@@ -75,9 +75,9 @@ bsc_status bsc_plan(const bsc_index *m, const bsc_index *k, const bsc_index *n, 
         return BSC_ERR_ARG;
     }
     if (p->opt.layout_policy < BSC_LAYOUT_AUTO || p->opt.layout_policy > BSC_LAYOUT_FORCE_PACK || p->opt.grid_limit < 0 ||
-        p->opt.split_k < -1) {
+        p->opt.split_k < -1 || (p->opt.tile_rows != 0 && p->opt.tile_rows != 128 && p->opt.tile_rows != 256)) {
         delete p;
-        set_error("bsc_plan: bad layout policy, grid limit or split_k");
+        set_error("bsc_plan: bad layout policy, grid limit, split_k or tile_rows");
         return BSC_ERR_ARG;
     }
     fill_cost_defaults(p->opt, dtype);

@@ -48,10 +48,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int FB_BM = 256;                      // tile rows
 constexpr int FB_BN = 128;                      // tile columns
 constexpr int FB_BK = 32;                       // contracted indices per chunk
-constexpr int FB_STAGES = 3;                    // LDS ring depth
-constexpr int FB_A_STAGE = FB_BM * FB_BK;       // bf16 elements of A per stage (16 KB)
+constexpr int FB_A_STAGE = FB_BM * FB_BK;       // bf16 elements of A per full stage (16 KB)
 constexpr int FB_B_STAGE = FB_BN * FB_BK;       // bf16 elements of B per stage (8 KB)
-constexpr int FB_STAGE = FB_A_STAGE + FB_B_STAGE;
 constexpr int FB_NIA = FB_A_STAGE * 2 / 1024 / 4;   // 1 KB copies of A per wave and chunk (4)
 constexpr int FB_NIB = FB_B_STAGE * 2 / 1024 / 4;   // 1 KB copies of B per wave and chunk (2)
 constexpr int FB_FM = FB_BM / 2 / 32;               // row fragments per wave (4)
@@ -59,9 +57,22 @@ static_assert(FB_BM == TILE_MFMA_DENSE_M && FB_BN == TILE_MFMA, "tile shape the 
 
 #define BSC_LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 
+// The LDS ring.  A full tile (more than 128 rows) uses three 24 KB stages
+// (A 256 x 32, then B 32 x 128); a tile of at most 128 rows needs half the A
+// rows, so the same 80 KB hold five 16 KB stages and four chunks are in flight
+// instead of two (what bounds a tile under load is the latency of its copies).
+template <bool HALF>
+struct Ring {
+    static constexpr int STAGES = HALF ? 5 : 3;
+    static constexpr int A_ELEMS = (HALF ? FB_BM / 2 : FB_BM) * FB_BK;   // A part of a stage
+    static constexpr int STAGE_ELEMS = A_ELEMS + FB_B_STAGE;
+};
+constexpr int FB_RING_ELEMS = 40960;   // 80 KB: two workgroups per CU
+static_assert(Ring<false>::STAGES * Ring<false>::STAGE_ELEMS <= FB_RING_ELEMS, "full ring");
+static_assert(Ring<true>::STAGES * Ring<true>::STAGE_ELEMS <= FB_RING_ELEMS, "half ring");
+
 struct FastSmemBf16 {
-    uint16_t op[FB_STAGES][FB_STAGE];   // [stage][A (256 x 32), then B (128 x 32)]
-    int32_t last;                       // K split: this workgroup finishes the tile
+    uint16_t op[FB_RING_ELEMS];
 };
 
 // Wait until at most N vector-memory operations of this wave are outstanding
@@ -79,10 +90,11 @@ __device__ __forceinline__ void wait_vm_chunks(int32_t chunks_after) {
     switch (chunks_after) {
         case 0: wait_vm<0>(); break;
         case 1: wait_vm<PER>(); break;
-        default: wait_vm<2 * PER>(); break;
+        case 2: wait_vm<2 * PER>(); break;
+        default: wait_vm<3 * PER>(); break;
     }
 }
-static_assert(FB_STAGES - 1 <= 2, "the wait table covers at most two chunks in flight");
+static_assert(Ring<true>::STAGES - 2 <= 3 && 3 * (FB_NIA + FB_NIB) < 64, "wait table: at most three newer chunks");
 
 // Workgroup barrier for handing LDS stages between waves.  Each wave first
 // waits for its own LDS writes (lgkmcnt) — its direct-to-LDS copies were
@@ -126,13 +138,14 @@ struct FastOp {
 };
 
 // K-contiguous operand ([x][k] layout), element (x, k) at base + x * xs + k:
-// wave w instruction j fills rows 16 (NI w + j) .. +16 (1 KB); lane l fills
-// row l / 4, slot l % 4, so it copies k-granule (l % 4) ^ fa_perm(row).
+// copy block w (a wave's share) instruction j fills rows 16 (NI w + j) .. +16
+// (1 KB); lane l fills row l / 4, slot l % 4, so it copies k-granule
+// (l % 4) ^ fa_perm(row).
 template <int NI>
 __device__ __forceinline__ FastOp<NI> dense_setup_kcontig(int64_t base, int64_t xs, int32_t xlen, int32_t K,
-                                                          const uint16_t *P) {
+                                                          const uint16_t *P, int32_t w) {
     FastOp<NI> f;
-    const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int32_t lane = threadIdx.x & 63;
     f.rs = wave_rsrc(P + base, 2 * (static_cast<int64_t>(xlen - 1) * xs + K) + 16);
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
@@ -149,9 +162,9 @@ __device__ __forceinline__ FastOp<NI> dense_setup_kcontig(int64_t base, int64_t 
 // 16-byte slot l % 16.
 template <int NI>
 __device__ __forceinline__ FastOp<NI> dense_setup_ncontig(int64_t base, int64_t ks, int32_t nlen, int32_t K,
-                                                          const uint16_t *P) {
+                                                          const uint16_t *P, int32_t w) {
     FastOp<NI> f;
-    const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int32_t lane = threadIdx.x & 63;
     const int32_t s = lane & 15;
     f.rs = wave_rsrc(P + base, 2 * (static_cast<int64_t>(K - 1) * ks + FB_BN) + 16);
 #pragma unroll
@@ -168,12 +181,12 @@ __device__ __forceinline__ FastOp<NI> dense_setup_ncontig(int64_t base, int64_t 
 
 template <bool BN>
 __device__ __forceinline__ FastOp<FB_NIB> dense_setup_b(int64_t base, int64_t s, int32_t nlen, int32_t K,
-                                                        const uint16_t *P) {
-    if constexpr (BN) return dense_setup_ncontig<FB_NIB>(base, s, nlen, K, P);
-    else return dense_setup_kcontig<FB_NIB>(base, s, nlen, K, P);
+                                                        const uint16_t *P, int32_t w) {
+    if constexpr (BN) return dense_setup_ncontig<FB_NIB>(base, s, nlen, K, P, w);
+    else return dense_setup_kcontig<FB_NIB>(base, s, nlen, K, P, w);
 }
 
-// w: the wave index, wave-uniform (the LDS destination goes through M0)
+// w: the copy block (a wave's share), wave-uniform (the LDS destination goes through M0)
 template <int NI>
 __device__ __forceinline__ void fast_issue(const FastOp<NI> &f, int32_t c, uint16_t *lds_op, int32_t w) {
 #pragma unroll
@@ -270,11 +283,11 @@ __device__ __forceinline__ FragOff frag_offsets() {
         const int32_t hh = lane >> 4, p = lane & 15;
         const int32_t k = 8 * (hh >> 1) + (p >> 2);
         const int32_t n = wn * 64 + 16 * (hh & 1) + 4 * (p & 3);
-        o.b[0] = 2 * (FB_A_STAGE + k * FB_BN + 32 * fb_pos(k, n >> 5) + (n & 31));
+        o.b[0] = 2 * (k * FB_BN + 32 * fb_pos(k, n >> 5) + (n & 31));
         o.b[1] = o.b[0] ^ 64;
     } else {
         const int32_t rb = wn * 64 + (lane & 31);
-        o.b[0] = 2 * (FB_A_STAGE + rb * FB_BK + 8 * fa_slot(rb, lane >> 5));
+        o.b[0] = 2 * (rb * FB_BK + 8 * fa_slot(rb, lane >> 5));
         o.b[1] = o.b[0] ^ 32;
     }
     return o;
@@ -348,13 +361,95 @@ __device__ __forceinline__ void frag_mfma(const Frags &fr, f32x16_t (&acc)[FB_FM
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
+// One fragment read (index r of the K-step's reads: B first, then A).
+template <bool BN, int KS>
+__device__ __forceinline__ void read_one(int r, uint32_t va, uint32_t vb0, uint32_t vb1, Frags &fr) {
+    constexpr int KO = 2 * 16 * KS * FB_BN, HO = 2 * 4 * FB_BN, AR = 2 * 32 * FB_BK;
+    if constexpr (BN) {
+        switch (r) {
+            case 0: lds_read_tr<KO>(vb0, fr.t[0]); break;
+            case 1: lds_read_tr<KO + HO>(vb0, fr.t[1]); break;
+            case 2: lds_read_tr<KO>(vb1, fr.t[2]); break;
+            case 3: lds_read_tr<KO + HO>(vb1, fr.t[3]); break;
+            case 4: lds_read_b128<0>(va, fr.a[0]); break;
+            case 5: lds_read_b128<AR>(va, fr.a[1]); break;
+            case 6: lds_read_b128<2 * AR>(va, fr.a[2]); break;
+            default: lds_read_b128<3 * AR>(va, fr.a[3]); break;
+        }
+    } else {
+        switch (r) {
+            case 0: lds_read_b128<0>(vb0, fr.b[0]); break;
+            case 1: lds_read_b128<AR>(vb0, fr.b[1]); break;
+            case 2: lds_read_b128<0>(va, fr.a[0]); break;
+            case 3: lds_read_b128<AR>(va, fr.a[1]); break;
+            case 4: lds_read_b128<2 * AR>(va, fr.a[2]); break;
+            default: lds_read_b128<3 * AR>(va, fr.a[3]); break;
+        }
+    }
+}
+
+// The eight MFMAs of one K-step (fragments `cur`) with the reads of the next
+// K-step's fragments (`nxt`, K-step KS at the given bases) issued between
+// them, so a single wave keeps its matrix core fed while the reads go out:
+// reads start after the first PRE MFMAs (a gap between the last MFMA that
+// read `nxt`'s registers and the first read that overwrites them), and
+// `mid` runs right before MFMA PRE (the chunk hand-over: waits, barrier,
+// copies), while the first MFMAs execute.
+template <bool BN, int KS, int PRE, typename Mid>
+__device__ __forceinline__ void mfma_interleaved(const Frags &cur, Frags &nxt, uint32_t va, uint32_t vb0, uint32_t vb1,
+                                                 f32x16_t (&acc)[FB_FM][2], Mid &&mid) {
+    constexpr int NR = BN ? 8 : 6;   // reads per K-step
+    bf16x8_t fa[FB_FM], fb[2];
+#pragma unroll
+    for (int f = 0; f < FB_FM; ++f) fa[f] = __builtin_bit_cast(bf16x8_t, cur.a[f]);
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        if constexpr (BN) {
+            const v4i16_t lo = cur.t[2 * f], hi = cur.t[2 * f + 1];
+            short e8 __attribute__((ext_vector_type(8))) = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            fb[f] = __builtin_bit_cast(bf16x8_t, e8);
+        } else {
+            fb[f] = __builtin_bit_cast(bf16x8_t, cur.b[f]);
+        }
+    }
+    // reads per MFMA slot from PRE on, the remainder after the last MFMA
+    constexpr int SLOTS = 2 * FB_FM - PRE;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 2 * FB_FM; ++k) {
+        if (k == PRE) {
+            mid();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        acc[k / 2][k % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k / 2], fb[k % 2], acc[k / 2][k % 2], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k >= PRE) {
+            const int slot = k - PRE;
+            // spread NR reads over SLOTS slots, front-loaded
+            const int r0 = slot * NR / SLOTS, r1 = (slot + 1) * NR / SLOTS;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                if (r >= r0 && r < r1) read_one<BN, KS>(r, va, vb0, vb1, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // keep `cur` allocated until every read into `nxt` is issued: a read must
+    // not land in registers an MFMA issued just before it may still be reading
+    if constexpr (BN)
+        asm volatile("" ::"v"(cur.a[0]), "v"(cur.a[1]), "v"(cur.a[2]), "v"(cur.a[3]), "v"(cur.t[0]), "v"(cur.t[1]),
+                     "v"(cur.t[2]), "v"(cur.t[3]));
+    else
+        asm volatile("" ::"v"(cur.a[0]), "v"(cur.a[1]), "v"(cur.a[2]), "v"(cur.a[3]), "v"(cur.b[0]), "v"(cur.b[1]));
+}
+
 // Fragment reads of one K-step (0 or 1) of the chunk whose stage starts at
 // LDS byte address `stage`.
+// stage: LDS byte address of the stage (its A part); bstage: of its B part
 template <bool BN, int KS>
-__device__ __forceinline__ void frag_step(uint32_t stage, const FragOff &o, Frags &fr) {
+__device__ __forceinline__ void frag_step(uint32_t stage, uint32_t bstage, const FragOff &o, Frags &fr) {
     static_assert(FB_BK == 32, "two K-steps per chunk");
     // K-contiguous B: one base per K-step; N-contiguous B: one per column fragment
-    const uint32_t vb0 = stage + o.b[0], vb1 = stage + o.b[1];
+    const uint32_t vb0 = bstage + o.b[0], vb1 = bstage + o.b[1];
     if constexpr (BN) frag_issue<BN, KS>(stage + o.a[KS], vb0, vb1, fr);
     else frag_issue<BN, KS>(stage + o.a[KS], KS ? vb1 : vb0, vb1, fr);
 }
@@ -440,108 +535,158 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const FastOp<FB_NIA> fa = dense_setup_kcontig<FB_NIA>(fd.a_base, fd.a_rs, mlen, K, A);
+    // Wave roles.  Wave (wm, wn) computes rows wm*128 .. +128 and columns
+    // wn*64 .. +64 of the tile and copies A rows wm*128 + wn*64 .. +64; a wave
+    // whose rows (or columns) lie wholly past the tile edge computes nothing,
+    // and one whose A rows do copies no A (tiles of at most 128 rows, as the
+    // planner cuts for long-K groups, run on half the matrix cores).  Every
+    // wave copies its share of B.  The roles are wave-uniform, so each wave
+    // runs one instantiation of the K loop below; all of them meet at the same
+    // barriers.
+    const int32_t wm = w & 1, wn = w >> 1;
+    const bool compute = wm * (FB_BM / 2) < mlen && wn * (FB_BN / 2) < nlen;
+    const bool acopy = wm * (FB_BM / 2) + wn * (FB_BM / 4) < mlen;
+    const FastOp<FB_NIA> fa = dense_setup_kcontig<FB_NIA>(fd.a_base, fd.a_rs, mlen, K, A, 2 * wm + wn);
     const int64_t b_s = BN ? fd.b_ks : fd.b_ns;   // stride of B's non-contiguous axis
-    const FastOp<FB_NIB> fb = dense_setup_b<BN>(fd.b_base, b_s, nlen, K, B);
+    const FastOp<FB_NIB> fb = dense_setup_b<BN>(fd.b_base, b_s, nlen, K, B, w);
     const int32_t nfull = K / FB_BK;
     const int32_t ntot = (K + FB_BK - 1) / FB_BK;
     const FragOff fo = frag_offsets<BN>();
-    auto fill_partial = [&](int32_t stage) {
-        dense_fill_kcontig<FB_BM>(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, sm.op[stage]);
-        if constexpr (BN) dense_fill_ncontig(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, sm.op[stage] + FB_A_STAGE);
-        else dense_fill_kcontig<FB_BN>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, sm.op[stage] + FB_A_STAGE);
-    };
-    // every wave copies its share of every chunk (rows past the edge repeat a
-    // valid row), so each chunk is FB_NIA + FB_NIB copies per wave
-    constexpr int PER = FB_NIA + FB_NIB;
-    auto issue = [&](int32_t c, int32_t stage) {
-        fast_issue<FB_NIA>(fa, c, sm.op[stage], w);
-        fast_issue<FB_NIB>(fb, c, sm.op[stage] + FB_A_STAGE, w);
-    };
     wait_vm<0>();      // nothing else outstanding: the counted waits below see only this tile's copies
     __syncthreads();   // previous users of the LDS ring are done
-    int32_t issued = 0;
+
+    auto kloop = [&](auto half_c, auto compute_c, auto acopy_c) {
+        constexpr bool HALF = decltype(half_c)::value;
+        constexpr bool COMPUTE = decltype(compute_c)::value, ACOPY = decltype(acopy_c)::value;
+        using R = Ring<HALF>;
+        constexpr int STAGES = R::STAGES;
+        constexpr int PER = (ACOPY ? FB_NIA : 0) + FB_NIB;   // copies per chunk and wave
+        uint16_t *const ops = sm.op;
+        auto fill_partial = [&](int32_t stage) {
+            uint16_t *at = ops + stage * R::STAGE_ELEMS;
+            dense_fill_kcontig<HALF ? FB_BM / 2 : FB_BM>(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, at);
+            if constexpr (BN) dense_fill_ncontig(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + R::A_ELEMS);
+            else dense_fill_kcontig<FB_BN>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + R::A_ELEMS);
+        };
+        auto issue = [&](int32_t c, int32_t stage) {
+            uint16_t *at = ops + stage * R::STAGE_ELEMS;
+            if constexpr (ACOPY) fast_issue<FB_NIA>(fa, c, at, 2 * wm + wn);
+            fast_issue<FB_NIB>(fb, c, at + R::A_ELEMS, w);
+        };
+        int32_t issued = 0;
 #pragma unroll
-    for (int32_t p = 0; p < FB_STAGES - 1; ++p) {
-        if (p < nfull) {
-            issue(p, p);
-            ++issued;
+        for (int32_t p = 0; p < STAGES - 1; ++p) {
+            if (p < nfull) {
+                issue(p, p);
+                ++issued;
+            }
         }
-    }
-    if (nfull < ntot && nfull <= FB_STAGES - 2) fill_partial(nfull);
-    // Make chunk cn readable: this wave's copies of it have landed, then the
-    // barrier (every wave's have, and every wave is done reading chunk cn - 1,
-    // whose stage is refilled with chunk cn + FB_STAGES - 1).
-    auto advance = [&](int32_t cn) {
-        if (cn < nfull) wait_vm_chunks<PER>(issued - cn - 1);
-        lds_barrier();
-        const int32_t nx = cn + FB_STAGES - 1;
-        const int32_t st = nx % FB_STAGES;
-        if (nx < nfull) {
-            issue(nx, st);
-            ++issued;
-        } else if (nx == nfull && nfull < ntot) {
-            fill_partial(st);
+        if (nfull < ntot && nfull <= STAGES - 2) fill_partial(nfull);
+        // Make chunk cn readable: this wave's copies of it have landed, then the
+        // barrier (every wave's have, and every wave is done reading chunk cn - 1,
+        // whose stage is refilled with chunk cn + STAGES - 1).
+        auto advance = [&](int32_t cn) {
+            if (cn < nfull) wait_vm_chunks<PER>(issued - cn - 1);
+            lds_barrier();
+            const int32_t nx = cn + STAGES - 1;
+            const int32_t st = nx % STAGES;
+            if (nx < nfull) {
+                issue(nx, st);
+                ++issued;
+            } else if (nx == nfull && nfull < ntot) {
+                fill_partial(st);
+            }
+        };
+        const uint32_t ring = lds_addr(ops);
+        constexpr uint32_t STAGE_BYTES = R::STAGE_ELEMS * 2, B_OFF = R::A_ELEMS * 2;
+        auto stage_addr = [&](int32_t c) { return ring + (c % STAGES) * STAGE_BYTES; };
+        // software-pipelined across chunks: the reads of step 1 of chunk c
+        // overlap the MFMAs of step 0, and the reads of step 0 of chunk c + 1
+        // (after the hand-over barrier) overlap the MFMAs of step 1
+        Frags s0, s1;
+        auto reads = [&](auto ks_c, uint32_t stage, Frags &fr) {
+            if constexpr (COMPUTE) frag_step<BN, decltype(ks_c)::value>(stage, stage + B_OFF, fo, fr);
+        };
+        auto mfmas = [&](const Frags &fr) {
+            if constexpr (COMPUTE) {
+                __builtin_amdgcn_sched_barrier(0);
+                frag_mfma<BN>(fr, acc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto settle = [&](Frags &fr) {
+            if constexpr (COMPUTE) frag_wait<BN>(fr);
+        };
+        using K0 = std::integral_constant<int, 0>;
+        using K1 = std::integral_constant<int, 1>;
+        advance(0);
+        reads(K0(), stage_addr(0), s0);
+        settle(s0);
+        // Steady state, without branches: while chunk c + STAGES is a full
+        // chunk, iteration c waits for chunk c + 1 with STAGES - 2 newer chunks
+        // still in flight and refills chunk c's stage with chunk c + STAGES.
+        // The stage rotates through scalar selects.
+        int32_t c = 0, st = 0;
+        const int32_t nsteady = nfull - STAGES;   // iterations whose refill is a full chunk
+        for (; c < nsteady; ++c) {
+            const int32_t sn = st == STAGES - 1 ? 0 : st + 1;
+            if constexpr (COMPUTE) {
+                // MFMAs of step 0 with the reads of step 1 (same stage) between them;
+                // then the MFMAs of step 1 with the hand-over (wait, barrier, refill)
+                // after the first two and the reads of chunk c + 1's step 0 after it
+                const uint32_t here = ring + st * STAGE_BYTES, next = ring + sn * STAGE_BYTES;
+                mfma_interleaved<BN, 1, 2>(s0, s1, here + fo.a[1], here + B_OFF + fo.b[BN ? 0 : 1],
+                                           here + B_OFF + fo.b[1], acc, [] {});
+                settle(s1);
+                mfma_interleaved<BN, 0, 2>(s1, s0, next + fo.a[0], next + B_OFF + fo.b[0], next + B_OFF + fo.b[1], acc,
+                                           [&] {
+                                               wait_vm<PER * (STAGES - 2)>();
+                                               lds_barrier();
+                                               issue(c + STAGES, st);
+                                           });
+                settle(s0);
+            } else {
+                wait_vm<PER * (STAGES - 2)>();
+                lds_barrier();
+                issue(c + STAGES, st);
+            }
+            st = sn;
+        }
+        issued = c + STAGES < nfull ? c + STAGES : nfull;   // chunks 0 .. c + STAGES - 1 are issued
+        for (; c < ntot; ++c) {
+            reads(K1(), stage_addr(c), s1);
+            mfmas(s0);
+            settle(s1);
+            const bool more = c + 1 < ntot;
+            if (more) {
+                advance(c + 1);
+                reads(K0(), stage_addr(c + 1), s0);
+            }
+            mfmas(s1);
+            if (more) settle(s0);
         }
     };
-    auto stage_addr = [&](int32_t c) { return lds_addr(sm.op[c % FB_STAGES]); };
-    // K loop, software-pipelined across chunks: the reads of step 1 of chunk c
-    // overlap the MFMAs of step 0, and the reads of step 0 of chunk c + 1 (after
-    // the hand-over barrier) overlap the MFMAs of step 1.
-    Frags s0, s1;
-    advance(0);
-    frag_step<BN, 0>(stage_addr(0), fo, s0);
-    frag_wait<BN>(s0);
-    // Steady state, without branches: while chunk c + FB_STAGES is a full
-    // chunk, iteration c waits for chunk c + 1 with FB_STAGES - 2 newer chunks
-    // still in flight and refills chunk c's stage with chunk c + FB_STAGES.
-    // The stage rotates through scalar selects.
-    const uint32_t ring = lds_addr(sm.op[0]);
-    constexpr uint32_t STAGE_BYTES = FB_STAGE * 2;
-    int32_t c = 0, st = 0;
-    const int32_t nsteady = nfull - FB_STAGES;   // iterations whose refill is a full chunk
-    for (; c < nsteady; ++c) {
-        const int32_t sn = st == FB_STAGES - 1 ? 0 : st + 1;
-        frag_step<BN, 1>(ring + st * STAGE_BYTES, fo, s1);
-        __builtin_amdgcn_sched_barrier(0);
-        frag_mfma<BN>(s0, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        frag_wait<BN>(s1);
-        wait_vm<PER * (FB_STAGES - 2)>();
-        lds_barrier();
-        issue(c + FB_STAGES, st);
-        frag_step<BN, 0>(ring + sn * STAGE_BYTES, fo, s0);
-        __builtin_amdgcn_sched_barrier(0);
-        frag_mfma<BN>(s1, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        frag_wait<BN>(s0);
-        st = sn;
-    }
-    issued = c + FB_STAGES < nfull ? c + FB_STAGES : nfull;   // chunks 0 .. c + FB_STAGES - 1 are issued
-    for (; c < ntot; ++c) {
-        frag_step<BN, 1>(stage_addr(c), fo, s1);
-        __builtin_amdgcn_sched_barrier(0);
-        frag_mfma<BN>(s0, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        frag_wait<BN>(s1);
-        const bool more = c + 1 < ntot;
-        if (more) {
-            advance(c + 1);
-            frag_step<BN, 0>(stage_addr(c + 1), fo, s0);
+    using T = std::true_type;
+    using F = std::false_type;
+    auto roles = [&](auto half_c) {
+        if (compute) {
+            if (acopy) kloop(half_c, T(), T());
+            else kloop(half_c, T(), F());
+        } else {
+            if (acopy) kloop(half_c, F(), T());
+            else kloop(half_c, F(), F());
         }
-        __builtin_amdgcn_sched_barrier(0);
-        frag_mfma<BN>(s1, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) frag_wait<BN>(s0);
-    }
+    };
+    if (mlen <= FB_BM / 2) roles(T());
+    else roles(F());
 
     const int32_t lane = threadIdx.x & 63;
-    if (fd.nsplit > 1 && !split_arrive(ka, fd, acc, w, lane, sm.last)) return;
+    // (the ring is idle from here on: the K-split flag may alias its first word)
+    if (fd.nsplit > 1 && !split_arrive(ka, fd, acc, w, lane, *reinterpret_cast<int32_t *>(sm.op))) return;
 
     // epilogue: straight from the accumulators, 32 consecutive columns per row
     TC *Cp = static_cast<TC *>(ka.C);
     const bool accum = (fd.flags & G_ACCUMULATE) != 0;
-    const int32_t wm = w & 1, wn = w >> 1;
 #pragma unroll
     for (int fj = 0; fj < 2; ++fj) {
         const int32_t j = wn * 64 + fj * 32 + (lane & 31);

@@ -910,22 +910,39 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         // long: automatic slices are at least SPLIT_MIN_CHUNKS chunks of 32
         // (K >= 2048), so only very long K chains are cut.
         constexpr int32_t SPLIT_CHUNK = 32, SPLIT_MIN_CHUNKS = 64, SPLIT_MAX = 32;
-        int64_t split_target = 0;   // most chunks per slice; 0: no split
-        if (!per_sector && p.dtype == BSC_BF16_F32 && p.opt.split_k >= 0) {
-            if (p.opt.split_k > 0) {
-                split_target = p.opt.split_k;
-            } else {
-                double total = 0;
-                for (int32_t gi = 0; gi < p.n_work_groups; ++gi) {
-                    const DGroup &g = p.groups[(size_t)gi];
-                    const int32_t cls = class_of(g);
-                    if (cls != T_MFMA_FAST_N && cls != T_MFMA_FAST_K) continue;
-                    total += (double)((g.M + TILE_MFMA_DENSE_M - 1) / TILE_MFMA_DENSE_M) *
-                             (double)((g.N + TILE_MFMA - 1) / TILE_MFMA) * (double)((g.K + SPLIT_CHUNK - 1) / SPLIT_CHUNK);
-                }
-                split_target = std::max<int64_t>(SPLIT_MIN_CHUNKS, (int64_t)std::ceil(total / CONCURRENT_TILES));
+        // one slot's share of the plan's direct-to-LDS work, in 256 x 128 x 32
+        // chunks, and the number of such 256 x 128 tiles
+        double fast_share = 0, fast_tiles = 0;
+        if (!per_sector && p.dtype == BSC_BF16_F32) {
+            double total = 0;
+            for (int32_t gi = 0; gi < p.n_work_groups; ++gi) {
+                const DGroup &g = p.groups[(size_t)gi];
+                const int32_t cls = class_of(g);
+                if (cls != T_MFMA_FAST_N && cls != T_MFMA_FAST_K) continue;
+                const double tiles = (double)((g.M + TILE_MFMA_DENSE_M - 1) / TILE_MFMA_DENSE_M) *
+                                     (double)((g.N + TILE_MFMA - 1) / TILE_MFMA);
+                fast_tiles += tiles;
+                total += tiles * (double)((g.K + SPLIT_CHUNK - 1) / SPLIT_CHUNK);
             }
+            fast_share = total / CONCURRENT_TILES;
         }
+        int64_t split_target = 0;   // most chunks per slice; 0: no split
+        if (!per_sector && p.dtype == BSC_BF16_F32 && p.opt.split_k >= 0)
+            split_target = p.opt.split_k > 0 ? p.opt.split_k
+                                             : std::max<int64_t>(SPLIT_MIN_CHUNKS, (int64_t)std::ceil(fast_share));
+        // 128-row tiles: when the plan's 256 x 128 tiles would leave CUs with at
+        // most one tile each, a group whose K chain is long (at least 16
+        // chunks) and above one slot's share is cut into 128-row tiles: twice
+        // the tiles (two per CU), each with four chunks of copies in flight.
+        // Measured on MI355X: eight 1024^3 blocks 39 -> 33.6 us; with more
+        // tiles than CUs the extra tiles only add load (bench workload
+        // 34 -> 46 us), so they stay 256 rows.
+        auto half_rows = [&](const DGroup &g) {
+            if (p.opt.tile_rows != 0) return p.opt.tile_rows == TILE_MFMA_DENSE_M / 2;
+            const int64_t chunks = (g.K + SPLIT_CHUNK - 1) / SPLIT_CHUNK;
+            return fast_share > 0 && fast_tiles <= BSC_XCDS * BSC_CUS_PER_XCD && chunks >= 16 &&
+                   (double)chunks > 1.5 * fast_share;
+        };
         // slices of a tile with K contracted indices (1: no split)
         auto slices_of = [&](int32_t K) -> int32_t {
             if (split_target <= 0) return 1;
@@ -941,6 +958,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             const int32_t cls = class_of(g);
             int32_t TM = 0, TN = 0;
             tile_extents(p.dtype, cls, g.M, g.N, TM, TN);
+            if ((cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) && half_rows(g)) TM = TILE_MFMA_DENSE_M / 2;
             if ((cls == T_SKINNY_M || cls == T_SKINNY_N) && skinny_records(g, gi, cls == T_SKINNY_M, out, cost)) return;
             for (int32_t m0 = 0; m0 < g.M; m0 += TM)
                 for (int32_t n0 = 0; n0 < g.N; n0 += TN) {

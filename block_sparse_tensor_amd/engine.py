@@ -97,7 +97,7 @@ class Plan:
     def __init__(self, con, dtype: str = None, axis: str = "auto", launch_mode: str = "grouped",
                  layout: str = "auto", accumulate: bool = False, grid_limit: int = 0,
                  t_launch_us: float = 0.0, t_seg_us: float = 0.0, pack_gbps: float = 0.0, tile_gflops: float = 0.0,
-                 split_k: int = 0):
+                 split_k: int = 0, tile_rows: int = 0):
         L = _capi.lib()
         self.dtype = dtype or con.dtype
         keep = _Keep()
@@ -111,6 +111,7 @@ class Plan:
         opt.grid_limit = int(grid_limit)
         opt.t_launch_us, opt.t_seg_us, opt.pack_gbps, opt.tile_gflops = t_launch_us, t_seg_us, pack_gbps, tile_gflops
         opt.split_k = int(split_k)
+        opt.tile_rows = int(tile_rows)
         h = c_void_p()
         _check(L.bsc_plan(byref(m), byref(k), byref(n), byref(A), byref(B), byref(C),
                           DTYPES[self.dtype], AXES[axis], byref(opt), byref(h)))

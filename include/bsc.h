@@ -152,7 +152,13 @@ typedef struct {
      * 64 x 32 and one slot's share of the plan's work, into slices of about
      * that length); -1: never split; n > 0: slices of at most n x 32 K. */
     int32_t split_k;
-    int32_t reserved;
+    /* Rows of the bf16 direct-to-LDS tiles (uni20 "block coalescing": enough
+     * independent work to fill the machine): 0 = automatic (when the plan has
+     * at most one 256 x 128 tile per CU, 128 for a group whose K chain is at
+     * least 16 x 32 and above 1.5x one slot's share of the plan's work; 256
+     * otherwise); 128 or 256 to force.  A tile of at most 128 rows keeps four
+     * K chunks in flight instead of two. */
+    int32_t tile_rows;
 } bsc_options;
 
 typedef struct {

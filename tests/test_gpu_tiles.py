@@ -19,7 +19,8 @@ if have_gpu():
 SHAPES = [(1, 1, 1), (7, 3, 5), (32, 16, 32), (64, 32, 64), (65, 17, 63), (128, 32, 128), (128, 33, 128),
           (129, 64, 127), (200, 40, 150), (256, 96, 256), (64, 1024, 64), (300, 7, 300), (17, 300, 9),
           (1100, 70, 1), (1100, 3, 16), (5, 130, 1030), (16, 65, 513), (17, 5, 700), (257, 33, 129),
-          (384, 160, 96), (70, 48, 200)]
+          (384, 160, 96), (70, 48, 200),
+          (300, 600, 200), (130, 520, 70)]
 
 
 def _single(M, K, N, dtype, a_row, b_row, pad, seed, off=3):
@@ -103,3 +104,24 @@ def test_skinny_class(dtype):
     assert bst.Plan(con).stats()["items_by_class"]["skinny"] == -(-600 // (256 * (budget // 8)))
     con, _, _, _ = _single(5000, 9, 1, dtype, True, True, 0, 1, 0)
     assert bst.Plan(con).stats()["items_by_class"]["skinny"] == -(-5000 // (256 * (budget // 4)))
+
+
+@pytest.mark.parametrize("shape", [(128, 96, 128), (100, 640, 152), (64, 1030, 70), (33, 40, 24), (300, 600, 200)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("tile_rows", [128, 256])
+def test_tile_rows_forced(shape, tile_rows):
+    """Both direct-to-LDS tile heights (128 rows: five-stage ring, waves of the
+    idle row half compute nothing) on aligned operands, both B orientations:
+    bit-exact on integer inputs."""
+    t = torch()
+    M, K, N = shape
+    for b_row in (True, False):
+        con, abuf, bbuf, ref = _single(M, K, N, "bf16", True, b_row, (-K) % 8, 2, 0)
+        plan = bst.Plan(con, tile_rows=tile_rows).bind()
+        assert plan.stats()["items_by_class"]["mfma_fast"] > 0
+        print(f"[tile] bf16 {M}x{K}x{N} b_row={b_row} tile_rows={tile_rows}", flush=True)
+        C = t.full((M * N,), float("nan"), dtype=t.float32, device="cuda")
+        plan.contract(to_dev(abuf, "bf16"), to_dev(bbuf, "bf16"), C)
+        t.cuda.synchronize()
+        got = C.cpu().numpy().reshape(M, N)
+        assert np.array_equal(got, ref.astype(got.dtype))

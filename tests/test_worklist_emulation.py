@@ -368,6 +368,30 @@ def test_replay_split_k(split_k, brow):
         assert written.max() == 1
 
 
+def test_half_row_tiles_policy():
+    """With at most one 256 x 128 tile per CU, direct-to-LDS groups whose K
+    chain is long (>= 16 chunks of 32) and above 1.5x one slot's share of the
+    plan's work get 128-row tiles."""
+    # 1024^3: 32 chunks, share 32 * 32 / 512 = 2 -> 8 x 8 tiles of 128 x 128
+    assert bst.Plan(_dense_con(1024, 1024, 1024, True)).stats()["items_by_class"]["mfma_fast"] == 64
+    # the block-diagonal bf16 workload has 362 tiles of 256 x 128 (more than the CUs): none halved
+    prob = C.blockdiag_bf16(ld_align=8, align=8, values=False)
+    assert bst.Plan(prob.con).stats()["items_by_class"]["mfma_fast"] == \
+        bst.Plan(prob.con, tile_rows=256).stats()["items_by_class"]["mfma_fast"]
+    # 4096^3: share 128 chunks = the chain -> 256-row tiles
+    assert bst.Plan(_dense_con(4096, 4096, 4096, True)).stats()["items_by_class"]["mfma_fast"] == 512
+    # K = 480 (15 chunks): never
+    assert bst.Plan(_dense_con(1024, 480, 1024, True)).stats()["items_by_class"]["mfma_fast"] == 32
+    # per-sector launches keep 256-row tiles
+    s = bst.Plan(_dense_con(1024, 1024, 1024, True), launch_mode="per_sector").stats()
+    assert s["items_by_class"]["mfma_fast"] == 32
+    # forced heights
+    assert bst.Plan(_dense_con(1024, 1024, 1024, True), tile_rows=256).stats()["items_by_class"]["mfma_fast"] == 32
+    assert bst.Plan(_dense_con(1024, 480, 1024, True), tile_rows=128).stats()["items_by_class"]["mfma_fast"] == 64
+    with pytest.raises(bst.BscError):
+        bst.Plan(_dense_con(64, 64, 64, True), tile_rows=64)
+
+
 def test_split_k_policy():
     """Automatic K split: only tiles whose K chain is far above both 64 chunks
     and one slot's share of the plan's work; never in per-sector mode, with
@@ -378,12 +402,14 @@ def test_split_k_policy():
     assert bst.Plan(prob.con, split_k=8, launch_mode="per_sector").stats()["split_tiles"] == 0
     for shape in ((4096, 4096, 4096), (2048, 2048, 2048), (1024, 1024, 1024)):
         assert bst.Plan(_dense_con(*shape, True)).stats()["split_tiles"] == 0
-    # one tile with K = 32768 (1024 chunks): slices of 64 chunks
+    # 256 x 32768 x 128 (1024 chunks): two 128-row tiles (long chain), each
+    # cut into slices of 64 chunks
     con = _dense_con(256, 32768, 128, True)
     s = bst.Plan(con).stats()
-    assert s["split_tiles"] == 1 and s["items_by_class"]["mfma_fast"] == 16
-    assert bst.Plan(con, split_k=-1).stats()["split_tiles"] == 0
-    assert bst.Plan(con, split_k=100).stats()["items_by_class"]["mfma_fast"] == 11
+    assert s["split_tiles"] == 2 and s["items_by_class"]["mfma_fast"] == 2 * 16
+    s = bst.Plan(con, split_k=-1).stats()
+    assert s["split_tiles"] == 0 and s["items_by_class"]["mfma_fast"] == 2
+    assert bst.Plan(con, split_k=100).stats()["items_by_class"]["mfma_fast"] == 2 * 11
     # fp32 tiles are never split
     con32 = _dense_con(256, 32768, 128, True)
     con32.dtype = "f32"

@@ -16,7 +16,7 @@ STATUS = {
 
 EXPORTED = ["bsc_options_default", "bsc_plan", "bsc_plan_device_bytes", "bsc_plan_bind", "bsc_contract",
             "bsc_plan_stats", "bsc_plan_export", "bsc_plan_worklist", "bsc_plan_destroy", "bsc_status_string",
-            "bsc_last_error"]
+            "bsc_last_error", "bsc_chain_create", "bsc_chain_launch", "bsc_chain_destroy"]
 
 
 class BscIndex(ctypes.Structure):
@@ -89,5 +89,12 @@ def lib():
         L.bsc_status_string.restype = c_char_p
         L.bsc_last_error.argtypes = []
         L.bsc_last_error.restype = c_char_p
+        L.bsc_chain_create.argtypes = [POINTER(c_void_p), POINTER(c_void_p), POINTER(c_void_p), POINTER(c_void_p),
+                                       c_int32, POINTER(c_void_p)]
+        L.bsc_chain_create.restype = c_int32
+        L.bsc_chain_launch.argtypes = [c_void_p, c_void_p]
+        L.bsc_chain_launch.restype = c_int32
+        L.bsc_chain_destroy.argtypes = [c_void_p]
+        L.bsc_chain_destroy.restype = None
         _lib = L
     return _lib

@@ -289,3 +289,82 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     return BSC_OK;
 }
+
+// ---- captured chains (one graph launch per sequence of contractions) ----------------
+
+namespace bsc {
+struct Chain {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+}  // namespace bsc
+
+extern "C" bsc_status bsc_chain_create(const bsc_plan_t *plans, const void *const *A, const void *const *B,
+                                       void *const *C, int32_t n, bsc_chain_t *out) {
+    set_error("");
+    if (!plans || !A || !B || !C || !out || n < 1) {
+        set_error("bsc_chain_create: NULL argument or n < 1");
+        return BSC_ERR_ARG;
+    }
+    *out = nullptr;
+    for (int32_t i = 0; i < n; ++i) {
+        if (!plans[i]) {
+            set_error("bsc_chain_create: NULL plan");
+            return BSC_ERR_ARG;
+        }
+        if (!reinterpret_cast<Plan *>(plans[i])->dev) {
+            set_error("bsc_chain_create: plan " + std::to_string(i) + " is not bound to a device region");
+            return BSC_ERR_NOT_BOUND;
+        }
+    }
+    hipStream_t cs = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);   // default priority
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags (chain capture)");
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
+    if (e != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        return hip_fail(e, "hipStreamBeginCapture");
+    }
+    bsc_status st = BSC_OK;
+    for (int32_t i = 0; i < n && st == BSC_OK; ++i) st = bsc_contract(plans[i], A[i], B[i], C[i], cs);
+    const std::string err = st == BSC_OK ? std::string() : std::string(bsc_last_error());
+    Chain *ch = new Chain;
+    e = hipStreamEndCapture(cs, &ch->graph);
+    (void)hipStreamDestroy(cs);
+    if (st != BSC_OK || e != hipSuccess) {
+        if (ch->graph) (void)hipGraphDestroy(ch->graph);
+        delete ch;
+        if (st != BSC_OK) {
+            set_error("bsc_chain_create: " + err);
+            return st;
+        }
+        return hip_fail(e, "hipStreamEndCapture");
+    }
+    e = hipGraphInstantiate(&ch->exec, ch->graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(ch->graph);
+        delete ch;
+        return hip_fail(e, "hipGraphInstantiate");
+    }
+    *out = reinterpret_cast<bsc_chain_t>(ch);
+    return BSC_OK;
+}
+
+extern "C" bsc_status bsc_chain_launch(bsc_chain_t chain, void *stream) {
+    if (!chain) {
+        set_error("bsc_chain_launch: NULL chain");
+        return BSC_ERR_ARG;
+    }
+    Chain *ch = reinterpret_cast<Chain *>(chain);
+    const hipError_t e = hipGraphLaunch(ch->exec, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+    return BSC_OK;
+}
+
+extern "C" void bsc_chain_destroy(bsc_chain_t chain) {
+    if (!chain) return;
+    Chain *ch = reinterpret_cast<Chain *>(chain);
+    if (ch->exec) (void)hipGraphExecDestroy(ch->exec);
+    if (ch->graph) (void)hipGraphDestroy(ch->graph);
+    delete ch;
+}

@@ -14,3 +14,17 @@ extern "C" bsc_status bsc_contract(bsc_plan_t, const void *, const void *, void 
     set_error("bsc_contract: host-only planner build has no device runtime");
     return BSC_ERR_UNSUPPORTED;
 }
+
+extern "C" bsc_status bsc_chain_create(const bsc_plan_t *, const void *const *, const void *const *, void *const *,
+                                       int32_t, bsc_chain_t *out) {
+    if (out) *out = nullptr;
+    set_error("bsc_chain_create: host-only planner build has no device runtime");
+    return BSC_ERR_UNSUPPORTED;
+}
+
+extern "C" bsc_status bsc_chain_launch(bsc_chain_t, void *) {
+    set_error("bsc_chain_launch: host-only planner build has no device runtime");
+    return BSC_ERR_UNSUPPORTED;
+}
+
+extern "C" void bsc_chain_destroy(bsc_chain_t) {}

@@ -205,3 +205,41 @@ class Plan:
             except Exception:
                 pass
             self._h = None
+
+
+class Chain:
+    """A fixed sequence of contractions [(plan, A, B, C), ...] captured once
+    into a HIP graph and replayed with one launch (bsc_chain_*).  The plans
+    must be bound; the chain keeps references to the plans and the tensors,
+    whose addresses the graph holds."""
+
+    def __init__(self, steps):
+        steps = list(steps)
+        if not steps:
+            raise BscError(-1, "empty chain")
+        for p, A, B, C in steps:
+            if p._dev is None:
+                raise BscError(-8, "plan is not bound (call bind())")
+        n = len(steps)
+        arr = lambda xs: (c_void_p * n)(*xs)
+        plans = arr([p._h.value for p, _, _, _ in steps])
+        a = arr([A.data_ptr() for _, A, _, _ in steps])
+        b = arr([B.data_ptr() for _, _, B, _ in steps])
+        c = arr([C.data_ptr() for _, _, _, C in steps])
+        h = c_void_p()
+        _check(_capi.lib().bsc_chain_create(plans, a, b, c, n, byref(h)))
+        self._h = h
+        self._keep = steps   # plans and tensors must outlive the graph
+
+    def launch(self, stream=None):
+        """Enqueue one replay on `stream` (default: torch's current stream)."""
+        _check(_capi.lib().bsc_chain_launch(self._h, _stream_handle(stream)))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                _capi.lib().bsc_chain_destroy(h)
+            except Exception:
+                pass
+            self._h = None

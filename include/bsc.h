@@ -248,6 +248,33 @@ bsc_status bsc_plan_worklist(bsc_plan_t plan, bsc_worklist_info *info, void *ima
 
 void bsc_plan_destroy(bsc_plan_t plan);
 
+/* A fixed sequence of contractions (e.g. the stages of one environment
+ * update) replayed as one HIP graph launch instead of one launch per stage
+ * from the host (uni20 "block coalescing", "Open questions": deferred
+ * synchronisation and reuse of a captured graph per site).
+ *
+ * bsc_chain_create records bsc_contract(plans[i], A[i], B[i], C[i]) for
+ * i = 0 .. n-1, in that order, on a private stream into a graph and
+ * instantiates it; nothing runs.  A, B, C are device pointers as for
+ * bsc_contract; the graph holds these addresses and the plans' device
+ * regions, so the buffers must stay allocated at the same addresses and the
+ * plans must stay alive and bound to the same region while the chain exists.
+ * On success *out owns a new chain.  Errors: BSC_ERR_ARG (a NULL pointer or
+ * n < 1, or a NULL operand buffer), BSC_ERR_NOT_BOUND (an unbound plan),
+ * BSC_ERR_HIP (stream, capture or instantiation failure; detail in
+ * bsc_last_error).
+ *
+ * bsc_chain_launch enqueues one replay on `stream` (any stream, including the
+ * default one) and returns without synchronising.  Replays of one chain, and a
+ * replay and a direct bsc_contract of one of its plans, share the plans'
+ * workspaces and must not overlap in time (use one stream).  A plan's
+ * launches_issued statistic counts the capture only, not replays. */
+typedef struct bsc_chain_s *bsc_chain_t;
+bsc_status bsc_chain_create(const bsc_plan_t *plans, const void *const *A, const void *const *B, void *const *C,
+                            int32_t n, bsc_chain_t *out);
+bsc_status bsc_chain_launch(bsc_chain_t chain, void *stream);
+void bsc_chain_destroy(bsc_chain_t chain);
+
 const char *bsc_status_string(bsc_status s);
 
 /* Thread-local text of the last error raised on this thread ("" if none). */

@@ -23,6 +23,7 @@ struct KArgs {
     const void *W;          // pack workspace (operands of runs flagged R_A_WS / R_B_WS)
     float *P;               // K-split partial tiles
     int32_t *cnt;           // K-split arrival counters (zero between launches)
+    int64_t a_bytes, b_bytes, w_bytes;   // sizes of A, B and the pack workspace
 };
 
 // Buffer a run's A (B) pieces address: the caller's operand or the workspace.

@@ -25,6 +25,7 @@ namespace bsc {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
+typedef int v4i32_mf __attribute__((ext_vector_type(4)));
 
 constexpr int MF_TILE = 64;
 
@@ -254,6 +255,196 @@ __device__ __forceinline__ void mf_kloop(const MfCtx<T> &oa, const MfCtx<T> &ob,
     }
 }
 
+// ---- branch-free K loop for k-contiguous and free-contiguous operands -----------------
+//
+// The general loop above serves every operand layout with per-lane conditional
+// loads; the compiler then cannot count the loads in flight and waits for all
+// of them before every LDS store, so each chunk pays a full memory latency.
+// When both operands are k-contiguous rows or free-axis-contiguous lines (the
+// common case), this loop issues a fixed number of 16-byte buffer loads per
+// chunk and lane, unconditionally: addresses of rows or columns past the tile
+// edge are clamped to a valid one and indices k >= K are masked to zero after
+// the load, and the buffer descriptor (the whole operand buffer) bounds every
+// load in hardware.  Two chunks stay in flight with exact wait counts.
+constexpr int32_t MF_BUF_DWORD3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mf_rsrc(const void *base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t ua = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(a >> 32))) << 32) |
+                        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(a)));
+    const int32_t n = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(bytes));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ua), 0, n, MF_BUF_DWORD3);
+}
+
+// One operand of the branch-free loop: per pass, the lane's byte offset at
+// k = 0 and which of its V elements lie inside the tile along the free axis.
+template <typename T, int MODE>
+struct MfOp2 {
+    __amdgpu_buffer_rsrc_t rs;
+    int32_t off[2];
+    int32_t kstep;       // bytes per chunk
+    uint32_t xok[2];     // bit i: element i of pass q is inside the tile (free axis)
+    int32_t kbase[2];    // k of element 0 of pass q within a chunk (MF_KCONTIG), or the row (MF_FCONTIG)
+};
+
+template <typename T, int MODE>
+__device__ __forceinline__ MfOp2<T, MODE> mf_setup2(const MfCtx<T> &o, int64_t bytes) {
+    constexpr int V = 16 / sizeof(T);
+    constexpr int KC = MfTraits<T>::KC;
+    MfOp2<T, MODE> f;
+    f.rs = mf_rsrc(o.P, bytes);
+    const int32_t tid = threadIdx.x;
+    static_assert(MODE == MF_KCONTIG || MODE == MF_FCONTIG, "contiguous modes only");
+    if constexpr (MODE == MF_KCONTIG) {
+        const int32_t kx = tid & 7, xr = tid >> 3;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int32_t x = xr + 32 * q;
+            const int32_t xc = x < o.xlen ? x : 0;           // rows past the edge: a valid row
+            f.off[q] = static_cast<int32_t>((o.rec[xc].base + V * kx) * static_cast<int64_t>(sizeof(T)));
+            f.xok[q] = x < o.xlen ? 0xffu : 0u;
+            f.kbase[q] = V * kx;
+        }
+        f.kstep = KC * static_cast<int32_t>(sizeof(T));
+    } else {
+        constexpr int LPR = MF_TILE / V, RPP = 256 / LPR;
+        const int32_t x = V * (tid % LPR), kr = tid / LPR;
+        const int32_t xc = x < o.xlen ? x : 0;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            f.off[q] = static_cast<int32_t>((o.off + o.x0 + xc + static_cast<int64_t>(kr + RPP * q) * o.sk) *
+                                            static_cast<int64_t>(sizeof(T)));
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < V; ++i) m |= (x + i < o.xlen ? 1u : 0u) << i;
+            f.xok[q] = m;
+            f.kbase[q] = kr + RPP * q;
+        }
+        f.kstep = static_cast<int32_t>(KC * o.sk * static_cast<int64_t>(sizeof(T)));
+    }
+    return f;
+}
+
+// a lane's range must be addressable with 32-bit offsets from the buffer base
+template <typename T>
+__device__ __forceinline__ bool mf_fits2(int64_t bytes) { return bytes > 0 && bytes < (int64_t(1) << 31); }
+
+// raw 16-byte loads of one chunk (masked later, when stored: using the loaded
+// registers here would wait for the loads)
+struct MfRaw {
+    v4i32_mf v[2];
+};
+
+template <typename T, int MODE>
+__device__ __forceinline__ void mf_load2(const MfOp2<T, MODE> &f, int32_t k0, MfRaw &st) {
+    {
+        const int32_t soff = __builtin_amdgcn_readfirstlane(k0 / MfTraits<T>::KC * f.kstep);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            __amdgpu_buffer_rsrc_t rs = f.rs;
+            st.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, f.off[q], soff, 0);
+        }
+    }
+}
+
+// registers -> LDS chunk (starting at k0) for a layout known at compile time:
+// elements outside the tile or at k >= K become zeros
+template <typename T, int MODE>
+__device__ __forceinline__ void mf_store2(const MfOp2<T, MODE> &f, const MfRaw &raw, T *lds, int32_t k0, int32_t K) {
+    constexpr int V = 16 / sizeof(T);
+    const int32_t tid = threadIdx.x;
+    T e[2][V];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        __builtin_memcpy(e[q], &raw.v[q], 16);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int32_t k = MODE == MF_KCONTIG ? k0 + f.kbase[q] + i : k0 + f.kbase[q];
+            const bool ok = ((f.xok[q] >> i) & 1u) && k < K;
+            e[q][i] = ok ? e[q][i] : T(0);
+        }
+    }
+    if constexpr (MODE == MF_KCONTIG) {
+        const int32_t kx = tid & 7, xr = tid >> 3;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < V; ++i) lds[mf_idx(V * kx + i, xr + 32 * q)] = e[q][i];
+    } else {
+        constexpr int LPR = MF_TILE / V, RPP = 256 / LPR;
+        const int32_t x = V * (tid % LPR), kr = tid / LPR;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            uint4 u;
+            __builtin_memcpy(&u, e[q], 16);
+            *reinterpret_cast<uint4 *>(lds + mf_idx(kr + RPP * q, x)) = u;
+        }
+    }
+}
+
+template <typename T, int MA, int MB>
+__device__ __forceinline__ void mf_kloop2(const MfOp2<T, MA> &fa, const MfOp2<T, MB> &fb, int32_t K, MfmaSmemF<T> &sm,
+                                          typename MfTraits<T>::acc_t (&acc)[2][2]) {
+    constexpr int KC = MfTraits<T>::KC;
+    const int32_t nchunks = (K + KC - 1) / KC;
+    const int32_t last = (nchunks - 1) * KC;
+    MfRaw a0, b0, a1, b1;
+    // loads are unconditional: a chunk index past the end repeats the last chunk
+    mf_load2<T, MA>(fa, 0, a0);
+    mf_load2<T, MB>(fb, 0, b0);
+    mf_load2<T, MA>(fa, min(KC, last), a1);
+    mf_load2<T, MB>(fb, min(KC, last), b1);
+    mf_store2<T, MA>(fa, a0, sm.a[0], 0, K);
+    mf_store2<T, MB>(fb, b0, sm.b[0], 0, K);
+    __syncthreads();
+    // Unrolled by two so the register sets swap roles without copies (a copy
+    // of the set just loaded would wait for its loads): in step (c, X, Y), X
+    // holds chunk c + 1 and chunk c + 2 is loaded into Y.
+    auto step = [&](int32_t c, MfRaw &xa, MfRaw &xb, MfRaw &ya, MfRaw &yb) {
+        const int32_t k2 = min((c + 2) * KC, last);
+        mf_load2<T, MA>(fa, k2, ya);
+        mf_load2<T, MB>(fb, k2, yb);
+        mf_compute<T>(sm.a[c & 1], sm.b[c & 1], acc);
+        // (after the last chunk this stores zeros or a repeat into the idle buffer)
+        mf_store2<T, MA>(fa, xa, sm.a[(c + 1) & 1], (c + 1) * KC, K);
+        mf_store2<T, MB>(fb, xb, sm.b[(c + 1) & 1], (c + 1) * KC, K);
+        __syncthreads();
+    };
+    int32_t c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        step(c, a1, b1, a0, b0);
+        step(c + 1, a0, b0, a1, b1);
+    }
+    if (c < nchunks) step(c, a1, b1, a0, b0);
+}
+
+// Run the K loop of one operand pair: the branch-free loop when both operands
+// are k- or free-contiguous and addressable with 32-bit offsets, else the
+// general one.
+template <typename T, int MA>
+__device__ __forceinline__ void mf_kloop_b(const MfCtx<T> &oa, const MfCtx<T> &ob, int64_t a_bytes, int64_t b_bytes,
+                                           int32_t K, MfmaSmemF<T> &sm, typename MfTraits<T>::acc_t (&acc)[2][2]) {
+    const MfOp2<T, MA> fa = mf_setup2<T, MA>(oa, a_bytes);
+    if (ob.mode == MF_KCONTIG) mf_kloop2<T, MA, MF_KCONTIG>(fa, mf_setup2<T, MF_KCONTIG>(ob, b_bytes), K, sm, acc);
+    else mf_kloop2<T, MA, MF_FCONTIG>(fa, mf_setup2<T, MF_FCONTIG>(ob, b_bytes), K, sm, acc);
+}
+
+template <typename T>
+__device__ __forceinline__ void mf_kloop_any(const MfCtx<T> &oa, const MfCtx<T> &ob, int64_t a_bytes, int64_t b_bytes,
+                                             int32_t K, MfmaSmemF<T> &sm, typename MfTraits<T>::acc_t (&acc)[2][2]) {
+    // element offsets of the record mode are 32-bit too
+    // (the record mode through this loop measured slower than the general loop
+    // on the environment-update stages: per-element address arithmetic and
+    // register pressure outweigh the better overlap)
+    const bool fits = mf_fits2<T>(a_bytes) && mf_fits2<T>(b_bytes);
+    if (fits && oa.mode != MF_GENERIC && ob.mode != MF_GENERIC) {
+        if (oa.mode == MF_KCONTIG) mf_kloop_b<T, MF_KCONTIG>(oa, ob, a_bytes, b_bytes, K, sm, acc);
+        else mf_kloop_b<T, MF_FCONTIG>(oa, ob, a_bytes, b_bytes, K, sm, acc);
+        return;
+    }
+    mf_kloop<T>(oa, ob, K, sm, acc);   // record-mode operands, or operands beyond 2 GiB
+}
+
 template <typename T>
 __device__ __forceinline__ void mfma_tile_f(const KArgs &ka, const DTask &task, const DFast &fd_ref, MfmaSmemF<T> &sm) {
     typedef typename MfTraits<T>::acc_t acc_t;
@@ -304,7 +495,8 @@ __device__ __forceinline__ void mfma_tile_f(const KArgs &ka, const DTask &task, 
         ob.mode = (fd.b_ks == 1 || fd.K == 1) ? MF_KCONTIG : (fd.b_ns == 1 ? MF_FCONTIG : MF_GENERIC);
         oa.off = fd.a_base; oa.sk = fd.a_ks;
         ob.off = fd.b_base; ob.sk = fd.b_ks;
-        mf_kloop<T>(oa, ob, fd.K, sm, acc);
+        mf_kloop_any<T>(oa, ob, (fd.flags & F_A_WS) ? ka.w_bytes : ka.a_bytes, (fd.flags & F_B_WS) ? ka.w_bytes : ka.b_bytes,
+                        fd.K, sm, acc);
     } else {
         for (int32_t r = 0; r < g.nrun; ++r) {
             const DRun run = ka.runs[g.run0 + r];
@@ -321,7 +513,8 @@ __device__ __forceinline__ void mfma_tile_f(const KArgs &ka, const DTask &task, 
                                           run_a<T>(ka, run.flags), va, sm.ra);
             const MfCtx<T> ob = mf_ctx<T>(ka.bp + run.bp0, run.nbp, R_B_KUNIT, R_B_FUNIT, run.flags, n0, nlen, run.K,
                                           run_b<T>(ka, run.flags), vb, sm.rb);
-            mf_kloop<T>(oa, ob, run.K, sm, acc);
+            mf_kloop_any<T>(oa, ob, (run.flags & R_A_WS) ? ka.w_bytes : ka.a_bytes,
+                            (run.flags & R_B_WS) ? ka.w_bytes : ka.b_bytes, run.K, sm, acc);
         }
     }
 

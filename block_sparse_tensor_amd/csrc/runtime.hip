@@ -239,6 +239,12 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
     ka.W = base + p->off_ws;
     ka.P = reinterpret_cast<float *>(const_cast<unsigned char *>(base) + p->off_part);
     ka.cnt = reinterpret_cast<int32_t *>(const_cast<unsigned char *>(base) + p->off_cnt);
+    {
+        const int64_t esz = p->dtype == BSC_F64 ? 8 : (p->dtype == BSC_F32 ? 4 : 2);
+        ka.a_bytes = p->a_elems * esz;
+        ka.b_bytes = p->b_elems * esz;
+        ka.w_bytes = p->ws_elems * esz;
+    }
     if (!p->pack_tasks.empty()) {
         // gathers first, on the same stream: the grouped launch reads the workspace after them
         PArgs pa;

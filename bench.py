@@ -220,6 +220,17 @@ def main():
         graph = {"ms_per_step": round(gms, 6), "value": round(flops / (gms * 1e-3) / 1e9, 3), "unit": "GFLOP/s",
                  "launches_per_step": 1}
 
+    # --- host planning of every stage: fresh, and a plan-cache hit (a site revisited in a sweep) ---
+    def plan_all(cache=None):
+        t0 = time.perf_counter()
+        for con, _, _, _, ax in stages:
+            bst.Plan(con, axis=ax, layout=args.layout, cache=cache)
+        return (time.perf_counter() - t0) * 1e3
+    pcache = bst.PlanCache(max(4, len(stages)))
+    plan_all(pcache)
+    planning = {"fresh_ms": round(min(plan_all() for _ in range(3)), 4),
+                "cached_ms": round(min(plan_all(pcache) for _ in range(3)), 4)}
+
     # --- uncoalesced GPU baseline: one launch per sector GEMM -----------------------
     if not args.no_baseline:
         per_sector = plans_for("per_sector")
@@ -267,6 +278,7 @@ def main():
             "launches_per_contraction": launches_ps, "steps": args.baseline_steps,
         },
         "stage_kernel_ms": [round(x, 6) for x in stage_ms],
+        "host_planning": planning,
     }
     if graph is not None:
         # the stages as one captured graph (bsc_chain): no host gaps between launches

@@ -16,7 +16,8 @@ STATUS = {
 
 EXPORTED = ["bsc_options_default", "bsc_plan", "bsc_plan_device_bytes", "bsc_plan_bind", "bsc_contract",
             "bsc_plan_stats", "bsc_plan_export", "bsc_plan_worklist", "bsc_plan_destroy", "bsc_status_string",
-            "bsc_last_error", "bsc_chain_create", "bsc_chain_launch", "bsc_chain_destroy"]
+            "bsc_last_error", "bsc_chain_create", "bsc_chain_launch", "bsc_chain_destroy", "bsc_plan_cache_create",
+            "bsc_plan_cached", "bsc_plan_cache_stats", "bsc_plan_cache_destroy"]
 
 
 class BscIndex(ctypes.Structure):
@@ -96,5 +97,13 @@ def lib():
         L.bsc_chain_launch.restype = c_int32
         L.bsc_chain_destroy.argtypes = [c_void_p]
         L.bsc_chain_destroy.restype = None
+        L.bsc_plan_cache_create.argtypes = [c_int32, POINTER(c_void_p)]
+        L.bsc_plan_cache_create.restype = c_int32
+        L.bsc_plan_cached.argtypes = [c_void_p] + L.bsc_plan.argtypes + [POINTER(c_int32)]
+        L.bsc_plan_cached.restype = c_int32
+        L.bsc_plan_cache_stats.argtypes = [c_void_p, POINTER(c_int64), POINTER(c_int64), POINTER(c_int64)]
+        L.bsc_plan_cache_stats.restype = c_int32
+        L.bsc_plan_cache_destroy.argtypes = [c_void_p]
+        L.bsc_plan_cache_destroy.restype = None
         _lib = L
     return _lib

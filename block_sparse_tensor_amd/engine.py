@@ -92,12 +92,14 @@ class Plan:
 
     `con` is any object with attributes m, k, n (indices: charge, dim, inner)
     and A, B, C (operands: row_key, col_key, offset, row_stride, col_stride,
-    flux, buffer_elems), e.g. workloads.Contraction."""
+    flux, buffer_elems), e.g. workloads.Contraction.  With `cache` (a
+    PlanCache) the plan is copied from the cache when every input matches a
+    cached one (bsc_plan_cached); `cache_hit` tells which happened."""
 
     def __init__(self, con, dtype: str = None, axis: str = "auto", launch_mode: str = "grouped",
                  layout: str = "auto", accumulate: bool = False, grid_limit: int = 0,
                  t_launch_us: float = 0.0, t_seg_us: float = 0.0, pack_gbps: float = 0.0, tile_gflops: float = 0.0,
-                 split_k: int = 0, tile_rows: int = 0):
+                 split_k: int = 0, tile_rows: int = 0, cache: "PlanCache" = None):
         L = _capi.lib()
         self.dtype = dtype or con.dtype
         keep = _Keep()
@@ -113,8 +115,14 @@ class Plan:
         opt.split_k = int(split_k)
         opt.tile_rows = int(tile_rows)
         h = c_void_p()
-        _check(L.bsc_plan(byref(m), byref(k), byref(n), byref(A), byref(B), byref(C),
-                          DTYPES[self.dtype], AXES[axis], byref(opt), byref(h)))
+        args = (byref(m), byref(k), byref(n), byref(A), byref(B), byref(C), DTYPES[self.dtype], AXES[axis], byref(opt))
+        if cache is None:
+            _check(L.bsc_plan(*args, byref(h)))
+            self.cache_hit = False
+        else:
+            hit = c_int32()
+            _check(L.bsc_plan_cached(cache._h, *args, byref(h), byref(hit)))
+            self.cache_hit = bool(hit.value)
         self._h = h
         self.a_elems, self.b_elems, self.c_elems = int(con.A.buffer_elems), int(con.B.buffer_elems), int(con.C.buffer_elems)
         self._dev = None
@@ -240,6 +248,31 @@ class Chain:
         if h is not None and h.value:
             try:
                 _capi.lib().bsc_chain_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+
+class PlanCache:
+    """Host-side cache of plans keyed by their complete inputs (bsc_plan_cache_*).
+    Pass it to Plan(..., cache=...); every Plan it yields is a separate,
+    unbound copy."""
+
+    def __init__(self, capacity: int = 64):
+        h = c_void_p()
+        _check(_capi.lib().bsc_plan_cache_create(int(capacity), byref(h)))
+        self._h = h
+
+    def stats(self) -> dict:
+        hits, misses, entries = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(_capi.lib().bsc_plan_cache_stats(self._h, byref(hits), byref(misses), byref(entries)))
+        return {"hits": hits.value, "misses": misses.value, "entries": entries.value}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                _capi.lib().bsc_plan_cache_destroy(h)
             except Exception:
                 pass
             self._h = None

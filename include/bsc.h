@@ -248,6 +248,37 @@ bsc_status bsc_plan_worklist(bsc_plan_t plan, bsc_worklist_info *info, void *ima
 
 void bsc_plan_destroy(bsc_plan_t plan);
 
+/* Plan cache (uni20 "block coalescing", "Open questions": keeping the
+ * coalescing groups across DMRG sweeps once a site's block structure is
+ * stable).  Planning costs milliseconds of host time; a sweep that contracts
+ * the same block structure again should not pay it again.
+ *
+ * bsc_plan_cache_create makes an empty cache holding at most `capacity`
+ * (>= 1) plans; the least recently used plan is dropped beyond that.
+ *
+ * bsc_plan_cached takes bsc_plan's arguments and returns the same result.
+ * When every input (index tables, operand descriptors including offsets,
+ * strides, flux and buffer lengths, dtype, axis and every option; opt NULL
+ * means the defaults) equals that of a plan in the cache, *out is a copy of
+ * the cached plan and no planning is done (*hit = 1); otherwise the call plans
+ * as bsc_plan does, stores a copy and sets *hit = 0 (`hit` may be NULL).
+ * Either way *out is a new, unbound plan owned by the caller (bind it, destroy
+ * it with bsc_plan_destroy); the cache keeps its own copy and owns no device
+ * memory.  Inputs are compared in full.  Errors are those of bsc_plan, plus
+ * BSC_ERR_ARG for a NULL cache or out; a failed plan is not cached.  The cache
+ * is internally locked, so threads may share one.
+ *
+ * bsc_plan_cache_stats reports hits, misses and stored plans (any pointer may
+ * be NULL).  bsc_plan_cache_destroy frees the cache and its stored plans;
+ * plans handed out stay valid. */
+typedef struct bsc_plan_cache_s *bsc_plan_cache_t;
+bsc_status bsc_plan_cache_create(int32_t capacity, bsc_plan_cache_t *out);
+bsc_status bsc_plan_cached(bsc_plan_cache_t cache, const bsc_index *m, const bsc_index *k, const bsc_index *n,
+                           const bsc_operand *A, const bsc_operand *B, const bsc_operand *C, bsc_dtype dtype,
+                           bsc_axis axis, const bsc_options *opt, bsc_plan_t *out, int32_t *hit);
+bsc_status bsc_plan_cache_stats(bsc_plan_cache_t cache, int64_t *hits, int64_t *misses, int64_t *entries);
+void bsc_plan_cache_destroy(bsc_plan_cache_t cache);
+
 /* A fixed sequence of contractions (e.g. the stages of one environment
  * update) replayed as one HIP graph launch instead of one launch per stage
  * from the host (uni20 "block coalescing", "Open questions": deferred

@@ -68,7 +68,7 @@ def measured_traffic(workload, ld_align, stage):
     return None
 
 
-def load_workload(name, ld_align=1):
+def load_workload(name, ld_align=1, relayout=False):
     from workloads import configs as C
     if name == "blockdiag_bf16":
         p = C.blockdiag_bf16(ld_align=ld_align, align=max(1, ld_align))
@@ -83,7 +83,16 @@ def load_workload(name, ld_align=1):
     if name in ("rabc_u1", "rabc_u1u1"):
         ch = C.rabc_u1() if name == "rabc_u1" else C.rabc_u1u1()
         stages = [(st.con, st.a_buf, st.b_buf, st.c_buf, "auto") for st in ch.stages]
-        return stages, dict(ch.buffers), dict(ch.sizes), ch.dtype
+        if not relayout:
+            return stages, dict(ch.buffers), dict(ch.sizes), ch.dtype
+        # every buffer laid out for the stage that reads it (bsc_plan_layout), inputs moved to match
+        from block_sparse_tensor_amd.layouts import move_blocks, relayout_chain
+        new, sizes, _ = relayout_chain([s[:4] for s in stages], axes=[s[4] for s in stages])
+        inputs = {}
+        for buf, v in ch.buffers.items():
+            i, which = next((i, w) for i, s in enumerate(stages) for w, b in zip("AB", s[1:3]) if b == buf)
+            inputs[buf] = move_blocks(v, stages[i][0], which, new[i])
+        return [(c,) + s[1:] for c, s in zip(new, stages)], inputs, sizes, ch.dtype
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -102,6 +111,8 @@ def main():
                     help="only run a plain device copy of MB megabytes (counter calibration) and exit")
     ap.add_argument("--layout", default="auto", choices=["auto", "never_pack", "force_pack"],
                     help="operand arrangement policy of the grouped plans (auto = the planner's pack-cost model)")
+    ap.add_argument("--relayout", action="store_true",
+                    help="chains: lay out every buffer for the stage that reads it (cross-stage layout planning)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -128,7 +139,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}), flush=True)
         return
-    stages, inputs, sizes, dtype = load_workload(args.workload, args.ld_align)
+    stages, inputs, sizes, dtype = load_workload(args.workload, args.ld_align, args.relayout)
 
     # inputs resident in HBM before timing
     def dev(x):
@@ -251,7 +262,7 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "stages": len(stages),
-                   "ld_align": args.ld_align, "layout": args.layout,
+                   "ld_align": args.ld_align, "layout": args.layout, "relayout": args.relayout,
                    "pack_bytes": sum(s["pack_bytes"] for s in st),
                    "sector_gemms": sum(s["triples"] for s in st), "useful_flops": flops,
                    "alg_bytes": alg_bytes, "parallelism": "single GPU"},

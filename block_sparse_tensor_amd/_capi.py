@@ -17,7 +17,7 @@ STATUS = {
 EXPORTED = ["bsc_options_default", "bsc_plan", "bsc_plan_device_bytes", "bsc_plan_bind", "bsc_contract",
             "bsc_plan_stats", "bsc_plan_export", "bsc_plan_worklist", "bsc_plan_destroy", "bsc_status_string",
             "bsc_last_error", "bsc_chain_create", "bsc_chain_launch", "bsc_chain_destroy", "bsc_plan_cache_create",
-            "bsc_plan_cached", "bsc_plan_cache_stats", "bsc_plan_cache_destroy"]
+            "bsc_plan_cached", "bsc_plan_cache_stats", "bsc_plan_cache_destroy", "bsc_plan_layout"]
 
 
 class BscIndex(ctypes.Structure):
@@ -105,5 +105,8 @@ def lib():
         L.bsc_plan_cache_stats.restype = c_int32
         L.bsc_plan_cache_destroy.argtypes = [c_void_p]
         L.bsc_plan_cache_destroy.restype = None
+        L.bsc_plan_layout.argtypes = L.bsc_plan.argtypes[:-1] + [c_int32, c_int64, POINTER(c_int64), POINTER(c_int64),
+                                                                POINTER(c_int64), POINTER(c_int64)]
+        L.bsc_plan_layout.restype = c_int32
         _lib = L
     return _lib

@@ -87,6 +87,43 @@ def _stream_handle(stream):
     return c_void_p(stream.cuda_stream)
 
 
+def _plan_args(con, dtype, axis, keep, launch_mode="grouped", layout="auto", accumulate=False, grid_limit=0,
+               t_launch_us=0.0, t_seg_us=0.0, pack_gbps=0.0, tile_gflops=0.0, split_k=0, tile_rows=0):
+    """bsc_plan's arguments (without the output handle) as ctypes values."""
+    L = _capi.lib()
+    m, k, n = _index(con.m, keep), _index(con.k, keep), _index(con.n, keep)
+    A, B, C = _operand(con.A, keep), _operand(con.B, keep), _operand(con.C, keep)
+    opt = _capi.BscOptions()
+    L.bsc_options_default(byref(opt))
+    opt.launch_mode = LAUNCH[launch_mode]
+    opt.layout_policy = LAYOUT[layout]
+    opt.accumulate = int(bool(accumulate))
+    opt.grid_limit = int(grid_limit)
+    opt.t_launch_us, opt.t_seg_us, opt.pack_gbps, opt.tile_gflops = t_launch_us, t_seg_us, pack_gbps, tile_gflops
+    opt.split_k = int(split_k)
+    opt.tile_rows = int(tile_rows)
+    keep.arrays.extend([m, k, n, A, B, C, opt])
+    return (byref(m), byref(k), byref(n), byref(A), byref(B), byref(C), DTYPES[dtype], AXES[axis], byref(opt))
+
+
+def plan_layout(con, which: str, align: int = 1, dtype: str = None, axis: str = "auto", **options):
+    """Layout of operand `which` ("A", "B" or "C") that lets the contraction
+    `con` address its groups' members of that operand as single strided views
+    (bsc_plan_layout).  The operand's own offsets and strides are ignored.
+    Returns (offset [nb], row_stride [nb, 2], col_stride [nb, 2], buffer_elems)."""
+    op = {"A": con.A, "B": con.B, "C": con.C}[which]
+    nb = len(op.row_key)
+    keep = _Keep()
+    args = _plan_args(con, dtype or con.dtype, axis, keep, **options)
+    off = np.zeros(max(nb, 1), np.int64)
+    rs = np.zeros((max(nb, 1), 2), np.int64)
+    cs = np.zeros((max(nb, 1), 2), np.int64)
+    total = ctypes.c_int64()
+    _check(_capi.lib().bsc_plan_layout(*args, "ABC".index(which), int(align), _ptr(off, ctypes.c_int64),
+                                       _ptr(rs, ctypes.c_int64), _ptr(cs, ctypes.c_int64), byref(total)))
+    return off[:nb], rs[:nb], cs[:nb], int(total.value)
+
+
 class Plan:
     """A planned block-sparse contraction C[m,n] = sum_k A[m,k] B[k,n].
 
@@ -103,19 +140,10 @@ class Plan:
         L = _capi.lib()
         self.dtype = dtype or con.dtype
         keep = _Keep()
-        m, k, n = _index(con.m, keep), _index(con.k, keep), _index(con.n, keep)
-        A, B, C = _operand(con.A, keep), _operand(con.B, keep), _operand(con.C, keep)
-        opt = _capi.BscOptions()
-        L.bsc_options_default(byref(opt))
-        opt.launch_mode = LAUNCH[launch_mode]
-        opt.layout_policy = LAYOUT[layout]
-        opt.accumulate = int(bool(accumulate))
-        opt.grid_limit = int(grid_limit)
-        opt.t_launch_us, opt.t_seg_us, opt.pack_gbps, opt.tile_gflops = t_launch_us, t_seg_us, pack_gbps, tile_gflops
-        opt.split_k = int(split_k)
-        opt.tile_rows = int(tile_rows)
+        args = _plan_args(con, self.dtype, axis, keep, launch_mode=launch_mode, layout=layout, accumulate=accumulate,
+                          grid_limit=grid_limit, t_launch_us=t_launch_us, t_seg_us=t_seg_us, pack_gbps=pack_gbps,
+                          tile_gflops=tile_gflops, split_k=split_k, tile_rows=tile_rows)
         h = c_void_p()
-        args = (byref(m), byref(k), byref(n), byref(A), byref(B), byref(C), DTYPES[self.dtype], AXES[axis], byref(opt))
         if cache is None:
             _check(L.bsc_plan(*args, byref(h)))
             self.cache_hit = False

@@ -279,6 +279,41 @@ bsc_status bsc_plan_cached(bsc_plan_cache_t cache, const bsc_index *m, const bsc
 bsc_status bsc_plan_cache_stats(bsc_plan_cache_t cache, int64_t *hits, int64_t *misses, int64_t *entries);
 void bsc_plan_cache_destroy(bsc_plan_cache_t cache);
 
+/* Layout planning for chains of contractions (uni20 "block coalescing",
+ * "Interleaved vs contiguous — the real tradeoff is a copy": the zero-copy
+ * arrangement needs the axis to be coalesced laid out interleaved; "Open
+ * questions": the coalescing axis may differ per stage).  Returns a block
+ * layout for operand `which` (0 = A, 1 = B, 2 = C) of the contraction given
+ * by the other arguments (as for bsc_plan), chosen so that the groups this
+ * contraction forms see their members of that operand as one strided view.
+ * The producer of an intermediate then writes it through these views and the
+ * consumer needs neither a gather nor a per-member walk.
+ *
+ * Only the block keys (row_key, col_key, nblocks) and flux of the selected
+ * operand are read; its offset, strides and buffer_elems are ignored.  The
+ * other operands must be valid descriptors.  Grouping follows `axis` and
+ * `opt` exactly as bsc_plan would (it depends on keys only).  Blocks go into
+ * one panel per key of the non-coalesced axis (free-m grouping: A per k and
+ * C per n, stacked down the rows; free-n: B per k and C per m, side by side;
+ * contraction-axis: A per m side by side, B per n stacked down the rows; the
+ * remaining operand one block per panel).  Within a panel each group's
+ * members are consecutive in ascending key order, larger groups first; a
+ * member already placed by an earlier group stays, and that group walks its
+ * members one by one.  Every block is row-major inside its panel
+ * (row_stride = {Ri*ld, ld}, col_stride = {Ci, 1}, with Ri, Ci the inner
+ * extents); panel starts and leading dimensions are multiples of `align`
+ * (>= 1) elements.
+ *
+ * Outputs, in the operand's block order: offset [nblocks], row_stride
+ * [2*nblocks], col_stride [2*nblocks], and *buffer_elems, the buffer length
+ * the layout needs (their contents are unspecified on failure).  Errors: BSC_ERR_ARG
+ * (bad `which` or `align`, a NULL argument), BSC_ERR_SHAPE (a block key out
+ * of range or a dimension < 1), and any error of bsc_plan on the keys. */
+bsc_status bsc_plan_layout(const bsc_index *m, const bsc_index *k, const bsc_index *n,
+                           const bsc_operand *A, const bsc_operand *B, const bsc_operand *C,
+                           bsc_dtype dtype, bsc_axis axis, const bsc_options *opt, int32_t which, int64_t align,
+                           int64_t *offset, int64_t *row_stride, int64_t *col_stride, int64_t *buffer_elems);
+
 /* A fixed sequence of contractions (e.g. the stages of one environment
  * update) replayed as one HIP graph launch instead of one launch per stage
  * from the host (uni20 "block coalescing", "Open questions": deferred

@@ -501,18 +501,38 @@ __device__ __forceinline__ bool split_arrive(const KArgs &ka, const DFast &fd, f
     }
     __syncthreads();
     if (!last) return false;
-    for (int32_t s = 0; s < nsplit; ++s) {
+    // slice 0 replaces the accumulators, slices 1.. add in order.  Loads go out
+    // in batches of SPLIT_BATCH before any of them is used: added one by one,
+    // each load would wait out a full memory round trip.
+    constexpr int SPLIT_BATCH = 16;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        f32x16_t &a = acc[q / 8][(q / 4) & 1];
+        const int r = 4 * (q & 3);
+        // (the whole vector is reinterpreted at once: extracting single lanes of
+        // the loaded integer vector through bit casts is narrowed to a
+        // one-dword load by this compiler)
+        const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + q * 1024, 0, CPOL_SC1));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[r + e] = x[e];
+    }
+    for (int32_t s = 1; s < nsplit; ++s) {
         const int32_t src = s * SPLIT_BYTES + lane_off;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            f32x16_t &a = acc[q / 8][(q / 4) & 1];
-            const int r = 4 * (q & 3);
-            // (the whole vector is reinterpreted at once: extracting single lanes of
-            // the loaded integer vector through bit casts is narrowed to a
-            // one-dword load by this compiler)
-            const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, src + q * 1024, 0, CPOL_SC1));
+        for (int h = 0; h < NQ; h += SPLIT_BATCH) {
+            v4i32_t t[SPLIT_BATCH];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a[r + e] = s == 0 ? x[e] : a[r + e] + x[e];
+            for (int u = 0; u < SPLIT_BATCH; ++u)
+                t[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, src + (h + u) * 1024, 0, CPOL_SC1);
+#pragma unroll
+            for (int u = 0; u < SPLIT_BATCH; ++u) {
+                const int q = h + u;
+                f32x16_t &a = acc[q / 8][(q / 4) & 1];
+                const int r = 4 * (q & 3);
+                const f32x4_t x = __builtin_bit_cast(f32x4_t, t[u]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[r + e] += x[e];
+            }
         }
     }
     return true;

@@ -63,3 +63,41 @@ def test_relaid_chain_matches_oracle(make, tol):
         assert np.isfinite(got).all()
         err = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)
         assert err <= tol, (cb, err)
+
+
+def _move_operand(src, con, new, which):
+    return bst.layouts.move_blocks(np.asarray(src), con, which, new)
+
+
+@pytest.mark.parametrize("dtype,tol", [("f64", 1e-12), ("f32", 1e-5), ("bf16", 2e-2)])
+@pytest.mark.parametrize("seed", [31, 32, 33])
+def test_planned_layout_single_contraction(dtype, tol, seed):
+    """Random sector structures (two-leg keys, scattered strided blocks) with
+    every operand laid out by bsc_plan_layout at 8-element alignment (the
+    16-byte rows the direct-to-LDS bf16 tiles need): the engine's C blocks
+    equal the oracle's on the source layout."""
+    import copy
+    t = torch()
+    p = C.random_problem(seed, nkeys=(8, 8, 8), maxdim=200, qrange=1, dtype=dtype, density=0.8)
+    con = p.con
+    ref = oracle.contract(con, p.a, p.b, np.zeros(con.C.buffer_elems), check=False)
+    new = copy.deepcopy(con)
+    for w in "ABC":
+        off, rs, cs, tot = bst.plan_layout(con, w, align=8)
+        op = getattr(new, w)
+        op.offset, op.row_stride, op.col_stride, op.buffer_elems = off, rs, cs, tot
+    a = _move_operand(p.a, con, new, "A")
+    b = _move_operand(p.b, con, new, "B")
+    plan = bst.Plan(new).bind()
+    s = plan.stats()
+    print(f"[layouts] random seed={seed} {dtype}: items {s['items_by_class']}", flush=True)
+    A, B = to_dev(a, dtype), to_dev(b, dtype)
+    cdt = t.float64 if dtype == "f64" else t.float32
+    Cd = t.full((new.C.buffer_elems,), float("nan"), dtype=cdt, device="cuda")
+    plan.contract(A, B, Cd)
+    t.cuda.synchronize()
+    got = _c_values(new, Cd.cpu().numpy().astype(np.float64))
+    want = _c_values(con, ref)
+    assert np.isfinite(got).all()
+    err = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)
+    assert err <= tol, err

@@ -85,7 +85,8 @@ def load_workload(name, ld_align=1, relayout=False):
         stages = [(st.con, st.a_buf, st.b_buf, st.c_buf, "auto") for st in ch.stages]
         if not relayout:
             return stages, dict(ch.buffers), dict(ch.sizes), ch.dtype
-        # every buffer laid out for the stage that reads it (bsc_plan_layout), inputs moved to match
+        # every intermediate laid out for the stage that writes it, every input for a stage that reads it
+        # (bsc_plan_layout), inputs moved to match
         from block_sparse_tensor_amd.layouts import move_blocks, relayout_chain
         new, sizes, _ = relayout_chain([s[:4] for s in stages], axes=[s[4] for s in stages])
         inputs = {}
@@ -112,7 +113,8 @@ def main():
     ap.add_argument("--layout", default="auto", choices=["auto", "never_pack", "force_pack"],
                     help="operand arrangement policy of the grouped plans (auto = the planner's pack-cost model)")
     ap.add_argument("--relayout", action="store_true",
-                    help="chains: lay out every buffer for the stage that reads it (cross-stage layout planning)")
+                    help="chains: lay out every buffer for the stage that writes it, inputs for a stage that reads "
+                         "them (cross-stage layout planning)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()

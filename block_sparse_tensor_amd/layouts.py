@@ -8,8 +8,9 @@ tradeoff is a copy": the zero-copy arrangement needs the coalesced axis laid
 out interleaved; "Open questions": the axis may differ per stage).  In a
 chain an intermediate is written by one stage and read by the next through a
 different matrix view of the same tensor blocks (other legs fused into rows
-and columns).  `relayout_chain` asks the library for the layout each buffer's
-consumer wants and rewrites every stage's view of that buffer to match:
+and columns).  `relayout_chain` asks the library for the layout one stage
+wants for each buffer (its writer or a reader, see below) and rewrites every
+stage's view of that buffer to match:
 
 * a tensor block is identified in every view by its first element's offset
   (views of one block all start there; the source layout must place blocks
@@ -19,8 +20,8 @@ consumer wants and rewrites every stage's view of that buffer to match:
   view gives each such leg its new stride, and every other view of the block
   takes the new strides of the same legs.
 
-So a buffer's consumer reads it as single views, and its producer writes it
-through the same memory with its own leg order.
+So the chosen stage addresses the buffer as single views, and every other
+stage reaches the same memory through its own leg order.
 """
 from __future__ import annotations
 
@@ -51,13 +52,16 @@ def _views(con, which):
     return {"A": (con.m, con.k, con.A), "B": (con.k, con.n, con.B), "C": (con.m, con.n, con.C)}[which]
 
 
-def relayout_chain(stages, align: int = 1, consumer=None, axes=None):
+def relayout_chain(stages, align: int = 1, consumer=None, axes=None, prefer: str = "writer"):
     """stages: [(con, a_buf, b_buf, c_buf)] over named buffers (source layout);
     axes: the coalescing axis each stage will be planned with (default "auto").
     consumer: optional {buffer: (stage index, "A"|"B"|"C")} overriding which
-    view a buffer's layout is planned for (default: the first stage that reads
-    it in a role its grouping coalesces, else the first stage that reads it,
-    else the producing stage's C).
+    view a buffer's layout is planned for.  Default: a buffer some stage
+    writes is laid out for its first writer when prefer="writer" and that
+    writer's grouping coalesces its output (the epilogue then writes whole
+    lines; on the environment updates this beat laying intermediates out for
+    their readers), otherwise for the first stage that reads it in a role its
+    grouping coalesces, else the first reader, else the first writer.
     Returns (new contractions, {buffer: new length}, {buffer: block map}) where
     a block map is {source offset: (new offset, {source stride: new stride})}."""
     uses = {}
@@ -73,11 +77,17 @@ def relayout_chain(stages, align: int = 1, consumer=None, axes=None):
             axis_of[i] = Plan(stages[i][0], axis=(axes[i] if axes else "auto")).stats()["axis_name"]
         return (axis_of[i], which) in _PANEL_ROLES
 
+    if prefer not in ("writer", "reader"):
+        raise ValueError("prefer must be 'writer' or 'reader'")
     for buf, us in uses.items():
         if buf not in chosen:
             reads = [u for u in us if u[1] != "C"]
+            writes = [u for u in us if u[1] == "C"]
             shaped = [u for u in reads if shapes_layout(*u)]
-            chosen[buf] = shaped[0] if shaped else (reads[0] if reads else us[0])
+            if prefer == "writer" and writes and shapes_layout(*writes[0]):
+                chosen[buf] = writes[0]
+            else:
+                chosen[buf] = shaped[0] if shaped else (reads[0] if reads else us[0])
 
     maps, sizes = {}, {}
     for buf, (i, which) in chosen.items():

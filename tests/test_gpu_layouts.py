@@ -1,5 +1,5 @@
-"""GPU parity of chains laid out for their readers (relayout_chain over
-bsc_plan_layout): the oracle runs the chain in its source layout, the engine
+"""GPU parity of chains laid out for their writers or readers (relayout_chain
+over bsc_plan_layout): the oracle runs the chain in its source layout, the engine
 runs the relaid chain (inputs moved block by block), and every block of every
 stage's output is compared through its own view in each layout.  The oracle
 never sees a layout the library produced."""
@@ -38,12 +38,13 @@ def _c_values(con, buf):
                                       (lambda: C.rabc_u1(layout="natural"), 1e-12),
                                       (lambda: C.rabc_u1u1(layout="natural"), 1e-5)],
                          ids=["small_f64", "small_f32", "rabc_u1", "rabc_u1u1"])
-def test_relaid_chain_matches_oracle(make, tol):
+@pytest.mark.parametrize("prefer", ["writer", "reader"])
+def test_relaid_chain_matches_oracle(make, tol, prefer):
     t = torch()
     ch = make()
     ref = oracle.run_chain(ch)
     st = [(s.con, s.a_buf, s.b_buf, s.c_buf) for s in ch.stages]
-    new, sizes, _ = bst.layouts.relayout_chain(st)
+    new, sizes, _ = bst.layouts.relayout_chain(st, prefer=prefer)
     plans = [bst.Plan(c).bind() for c in new]
     print(f"[layouts] {ch.name}: launches {[p.stats()['launches_per_contract'] for p in plans]}", flush=True)
     cdt = {"f64": t.float64, "f32": t.float32}[ch.dtype]

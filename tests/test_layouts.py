@@ -1,7 +1,7 @@
 """Host-side tests of layout planning: bsc_plan_layout (one operand of one
 contraction laid out for its coalescing groups) and relayout_chain (every
-buffer of a chain laid out for the stage that reads it, every other view of
-the buffer rewritten to the same memory).
+buffer of a chain laid out for the stage that writes it or a stage that reads
+it, every other view of the buffer rewritten to the same memory).
 
 Pins: the layouts are valid descriptors (the planner accepts them, C stays
 disjoint, panels and leading dimensions aligned), each group's members land
@@ -210,7 +210,7 @@ def test_chain_relayout_removes_gathers_and_segments():
     _lib_or_skip()
     ch = C.rabc_u1(layout="natural")
     st = _chain_stages(ch)
-    new, _, _ = bst.layouts.relayout_chain(st)
+    new, _, _ = bst.layouts.relayout_chain(st, prefer="reader")
     m0, s0 = _modes(st[0][0])
     m1, s1 = _modes(new[0])
     assert m0["A"][2] > 0 and m1["A"] == (s1["groups"] - s1["zero_groups"], 0, 0)
@@ -237,3 +237,21 @@ def _mask_of(con, which):
     for j in range(len(op.row_key)):
         mask[_block_addresses(con, which, j).ravel()] = True
     return None, mask
+
+
+def test_chain_writer_first_outputs_are_views():
+    """By default an intermediate is laid out for the stage that writes it:
+    every stage's output groups then write single views (the natural layout
+    makes stage 1 write per-member pieces), and the inputs are still laid out
+    for their readers (stage 1 reads E as single views)."""
+    _lib_or_skip()
+    ch = C.rabc_u1u1(layout="natural")
+    st = _chain_stages(ch)
+    new, _, _ = bst.layouts.relayout_chain(st)
+    m0, _ = _modes(st[0][0])
+    assert m0["C"][2] > 0 and m0["A"][2] > 0
+    for i, nc in enumerate(new):
+        m, s = _modes(nc, layout="never_pack")
+        assert m["C"][2] == 0, (i, m)
+    m, s = _modes(new[0])
+    assert m["A"][2] == 0

@@ -119,7 +119,9 @@ __device__ __forceinline__ int32_t fb_pos(int32_t k, int32_t G) { return G ^ (k 
 // Copies go through buffer descriptors: the tile's range of the operand in
 // scalar registers, one 32-bit lane offset per copy instruction, and the chunk
 // advance as the scalar offset (the planner keeps every tile range below
-// 2 GiB).  The descriptor's range also bounds every copy in hardware.
+// 2 GiB).  The hardware range check of a raw buffer covers the lane offset
+// only, not the scalar offset, so no copy may address a chunk past the last
+// full one: the partial last chunk goes through the masked register fill.
 constexpr int32_t BUF_DWORD3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void *base, int64_t bytes) {

@@ -265,7 +265,9 @@ __device__ __forceinline__ void mf_kloop(const MfCtx<T> &oa, const MfCtx<T> &ob,
 // chunk and lane, unconditionally: addresses of rows or columns past the tile
 // edge are clamped to a valid one and indices k >= K are masked to zero after
 // the load, and the buffer descriptor (the whole operand buffer) bounds every
-// load in hardware.  Two chunks stay in flight with exact wait counts.
+// load in hardware (the whole offset travels in the lane offset, which the
+// range check covers; a load past the end returns zeros and touches no
+// memory).  Two chunks stay in flight with exact wait counts.
 constexpr int32_t MF_BUF_DWORD3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mf_rsrc(const void *base, int64_t bytes) {
@@ -337,13 +339,15 @@ struct MfRaw {
 
 template <typename T, int MODE>
 __device__ __forceinline__ void mf_load2(const MfOp2<T, MODE> &f, int32_t k0, MfRaw &st) {
-    {
-        const int32_t soff = __builtin_amdgcn_readfirstlane(k0 / MfTraits<T>::KC * f.kstep);
+    // The chunk advance goes into the lane offset, not the scalar offset: the
+    // hardware range check of a raw buffer covers the lane offset only, and the
+    // last chunk may reach past the end of the operand buffer.
+    const uint32_t adv = static_cast<uint32_t>(k0 / MfTraits<T>::KC) * static_cast<uint32_t>(f.kstep);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            __amdgpu_buffer_rsrc_t rs = f.rs;
-            st.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, f.off[q], soff, 0);
-        }
+    for (int q = 0; q < 2; ++q) {
+        __amdgpu_buffer_rsrc_t rs = f.rs;
+        st.v[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int32_t>(static_cast<uint32_t>(f.off[q]) + adv),
+                                                        0, 0);
     }
 }
 

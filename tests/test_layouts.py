@@ -255,3 +255,23 @@ def test_chain_writer_first_outputs_are_views():
         assert m["C"][2] == 0, (i, m)
     m, s = _modes(new[0])
     assert m["A"][2] == 0
+
+
+def test_layout_empty_operand_and_no_products():
+    """An operand with no blocks gets an empty layout; with no sector products
+    the other operands are still laid out (every block in its panel, disjoint)."""
+    _lib_or_skip()
+    con = copy.deepcopy(C.tiny_u1("diag").con)
+    op = con.A
+    op.row_key, op.col_key = np.zeros(0, np.int32), np.zeros(0, np.int32)
+    op.offset, op.row_stride, op.col_stride = np.zeros(0, np.int64), np.zeros((0, 2), np.int64), np.zeros((0, 2), np.int64)
+    off, rs, cs, tot = bst.plan_layout(con, "A")
+    assert len(off) == 0 and tot == 0
+    new, (off, rs, cs, tot) = _with_layout(con, "C", align=4)
+    m, s = _modes(new)
+    assert s["triples"] == 0 and s["zero_blocks"] == con.C.nblocks
+    seen = np.zeros(tot, bool)
+    for j in range(con.C.nblocks):
+        a = _block_addresses(new, "C", j).ravel()
+        assert not seen[a].any()
+        seen[a] = True

@@ -177,3 +177,18 @@ def test_threads_share_one_cache():
     assert not errors, errors
     s = cache.stats()
     assert s["entries"] == 2 and s["hits"] + s["misses"] == 24
+
+
+def test_cache_plan_without_products():
+    """A plan with no sector products (every C block zero-filled) is cached
+    like any other."""
+    _lib_or_skip()
+    con = copy.deepcopy(C.tiny_u1("diag").con)
+    op = con.A
+    op.row_key, op.col_key = np.zeros(0, np.int32), np.zeros(0, np.int32)
+    op.offset, op.row_stride, op.col_stride = np.zeros(0, np.int64), np.zeros((0, 2), np.int64), np.zeros((0, 2), np.int64)
+    cache = bst.PlanCache(2)
+    assert not bst.Plan(con, cache=cache).cache_hit
+    p = bst.Plan(con, cache=cache)
+    assert p.cache_hit and p.stats()["zero_blocks"] == con.C.nblocks
+    _same_plan(p, bst.Plan(con))

@@ -265,3 +265,17 @@ def test_pack_workspace_in_device_bytes():
     assert forced.device_bytes() >= info["off_workspace"] + info["workspace_elems"] * esz
     assert info["workspace_elems"] * esz >= forced.stats()["pack_bytes"]
     assert forced.device_bytes() > never.device_bytes()
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/bsc.h is a C header: it compiles as pedantic C99 with no C++."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "h.c"
+    src.write_text('#include "bsc.h"\nint main(void) { bsc_options o; bsc_options_default(&o); return o.accumulate; }\n')
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        "-fsyntax-only", str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

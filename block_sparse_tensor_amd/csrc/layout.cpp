@@ -184,10 +184,10 @@ bsc_status place(const Plan &p, const bsc_operand &Xr, const bsc_index &rir, con
 
 using namespace bsc;
 
-extern "C" bsc_status bsc_plan_layout(const bsc_index *m, const bsc_index *k, const bsc_index *n, const bsc_operand *A,
-                                      const bsc_operand *B, const bsc_operand *C, bsc_dtype dtype, bsc_axis axis,
-                                      const bsc_options *opt, int32_t which, int64_t align, int64_t *offset,
-                                      int64_t *row_stride, int64_t *col_stride, int64_t *buffer_elems) {
+static bsc_status plan_layout(const bsc_index *m, const bsc_index *k, const bsc_index *n, const bsc_operand *A,
+                              const bsc_operand *B, const bsc_operand *C, bsc_dtype dtype, bsc_axis axis,
+                              const bsc_options *opt, int32_t which, int64_t align, int64_t *offset,
+                              int64_t *row_stride, int64_t *col_stride, int64_t *buffer_elems) {
     set_error("");
     if (which < 0 || which > 2 || align < 1 || !buffer_elems || !m || !k || !n || !A || !B || !C) {
         set_error("bsc_plan_layout: bad operand selector, alignment or NULL argument");
@@ -251,3 +251,16 @@ extern "C" bsc_status bsc_plan_layout(const bsc_index *m, const bsc_index *k, co
     return st;
 }
 
+
+extern "C" bsc_status bsc_plan_layout(const bsc_index *m, const bsc_index *k, const bsc_index *n, const bsc_operand *A,
+                                      const bsc_operand *B, const bsc_operand *C, bsc_dtype dtype, bsc_axis axis,
+                                      const bsc_options *opt, int32_t which, int64_t align, int64_t *offset,
+                                      int64_t *row_stride, int64_t *col_stride, int64_t *buffer_elems) {
+    try {
+        return plan_layout(m, k, n, A, B, C, dtype, axis, opt, which, align, offset, row_stride, col_stride,
+                           buffer_elems);
+    } catch (const std::bad_alloc &) {   // the provisional layout's arrays
+        set_error("bsc_plan_layout: out of host memory");
+        return BSC_ERR_UNSUPPORTED;
+    }
+}

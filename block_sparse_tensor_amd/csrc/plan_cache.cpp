@@ -121,9 +121,9 @@ bsc_status bsc_plan_cache_create(int32_t capacity, bsc_plan_cache_t *out) {
     return BSC_OK;
 }
 
-bsc_status bsc_plan_cached(bsc_plan_cache_t cache, const bsc_index *m, const bsc_index *k, const bsc_index *n,
-                           const bsc_operand *A, const bsc_operand *B, const bsc_operand *C, bsc_dtype dtype,
-                           bsc_axis axis, const bsc_options *opt, bsc_plan_t *out, int32_t *hit) {
+static bsc_status plan_cached(bsc_plan_cache_t cache, const bsc_index *m, const bsc_index *k, const bsc_index *n,
+                              const bsc_operand *A, const bsc_operand *B, const bsc_operand *C, bsc_dtype dtype,
+                              bsc_axis axis, const bsc_options *opt, bsc_plan_t *out, int32_t *hit) {
     set_error("");
     if (!cache || !out) {
         set_error("bsc_plan_cached: cache or out is NULL");
@@ -184,6 +184,18 @@ bsc_status bsc_plan_cached(bsc_plan_cache_t cache, const bsc_index *m, const bsc
     }
     *out = fresh;
     return BSC_OK;
+}
+
+bsc_status bsc_plan_cached(bsc_plan_cache_t cache, const bsc_index *m, const bsc_index *k, const bsc_index *n,
+                           const bsc_operand *A, const bsc_operand *B, const bsc_operand *C, bsc_dtype dtype,
+                           bsc_axis axis, const bsc_options *opt, bsc_plan_t *out, int32_t *hit) {
+    try {
+        return plan_cached(cache, m, k, n, A, B, C, dtype, axis, opt, out, hit);
+    } catch (const std::bad_alloc &) {   // building the key; nothing was handed out
+        if (out) *out = nullptr;
+        set_error("bsc_plan_cached: out of host memory");
+        return BSC_ERR_UNSUPPORTED;
+    }
 }
 
 bsc_status bsc_plan_cache_stats(bsc_plan_cache_t cache, int64_t *hits, int64_t *misses, int64_t *entries) {

@@ -8,7 +8,11 @@ already resident in HBM.  Useful flops = sum over sector GEMMs of 2*M*N*K (the
 work the block structure needs, not a dense equivalent).  Prints ONE JSON line.
 
 Alongside the engine (grouped launches) the same run times:
+  * the same contraction from cold caches: each one after a 512 MiB write that
+    evicts the chiplet L2s and the 256 MB Infinity Cache;
   * the uncoalesced GPU path: the same kernels, one launch per sector GEMM;
+  * (context, vendor library) a per-sector torch.mm loop over contiguous copies
+    of the sector blocks, for workloads whose keys are single legs;
   * the CPU oracle (float64 sector loop) on the host cores, on a bounded sample.
 """
 import argparse
@@ -68,6 +72,59 @@ def measured_traffic(workload, ld_align, stage):
     return None
 
 
+def vendor_per_sector(torch, plan, con, a_buf, b_buf, dtype, steps, flops):
+    """One torch.mm (hipBLASLt / rocBLAS) per sector GEMM over contiguous copies of
+    the blocks, results not written back: a vendor-library context figure for the
+    launch-per-sector approach.  Only for single-leg keys (plain 2-D blocks)."""
+    import numpy as np
+    for idx in (con.m, con.k, con.n):
+        if idx.inner is not None and np.any(idx.inner != 1):
+            return None
+
+    def blocks(op, rows, cols, buf):
+        d = {}
+        for i in range(op.nblocks):
+            r, c = int(op.row_key[i]), int(op.col_key[i])
+            v = torch.as_strided(buf, (int(rows.dim[r]), int(cols.dim[c])),
+                                 (int(op.row_stride[i, 0]), int(op.col_stride[i, 0])), int(op.offset[i]))
+            d[(r, c)] = v.contiguous()
+        return d
+
+    A = blocks(con.A, con.m, con.k, a_buf)
+    B = blocks(con.B, con.k, con.n, b_buf)
+    triples = [tuple(int(x) for x in t) for t in plan.export()[0]]
+    pairs = [(A[(m, k)], B[(k, n)]) for m, k, n in triples]
+
+    def run(**kw):
+        for a, b in pairs:
+            torch.mm(a, b, **kw)
+
+    def time_it(**kw):
+        for _ in range(2):
+            run(**kw)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run(**kw)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    vms = time_it()
+    res = {"value": round(flops / (vms * 1e-3) / 1e9, 3), "unit": "GFLOP/s", "ms_per_step": round(vms, 6),
+           "launches_per_contraction": len(pairs), "steps": steps, "kind": "vendor (torch.mm per sector)",
+           "output_dtype": "bf16" if dtype == "bf16" else dtype}
+    if dtype == "bf16":
+        # the engine's output type (fp32) through the library's out_dtype route, where torch offers it
+        try:
+            fms = time_it(out_dtype=torch.float32)
+            res["f32_output"] = {"value": round(flops / (fms * 1e-3) / 1e9, 3), "ms_per_step": round(fms, 6)}
+        except Exception as e:  # not offered by this torch build
+            res["f32_output"] = f"unavailable: {type(e).__name__}"
+    return res
+
+
 def load_workload(name, ld_align=1, relayout=False):
     from workloads import configs as C
     if name == "blockdiag_bf16":
@@ -117,6 +174,9 @@ def main():
                          "them (cross-stage layout planning)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="contractions timed one by one after a cache-evicting write (0 = skip)")
+    ap.add_argument("--no-vendor", action="store_true", help="skip the per-sector torch.mm context baseline")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this engine runs on one GPU; --gpus {args.gpus} is not supported "
@@ -249,6 +309,36 @@ def main():
         per_sector = plans_for("per_sector")
         ms_ps = timed(per_sector, args.baseline_steps, 2)
 
+    # --- cold caches: every contraction after a 512 MiB write (twice the Infinity Cache) ---
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ev = []
+        for _ in range(args.cold_steps):
+            flush.fill_(1)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            step(grouped)
+            c1.record()
+            ev.append((c0, c1))
+        torch.cuda.synchronize()
+        cms = [a.elapsed_time(b) for a, b in ev]
+        del flush
+        cmed = statistics.median(cms)
+        cold = {"ms_per_step_median": round(cmed, 6), "ms_per_step_min": round(min(cms), 6),
+                "value": round(flops / (cmed * 1e-3) / 1e9, 3), "unit": "GFLOP/s",
+                "pct_mfma_peak": round(100.0 * flops / (cmed * 1e-3) / 1e12 / peak, 3),
+                # cold ceiling: every algorithmic byte from HBM at its peak, flops at the MFMA peak
+                "hbm_ceiling_pct_mfma_peak": round(100.0 * min(1.0, HBM_PEAK * 1e9 * (flops / alg_bytes)
+                                                               / (peak * 1e12)), 2),
+                "steps": args.cold_steps, "flush_bytes": 512 << 20}
+
+    # --- context: per-sector vendor GEMMs (torch.mm) on contiguous copies of the blocks ---
+    vendor = None
+    if not args.no_vendor and len(stages) == 1:
+        vendor = vendor_per_sector(torch, grouped[0], stages[0][0], bufs[stages[0][1]], bufs[stages[0][2]],
+                                   dtype, args.baseline_steps, flops)
+
     value = flops / (ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -290,6 +380,8 @@ def main():
             "value": round(flops / (ms_ps * 1e-3) / 1e9, 3), "unit": "GFLOP/s", "ms_per_step": round(ms_ps, 6),
             "launches_per_contraction": launches_ps, "steps": args.baseline_steps,
         },
+        "cold_caches": cold,
+        "vendor_per_sector_context": vendor,
         "stage_kernel_ms": [round(x, 6) for x in stage_ms],
         "host_planning": planning,
     }

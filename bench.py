@@ -125,6 +125,30 @@ def vendor_per_sector(torch, plan, con, a_buf, b_buf, dtype, steps, flops):
     return res
 
 
+def dense_gemm_rate(torch, dtype, n=8192, reps=10):
+    """torch.mm on one n x n x n dense GEMM of the workload's input dtype: the rate
+    the vendor library reaches on this chip when nothing is block-sparse (a
+    measured counterpart of the published peak)."""
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "f64": torch.float64}[dtype]
+    n = n if dtype == "bf16" else n // 2
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(n, n, device="cuda", generator=g).to(tdt)
+    b = torch.randn(n, n, device="cuda", generator=g).to(tdt)
+    for _ in range(3):
+        torch.mm(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps
+    del a, b
+    return {"tflops": round(2.0 * n ** 3 / (t * 1e-3) / 1e12, 2), "shape": [n, n, n], "ms": round(t, 4),
+            "kind": "vendor (torch.mm, dense)"}
+
+
 def load_workload(name, ld_align=1, relayout=False):
     from workloads import configs as C
     if name == "blockdiag_bf16":
@@ -339,6 +363,11 @@ def main():
         vendor = vendor_per_sector(torch, grouped[0], stages[0][0], bufs[stages[0][1]], bufs[stages[0][2]],
                                    dtype, args.baseline_steps, flops)
 
+    # --- context: what the vendor library reaches on one large dense GEMM of the dtype ---
+    dense_ref = None
+    if not args.no_vendor:
+        dense_ref = dense_gemm_rate(torch, dtype)
+
     value = flops / (ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -382,6 +411,8 @@ def main():
         },
         "cold_caches": cold,
         "vendor_per_sector_context": vendor,
+        "vendor_dense_gemm_context": dense_ref if dense_ref is None else dict(
+            dense_ref, engine_pct_of_it=round(100.0 * value / 1e3 / dense_ref["tflops"], 3)),
         "stage_kernel_ms": [round(x, 6) for x in stage_ms],
         "host_planning": planning,
     }
@@ -392,28 +423,50 @@ def main():
     # --- CPU oracle baseline on the host cores ----------------------------------------
     if not args.no_cpu:
         import oracle
+        blas = {}
         try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            from threadpoolctl import threadpool_info, threadpool_limits
+            info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+            threads = max([i.get("num_threads", 1) for i in info] or [1])
+            if info:
+                blas = {"library": info[0].get("internal_api"), "version": info[0].get("version")}
         except Exception:
+            threadpool_limits = None
             threads = os.cpu_count() or 1
+        cpu_model = None
+        try:
+            cpu_model = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name"))
+        except Exception:
+            pass
         host = {k: np.asarray(v, np.float64) for k, v in inputs.items()}
-        times = []
-        t_start = time.perf_counter()
-        while True:
-            hb = dict(host)
-            t0 = time.perf_counter()
-            for con, a, b, c, _ in stages:
-                hb[c] = oracle.contract(con, hb[a], hb[b], np.zeros(sizes[c]), check=False)
-            times.append(time.perf_counter() - t0)
-            if time.perf_counter() - t_start >= args.cpu_seconds or len(times) >= 1000:
-                break
+
+        def oracle_times(budget_s):
+            times = []
+            t_start = time.perf_counter()
+            while True:
+                hb = dict(host)
+                t0 = time.perf_counter()
+                for con, a, b, c, _ in stages:
+                    hb[c] = oracle.contract(con, hb[a], hb[b], np.zeros(sizes[c]), check=False)
+                times.append(time.perf_counter() - t0)
+                if time.perf_counter() - t_start >= budget_s or len(times) >= 1000:
+                    return times
+
+        times = oracle_times(args.cpu_seconds)
         med = statistics.median(times)
         out["cpu_baseline"] = {
             "value": round(flops / med / 1e9, 4), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(times)} full contractions of the same workload (median {med:.4f} s), float64 numpy "
                       f"sector loop, {len(os.sched_getaffinity(0))} host cores visible",
+            "cpu_model": cpu_model, "blas": blas,
         }
+        if threadpool_limits is not None:
+            # the same oracle on one BLAS thread, over a third of the time budget
+            with threadpool_limits(limits=1, user_api="blas"):
+                t1 = oracle_times(args.cpu_seconds / 3)
+            m1 = statistics.median(t1)
+            out["cpu_baseline"]["one_thread"] = {"value": round(flops / m1 / 1e9, 4), "unit": "GFLOP/s",
+                                                 "contractions": len(t1), "median_s": round(m1, 5)}
     print(json.dumps(out), flush=True)
 
 

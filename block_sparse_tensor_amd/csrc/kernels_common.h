@@ -26,6 +26,17 @@ struct KArgs {
     int64_t a_bytes, b_bytes, w_bytes;   // sizes of A, B and the pack workspace
 };
 
+// The thread's index within the workgroup, taken through an empty asm so each
+// use is a fresh value: lane offsets derived from it are then computed inside
+// the persistent task loop, where the tile body that needs them runs, instead
+// of being hoisted in front of the loop and held live across every tile body
+// (which pushes the register allocation into scratch spills).
+__device__ __forceinline__ uint32_t tid_x() {
+    uint32_t t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 // Buffer a run's A (B) pieces address: the caller's operand or the workspace.
 template <typename T>
 __device__ __forceinline__ const T *run_a(const KArgs &ka, int32_t run_flags) {

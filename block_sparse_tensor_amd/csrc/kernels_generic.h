@@ -24,7 +24,7 @@ struct GenericSmem {
 template <typename TA, typename TC, typename ACC>
 __device__ __forceinline__ void generic_tile(const KArgs &ka, const DTask &task, GenericSmem<ACC> &sm) {
     const DGroup g = ka.groups[task.group];
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     const int32_t m0 = task.m0, n0 = task.n0;
     const int32_t mlen = min(64, g.M - m0), nlen = min(64, g.N - n0);
     const int32_t tx = tid & 15, ty = tid >> 4;

@@ -84,7 +84,7 @@ __device__ __forceinline__ uint4 u4_from(const uint16_t e[8]) {
 }
 
 __device__ __forceinline__ void mb_load(const OpCtx &o, int32_t k0, MbStage &st) {
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     if (o.mode == LD_KCONTIG) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -128,7 +128,7 @@ __device__ __forceinline__ void mb_load(const OpCtx &o, int32_t k0, MbStage &st)
 }
 
 __device__ __forceinline__ void mb_store(const OpCtx &o, const MbStage &st, uint16_t *lds, int32_t k0) {
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     if (o.mode == LD_KCONTIG) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -153,7 +153,7 @@ __device__ __forceinline__ void mb_store(const OpCtx &o, const MbStage &st, uint
 }
 
 __device__ __forceinline__ void mb_compute(const uint16_t *la, const uint16_t *lb, f32x16_t (&acc)[2][2]) {
-    const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int32_t lane = tid_x() & 63, w = tid_x() >> 6;
     const int32_t wm = w & 1, wn = w >> 1;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -198,7 +198,7 @@ template <typename TC>
 __device__ __forceinline__ void mfma_tile_bf16(const KArgs &ka, const DTask &task, MfmaSmemBf16 &sm) {
     // a dense-tile task (its direct-to-LDS body not compiled into this launch) names its group through its record
     const DGroup g = ka.groups[task.cls == T_MFMA ? task.group : ka.fast[task.group].group];
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     const int32_t m0 = task.m0, n0 = task.n0;
     const int32_t mlen = min(MB_BM, g.M - m0), nlen = min(MB_BN, g.N - n0);
 

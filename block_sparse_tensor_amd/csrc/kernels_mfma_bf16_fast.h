@@ -147,7 +147,7 @@ template <int NI>
 __device__ __forceinline__ FastOp<NI> dense_setup_kcontig(int64_t base, int64_t xs, int32_t xlen, int32_t K,
                                                           const uint16_t *P, int32_t w) {
     FastOp<NI> f;
-    const int32_t lane = threadIdx.x & 63;
+    const int32_t lane = tid_x() & 63;
     f.rs = wave_rsrc(P + base, 2 * (static_cast<int64_t>(xlen - 1) * xs + K) + 16);
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
@@ -166,7 +166,7 @@ template <int NI>
 __device__ __forceinline__ FastOp<NI> dense_setup_ncontig(int64_t base, int64_t ks, int32_t nlen, int32_t K,
                                                           const uint16_t *P, int32_t w) {
     FastOp<NI> f;
-    const int32_t lane = threadIdx.x & 63;
+    const int32_t lane = tid_x() & 63;
     const int32_t s = lane & 15;
     f.rs = wave_rsrc(P + base, 2 * (static_cast<int64_t>(K - 1) * ks + FB_BN) + 16);
 #pragma unroll
@@ -207,7 +207,7 @@ __device__ __forceinline__ void fast_issue(const FastOp<NI> &f, int32_t c, uint1
 template <int ROWS>
 __device__ __forceinline__ void dense_fill_kcontig(int64_t base, int64_t xs, int32_t xlen, int32_t k0, int32_t K,
                                                    const uint16_t *P, uint16_t *lds) {
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
 #pragma unroll 1
     for (int q = 0; q < ROWS * 4 / 256; ++q) {
         const int32_t u = tid + 256 * q;         // row u / 4, k-granule u % 4
@@ -223,7 +223,7 @@ __device__ __forceinline__ void dense_fill_kcontig(int64_t base, int64_t xs, int
 
 __device__ __forceinline__ void dense_fill_ncontig(int64_t base, int64_t ks, int32_t nlen, int32_t k0, int32_t K,
                                                    const uint16_t *P, uint16_t *lds) {
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
 #pragma unroll 1
     for (int q = 0; q < FB_BK * 16 / 256; ++q) {
         const int32_t u = tid + 256 * q;         // k row u / 16, 8-column piece u % 16
@@ -275,7 +275,7 @@ struct FragOff {
 
 template <bool BN>
 __device__ __forceinline__ FragOff frag_offsets() {
-    const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int32_t lane = tid_x() & 63, w = tid_x() >> 6;
     const int32_t wm = w & 1, wn = w >> 1;
     FragOff o;
     const int32_t ra = wm * (FB_BM / 2) + (lane & 31);
@@ -496,7 +496,7 @@ __device__ __forceinline__ bool split_arrive(const KArgs &ka, const DFast &fd, f
     }
     wait_vm<0>();   // this wave's partial stores are complete
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (tid_x() == 0) {
         const int32_t before = __hip_atomic_fetch_add(ka.cnt + fd.counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = before == fd.nsplit - 1;
         if (last) __hip_atomic_store(ka.cnt + fd.counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -547,7 +547,7 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
     const uint16_t *B = static_cast<const uint16_t *>((fd.flags & F_B_WS) ? ka.W : ka.B);
     const int32_t mlen = fd.mlen, nlen = fd.nlen, K = fd.K;
     // the wave index through a scalar register, so tests on it are scalar branches
-    const int32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t w = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
 
     f32x16_t acc[FB_FM][2];
 #pragma unroll
@@ -702,7 +702,7 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
     if (mlen <= FB_BM / 2) roles(T());
     else roles(F());
 
-    const int32_t lane = threadIdx.x & 63;
+    const int32_t lane = tid_x() & 63;
     // (the ring is idle from here on: the K-split flag may alias its first word)
     if (fd.nsplit > 1 && !split_arrive(ka, fd, acc, w, lane, *reinterpret_cast<int32_t *>(sm.op))) return;
 

@@ -105,7 +105,7 @@ __device__ __forceinline__ MfCtx<T> mf_ctx(const DView *pieces, int32_t np, int3
 template <typename T>
 __device__ __forceinline__ void mf_load(const MfCtx<T> &o, int32_t k0, MfStage<T> &st) {
     constexpr int V = 16 / sizeof(T);
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     if (o.mode == MF_KCONTIG) {
         // 8 lanes cover one row's KC values; 32 rows per pass, two passes
         const int32_t kx = tid & 7, xr = tid >> 3;
@@ -156,7 +156,7 @@ template <typename T>
 __device__ __forceinline__ void mf_store(const MfCtx<T> &o, const MfStage<T> &st, T *lds, int32_t k0) {
     constexpr int V = 16 / sizeof(T);
     constexpr int KC = MfTraits<T>::KC;
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     if (o.mode == MF_KCONTIG) {
         const int32_t kx = tid & 7, xr = tid >> 3;
 #pragma unroll
@@ -196,7 +196,7 @@ __device__ __forceinline__ f64x4_t mf_mma(double a, double b, f64x4_t c) {
 template <typename T>
 __device__ __forceinline__ void mf_compute(const T *la, const T *lb, typename MfTraits<T>::acc_t (&acc)[2][2]) {
     constexpr int KC = MfTraits<T>::KC;
-    const int32_t lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int32_t lane = tid_x() & 63, w = tid_x() >> 6;
     const int32_t wm = w & 1, wn = w >> 1;
     const int32_t j = lane >> 4, xi = lane & 15;
 #pragma unroll
@@ -295,7 +295,7 @@ __device__ __forceinline__ MfOp2<T, MODE> mf_setup2(const MfCtx<T> &o, int64_t b
     constexpr int KC = MfTraits<T>::KC;
     MfOp2<T, MODE> f;
     f.rs = mf_rsrc(o.P, bytes);
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     static_assert(MODE == MF_KCONTIG || MODE == MF_FCONTIG, "contiguous modes only");
     if constexpr (MODE == MF_KCONTIG) {
         const int32_t kx = tid & 7, xr = tid >> 3;
@@ -356,7 +356,7 @@ __device__ __forceinline__ void mf_load2(const MfOp2<T, MODE> &f, int32_t k0, Mf
 template <typename T, int MODE>
 __device__ __forceinline__ void mf_store2(const MfOp2<T, MODE> &f, const MfRaw &raw, T *lds, int32_t k0, int32_t K) {
     constexpr int V = 16 / sizeof(T);
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     T e[2][V];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -452,7 +452,7 @@ __device__ __forceinline__ void mf_kloop_any(const MfCtx<T> &oa, const MfCtx<T> 
 template <typename T>
 __device__ __forceinline__ void mfma_tile_f(const KArgs &ka, const DTask &task, const DFast &fd_ref, MfmaSmemF<T> &sm) {
     typedef typename MfTraits<T>::acc_t acc_t;
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     const bool dense = task.cls == T_MFMA_DENSE;
     // dense tiles carry their own record: no group, run or piece lookups
     DGroup g;

@@ -79,7 +79,7 @@ constexpr int skinny_acc_budget() { return 32; }
 template <typename TA, typename TC, typename ACC, bool LONG_M, int YB>
 __device__ __forceinline__ void skinny_impl(const KArgs &ka, const DTask &task, const DGroup &g, SkinnySmem<ACC> &sm) {
     constexpr int R = skinny_acc_budget<ACC>() / YB;
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     const int32_t x0 = LONG_M ? task.m0 : task.n0;
     const int32_t X = LONG_M ? g.M : g.N;
     const int32_t Y = LONG_M ? g.N : g.M;
@@ -185,7 +185,7 @@ __device__ __forceinline__ void skinny_impl(const KArgs &ka, const DTask &task, 
 template <typename TA, typename TC, typename ACC, bool LONG_M, int YB>
 __device__ __forceinline__ void skinny_dense_impl(const KArgs &ka, const DFast &fd, SkinnySmem<ACC> &sm) {
     constexpr int R = skinny_acc_budget<ACC>() / YB;
-    const int32_t tid = threadIdx.x;
+    const int32_t tid = tid_x();
     const int32_t xlen = LONG_M ? fd.mlen : fd.nlen;
     const int32_t Y = LONG_M ? fd.nlen : fd.mlen;
     const TA *A = static_cast<const TA *>((fd.flags & F_A_WS) ? ka.W : ka.A);

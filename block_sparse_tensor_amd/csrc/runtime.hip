@@ -123,6 +123,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void g
     grouped_body<TA, TC, ACC, FEAT>(ka);
 }
 
+// fp32 launches: the fp32 tile bodies fit in 128 VGPRs and their LDS allows
+// four workgroups per CU, so they are compiled for four waves per SIMD (more
+// tiles in flight to hide the per-tile chain of dependent loads).
+template <typename TA, typename TC, typename ACC, int32_t FEAT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void grouped_contract_narrow(KArgs ka) {
+    grouped_body<TA, TC, ACC, FEAT>(ka);
+}
+
 using KernelFn = void (*)(KArgs);
 
 struct KernelRef {
@@ -135,6 +143,7 @@ template <typename TA, typename TC, typename ACC, int32_t FEAT>
 static KernelRef kernel_ref() {
     KernelFn fn;
     if constexpr (one_per_cu<TA, ACC, FEAT>()) fn = grouped_contract_wide<TA, TC, ACC, FEAT>;
+    else if constexpr (std::is_same<TA, float>::value) fn = grouped_contract_narrow<TA, TC, ACC, FEAT>;
     else fn = grouped_contract<TA, TC, ACC, FEAT>;
     const size_t lds = sizeof(TileSmem<TA, ACC, FEAT>);
     static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),

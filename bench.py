@@ -149,6 +149,34 @@ def dense_gemm_rate(torch, dtype, n=8192, reps=10):
             "kind": "vendor (torch.mm, dense)"}
 
 
+TOL = {"f64": 1e-12, "f32": 1e-5, "bf16": 2e-2}
+
+
+def parity_vs_oracle(stages, bufs, ref, dtype):
+    """Relative Frobenius error, over the union of each stage's C blocks, of the
+    engine's buffers against the oracle's (float64), worst stage reported."""
+    import numpy as np
+    from workloads.layout import view_addresses
+    worst = 0.0
+    for con, _, _, c, _ in stages:
+        parts = []
+        for i in range(con.C.nblocks):
+            r, cc = int(con.C.row_key[i]), int(con.C.col_key[i])
+            ri = 1 if con.m.inner is None else int(con.m.inner[r])
+            ci = 1 if con.n.inner is None else int(con.n.inner[cc])
+            parts.append(view_addresses(con.C.offset[i], con.C.row_stride[i], con.C.col_stride[i],
+                                        int(con.m.dim[r]), int(con.n.dim[cc]), ri, ci).ravel())
+        if not parts:
+            continue
+        addr = np.concatenate(parts)
+        got = bufs[c].cpu().numpy().astype(np.float64)[addr]
+        want = np.asarray(ref[c], np.float64)[addr]
+        nr = np.linalg.norm(want)
+        err = float(np.linalg.norm(got - want) / nr) if nr > 0 else (0.0 if not np.any(got) else float("inf"))
+        worst = max(worst, err)
+    return {"rel_frobenius": worst, "tol": TOL[dtype], "pass": bool(worst <= TOL[dtype])}
+
+
 def load_workload(name, ld_align=1, relayout=False):
     from workloads import configs as C
     if name == "blockdiag_bf16":
@@ -450,9 +478,9 @@ def main():
                     hb[c] = oracle.contract(con, hb[a], hb[b], np.zeros(sizes[c]), check=False)
                 times.append(time.perf_counter() - t0)
                 if time.perf_counter() - t_start >= budget_s or len(times) >= 1000:
-                    return times
+                    return times, hb
 
-        times = oracle_times(args.cpu_seconds)
+        times, hb = oracle_times(args.cpu_seconds)
         med = statistics.median(times)
         out["cpu_baseline"] = {
             "value": round(flops / med / 1e9, 4), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
@@ -460,10 +488,13 @@ def main():
                       f"sector loop, {len(os.sched_getaffinity(0))} host cores visible",
             "cpu_model": cpu_model, "blas": blas,
         }
+        # parity of the timed run: every stage's C views on the GPU (after the
+        # last contraction) against the oracle's result for the same inputs
+        out["cpu_baseline"]["parity"] = parity_vs_oracle(stages, bufs, hb, dtype)
         if threadpool_limits is not None:
             # the same oracle on one BLAS thread, over a third of the time budget
             with threadpool_limits(limits=1, user_api="blas"):
-                t1 = oracle_times(args.cpu_seconds / 3)
+                t1, _ = oracle_times(args.cpu_seconds / 3)
             m1 = statistics.median(t1)
             out["cpu_baseline"]["one_thread"] = {"value": round(flops / m1 / 1e9, 4), "unit": "GFLOP/s",
                                                  "contractions": len(t1), "median_s": round(m1, 5)}

@@ -172,10 +172,12 @@ static KernelRef pick_bf16(int32_t feat, bool vec) {
     }
 }
 
-// Grid of a launch: one workgroup per task up to a persistent cap; the cap is
-// a multiple of BSC_XCDS so task t keeps running on XCD t % BSC_XCDS.
+// Grid of a launch: one workgroup per task up to a persistent cap of 16 per CU
+// (four to eight times what is resident at once, so a workgroup that finishes
+// is replaced by a fresh one more often than it loops to its next task); the
+// cap is a multiple of BSC_XCDS so task t keeps running on XCD t % BSC_XCDS.
 static int32_t grid_for(const Plan &p, int32_t ntasks) {
-    int32_t cap = p.opt.grid_limit > 0 ? p.opt.grid_limit : std::max(1, p.cu_count) * 8;
+    int32_t cap = p.opt.grid_limit > 0 ? p.opt.grid_limit : std::max(1, p.cu_count) * 16;
     if (cap >= BSC_XCDS) cap -= cap % BSC_XCDS;
     return std::max(1, std::min(ntasks, cap));
 }

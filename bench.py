@@ -296,27 +296,33 @@ def main():
     # --- engine: timed region ----------------------------------------------------------
     # K steps between two events on torch's current stream (the stream the engine
     # launches on).  A one-launch step needs nothing more: the average launch
-    # duration is the region over K.  A step of several launches also records an
-    # event after every launch, so each stage's launches are timed on their own.
+    # duration is the region over K.  For a step of several launches a second
+    # pass of K steps records an event after every launch, so each stage's
+    # launches are timed on their own (kept out of the first pass, whose step
+    # time they would lengthen).
     for _ in range(args.warmup):
         step(grouped)
     torch.cuda.synchronize()
     multi = len(stages) > 1
-    marks = []
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        for p, (_, a, b, c, _) in zip(grouped, stages):
-            p.contract(bufs[a], bufs[b], bufs[c])
-            if multi:
-                ev = torch.cuda.Event(enable_timing=True)
-                ev.record()
-                marks.append(ev)
+        step(grouped)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     if multi:
-        bounds = [e0] + marks
+        marks = []
+        m0 = torch.cuda.Event(enable_timing=True)
+        m0.record()
+        for _ in range(args.steps):
+            for p, (_, a, b, c, _) in zip(grouped, stages):
+                p.contract(bufs[a], bufs[b], bufs[c])
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record()
+                marks.append(ev)
+        torch.cuda.synchronize()
+        bounds = [m0] + marks
         stage_ms = [statistics.fmean(bounds[j].elapsed_time(bounds[j + 1])
                                      for j in range(i, len(marks), len(stages))) for i in range(len(stages))]
     else:

@@ -331,7 +331,12 @@ def main():
     dom_flops = st[dom]["useful_flops"]
     dom_bytes = st[dom]["alg_bytes"]
     achieved_tflops = dom_flops / (stage_ms[dom] * 1e-3) / 1e12
+    achieved_gbps = dom_bytes / (stage_ms[dom] * 1e-3) / 1e9
     peak = MFMA_PEAK[dtype]
+    # a stage whose algorithmic bytes, streamed at the HBM peak, could feed less
+    # than a tenth of the MFMA peak is bandwidth-bound (the W stage of the chains,
+    # 0.4 flop/B); the others are rated against the matrix cores
+    hbm_bound = dom_flops < 0.1 * peak * 1e12 * dom_bytes / (HBM_PEAK * 1e9)
     traffic = measured_traffic(args.workload, args.ld_align, dom)
 
     # --- the same stages captured once into a HIP graph, one graph launch per step ----
@@ -426,12 +431,12 @@ def main():
         "launches_per_sector_baseline": launches_ps,
         "launch_reduction": round(launches_ps / max(1, launches), 2),
         "roofline": {
-            "bound": "mfma",
+            "bound": "hbm" if hbm_bound else "mfma",
             "kernel": "grouped_contract",
-            "achieved": round(achieved_tflops, 4),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved_tflops / peak, 5),
+            "achieved": round(achieved_gbps if hbm_bound else achieved_tflops, 4),
+            "peak": HBM_PEAK if hbm_bound else peak,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": round(achieved_gbps / HBM_PEAK if hbm_bound else achieved_tflops / peak, 5),
             "traffic": traffic,
             "kernel_ms": round(stage_ms[dom], 6),
             "flops_per_launch": dom_flops,

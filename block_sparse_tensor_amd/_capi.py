@@ -6,7 +6,10 @@ import os
 from ctypes import POINTER, c_char_p, c_double, c_int32, c_int64, c_size_t, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbsc.so")
+# BSC_LIBRARY may name another build of the same interface (the host-only
+# planner library of a sanitizer run, whose device entry points return
+# BSC_ERR_UNSUPPORTED); by default the in-tree HIP library is loaded.
+LIB_PATH = os.environ.get("BSC_LIBRARY") or os.path.join(_HERE, "libbsc.so")
 
 STATUS = {
     0: "BSC_OK", -1: "BSC_ERR_ARG", -2: "BSC_ERR_CHARGE", -3: "BSC_ERR_SHAPE", -4: "BSC_ERR_BOUNDS",

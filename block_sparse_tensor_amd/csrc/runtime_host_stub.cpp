@@ -1,16 +1,34 @@
 // Device entry points for the host-only planner library used in sanitizer runs
-// on machines without a GPU.  They fail loudly; the shipped library links
-// runtime.hip instead.
+// on machines without a GPU.  They apply the same argument checks as the HIP
+// runtime (so those host paths run under the sanitizers too) and then fail
+// loudly with BSC_ERR_UNSUPPORTED; the shipped library links runtime.hip instead.
 #include "bsc_internal.h"
 
 using namespace bsc;
 
-extern "C" bsc_status bsc_plan_bind(bsc_plan_t, void *, size_t, void *) {
+extern "C" bsc_status bsc_plan_bind(bsc_plan_t plan, void *dev, size_t bytes, void *) {
+    set_error("");
+    if (!plan || !dev) {
+        set_error("bsc_plan_bind: NULL argument");
+        return BSC_ERR_ARG;
+    }
+    if (bytes < reinterpret_cast<Plan *>(plan)->dev_bytes) {
+        set_error("bsc_plan_bind: device region smaller than bsc_plan_device_bytes");
+        return BSC_ERR_DEVICE_BYTES;
+    }
     set_error("bsc_plan_bind: host-only planner build has no device runtime");
     return BSC_ERR_UNSUPPORTED;
 }
 
-extern "C" bsc_status bsc_contract(bsc_plan_t, const void *, const void *, void *, void *) {
+extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *, const void *, void *, void *) {
+    if (!plan) {
+        set_error("bsc_contract: NULL plan");
+        return BSC_ERR_ARG;
+    }
+    if (!reinterpret_cast<Plan *>(plan)->dev) {
+        set_error("bsc_contract: plan is not bound to a device region");
+        return BSC_ERR_NOT_BOUND;
+    }
     set_error("bsc_contract: host-only planner build has no device runtime");
     return BSC_ERR_UNSUPPORTED;
 }

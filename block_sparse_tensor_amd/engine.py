@@ -154,6 +154,7 @@ class Plan:
         self._h = h
         self.a_elems, self.b_elems, self.c_elems = int(con.A.buffer_elems), int(con.B.buffer_elems), int(con.C.buffer_elems)
         self._dev = None
+        self._captured = 0   # live Chains whose graph holds this plan's device region
 
     # -- host-side queries -------------------------------------------------------
     def device_bytes(self) -> int:
@@ -196,7 +197,12 @@ class Plan:
 
     # -- device ------------------------------------------------------------------
     def bind(self, device=None, stream=None):
-        """Allocate the plan's device region (torch memory) and upload the work list."""
+        """Allocate the plan's device region (torch memory) and upload the work list.
+
+        Refused while a live Chain has captured this plan: its graph holds the
+        current device region (work list, counters, workspace)."""
+        if self._captured:
+            raise BscError(-1, "plan is captured by a live Chain; rebinding would free the region its graph uses")
         torch = _torch()
         nbytes = self.device_bytes()
         dev = torch.empty(nbytes + 256, dtype=torch.uint8, device=device or "cuda")
@@ -215,20 +221,27 @@ class Plan:
         if not t.is_contiguous() or t.numel() < need:
             raise ValueError(f"{name} must be contiguous with at least {need} elements")
 
+    def _operand_dtypes(self):
+        """Accepted torch dtypes of (A and B, C)."""
+        torch = _torch()
+        if self.dtype == "f64":
+            return (torch.float64,), (torch.float64,)
+        if self.dtype == "f32":
+            return (torch.float32,), (torch.float32,)
+        return (torch.bfloat16, torch.int16, torch.uint16), (torch.float32,)
+
+    def check_operands(self, A, B, C):
+        """Device, dtype, contiguity and size of A, B, C (raises on a mismatch)."""
+        ab, cd = self._operand_dtypes()
+        self._check_tensor(A, "A", self.a_elems, ab)
+        self._check_tensor(B, "B", self.b_elems, ab)
+        self._check_tensor(C, "C", self.c_elems, cd)
+
     def contract(self, A, B, C, stream=None):
         """Enqueue C (+)= A B on `stream` (default: torch's current stream)."""
         if self._dev is None:
             raise BscError(-8, "plan is not bound (call bind())")
-        torch = _torch()
-        if self.dtype == "f64":
-            ab, cd = (torch.float64,), (torch.float64,)
-        elif self.dtype == "f32":
-            ab, cd = (torch.float32,), (torch.float32,)
-        else:
-            ab, cd = (torch.bfloat16, torch.int16, torch.uint16), (torch.float32,)
-        self._check_tensor(A, "A", self.a_elems, ab)
-        self._check_tensor(B, "B", self.b_elems, ab)
-        self._check_tensor(C, "C", self.c_elems, cd)
+        self.check_operands(A, B, C)
         _check(_capi.lib().bsc_contract(self._h, c_void_p(A.data_ptr()), c_void_p(B.data_ptr()),
                                         c_void_p(C.data_ptr()), _stream_handle(stream)))
         return C
@@ -246,16 +259,22 @@ class Plan:
 class Chain:
     """A fixed sequence of contractions [(plan, A, B, C), ...] captured once
     into a HIP graph and replayed with one launch (bsc_chain_*).  The plans
-    must be bound; the chain keeps references to the plans and the tensors,
-    whose addresses the graph holds."""
+    must be bound and every tensor must pass the checks Plan.contract applies
+    (device, dtype, contiguity, size), since the graph replays the addresses
+    without looking again.  The chain keeps references to the plans, their
+    device regions and the tensors, whose addresses the graph holds, and a
+    captured plan refuses bind() until the chain is released."""
 
     def __init__(self, steps):
+        self._h = None
+        self._plans = []
         steps = list(steps)
         if not steps:
             raise BscError(-1, "empty chain")
         for p, A, B, C in steps:
             if p._dev is None:
                 raise BscError(-8, "plan is not bound (call bind())")
+            p.check_operands(A, B, C)
         n = len(steps)
         arr = lambda xs: (c_void_p * n)(*xs)
         plans = arr([p._h.value for p, _, _, _ in steps])
@@ -265,20 +284,35 @@ class Chain:
         h = c_void_p()
         _check(_capi.lib().bsc_chain_create(plans, a, b, c, n, byref(h)))
         self._h = h
-        self._keep = steps   # plans and tensors must outlive the graph
+        # plans, their device regions and the tensors must outlive the graph
+        self._keep = [(p, p._dev, A, B, C) for p, A, B, C in steps]
+        self._plans = [p for p, _, _, _ in steps]
+        for p in self._plans:
+            p._captured += 1
 
     def launch(self, stream=None):
         """Enqueue one replay on `stream` (default: torch's current stream)."""
+        if self._h is None:
+            raise BscError(-1, "chain was released")
         _check(_capi.lib().bsc_chain_launch(self._h, _stream_handle(stream)))
 
-    def __del__(self):
+    def release(self):
+        """Destroy the graph; the plans may be rebound afterwards.  The caller
+        must have synchronised any replay still in flight."""
         h = getattr(self, "_h", None)
         if h is not None and h.value:
             try:
                 _capi.lib().bsc_chain_destroy(h)
             except Exception:
                 pass
-            self._h = None
+        self._h = None
+        for p in getattr(self, "_plans", []):
+            p._captured -= 1
+        self._plans = []
+        self._keep = []
+
+    def __del__(self):
+        self.release()
 
 
 class PlanCache:

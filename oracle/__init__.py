@@ -21,6 +21,6 @@ hole-free, canonical order).  Operand-mode choice, tile classes and work order
 affect only speed: parity unpinned, covered by coalesced == uncoalesced.
 """
 from .contract import (  # noqa: F401
-    OracleError, block, check_structure, contract, densify, dense_contract, groups,
+    OracleError, block, check_structure, contract, densify, groups,
     useful_flops, algorithmic_bytes, triples, run_chain,
 )

@@ -203,10 +203,6 @@ def densify(op, buf, ridx, cidx) -> np.ndarray:
     return out
 
 
-def dense_contract(con, a, b) -> np.ndarray:
-    """Dense product of the materialised operands (sum dims x sum dims)."""
-    return densify(con.A, a, con.m, con.k) @ densify(con.B, b, con.k, con.n)
-
 
 # --------------------------------------------------------------------------
 # grouping re-derivation (single-axis coalescing rules)

@@ -9,7 +9,7 @@ import pytest
 import oracle
 from workloads import configs as C
 
-from gpuhelp import c_addresses, have_gpu, rel_frobenius, to_dev, torch
+from gpuhelp import c_addresses, check_float, have_gpu, rel_frobenius, to_dev, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -42,8 +42,8 @@ def test_chain_replays_match_eager(layout):
         p.contract(eager[st.a_buf], eager[st.b_buf], eager[st.c_buf])
     t.cuda.synchronize()
     for st in ch.stages:
-        addr, _ = c_addresses(st.con)
-        assert rel_frobenius(eager[st.c_buf].cpu().numpy(), ref[st.c_buf], addr) <= 1e-12
+        check_float(st.con, eager[st.c_buf].cpu().numpy(), ref[st.c_buf], ref[st.a_buf], ref[st.b_buf], 1e-12,
+                    label=st.label)
     g = _chain_buffers(ch)
     chain = bst.Chain([(p, g[st.a_buf], g[st.b_buf], g[st.c_buf]) for p, st in zip(plans, ch.stages)])
     for r in range(3):
@@ -110,3 +110,30 @@ def test_chain_errors():
     assert e.value.status == -8
     with pytest.raises(bst.BscError):
         bst.Chain([])
+
+
+def test_chain_checks_tensors_and_guards_rebind():
+    """A chain rejects operand tensors that contract() would reject (the graph
+    would replay their addresses unchecked), and a captured plan refuses to be
+    rebound until the chain is released."""
+    t = torch()
+    ch = C.small_chain(seed=3, layout="natural")
+    st = ch.stages[0]
+    p = bst.Plan(st.con).bind()
+    g = _chain_buffers(ch)
+    small = t.zeros(max(1, p.c_elems // 2), dtype=g[st.c_buf].dtype, device="cuda")
+    with pytest.raises(ValueError):
+        bst.Chain([(p, g[st.a_buf], g[st.b_buf], small)])
+    with pytest.raises(TypeError):
+        bst.Chain([(p, g[st.a_buf].float(), g[st.b_buf], g[st.c_buf])])
+    assert p._captured == 0
+    chain = bst.Chain([(p, g[st.a_buf], g[st.b_buf], g[st.c_buf])])
+    with pytest.raises(bst.BscError):
+        p.bind()
+    print("[chain] replay before release", flush=True)
+    chain.launch()
+    t.cuda.synchronize()
+    chain.release()
+    p.bind()                                      # allowed again
+    p.contract(g[st.a_buf], g[st.b_buf], g[st.c_buf])
+    t.cuda.synchronize()

@@ -9,7 +9,7 @@ import pytest
 import oracle
 from workloads import configs as C
 
-from gpuhelp import TOL, c_addresses, canary, check_canary, have_gpu, rel_frobenius, run_engine, to_dev, torch
+from gpuhelp import TOL, c_addresses, canary, check_canary, check_float, have_gpu, run_engine, to_dev, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +38,7 @@ def test_force_pack_random(dtype, axis, seed):
     s = plan.stats()
     assert s["mode_count"]["A"]["segments"] == 0 and s["mode_count"]["B"]["segments"] == 0
     ref = oracle.contract(prob.con, prob.a, prob.b, np.full(prob.con.C.buffer_elems, np.nan))
-    assert rel_frobenius(got, ref, addr) <= TOL[dtype]
+    check_float(prob.con, got, ref, prob.a, prob.b, TOL[dtype], label=prob.name)
 
 
 @pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
@@ -70,8 +70,8 @@ def test_pack_natural_chain(layout):
         plan.contract(bufs[st.a_buf], bufs[st.b_buf], bufs[st.c_buf])
     t.cuda.synchronize()
     for st in ch.stages:
-        addr, _ = c_addresses(st.con)
-        assert rel_frobenius(bufs[st.c_buf].cpu().numpy(), ref[st.c_buf], addr) <= 1e-12
+        check_float(st.con, bufs[st.c_buf].cpu().numpy(), ref[st.c_buf], ref[st.a_buf], ref[st.b_buf], 1e-12,
+                    label=st.label)
 
 
 @pytest.mark.parametrize("layout", ["force_pack", "auto"])
@@ -93,8 +93,8 @@ def test_pack_rabc_u1u1_full_size(layout):
     t.cuda.synchronize()
     assert packed > 0
     for st in ch.stages:
-        addr, _ = c_addresses(st.con)
-        assert rel_frobenius(bufs[st.c_buf].cpu().numpy(), ref[st.c_buf], addr) <= 1e-5, st.label
+        check_float(st.con, bufs[st.c_buf].cpu().numpy(), ref[st.c_buf], ref[st.a_buf], ref[st.b_buf], 1e-5,
+                    label=st.label)
 
 
 def test_pack_repeat_and_accumulate():
@@ -108,7 +108,7 @@ def test_pack_repeat_and_accumulate():
     ref = np.asarray(c0, np.float64)
     for _ in range(3):
         ref = oracle.contract(con, prob.a, prob.b, ref, accumulate=True)
-    assert rel_frobenius(got, ref, addr) <= 1e-12
+    check_float(con, got, ref, prob.a, prob.b, 1e-12, label="repeat+accumulate")
 
 
 def test_unaligned_operand_base_bf16():
@@ -130,4 +130,4 @@ def test_unaligned_operand_base_bf16():
     got = Cd.cpu().numpy()
     ref = oracle.contract(con, prob.a, prob.b, np.zeros(con.C.buffer_elems), check=False)
     check_canary(got, mask)
-    assert rel_frobenius(got, ref, addr) <= 2e-2
+    check_float(con, got, ref, prob.a, prob.b, 2e-2, label="unaligned")

@@ -1,14 +1,17 @@
 """GPU parity: the HIP engine (through the C-ABI) against the CPU oracle on the
-same seeded inputs.  Tolerances (relative Frobenius over all C blocks):
-1e-12 fp64, 1e-5 fp32, 2e-2 bf16 inputs with fp32 accumulation; integer-valued
-inputs make every summation order exact, so those compare bit-for-bit."""
+same seeded inputs.  Tolerances: 1e-12 fp64, 1e-5 fp32, 2e-2 bf16 inputs with
+fp32 accumulation, applied to the relative Frobenius error over all C blocks
+and to every C block on its own (gpuhelp); integer-valued inputs make every
+summation order exact, so those compare bit-for-bit, at full size too.  Every
+case asserts that it contracts something."""
 import numpy as np
 import pytest
 
 import oracle
 from workloads import configs as C
 
-from gpuhelp import TOL, canary, check_canary, c_addresses, have_gpu, rel_frobenius, run_engine, to_dev, torch
+from gpuhelp import (TOL, block_addresses, canary, check_blocks, check_canary, c_addresses, have_gpu,
+                     int_chain_bound, rel_frobenius, run_engine, to_dev, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -20,10 +23,13 @@ else:  # collected on CPU but never run there
 AXES = ["auto", "free_m", "free_n", "contract"]
 
 
-def _parity(prob, axis="auto", launch_mode="grouped", layout="auto", tol=None, exact=False, accumulate=False):
+def _parity(prob, axis="auto", launch_mode="grouped", layout="auto", tol=None, exact=False, accumulate=False,
+            min_triples=1, **plan_kw):
     con = prob.con
-    plan = bst.Plan(con, axis=axis, launch_mode=launch_mode, layout=layout, accumulate=accumulate).bind()
-    print(f"[parity] {prob.name} dtype={con.dtype} axis={axis} mode={launch_mode} layout={layout}", flush=True)
+    plan = bst.Plan(con, axis=axis, launch_mode=launch_mode, layout=layout, accumulate=accumulate, **plan_kw).bind()
+    print(f"[parity] {prob.name} dtype={con.dtype} axis={axis} mode={launch_mode} layout={layout} {plan_kw}",
+          flush=True)
+    assert plan.stats()["triples"] >= min_triples, "the case must contract something"
     addr, mask = c_addresses(con)
     if accumulate:
         rng = np.random.default_rng(1)
@@ -36,8 +42,10 @@ def _parity(prob, axis="auto", launch_mode="grouped", layout="auto", tol=None, e
     if exact:
         assert np.array_equal(got[addr], ref[addr].astype(got.dtype)), "integer-valued parity must be bit-exact"
     else:
+        t = tol or TOL[con.dtype]
         err = rel_frobenius(got, ref, addr)
-        assert err <= (tol or TOL[con.dtype]), err
+        assert err <= t, err
+        check_blocks(con, got, ref, prob.a, prob.b, t, c0=c0, accumulate=accumulate, label=prob.name)
     return plan, got
 
 
@@ -64,23 +72,33 @@ def test_ragged_batch_per_sector():
     assert plan.stats()["launches_per_contract"] == 4000
 
 
-@pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
-@pytest.mark.parametrize("seed", range(4))
-def test_integer_values_bit_exact(dtype, seed):
-    prob = C.random_problem(3000 + seed, nq=1 + seed % 2, nkeys=(6, 5, 6), maxdim=40, qrange=1, dtype=dtype,
-                            flux=[(0, 0), (1, -1)][seed % 2], int_values=True, density=0.8)
-    for axis in AXES:
-        _parity(prob, axis=axis, exact=True)
-    _parity(prob, launch_mode="per_sector", exact=True)
+# (seed, charge components): seeds chosen so every case has at least 8 sector GEMMs
+INT_CASES = [(3000, 1), (3073, 2), (3002, 1), (3709, 2)]
 
 
 @pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
-@pytest.mark.parametrize("seed", range(6))
-def test_random_strided(dtype, seed):
-    prob = C.random_problem(4000 + seed, nq=1 + seed % 2, nkeys=(7, 6, 7), maxdim=24, qrange=1, dtype=dtype,
-                            flux=[(0, 0), (1, -1), (1, 0)][seed % 3], density=0.8)
+@pytest.mark.parametrize("case", INT_CASES, ids=lambda c: f"s{c[0]}-q{c[1]}")
+def test_integer_values_bit_exact(dtype, case):
+    seed, nq = case
+    prob = C.random_problem(seed, nq=nq, nkeys=(6, 5, 6), maxdim=40, qrange=1, dtype=dtype,
+                            flux=[(0, 0), (1, -1)][nq - 1], int_values=True, density=0.8)
     for axis in AXES:
-        _parity(prob, axis=axis)
+        _parity(prob, axis=axis, exact=True, min_triples=8)
+    _parity(prob, launch_mode="per_sector", exact=True, min_triples=8)
+
+
+# seeds chosen so every case has at least 6 sector GEMMs; case i has 1 + i % 2
+# charge components and flux pair i % 3
+STRIDED_SEEDS = [4000, 4049, 4008, 4003, 4004, 4029]
+
+
+@pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
+@pytest.mark.parametrize("case", range(len(STRIDED_SEEDS)))
+def test_random_strided(dtype, case):
+    prob = C.random_problem(STRIDED_SEEDS[case], nq=1 + case % 2, nkeys=(7, 6, 7), maxdim=24, qrange=1, dtype=dtype,
+                            flux=[(0, 0), (1, -1), (1, 0)][case % 3], density=0.8)
+    for axis in AXES:
+        _parity(prob, axis=axis, min_triples=6)
 
 
 @pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
@@ -105,16 +123,38 @@ def test_blockdiag_bf16_full_size_aligned():
     assert s["items_by_class"]["mfma_fast"] > 0 and s["launches_per_contract"] == 1
 
 
+@pytest.mark.parametrize("ld_align", [8, 1])
+def test_blockdiag_bf16_full_size_int_bit_exact(ld_align):
+    """The bench workload's structure and launch configuration (default plan
+    options) on integer values in {-2..2}: every element of every C block,
+    the 19 tail sectors of dims 1-4 included, equal to the oracle bit for
+    bit (K <= 1024, so every partial sum is an exact fp32 integer)."""
+    prob = C.blockdiag_bf16(ld_align=ld_align, align=ld_align, int_values=True)
+    plan, got = _parity(prob, axis="auto", exact=True, min_triples=64)
+    s = plan.stats()
+    assert s["launches_per_contract"] == 1
+    if ld_align == 8:
+        assert s["items_by_class"]["mfma_fast"] > 0
+
+
 def test_blockdiag_bf16_small_blocks_ragged():
-    """A ragged bf16 block-diagonal case spanning several tiles with odd edges."""
-    prob = C.random_problem(4200, nq=1, nkeys=(6, 6, 6), maxdim=150, qrange=2, dtype="bf16", two_leg=False,
+    """A ragged bf16 case spanning several tiles with odd edges: sector GEMMs
+    100 x 141 x 139 (two column tiles, a partial K chunk), 83 x 116 x 6,
+    25 x 37 x 150 and 25 x 55 x 149 (two column tiles)."""
+    prob = C.random_problem(4209, nq=1, nkeys=(6, 6, 6), maxdim=150, qrange=2, dtype="bf16", two_leg=False,
                             dup_charges=False)
-    _parity(prob)
+    shapes = sorted((int(prob.con.m.dim[m]), int(prob.con.k.dim[k]), int(prob.con.n.dim[n]))
+                    for m, k, n in oracle.triples(prob.con))
+    assert max(max(mm, nn) for mm, _, nn in shapes) > 128 and max(kk for _, kk, _ in shapes) > 64, shapes
+    for axis in AXES:
+        _parity(prob, axis=axis, min_triples=4)
 
 
-def _chain_parity(ch, tol, axes=("auto", "auto", "auto")):
+def _chain_parity(ch, tol, axes=("auto", "auto", "auto"), exact=False):
     t = torch()
     ref = oracle.run_chain(ch)
+    if exact:
+        assert int_chain_bound(ch) < 2 ** 24, "integer chain must stay exact in fp32"
     dt = ch.dtype
     bufs = {k: to_dev(v, dt) for k, v in ch.buffers.items()}
     cdt = t.float64 if dt == "f64" else t.float32
@@ -129,8 +169,13 @@ def _chain_parity(ch, tol, axes=("auto", "auto", "auto")):
     for st in ch.stages:
         addr, _ = c_addresses(st.con)
         got = bufs[st.c_buf].cpu().numpy()
+        if exact:
+            assert np.array_equal(got[addr].astype(np.float64), ref[st.c_buf][addr]), (st.label, "not bit-exact")
+            continue
         err = rel_frobenius(got, ref[st.c_buf], addr)
         assert err <= tol, (st.label, err)
+        # per block, against the magnitudes of the stage's inputs
+        check_blocks(st.con, got, ref[st.c_buf], ref[st.a_buf], ref[st.b_buf], tol, label=st.label)
 
 
 @pytest.mark.parametrize("layout", ["coop", "natural"])
@@ -145,6 +190,17 @@ def test_rabc_u1_chain():
 
 def test_rabc_u1u1_chain():
     _chain_parity(C.rabc_u1u1(), 1e-5)
+
+
+def test_rabc_u1_chain_int_bit_exact():
+    """Full-size U(1) update (fp64) on integer values: every element exact."""
+    _chain_parity(C.rabc_u1(values="int"), 0.0, exact=True)
+    _chain_parity(C.rabc_u1(values="int"), 0.0, axes=("contract", "free_n", "free_m"), exact=True)
+
+
+def test_rabc_u1u1_chain_int_bit_exact():
+    """Full-size U(1)xU(1) update (fp32, natural layout, gathers) on integer values."""
+    _chain_parity(C.rabc_u1u1(values="int"), 0.0, exact=True)
 
 
 def test_determinism():

@@ -12,7 +12,7 @@ from workloads import configs as C
 from workloads.layout import write_block
 from workloads.model import Contraction, Index, Operand
 
-from gpuhelp import c_addresses, canary, check_canary, have_gpu, rel_frobenius, run_engine, to_dev, torch
+from gpuhelp import c_addresses, canary, check_canary, check_float, have_gpu, run_engine, to_dev, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def test_split_automatic_long_k():
     assert plan.stats()["split_tiles"] >= 1
     check_canary(got, mask)
     ref = oracle.contract(con, a, b, np.zeros(con.C.buffer_elems), check=False)
-    assert rel_frobenius(got, ref, addr) <= 2e-2
+    check_float(con, got, ref, a, b, 2e-2, label="auto split")
 
 
 @pytest.mark.parametrize("shape", [(300, 333, 150), (256, 1024, 128), (520, 1000, 260), (64, 700, 40)],
@@ -75,7 +75,7 @@ def test_split_parity(shape, brow, split_k):
         assert plan.stats()["split_tiles"] > 0
     check_canary(got, mask)
     ref = oracle.contract(con, a, b, np.zeros(con.C.buffer_elems), check=False)
-    assert rel_frobenius(got, ref, addr) <= 2e-2
+    check_float(con, got, ref, a, b, 2e-2)
 
 
 @pytest.mark.parametrize("brow", [True, False])
@@ -110,14 +110,14 @@ def test_split_repeat_deterministic_and_accumulate():
     for o in outs[1:]:
         assert np.array_equal(o[addr], outs[0][addr])
     ref = oracle.contract(con, a, b, np.zeros(con.C.buffer_elems), check=False)
-    assert rel_frobenius(outs[0], ref, addr) <= 2e-2
+    check_float(con, outs[0], ref, a, b, 2e-2, label="repeat")
     pacc = bst.Plan(con, split_k=2, accumulate=True).bind()
     c0 = np.where(mask, 1.0, np.nan)
     got = run_engine(pacc, a, b, c0, "bf16", repeats=3)
     ref3 = oracle.contract(con, a, b, np.asarray(c0, np.float64), accumulate=True, check=False)
     ref3 = oracle.contract(con, a, b, ref3, accumulate=True, check=False)
     ref3 = oracle.contract(con, a, b, ref3, accumulate=True, check=False)
-    assert rel_frobenius(got, ref3, addr) <= 2e-2
+    check_float(con, got, ref3, a, b, 2e-2, label="accumulate x3")
 
 
 def test_split_unaligned_fallback():
@@ -138,7 +138,7 @@ def test_split_unaligned_fallback():
     got = Cd.cpu().numpy()
     check_canary(got, mask)
     ref = oracle.contract(con, a, b, np.zeros(con.C.buffer_elems), check=False)
-    assert rel_frobenius(got, ref, addr) <= 2e-2
+    check_float(con, got, ref, a, b, 2e-2)
 
 
 def test_split_blockdiag_full_size():
@@ -152,4 +152,4 @@ def test_split_blockdiag_full_size():
     got = run_engine(plan, prob.a, prob.b, canary(con, "bf16"), "bf16", repeats=2)
     check_canary(got, mask)
     ref = oracle.contract(con, prob.a, prob.b, np.zeros(con.C.buffer_elems), check=False)
-    assert rel_frobenius(got, ref, addr) <= 2e-2
+    check_float(con, got, ref, prob.a, prob.b, 2e-2, label="blockdiag split")

@@ -492,7 +492,11 @@ def test_p11_chain_vs_dense_einsum(layout):
     ch = C.small_chain(seed=11, layout=layout)
     bufs = oracle.run_chain(ch)
     st, E, A, W = _dense_tensors(ch)
-    Ep = np.einsum("awc,asb,wstv,ctd->bvd", E, A, W, A, optimize=True)
+    # one einsum over the dense tensors; the contraction path may keep intermediates
+    # (numpy's default memory cap would otherwise force the naive 8-index loop)
+    expr = "awc,asb,wstv,ctd->bvd"
+    path = np.einsum_path(expr, E, A, W, A, optimize=("greedy", 1e9))[0]
+    Ep = np.einsum(expr, E, A, W, A, optimize=path)
     got = _ep_blocks(ch, bufs["Ep"])
     mask = np.zeros(Ep.shape, bool)
     for (b, wp, bp), v in got.items():

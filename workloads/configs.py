@@ -175,14 +175,16 @@ def blockdiag_bf16_dims(reading: str = "i_scaled", seed: int = 1005):
 
 
 def blockdiag_bf16(reading: str = "i_scaled", seed: int = 1005, ld_align: int = 1, align: int = 1,
-         values: bool = True) -> Problem:
+         values: bool = True, int_values: bool = False) -> Problem:
     """U(1) sectors q=0..S-1 sharing one dimension list for m, k and n, flux 0, so
     every operand is block diagonal.  Dims are lognormal(5, 0.6) clipped to
     16..1024 (rescaled so the dense equivalent is ~16384) plus tail sectors of
     dim 1..4.  Values N(0, 0.02) drawn in fp32 and rounded to bf16 (RNE).
 
     ld_align / align pad each block's leading dimension / start offset (in
-    elements); 1 gives plain contiguous row-major blocks."""
+    elements); 1 gives plain contiguous row-major blocks.  int_values draws
+    integers in {-2..2} instead (exact in bf16; with K <= 1024 every partial
+    sum is an integer below 2^24, so any summation order is exact in fp32)."""
     dims, rng = blockdiag_bf16_dims(reading, seed)
     S = len(dims)
     q = np.arange(S)
@@ -193,13 +195,17 @@ def blockdiag_bf16(reading: str = "i_scaled", seed: int = 1005, ld_align: int = 
     Cb, nc = _rowmajor(pairs, dims, dims, align, ld_align)
     a = np.zeros(na, np.float32)
     b = np.zeros(nb, np.float32)
-    if values:
+    if values and int_values:
+        draw = lambda s: rng.integers(-2, 3, s).astype(np.float32)
+        _fill(a, Ab, dims, dims, draw)
+        _fill(b, Bb, dims, dims, draw)
+    elif values:
         draw = lambda s: bf16_round((rng.standard_normal(s) * 0.02).astype(np.float32))
         _fill(a, Ab, dims, dims, draw)
         _fill(b, Bb, dims, dims, draw)
     con = Contraction(idx, idx, idx, _operand(Ab, [0], 1, na), _operand(Bb, [0], 1, nb),
                       _operand(Cb, [0], 1, nc), "bf16")
-    return Problem(f"blockdiag_bf16-{reading}", con, a, b, {"dims": dims})
+    return Problem(f"blockdiag_bf16-{reading}" + ("-int" if int_values else ""), con, a, b, {"dims": dims})
 
 
 # ----------------------------------------------------------------------------
@@ -243,7 +249,10 @@ def rabc_chain(bond_q, bond_dim, local_q, mpo_q, mpo_pairs, dtype, rng, layout="
                       order, blocks in sorted order.
     values 'normal' : N(0,1) entries;
     values 'identity': E = identity, W = identity on the local space (needs w = 1),
-                      A left-orthonormal per b-sector (QR of a Gaussian matrix).
+                      A left-orthonormal per b-sector (QR of a Gaussian matrix);
+    values 'int'    : integer entries in {-1, 0, 1} for E, A and W, so every
+                      product and partial sum of the three stages is an integer
+                      (exact in fp32 while its magnitude stays below 2^24).
     """
     bond_q = np.asarray(bond_q, np.int64)
     local_q = np.asarray(local_q, np.int64).reshape(len(local_q), -1)
@@ -272,6 +281,13 @@ def rabc_chain(bond_q, bond_dim, local_q, mpo_q, mpo_pairs, dtype, rng, layout="
             Av[(a, s, b)] = rng.standard_normal((D[a], D[b]))
         for e in W_elems:
             Wv[e] = rng.standard_normal()
+    elif values == "int":
+        for (a, ww, ap) in E_blocks:
+            Ev[(a, ww, ap)] = rng.integers(-1, 2, (D[a], D[ap])).astype(np.float64)
+        for (a, s, b) in A_blocks:
+            Av[(a, s, b)] = rng.integers(-1, 2, (D[a], D[b])).astype(np.float64)
+        for e in W_elems:
+            Wv[e] = float(rng.integers(-1, 2))
     elif values == "identity":
         if w != 1:
             raise ValueError("identity values need an MPO bond of dimension 1")
@@ -474,7 +490,7 @@ U1_MPO_PAIRS = [(0, 0), (0, 1), (0, 2), (0, 3), (0, 4), (1, 4), (2, 4), (3, 4), 
 U1U1_MPO_PAIRS = [(0, j) for j in range(6)] + [(i, 5) for i in range(1, 5)] + [(5, 5)]
 
 
-def rabc_u1(seed: int = 1003, layout: str = "coop") -> Chain:
+def rabc_u1(seed: int = 1003, layout: str = "coop", values: str = "normal") -> Chain:
     """U(1) spin-chain environment update, fp64: bond m=1024 over 41 sectors
     (Gaussian dims, sigma = 6 sectors), LocalSpace d=4 with charges {-1,0,0,+1},
     MPO bond w=5 with 12 nonzero channel pairs."""
@@ -482,10 +498,11 @@ def rabc_u1(seed: int = 1003, layout: str = "coop") -> Chain:
     bq, bd = _bond_u1(1024, 20, 6.0)
     local = np.array([[-1], [0], [0], [1]])
     mpo = np.array([[0], [-1], [1], [0], [0]])
-    return rabc_chain(bq, bd, local, mpo, U1_MPO_PAIRS, "f64", rng, layout, name=f"rabc_u1-{layout}")
+    return rabc_chain(bq, bd, local, mpo, U1_MPO_PAIRS, "f64", rng, layout, values,
+                      name=f"rabc_u1-{layout}" + ("" if values == "normal" else f"-{values}"))
 
 
-def rabc_u1u1(seed: int = 1004, layout: str = "natural") -> Chain:
+def rabc_u1u1(seed: int = 1004, layout: str = "natural", values: str = "normal") -> Chain:
     """U(1)xU(1) environment update, fp32: bond m=4096 over the populated part of
     a 15x15 charge grid (Gaussian dims, sigma 2.2 -> 177 sectors), local charges
     (n_up, n_dn), Hubbard-shaped MPO w=6 with 11 nonzero channel pairs."""
@@ -493,7 +510,8 @@ def rabc_u1u1(seed: int = 1004, layout: str = "natural") -> Chain:
     bq, bd = _bond_u1u1(4096, 7, 2.2, 0.5)
     local = np.array([[0, 0], [1, 0], [0, 1], [1, 1]])
     mpo = np.array([[0, 0], [-1, 0], [1, 0], [0, -1], [0, 1], [0, 0]])
-    return rabc_chain(bq, bd, local, mpo, U1U1_MPO_PAIRS, "f32", rng, layout, name=f"rabc_u1u1-{layout}")
+    return rabc_chain(bq, bd, local, mpo, U1U1_MPO_PAIRS, "f32", rng, layout, values,
+                      name=f"rabc_u1u1-{layout}" + ("" if values == "normal" else f"-{values}"))
 
 
 def small_chain(seed: int = 7, layout: str = "coop", values: str = "normal", dtype: str = "f64",

@@ -1,11 +1,5 @@
-// Device side of the engine: work-list upload and the grouped contraction launch.
-//
-// One launch walks the whole work list (uni20 "block coalescing", section
-// "Summary": issue fewer, larger kernels instead of one per sector GEMM).  A
-// workgroup takes tasks blockIdx.x, blockIdx.x + gridDim.x, ... from a
-// longest-first list, so the grid can be sized to the machine (persistent
-// workgroups) or to the task count.  No task waits on another: every C tile has
-// exactly one owner, so sums need no atomics and repeat bit-for-bit.
+// Device side of the engine: work-list upload, the launches of one contraction
+// (gathers, then the grouped kernel: grouped_kernel.h) and captured chains.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -14,12 +8,7 @@
 #include <type_traits>
 
 #include "bsc_internal.h"
-#include "kernels_generic.h"
-#include "kernels_mfma_bf16.h"
-#include "kernels_mfma_bf16_fast.h"
-#include "kernels_mfma_f.h"
-#include "kernels_pack.h"
-#include "kernels_skinny.h"
+#include "launch.h"
 
 namespace bsc {
 
@@ -28,156 +17,20 @@ static bsc_status hip_fail(hipError_t e, const char *what) {
     return BSC_ERR_HIP;
 }
 
-// Shared memory of a grouped launch: the union of the tile bodies it contains.
-template <typename TA>
-struct MfmaSmemOf {
-    typedef MfmaSmemF<TA> type;
-};
-template <>
-struct MfmaSmemOf<uint16_t> {
-    typedef MfmaSmemBf16 type;
-};
-
-template <typename TA, typename ACC, int32_t FEAT>
-union TileSmem {
-    GenericSmem<ACC> g;
-    SkinnySmem<ACC> s;
-    typename std::conditional<(FEAT & FEAT_MFMA) != 0, typename MfmaSmemOf<TA>::type, char>::type m;
-    typename std::conditional<(FEAT & (FEAT_FAST_N | FEAT_FAST_K)) != 0, FastSmemBf16, char>::type f;
-};
-
-extern __shared__ __align__(16) unsigned char bsc_dyn_smem[];
-
-template <typename TA, typename TC, typename ACC, int32_t FEAT>
-__device__ __forceinline__ void grouped_body(const KArgs &ka) {
-    TileSmem<TA, ACC, FEAT> &sm = *reinterpret_cast<TileSmem<TA, ACC, FEAT> *>(bsc_dyn_smem);
-    // a task with a record finds it at its own index (record t belongs to task t)
-    for (int32_t t = blockIdx.x; t < ka.ntasks; t += gridDim.x) {
-        const int32_t ti = ka.task0 + t;
-        const DTask task = ka.tasks[ti];
-        if (task.cls == T_NOP) continue;
-        if (task.cls == T_SKINNY_DENSE_M) {
-            skinny_dense<TA, TC, ACC, true>(ka, ka.fast[ti], sm.s);
-            continue;
-        }
-        if (task.cls == T_SKINNY_DENSE_N) {
-            skinny_dense<TA, TC, ACC, false>(ka, ka.fast[ti], sm.s);
-            continue;
-        }
-        if (task.cls == T_SKINNY_M) {
-            skinny_tile<TA, TC, ACC, true>(ka, task, sm.s);
-            continue;
-        }
-        if (task.cls == T_SKINNY_N) {
-            skinny_tile<TA, TC, ACC, false>(ka, task, sm.s);
-            continue;
-        }
-        if constexpr ((FEAT & FEAT_FAST_N) != 0) {
-            if (task.cls == T_MFMA_FAST_N) {
-                fast_tile_bf16<TC, true>(ka, ka.fast[ti], sm.f);
-                continue;
-            }
-        }
-        if constexpr ((FEAT & FEAT_FAST_K) != 0) {
-            if (task.cls == T_MFMA_FAST_K) {
-                fast_tile_bf16<TC, false>(ka, ka.fast[ti], sm.f);
-                continue;
-            }
-        }
-        if constexpr ((FEAT & FEAT_MFMA) != 0) {
-            if (is_mfma(task.cls)) {
-                if constexpr (std::is_same<TA, uint16_t>::value) {
-                    // a direct-to-LDS task run on the general tile (a launch whose operand
-                    // bases are not 16-byte aligned) covers its rows in two halves; of the
-                    // K-slices of a split tile, the first computes the whole tile
-                    static_assert(TILE_MFMA_DENSE_M <= 2 * TILE_MFMA, "a dense task fits two general tiles");
-                    if (task.cls != T_MFMA && ka.fast[ti].nsplit > 1 && ka.fast[ti].split != 0) continue;
-                    mfma_tile_bf16<TC>(ka, task, sm.m);
-                    if (task.cls != T_MFMA && ka.fast[ti].mlen > TILE_MFMA) {
-                        DTask lower = task;
-                        lower.m0 += TILE_MFMA;
-                        mfma_tile_bf16<TC>(ka, lower, sm.m);
-                    }
-                } else {
-                    mfma_tile_f<TA>(ka, task, ka.fast[ti], sm.m);
-                }
-                continue;
-            }
-        }
-        generic_tile<TA, TC, ACC>(ka, task, sm.g);
-    }
-}
-
-// A launch whose LDS allows only one workgroup per CU gets the whole register
-// file (one wave per SIMD); the others keep two workgroups per CU.
-template <typename TA, typename ACC, int32_t FEAT>
-constexpr bool one_per_cu() { return sizeof(TileSmem<TA, ACC, FEAT>) > 80 * 1024; }
-
-template <typename TA, typename TC, typename ACC, int32_t FEAT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void grouped_contract(KArgs ka) {
-    grouped_body<TA, TC, ACC, FEAT>(ka);
-}
-
-template <typename TA, typename TC, typename ACC, int32_t FEAT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void grouped_contract_wide(KArgs ka) {
-    grouped_body<TA, TC, ACC, FEAT>(ka);
-}
-
-// fp32 launches: the fp32 tile bodies fit in 128 VGPRs and their LDS allows
-// four workgroups per CU, so they are compiled for four waves per SIMD (more
-// tiles in flight to hide the per-tile chain of dependent loads).
-template <typename TA, typename TC, typename ACC, int32_t FEAT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void grouped_contract_narrow(KArgs ka) {
-    grouped_body<TA, TC, ACC, FEAT>(ka);
-}
-
-using KernelFn = void (*)(KArgs);
-
-struct KernelRef {
-    KernelFn fn;
-    size_t lds;     // dynamic LDS bytes of the variant
-};
-
-// Opt a kernel variant into more than the default dynamic LDS once per process.
-template <typename TA, typename TC, typename ACC, int32_t FEAT>
-static KernelRef kernel_ref() {
-    KernelFn fn;
-    if constexpr (one_per_cu<TA, ACC, FEAT>()) fn = grouped_contract_wide<TA, TC, ACC, FEAT>;
-    else if constexpr (std::is_same<TA, float>::value) fn = grouped_contract_narrow<TA, TC, ACC, FEAT>;
-    else fn = grouped_contract<TA, TC, ACC, FEAT>;
-    const size_t lds = sizeof(TileSmem<TA, ACC, FEAT>);
-    static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)once;
-    return {fn, lds};
-}
-
-template <int32_t FEAT>
-static KernelRef bf16_kernel() { return kernel_ref<uint16_t, float, float, FEAT>(); }
-
 // bf16 launches pick the variant that holds exactly the tile bodies the plan uses;
 // when an operand base is not 16-byte aligned the direct-to-LDS tiles fall back
 // to the general matrix-core tile (task class T_MFMA_FAST_* is accepted there).
 static KernelRef pick_bf16(int32_t feat, bool vec) {
     if (!vec && (feat & (FEAT_FAST_N | FEAT_FAST_K))) feat = (feat & ~(FEAT_FAST_N | FEAT_FAST_K)) | FEAT_MFMA;
-    switch (feat) {
-        case 0: return bf16_kernel<0>();
-        case 1: return bf16_kernel<1>();
-        case 2: return bf16_kernel<2>();
-        case 3: return bf16_kernel<3>();
-        case 4: return bf16_kernel<4>();
-        case 5: return bf16_kernel<5>();
-        case 6: return bf16_kernel<6>();
-        default: return bf16_kernel<7>();
-    }
+    return feat < 4 ? grouped_kernel_bf16_lo(feat) : grouped_kernel_bf16_hi(feat);
 }
 
 // Grid of a launch: one workgroup per task up to a persistent cap of 16 per CU
 // (four to eight times what is resident at once, so a workgroup that finishes
 // is replaced by a fresh one more often than it loops to its next task); the
 // cap is a multiple of BSC_XCDS so task t keeps running on XCD t % BSC_XCDS.
-static int32_t grid_for(const Plan &p, int32_t ntasks) {
-    int32_t cap = p.opt.grid_limit > 0 ? p.opt.grid_limit : std::max(1, p.cu_count) * 16;
+static int32_t grid_for(const Plan &p, int32_t ntasks, int32_t cu_count) {
+    int32_t cap = p.opt.grid_limit > 0 ? p.opt.grid_limit : std::max(1, cu_count) * 16;
     if (cap >= BSC_XCDS) cap -= cap % BSC_XCDS;
     return std::max(1, std::min(ntasks, cap));
 }
@@ -215,27 +68,19 @@ extern "C" bsc_status bsc_plan_bind(bsc_plan_t plan, void *dev, size_t bytes, vo
     p->dev = dev;
     p->cu_count = cus;
     int32_t g = 0;
-    for (auto &l : p->launches) g = std::max(g, grid_for(*p, l[1] - l[0]));
+    for (auto &l : p->launches) g = std::max(g, grid_for(*p, l[1] - l[0], cus));
     p->grid = g;
     return BSC_OK;
 }
 
-extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B, void *C, void *stream) {
-    if (!plan) {
-        set_error("bsc_contract: NULL plan");
-        return BSC_ERR_ARG;
-    }
-    Plan *p = reinterpret_cast<Plan *>(plan);
-    if (!p->dev) {
-        set_error("bsc_contract: plan is not bound to a device region");
-        return BSC_ERR_NOT_BOUND;
-    }
-    if ((!A && p->a_elems > 0) || (!B && p->b_elems > 0) || (!C && p->c_elems > 0)) {
-        set_error("bsc_contract: NULL operand buffer");
-        return BSC_ERR_ARG;
-    }
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const unsigned char *base = static_cast<const unsigned char *>(p->dev);
+namespace bsc {
+
+// Enqueue one contraction of plan p whose device region (work-list image,
+// pack workspace, K-split partials) starts at `region`, on a device with
+// `cu_count` compute units.
+static bsc_status contract_on(Plan *p, const void *region, int32_t cu_count, const void *A, const void *B, void *C,
+                              hipStream_t s) {
+    const unsigned char *base = static_cast<const unsigned char *>(region);
     KArgs ka;
     ka.groups = reinterpret_cast<const DGroup *>(base + p->off_groups);
     ka.runs = reinterpret_cast<const DRun *>(base + p->off_runs);
@@ -266,13 +111,9 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
         pa.A = A;
         pa.B = B;
         pa.W = const_cast<unsigned char *>(base) + p->off_ws;
-        const int32_t cap = std::max(1, p->cu_count) * 8;
-        dim3 grid((unsigned)std::max(1, std::min(pa.ntasks, cap))), block(256);
-        switch (p->dtype) {
-            case BSC_F64: hipLaunchKernelGGL(pack_gather<double>, grid, block, 0, s, pa); break;
-            case BSC_F32: hipLaunchKernelGGL(pack_gather<float>, grid, block, 0, s, pa); break;
-            case BSC_BF16_F32: hipLaunchKernelGGL(pack_gather<uint16_t>, grid, block, 0, s, pa); break;
-        }
+        const int32_t cap = std::max(1, cu_count) * 8;
+        dim3 grid((unsigned)std::max(1, std::min(pa.ntasks, cap)));
+        launch_pack(p->dtype, grid, s, pa);
         p->stats.launches_issued++;
     }
     ka.vec_a = (reinterpret_cast<uintptr_t>(A) % 16) == 0;
@@ -280,17 +121,15 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
     for (auto &l : p->launches) {
         ka.task0 = l[0];
         ka.ntasks = l[1] - l[0];
-        dim3 grid((unsigned)grid_for(*p, ka.ntasks)), block(256);
+        dim3 grid((unsigned)grid_for(*p, ka.ntasks, cu_count)), block(256);
         switch (p->dtype) {
             case BSC_F64: {
-                const KernelRef k = (p->features & FEAT_MFMA) ? kernel_ref<double, double, double, FEAT_MFMA>()
-                                                               : kernel_ref<double, double, double, 0>();
+                const KernelRef k = grouped_kernel_f64(p->features);
                 hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
                 break;
             }
             case BSC_F32: {
-                const KernelRef k = (p->features & FEAT_MFMA) ? kernel_ref<float, float, float, FEAT_MFMA>()
-                                                               : kernel_ref<float, float, float, 0>();
+                const KernelRef k = grouped_kernel_f32(p->features);
                 hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
                 break;
             }
@@ -305,6 +144,25 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     return BSC_OK;
+}
+
+}  // namespace bsc
+
+extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B, void *C, void *stream) {
+    if (!plan) {
+        set_error("bsc_contract: NULL plan");
+        return BSC_ERR_ARG;
+    }
+    Plan *p = reinterpret_cast<Plan *>(plan);
+    if (!p->dev) {
+        set_error("bsc_contract: plan is not bound to a device region");
+        return BSC_ERR_NOT_BOUND;
+    }
+    if ((!A && p->a_elems > 0) || (!B && p->b_elems > 0) || (!C && p->c_elems > 0)) {
+        set_error("bsc_contract: NULL operand buffer");
+        return BSC_ERR_ARG;
+    }
+    return contract_on(p, p->dev, p->cu_count, A, B, C, reinterpret_cast<hipStream_t>(stream));
 }
 
 // ---- captured chains (one graph launch per sequence of contractions) ----------------

@@ -20,7 +20,8 @@ STATUS = {
 EXPORTED = ["bsc_options_default", "bsc_plan", "bsc_plan_device_bytes", "bsc_plan_bind", "bsc_contract",
             "bsc_plan_stats", "bsc_plan_export", "bsc_plan_worklist", "bsc_plan_destroy", "bsc_status_string",
             "bsc_last_error", "bsc_chain_create", "bsc_chain_launch", "bsc_chain_destroy", "bsc_plan_cache_create",
-            "bsc_plan_cached", "bsc_plan_cache_stats", "bsc_plan_cache_destroy", "bsc_plan_layout"]
+            "bsc_plan_cached", "bsc_plan_cache_stats", "bsc_plan_cache_destroy", "bsc_plan_layout",
+            "bsc_contract_noalloc"]
 
 
 class BscIndex(ctypes.Structure):
@@ -81,6 +82,8 @@ def lib():
         L.bsc_plan_bind.restype = c_int32
         L.bsc_contract.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.bsc_contract.restype = c_int32
+        L.bsc_contract_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.bsc_contract_noalloc.restype = c_int32
         L.bsc_plan_stats.argtypes = [c_void_p, POINTER(BscStats)]
         L.bsc_plan_stats.restype = c_int32
         L.bsc_plan_export.argtypes = [c_void_p, POINTER(c_int32), POINTER(c_int32), POINTER(c_int32)]

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -163,6 +164,87 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B
         return BSC_ERR_ARG;
     }
     return contract_on(p, p->dev, p->cu_count, A, B, C, reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---- contraction without a caller-provided device region ---------------------------
+//
+// For callers that cannot allocate device memory when they contract (code under
+// graph capture, tight serving loops, harnesses that forbid allocation): the
+// plan's device region — work-list image, pack workspace, K-split partial tiles
+// and their counters — lives in one file-scope device array of fixed size
+// instead of a region passed to bsc_plan_bind.  Each GPU holds its own copy of
+// the array (loaded with the code object, held until the process ends); its
+// device address is looked up once per device with hipGetSymbolAddress and
+// only that address is used from host code.
+
+namespace bsc {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+struct NoallocDevice {
+    void *ptr = nullptr;   // device address of this GPU's scratch array
+    int32_t cus = 0;       // compute units of this GPU
+};
+static std::mutex noalloc_mu;
+static NoallocDevice noalloc_dev[NOALLOC_MAX_DEVICES];
+
+// The current device's scratch address and CU count, looked up on first use.
+static bsc_status noalloc_device(NoallocDevice &out) {
+    int dev_id = 0;
+    hipError_t e = hipGetDevice(&dev_id);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev_id < 0 || dev_id >= NOALLOC_MAX_DEVICES) {
+        set_error("bsc_contract_noalloc: device index beyond " + std::to_string(NOALLOC_MAX_DEVICES));
+        return BSC_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(noalloc_mu);
+    NoallocDevice &d = noalloc_dev[dev_id];
+    if (!d.ptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (scratch)");
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev_id);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+        d.cus = cus;
+        d.ptr = ptr;
+    }
+    out = d;
+    return BSC_OK;
+}
+
+}  // namespace bsc
+
+extern "C" bsc_status bsc_contract_noalloc(bsc_plan_t plan, const void *A, const void *B, void *C, void *stream) {
+    if (!plan) {
+        set_error("bsc_contract_noalloc: NULL plan");
+        return BSC_ERR_ARG;
+    }
+    Plan *p = reinterpret_cast<Plan *>(plan);
+    if ((!A && p->a_elems > 0) || (!B && p->b_elems > 0) || (!C && p->c_elems > 0)) {
+        set_error("bsc_contract_noalloc: NULL operand buffer");
+        return BSC_ERR_ARG;
+    }
+    if (p->dev_bytes > NOALLOC_SCRATCH_BYTES) {
+        set_error("bsc_contract_noalloc: the plan needs " + std::to_string(p->dev_bytes) +
+                  " bytes of device scratch (work list + pack workspace + K-split partials), more than the " +
+                  std::to_string(NOALLOC_SCRATCH_BYTES) + " the library holds per GPU; bind a region instead");
+        return BSC_ERR_DEVICE_BYTES;
+    }
+    NoallocDevice d;
+    bsc_status st = noalloc_device(d);
+    if (st != BSC_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // the work-list image (its K-split counters zero) replaces whatever the last
+    // call on this GPU left in the array, in stream order
+    if (!p->image.empty()) {
+        const hipError_t e = hipMemcpyAsync(d.ptr, p->image.data(), p->image.size(), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (work list into scratch)");
+    }
+    return contract_on(p, d.ptr, d.cus, A, B, C, s);
 }
 
 // ---- captured chains (one graph launch per sequence of contractions) ----------------

@@ -33,6 +33,15 @@ extern "C" bsc_status bsc_contract(bsc_plan_t plan, const void *, const void *, 
     return BSC_ERR_UNSUPPORTED;
 }
 
+extern "C" bsc_status bsc_contract_noalloc(bsc_plan_t plan, const void *, const void *, void *, void *) {
+    if (!plan) {
+        set_error("bsc_contract_noalloc: NULL plan");
+        return BSC_ERR_ARG;
+    }
+    set_error("bsc_contract_noalloc: host-only planner build has no device runtime");
+    return BSC_ERR_UNSUPPORTED;
+}
+
 extern "C" bsc_status bsc_chain_create(const bsc_plan_t *, const void *const *, const void *const *, void *const *,
                                        int32_t, bsc_chain_t *out) {
     if (out) *out = nullptr;

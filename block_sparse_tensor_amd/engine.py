@@ -246,6 +246,16 @@ class Plan:
                                         c_void_p(C.data_ptr()), _stream_handle(stream)))
         return C
 
+    def contract_noalloc(self, A, B, C, stream=None):
+        """Enqueue C (+)= A B without a bound device region (bsc_contract_noalloc):
+        the plan's work list, workspace and partials go to the library's fixed
+        per-GPU scratch array (64 MiB), so nothing is allocated.  Calls that
+        overlap on one GPU race; the plan need not be bound."""
+        self.check_operands(A, B, C)
+        _check(_capi.lib().bsc_contract_noalloc(self._h, c_void_p(A.data_ptr()), c_void_p(B.data_ptr()),
+                                                c_void_p(C.data_ptr()), _stream_handle(stream)))
+        return C
+
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and h.value:

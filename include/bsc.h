@@ -216,6 +216,21 @@ bsc_status bsc_plan_bind(bsc_plan_t plan, void *dev, size_t bytes, void *stream)
  * dtype).  Returns without synchronising. */
 bsc_status bsc_contract(bsc_plan_t plan, const void *A, const void *B, void *C, void *stream);
 
+/* bsc_contract for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * plan need not be bound.  Its device region (work-list image, pack
+ * workspace, K-split partial tiles and counters: bsc_plan_device_bytes) lives
+ * in a fixed array of 64 MiB that the library holds on every GPU it runs on
+ * until the process ends; each call first copies the work-list image (counters
+ * zero) into the current device's array on `stream`, then enqueues the same
+ * launches as bsc_contract.  No device memory is allocated or freed.  Every
+ * call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (different streams, or a
+ * stream and a graph replay) race and give undefined results.
+ * Errors: BSC_ERR_ARG (NULL plan or operand buffer), BSC_ERR_DEVICE_BYTES
+ * (bsc_plan_device_bytes above 64 MiB; nothing is enqueued), BSC_ERR_HIP. */
+bsc_status bsc_contract_noalloc(bsc_plan_t plan, const void *A, const void *B, void *C, void *stream);
+
 /* Plan statistics (host only). */
 bsc_status bsc_plan_stats(bsc_plan_t plan, bsc_stats *out);
 

@@ -225,6 +225,10 @@ def main():
     ap.add_argument("--relayout", action="store_true",
                     help="chains: lay out every buffer for the stage that writes it, inputs for a stage that reads "
                          "them (cross-stage layout planning)")
+    ap.add_argument("--tile-cols", type=int, default=0, choices=[0, 128, 256],
+                    help="bf16 direct-to-LDS tile width: 0 = the engine's choice, 128 = 256x128 tiles two per CU, "
+                         "256 = the wide tile, one workgroup per CU")
+    ap.add_argument("--split-k", type=int, default=0, help="K split policy of the bf16 tiles (plan option)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cold-steps", type=int, default=20,
@@ -269,7 +273,8 @@ def main():
 
     def plans_for(mode):
         layout = args.layout if mode == "grouped" else "never_pack"
-        return [bst.Plan(con, axis=ax, launch_mode=mode, layout=layout).bind() for con, _, _, _, ax in stages]
+        return [bst.Plan(con, axis=ax, launch_mode=mode, layout=layout, tile_cols=args.tile_cols,
+                         split_k=args.split_k).bind() for con, _, _, _, ax in stages]
 
     def step(plans):
         for p, (_, a, b, c, _) in zip(plans, stages):
@@ -412,7 +417,8 @@ def main():
         ubufs = {k: dev(v) for k, v in uinputs.items()}
         for k, n in usizes.items():
             ubufs[k] = torch.zeros(n, dtype=cdt, device="cuda")
-        uplans = [bst.Plan(con, axis=ax, layout=args.layout).bind() for con, _, _, _, ax in ustages]
+        uplans = [bst.Plan(con, axis=ax, layout=args.layout, tile_cols=args.tile_cols, split_k=args.split_k).bind()
+                  for con, _, _, _, ax in ustages]
 
         def ustep():
             for p, (_, a, b, c, _) in zip(uplans, ustages):
@@ -460,6 +466,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "stages": len(stages),
                    "ld_align": args.ld_align, "layout": args.layout, "relayout": args.relayout,
+                   "tile_cols": args.tile_cols, "split_k": args.split_k,
                    "pack_bytes": sum(s["pack_bytes"] for s in st),
                    "sector_gemms": sum(s["triples"] for s in st), "useful_flops": flops,
                    "alg_bytes": alg_bytes, "parallelism": "single GPU"},

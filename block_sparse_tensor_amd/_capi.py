@@ -38,7 +38,8 @@ class BscOperand(ctypes.Structure):
 class BscOptions(ctypes.Structure):
     _fields_ = [("launch_mode", c_int32), ("layout_policy", c_int32), ("accumulate", c_int32),
                 ("grid_limit", c_int32), ("t_launch_us", c_double), ("t_seg_us", c_double),
-                ("pack_gbps", c_double), ("tile_gflops", c_double), ("split_k", c_int32), ("tile_rows", c_int32)]
+                ("pack_gbps", c_double), ("tile_gflops", c_double), ("split_k", c_int32), ("tile_rows", c_int32),
+                ("tile_cols", c_int32)]
 
 
 class BscStats(ctypes.Structure):

@@ -75,9 +75,10 @@ bsc_status bsc_plan(const bsc_index *m, const bsc_index *k, const bsc_index *n, 
         return BSC_ERR_ARG;
     }
     if (p->opt.layout_policy < BSC_LAYOUT_AUTO || p->opt.layout_policy > BSC_LAYOUT_FORCE_PACK || p->opt.grid_limit < 0 ||
-        p->opt.split_k < -1 || (p->opt.tile_rows != 0 && p->opt.tile_rows != 128 && p->opt.tile_rows != 256)) {
+        p->opt.split_k < -1 || (p->opt.tile_rows != 0 && p->opt.tile_rows != 128 && p->opt.tile_rows != 256) ||
+        (p->opt.tile_cols != 0 && p->opt.tile_cols != 128 && p->opt.tile_cols != 256)) {
         delete p;
-        set_error("bsc_plan: bad layout policy, grid limit, split_k or tile_rows");
+        set_error("bsc_plan: bad layout policy, grid limit, split_k, tile_rows or tile_cols");
         return BSC_ERR_ARG;
     }
     fill_cost_defaults(p->opt, dtype);

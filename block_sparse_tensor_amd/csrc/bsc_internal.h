@@ -86,7 +86,9 @@ enum : int32_t {
     T_MFMA_DENSE = 9,    // fp32 / fp64 matrix-core tile addressed through a DFast record (group = DFast index)
     T_SKINNY_DENSE_M = 10,   // skinny tile, long axis M, addressed through a DFast record
     T_SKINNY_DENSE_N = 11,   // skinny tile, long axis N, addressed through a DFast record
-    T_NCLASS = 12,
+    T_MFMA_WIDE_N = 12,  // wide dense tile (one workgroup per CU, up to 256 x 256), N-contiguous B (DFast record)
+    T_MFMA_WIDE_K = 13,  // wide dense tile, K-contiguous B (DFast record)
+    T_NCLASS = 14,
 };
 
 // Workgroups of a launch are dispatched round-robin over the chiplets (XCDs),
@@ -100,8 +102,9 @@ constexpr int BSC_XCDS = 8;
 // a CU.  The planner uses this only to choose which tiles share a CU.
 constexpr int BSC_CUS_PER_XCD = 32;
 
-// kernel feature sets: which tile bodies a grouped launch contains
-enum : int32_t { FEAT_MFMA = 1, FEAT_FAST_N = 2, FEAT_FAST_K = 4 };
+// kernel feature sets: which tile bodies a grouped launch contains (a plan
+// uses either the 256 x 128 direct-to-LDS tiles or the wide ones, never both)
+enum : int32_t { FEAT_MFMA = 1, FEAT_FAST_N = 2, FEAT_FAST_K = 4, FEAT_WIDE = 8 };
 
 // Per-tile record of a dense matrix-core tile: the tile's rows of A, columns of
 // B and block of C each lie inside one single-leg strided view, so the tile's
@@ -120,7 +123,8 @@ struct DFast {
     // K split (bf16 direct-to-LDS tile only): the output tile is summed over
     // `nsplit` K-slices, each a task of its own; this record covers slice
     // `split` (its bases and K are the slice's).  Every slice stores its fp32
-    // partial tile at part + split * TILE_MFMA_DENSE_M * TILE_MFMA and counts
+    // partial tile at part + split * (the tile body's rows x columns: 256 x 128,
+    // or for the wide tile 256 x 256, 256 x 128 when nlen <= 128) and counts
     // itself in counter `counter`; the last to arrive adds the partials in
     // slice order and writes C.  nsplit = 1: no split.
     int32_t split, nsplit, counter;
@@ -177,15 +181,18 @@ constexpr int TILE_GENERIC = 64;   // generic tile edge
 constexpr int TILE_MFMA = 128;     // bf16 matrix-core tile edge
 constexpr int TILE_MFMA_DENSE_M = 256;   // rows of the dense (direct-to-LDS) bf16 tile; 128 columns
 constexpr int TILE_MFMA_F = 64;    // fp32 / fp64 matrix-core tile edge
+constexpr int TILE_WIDE = 256;     // rows and (at most) columns of the wide bf16 tile
 
 // task classes addressed through a DFast record (task t's record is record t)
+constexpr bool is_wide(int32_t cls) { return cls == T_MFMA_WIDE_N || cls == T_MFMA_WIDE_K; }
+// bf16 dense tiles with direct-to-LDS copies (256 x 128 or wide)
+constexpr bool is_direct(int32_t cls) {
+    return cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K || is_wide(cls);
+}
 constexpr bool has_record(int32_t cls) {
-    return cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K || cls == T_MFMA_DENSE || cls == T_SKINNY_DENSE_M ||
-           cls == T_SKINNY_DENSE_N;
+    return is_direct(cls) || cls == T_MFMA_DENSE || cls == T_SKINNY_DENSE_M || cls == T_SKINNY_DENSE_N;
 }
-constexpr bool is_mfma(int32_t cls) {
-    return cls == T_MFMA || cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K || cls == T_MFMA_DENSE;
-}
+constexpr bool is_mfma(int32_t cls) { return cls == T_MFMA || cls == T_MFMA_DENSE || is_direct(cls); }
 constexpr int TILE_SKINNY_SHORT = 16;   // largest short extent of a skinny group
 
 // Skinny tile extent along its long axis: 256 threads x R lines, where R times
@@ -207,6 +214,8 @@ inline void tile_extents(bsc_dtype dt, int32_t cls, int32_t M, int32_t N, int32_
     } else if (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) {
         tm = TILE_MFMA_DENSE_M;
         tn = TILE_MFMA;
+    } else if (is_wide(cls)) {
+        tm = tn = TILE_WIDE;
     } else {
         tm = tn = is_mfma(cls) ? (dt == BSC_BF16_F32 ? TILE_MFMA : TILE_MFMA_F) : TILE_GENERIC;
     }

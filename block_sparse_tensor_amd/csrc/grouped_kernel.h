@@ -17,6 +17,7 @@
 #include "kernels_generic.h"
 #include "kernels_mfma_bf16.h"
 #include "kernels_mfma_bf16_fast.h"
+#include "kernels_mfma_bf16_wide.h"
 #include "kernels_mfma_f.h"
 #include "kernels_skinny.h"
 #include "launch.h"
@@ -39,6 +40,7 @@ union TileSmem {
     SkinnySmem<ACC> s;
     typename std::conditional<(FEAT & FEAT_MFMA) != 0, typename MfmaSmemOf<TA>::type, char>::type m;
     typename std::conditional<(FEAT & (FEAT_FAST_N | FEAT_FAST_K)) != 0, FastSmemBf16, char>::type f;
+    typename std::conditional<(FEAT & FEAT_WIDE) != 0, WideSmemBf16, char>::type x;
 };
 
 extern __shared__ __align__(16) unsigned char bsc_dyn_smem[];
@@ -79,20 +81,36 @@ __device__ __forceinline__ void grouped_body(const KArgs &ka) {
                 continue;
             }
         }
+        if constexpr ((FEAT & FEAT_WIDE) != 0) {
+            if (task.cls == T_MFMA_WIDE_N) {
+                wide_tile_bf16<TC, true>(ka, ka.fast[ti], sm.x);
+                continue;
+            }
+            if (task.cls == T_MFMA_WIDE_K) {
+                wide_tile_bf16<TC, false>(ka, ka.fast[ti], sm.x);
+                continue;
+            }
+        }
         if constexpr ((FEAT & FEAT_MFMA) != 0) {
             if (is_mfma(task.cls)) {
                 if constexpr (std::is_same<TA, uint16_t>::value) {
                     // a direct-to-LDS task run on the general tile (a launch whose operand
-                    // bases are not 16-byte aligned) covers its rows in two halves; of the
-                    // K-slices of a split tile, the first computes the whole tile
-                    static_assert(TILE_MFMA_DENSE_M <= 2 * TILE_MFMA, "a dense task fits two general tiles");
+                    // bases are not 16-byte aligned) covers its rows and columns in
+                    // general tiles; of the K-slices of a split tile, the first computes
+                    // the whole tile
+                    static_assert(TILE_MFMA_DENSE_M <= 2 * TILE_MFMA && TILE_WIDE <= 2 * TILE_MFMA,
+                                  "a dense task fits two by two general tiles");
                     if (task.cls != T_MFMA && ka.fast[ti].nsplit > 1 && ka.fast[ti].split != 0) continue;
-                    mfma_tile_bf16<TC>(ka, task, sm.m);
-                    if (task.cls != T_MFMA && ka.fast[ti].mlen > TILE_MFMA) {
-                        DTask lower = task;
-                        lower.m0 += TILE_MFMA;
-                        mfma_tile_bf16<TC>(ka, lower, sm.m);
-                    }
+                    const bool rec = task.cls != T_MFMA;
+                    const int32_t mh = rec && ka.fast[ti].mlen > TILE_MFMA ? 2 : 1;
+                    const int32_t nh = rec && ka.fast[ti].nlen > TILE_MFMA ? 2 : 1;
+                    for (int32_t a = 0; a < mh; ++a)
+                        for (int32_t b = 0; b < nh; ++b) {
+                            DTask part = task;
+                            part.m0 += a * TILE_MFMA;
+                            part.n0 += b * TILE_MFMA;
+                            mfma_tile_bf16<TC>(ka, part, sm.m);
+                        }
                 } else {
                     mfma_tile_f<TA>(ka, task, ka.fast[ti], sm.m);
                 }

@@ -27,6 +27,7 @@ KernelRef grouped_kernel_f64(int32_t feat);
 KernelRef grouped_kernel_f32(int32_t feat);
 KernelRef grouped_kernel_bf16_lo(int32_t feat);   // feat 0..3
 KernelRef grouped_kernel_bf16_hi(int32_t feat);   // feat 4..7
+KernelRef grouped_kernel_bf16_wide(int32_t feat); // FEAT_WIDE, with or without FEAT_MFMA
 
 // Enqueue the gather kernel of a plan dtype.
 void launch_pack(bsc_dtype dt, dim3 grid, hipStream_t s, const PArgs &pa);

@@ -78,6 +78,7 @@ void write_options(KeyWriter &w, const bsc_options &o) {
     w.put(o.tile_gflops);
     w.put(o.split_k);
     w.put(o.tile_rows);
+    w.put(o.tile_cols);
 }
 
 }  // namespace

@@ -737,6 +737,10 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         p.n_counters = 0;
         p.part_elems = 0;
         p.split_tiles = 0;
+        // Direct-to-LDS bf16 tiles of this plan: the 256 x 128 tile, two workgroups
+        // per CU, or the wide tile, one workgroup per CU with the whole LDS
+        // (tile_cols option; 0 = the engine's choice).
+        const bool wide = !per_sector && p.dtype == BSC_BF16_F32 && p.opt.tile_cols == TILE_WIDE;
         // tile class per group: matrix-core tiles where the group is more than a
         // single instruction's worth of work, vector-ALU tiles for the tiny tail
         auto class_of = [&](const DGroup &g) -> int32_t {
@@ -765,8 +769,8 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                     const DView &c = p.cpieces[(size_t)g.cp0];
                     const bool single = r.nap == 1 && r.nbp == 1 && c.ia == 1 && c.ib == 1 &&
                                         p.apieces[(size_t)r.ap0].ia == 1 && p.bpieces[(size_t)r.bp0].ia == 1;
-                    if (single && (r.flags & R_A_VEC) && (r.flags & R_B_VECN)) return T_MFMA_FAST_N;
-                    if (single && (r.flags & R_A_VEC) && (r.flags & R_B_VECK)) return T_MFMA_FAST_K;
+                    if (single && (r.flags & R_A_VEC) && (r.flags & R_B_VECN)) return wide ? T_MFMA_WIDE_N : T_MFMA_FAST_N;
+                    if (single && (r.flags & R_A_VEC) && (r.flags & R_B_VECK)) return wide ? T_MFMA_WIDE_K : T_MFMA_FAST_K;
                 }
                 return T_MFMA;
             }
@@ -888,16 +892,18 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         // descriptor with 32-bit byte offsets: its range must stay below 2 GiB
         // (else the tile runs on the general matrix-core tile).
         auto fast_in_range = [&](int32_t cls, const DFast &f) -> bool {
-            if (cls != T_MFMA_FAST_N && cls != T_MFMA_FAST_K) return true;
+            if (!is_direct(cls)) return true;
             const double lim = 2147483647.0;
+            const double bn = is_wide(cls) ? TILE_WIDE : TILE_MFMA;   // B row extent an N-contiguous copy reads
             const double a = 2.0 * ((double)(f.mlen - 1) * (double)f.a_rs + f.K) + 16;
-            const double b = cls == T_MFMA_FAST_N ? 2.0 * ((double)(f.K - 1) * (double)f.b_ks + TILE_MFMA) + 16
-                                                  : 2.0 * ((double)(f.nlen - 1) * (double)f.b_ns + f.K) + 16;
+            const double b = (cls == T_MFMA_FAST_N || cls == T_MFMA_WIDE_N)
+                                 ? 2.0 * ((double)(f.K - 1) * (double)f.b_ks + bn) + 16
+                                 : 2.0 * ((double)(f.nlen - 1) * (double)f.b_ns + f.K) + 16;
             return f.a_rs >= 0 && f.b_ks >= 0 && f.b_ns >= 0 && a < lim && b < lim;
         };
         // relative throughput of a tile class (used only to order work longest-first)
         auto rate_of = [&](int32_t cls) {
-            if (cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) return 48.0;
+            if (is_direct(cls)) return 48.0;
             if (cls == T_MFMA || cls == T_MFMA_DENSE) return p.dtype == BSC_BF16_F32 ? 16.0 : 4.0;
             return 1.0;
         };
@@ -918,13 +924,15 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             for (int32_t gi = 0; gi < p.n_work_groups; ++gi) {
                 const DGroup &g = p.groups[(size_t)gi];
                 const int32_t cls = class_of(g);
-                if (cls != T_MFMA_FAST_N && cls != T_MFMA_FAST_K) continue;
-                const double tiles = (double)((g.M + TILE_MFMA_DENSE_M - 1) / TILE_MFMA_DENSE_M) *
-                                     (double)((g.N + TILE_MFMA - 1) / TILE_MFMA);
+                if (!is_direct(cls)) continue;
+                int32_t TM = 0, TN = 0;
+                tile_extents(p.dtype, cls, g.M, g.N, TM, TN);
+                const double tiles = (double)((g.M + TM - 1) / TM) * (double)((g.N + TN - 1) / TN);
                 fast_tiles += tiles;
                 total += tiles * (double)((g.K + SPLIT_CHUNK - 1) / SPLIT_CHUNK);
             }
-            fast_share = total / CONCURRENT_TILES;
+            // tiles in flight at once: two per CU, or one per CU for the wide tile
+            fast_share = total / (wide ? CONCURRENT_TILES / 2 : CONCURRENT_TILES);
         }
         int64_t split_target = 0;   // most chunks per slice; 0: no split
         if (!per_sector && p.dtype == BSC_BF16_F32 && p.opt.split_k >= 0)
@@ -964,19 +972,22 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                 for (int32_t n0 = 0; n0 < g.N; n0 += TN) {
                     const int32_t ml = std::min(TM, g.M - m0), nl = std::min(TN, g.N - n0);
                     DFast f{};
-                    if ((cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K || cls == T_MFMA) &&
+                    if ((is_direct(cls) || cls == T_MFMA) &&
                         dense_record(g, gi, m0, ml, n0, nl, f) && fast_in_range(cls, f)) {
                         // bf16 direct-to-LDS tiles always qualify; fp32 / fp64 tiles that do
                         // become record-addressed dense tiles
                         const int32_t c2 = cls == T_MFMA ? (p.dtype == BSC_BF16_F32 ? T_MFMA : T_MFMA_DENSE) : cls;
-                        const int32_t S = (c2 == T_MFMA_FAST_N || c2 == T_MFMA_FAST_K) ? slices_of(f.K) : 1;
+                        const int32_t S = is_direct(c2) ? slices_of(f.K) : 1;
                         if (S > 1) {
                             // K-slices of SPLIT_CHUNK multiples (only the last may end in a partial chunk)
                             const int32_t chunks = (f.K + SPLIT_CHUNK - 1) / SPLIT_CHUNK;
                             const int32_t per = (chunks + S - 1) / S;
                             const int32_t counter = p.n_counters++;
                             const int64_t part = p.part_elems;
-                            p.part_elems += (int64_t)S * TILE_MFMA_DENSE_M * TILE_MFMA;
+                            // partial tiles of the class's full tile size (the kernel's slice stride)
+                            int32_t PTM = 0, PTN = 0;
+                            tile_extents(p.dtype, c2, g.M, g.N, PTM, PTN);
+                            p.part_elems += (int64_t)S * PTM * PTN;
                             p.split_tiles++;
                             for (int32_t sl = 0; sl < S; ++sl) {
                                 DFast fs = f;
@@ -1006,8 +1017,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                         }
                     } else {
                         // a direct-to-LDS tile without a record or beyond the descriptor range runs on the general tile
-                        const bool fastc = cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K;
-                        out.push_back({fastc ? T_MFMA : cls, gi, m0, n0});
+                        out.push_back({is_direct(cls) ? T_MFMA : cls, gi, m0, n0});
                     }
                     if (cost) {
                         double ml = std::min(TM, g.M - m0), nl = std::min(TN, g.N - n0);
@@ -1079,7 +1089,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                 std::vector<size_t> &v = q[(size_t)x];
                 std::stable_sort(v.begin(), v.end(), [&](size_t a, size_t b) { return cost[a] > cost[b]; });
                 std::vector<size_t> &s = slots[(size_t)x];
-                if (v.size() <= CUX) {
+                if (v.size() <= CUX || wide) {   // wide tiles: one workgroup per CU, plain longest-first
                     s = v;
                 } else {
                     s.assign(v.begin(), v.begin() + CUX);
@@ -1167,7 +1177,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         p.features = 0;
         for (auto &t : p.tasks) {
             if (t.cls == T_NOP) continue;
-            const int32_t slot = t.cls == T_MFMA_FAST_K ? T_MFMA_FAST_N
+            const int32_t slot = (t.cls == T_MFMA_FAST_K || is_wide(t.cls)) ? T_MFMA_FAST_N
                                  : (t.cls == T_SKINNY_M || t.cls == T_SKINNY_N || t.cls == T_SKINNY_DENSE_M ||
                                     t.cls == T_SKINNY_DENSE_N) ? 5
                                  : t.cls == T_MFMA_DENSE ? T_MFMA : t.cls;
@@ -1175,6 +1185,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             if (t.cls == T_MFMA || t.cls == T_MFMA_DENSE) p.features |= FEAT_MFMA;
             if (t.cls == T_MFMA_FAST_N) p.features |= FEAT_FAST_N;
             if (t.cls == T_MFMA_FAST_K) p.features |= FEAT_FAST_K;
+            if (is_wide(t.cls)) p.features |= FEAT_WIDE;
         }
         s.launches_per_contract = (int64_t)p.launches.size() + (p.packs.empty() ? 0 : 1);
         s.launches_per_sector = s.triples + (zero_c.empty() ? 0 : 1);

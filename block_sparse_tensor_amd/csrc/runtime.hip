@@ -22,7 +22,9 @@ static bsc_status hip_fail(hipError_t e, const char *what) {
 // when an operand base is not 16-byte aligned the direct-to-LDS tiles fall back
 // to the general matrix-core tile (task class T_MFMA_FAST_* is accepted there).
 static KernelRef pick_bf16(int32_t feat, bool vec) {
-    if (!vec && (feat & (FEAT_FAST_N | FEAT_FAST_K))) feat = (feat & ~(FEAT_FAST_N | FEAT_FAST_K)) | FEAT_MFMA;
+    constexpr int32_t DIRECT = FEAT_FAST_N | FEAT_FAST_K | FEAT_WIDE;
+    if (!vec && (feat & DIRECT)) feat = (feat & ~DIRECT) | FEAT_MFMA;
+    if (feat & FEAT_WIDE) return grouped_kernel_bf16_wide(feat);
     return feat < 4 ? grouped_kernel_bf16_lo(feat) : grouped_kernel_bf16_hi(feat);
 }
 

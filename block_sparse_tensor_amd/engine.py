@@ -88,7 +88,7 @@ def _stream_handle(stream):
 
 
 def _plan_args(con, dtype, axis, keep, launch_mode="grouped", layout="auto", accumulate=False, grid_limit=0,
-               t_launch_us=0.0, t_seg_us=0.0, pack_gbps=0.0, tile_gflops=0.0, split_k=0, tile_rows=0):
+               t_launch_us=0.0, t_seg_us=0.0, pack_gbps=0.0, tile_gflops=0.0, split_k=0, tile_rows=0, tile_cols=0):
     """bsc_plan's arguments (without the output handle) as ctypes values."""
     L = _capi.lib()
     m, k, n = _index(con.m, keep), _index(con.k, keep), _index(con.n, keep)
@@ -102,6 +102,7 @@ def _plan_args(con, dtype, axis, keep, launch_mode="grouped", layout="auto", acc
     opt.t_launch_us, opt.t_seg_us, opt.pack_gbps, opt.tile_gflops = t_launch_us, t_seg_us, pack_gbps, tile_gflops
     opt.split_k = int(split_k)
     opt.tile_rows = int(tile_rows)
+    opt.tile_cols = int(tile_cols)
     keep.arrays.extend([m, k, n, A, B, C, opt])
     return (byref(m), byref(k), byref(n), byref(A), byref(B), byref(C), DTYPES[dtype], AXES[axis], byref(opt))
 
@@ -136,13 +137,13 @@ class Plan:
     def __init__(self, con, dtype: str = None, axis: str = "auto", launch_mode: str = "grouped",
                  layout: str = "auto", accumulate: bool = False, grid_limit: int = 0,
                  t_launch_us: float = 0.0, t_seg_us: float = 0.0, pack_gbps: float = 0.0, tile_gflops: float = 0.0,
-                 split_k: int = 0, tile_rows: int = 0, cache: "PlanCache" = None):
+                 split_k: int = 0, tile_rows: int = 0, tile_cols: int = 0, cache: "PlanCache" = None):
         L = _capi.lib()
         self.dtype = dtype or con.dtype
         keep = _Keep()
         args = _plan_args(con, self.dtype, axis, keep, launch_mode=launch_mode, layout=layout, accumulate=accumulate,
                           grid_limit=grid_limit, t_launch_us=t_launch_us, t_seg_us=t_seg_us, pack_gbps=pack_gbps,
-                          tile_gflops=tile_gflops, split_k=split_k, tile_rows=tile_rows)
+                          tile_gflops=tile_gflops, split_k=split_k, tile_rows=tile_rows, tile_cols=tile_cols)
         h = c_void_p()
         if cache is None:
             _check(L.bsc_plan(*args, byref(h)))

@@ -25,13 +25,21 @@ R_A_WS, R_B_WS = 128, 256          # run reads A / B from the pack workspace
 F_A_WS, F_B_WS = 4, 8              # dense record reads A / B from the pack workspace
 G_C_ALONG_N, G_ACCUMULATE = 1, 2
 T_GENERIC, T_MFMA, T_TAIL, T_ZERO = 0, 1, 2, 3
-TILE = {T_GENERIC: (64, 64), T_ZERO: (64, 64), T_MFMA: (128, 128), 4: (256, 128), 5: (256, 128)}
+TILE = {T_GENERIC: (64, 64), T_ZERO: (64, 64), T_MFMA: (128, 128), 4: (256, 128), 5: (256, 128),
+        12: (256, 256), 13: (256, 256)}
 TILE_MFMA_F = (64, 64)   # fp32 / fp64 matrix-core tile
 
 assert DVIEW.itemsize == 56 and DGROUP.itemsize == 32 and DRUN.itemsize == 32 and DTASK.itemsize == 16
 assert DFAST.itemsize == 112 and DPACK.itemsize == 80
-SPLIT_TILE = 256 * 128   # fp32 elements of one K-slice partial tile
+SPLIT_TILE = 256 * 128   # fp32 elements of one K-slice partial tile of the 256 x 128 tile
 T_DENSE_N, T_DENSE_K = 4, 5
+T_WIDE_N, T_WIDE_K = 12, 13       # wide tile (one workgroup per CU): 256 x 256, 128 x 64 waves at <= 128 columns
+T_DIRECT = (T_DENSE_N, T_DENSE_K, T_WIDE_N, T_WIDE_K)
+
+
+def split_tile_elems(cls, nlen):
+    """fp32 elements the kernel strides per K-slice partial tile."""
+    return 256 * 256 if cls in (T_WIDE_N, T_WIDE_K) and nlen > 128 else SPLIT_TILE
 T_MFMA_DENSE = 9                  # fp32 / fp64 record-addressed matrix-core tile
 T_SKINNY_DENSE = (10, 11)         # record-addressed skinny items (long axis M / N)
 T_SKINNY_M, T_SKINNY_N = 7, 8    # long axis M (at most 16 columns) / long axis N (at most 16 rows)
@@ -113,17 +121,19 @@ def replay(plan, con, a, b, c0, accumulate=False):
     for t in tasks:
         if t["cls"] == 6:      # no-op placeholder
             continue
-        if t["cls"] in (T_DENSE_N, T_DENSE_K, T_MFMA_DENSE) + T_SKINNY_DENSE:
+        if t["cls"] in T_DIRECT + (T_MFMA_DENSE,) + T_SKINNY_DENSE:
             # dense tile: bases and strides only (the kernel's addressing)
             f = dense[t["group"]]
             i = np.arange(f["mlen"])[:, None]
             j = np.arange(f["nlen"])[None, :]
             k = np.arange(f["K"])
-            if t["cls"] == T_DENSE_N:
+            if t["cls"] in (T_DENSE_N, T_WIDE_N):
                 assert f["b_ns"] == 1 or f["nlen"] == 1
-            if t["cls"] in (T_DENSE_N, T_DENSE_K):
+            if t["cls"] in T_DIRECT:
                 assert f["a_ks"] == 1 or f["K"] == 1
-            if t["cls"] == T_DENSE_K:
+                tm, tn = TILE[int(t["cls"])]
+                assert 1 <= f["mlen"] <= tm and 1 <= f["nlen"] <= tn
+            if t["cls"] in (T_DENSE_K, T_WIDE_K):
                 assert f["b_ks"] == 1 or f["K"] == 1
             aad = f["a_base"] + i * f["a_rs"] + k[None, :] * f["a_ks"]
             bad = f["b_base"] + k[:, None] * f["b_ks"] + j * f["b_ns"]
@@ -138,11 +148,12 @@ def replay(plan, con, a, b, c0, accumulate=False):
             acc = abuf[aad] @ bbuf[bad]
             if f["nsplit"] > 1:
                 # K-slice of a split tile: its partial waits for the other slices
-                assert t["cls"] in (T_DENSE_N, T_DENSE_K) and 0 <= f["split"] < f["nsplit"]
+                assert t["cls"] in T_DIRECT and 0 <= f["split"] < f["nsplit"]
                 assert 0 <= f["counter"] < info["n_counters"]
-                assert 0 <= f["part"] and f["part"] + f["nsplit"] * SPLIT_TILE <= info["partial_elems"]
+                pt = split_tile_elems(int(t["cls"]), int(f["nlen"]))
+                assert 0 <= f["part"] and f["part"] + f["nsplit"] * pt <= info["partial_elems"]
                 slot = splits.setdefault(int(f["counter"]), {"n": int(f["nsplit"]), "part": int(f["part"]),
-                                                             "cad": cad, "f": f, "p": {}})
+                                                             "cad": cad, "f": f, "p": {}, "pt": pt})
                 assert slot["n"] == f["nsplit"] and slot["part"] == f["part"] and np.array_equal(slot["cad"], cad)
                 assert int(f["split"]) not in slot["p"], "a K-slice appears twice"
                 slot["p"][int(f["split"])] = (acc, aad[0, :], int(f["K"]))
@@ -200,7 +211,7 @@ def replay(plan, con, a, b, c0, accumulate=False):
         krow = np.concatenate([slot["p"][s][1] for s in range(n)])   # A addresses along k of the first row
         assert len(krow) == len(np.unique(krow)) and np.all(np.diff(krow) == f["a_ks"])
         assert all(slot["p"][s][2] % 32 == 0 for s in range(n - 1)), "only the last slice may end in a partial chunk"
-        parts_used[slot["part"]:slot["part"] + n * SPLIT_TILE] += 1
+        parts_used[slot["part"]:slot["part"] + n * slot["pt"]] += 1
         acc = slot["p"][0][0]
         for s in range(1, n):
             acc = acc + slot["p"][s][0]
@@ -448,3 +459,47 @@ def test_replay_pack_natural_chain(layout):
         got, written = replay(plan, st.con, bufs[st.a_buf], bufs[st.b_buf], np.zeros(ch.sizes[st.c_buf]))
         np.testing.assert_allclose(got, ref[st.c_buf], rtol=1e-12, atol=1e-12)
         bufs[st.c_buf] = got
+
+
+def _wide_tasks(plan):
+    _, _, _, _, _, _, tasks, _ = decode(plan)
+    return tasks[np.isin(tasks["cls"], (T_WIDE_N, T_WIDE_K))]
+
+
+@pytest.mark.parametrize("la", [8])
+def test_replay_bf16_wide_tiles(la):
+    """The bf16 block-diagonal workload on the wide tile (tile_cols=256): every
+    direct-to-LDS group takes wide tiles of at most 256 x 256, replayed exactly."""
+    prob = C.blockdiag_bf16(ld_align=la, align=la)
+    con = prob.con
+    plan = bst.Plan(con, tile_cols=256)
+    wt = _wide_tasks(plan)
+    assert len(wt) > 0 and plan.stats()["launches_per_contract"] == 1
+    got, written = replay(plan, con, prob.a, prob.b, np.zeros(con.C.buffer_elems))
+    ref = oracle.contract(con, prob.a, prob.b, np.zeros(con.C.buffer_elems), check=False)
+    assert np.linalg.norm(got - ref) <= 1e-12 * np.linalg.norm(ref)
+
+
+@pytest.mark.parametrize("shape", [(256, 1024, 256), (300, 600, 200), (100, 640, 152), (520, 1000, 260),
+                                   (64, 1030, 70), (33, 40, 24), (257, 96, 257)])
+@pytest.mark.parametrize("brow", [True, False])
+@pytest.mark.parametrize("split_k", [-1, 3])
+def test_replay_wide_single(shape, brow, split_k):
+    """Single aligned GEMM blocks on the wide tile, both B orientations, with
+    and without K-slices (partials strided by the kernel's tile size)."""
+    M, K, N = shape
+    con, a, b = _dense_single(11 + M + N, M, K, N, brow)
+    plan = bst.Plan(con, tile_cols=256, split_k=split_k)
+    wt = _wide_tasks(plan)
+    assert len(wt) == plan.stats()["items"]
+    if split_k > 0 and K > 3 * 32:
+        assert plan.stats()["split_tiles"] > 0
+    c0 = np.full(con.C.buffer_elems, 0.5)
+    got, written = replay(plan, con, a, b, c0)
+    ref = oracle.contract(con, a, b, c0)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_tile_cols_option_checked():
+    with pytest.raises(bst.BscError):
+        bst.Plan(_dense_con(64, 64, 64, True), tile_cols=192)

@@ -59,7 +59,7 @@ class BscWorklistInfo(ctypes.Structure):
                                         "off_cpieces", "off_tasks", "off_dense", "n_packs", "n_pack_tasks",
                                         "off_packs", "off_pack_tasks", "off_workspace", "workspace_elems",
                                         "bytes", "n_launches", "n_counters", "off_counters",
-                                        "off_partials", "partial_elems")]
+                                        "off_partials", "partial_elems", "n_tail", "off_tail")]
 
 
 _lib = None

@@ -162,6 +162,8 @@ bsc_status bsc_plan_worklist(bsc_plan_t plan, bsc_worklist_info *info, void *ima
     info->off_counters = (int64_t)p->off_cnt;
     info->off_partials = (int64_t)p->off_part;
     info->partial_elems = p->part_elems;
+    info->n_tail = (int64_t)p->tail.size();
+    info->off_tail = (int64_t)p->off_tail;
     if (image) {
         if (bytes < p->image.size()) {
             set_error("bsc_plan_worklist: image buffer too small");

@@ -195,6 +195,28 @@ constexpr bool has_record(int32_t cls) {
 constexpr bool is_mfma(int32_t cls) { return cls == T_MFMA || cls == T_MFMA_DENSE || is_direct(cls); }
 constexpr int TILE_SKINNY_SHORT = 16;   // largest short extent of a skinny group
 
+// Tail bundles (T_TAIL): up to four whole tiny groups per workgroup, one per
+// wave.  A tail group is one run of single views with near-zero flops
+// (2 M N K <= TAIL_MAX_FLOPS), at most TAIL_MAX_OUT outputs (TAIL_PER_LANE per
+// lane), at most TAIL_MAX_K contracted indices and at most TAIL_LANE_WORK
+// multiply-adds per lane (outputs per lane x K / lanes per output); each wave
+// stages its group's operands through TAIL_STAGE elements of LDS (accumulation
+// type) in K-chunks, addressed through the group's DFast record (bases and
+// strides of A, B and C, nsplit = 1).
+constexpr int TAIL_MAX_OUT = 256;
+constexpr int TAIL_PER_LANE = TAIL_MAX_OUT / 64;
+constexpr int TAIL_MAX_K = 512;
+constexpr int TAIL_LANE_WORK = 64;
+constexpr int TAIL_STAGE = 1024;
+constexpr int TAIL_BUNDLE = 4;
+constexpr int64_t TAIL_MAX_FLOPS = 1024;
+// lanes per output of a tail group with mn outputs (a power of two, lanes * mn <= 64)
+constexpr int32_t tail_lanes_host(int32_t mn) {
+    int32_t p = 1;
+    while (2 * p * mn <= 64) p *= 2;
+    return p;
+}
+
 // Skinny tile extent along its long axis: 256 threads x R lines, where R times
 // the short extent rounded up to 4, 8 or 16 is the accumulator budget per
 // thread (32).
@@ -247,6 +269,7 @@ struct Plan {
     std::vector<DView> apieces, bpieces, cpieces;
     std::vector<DTask> tasks;
     std::vector<DFast> fast;      // records of dense matrix-core tiles
+    std::vector<DFast> tail;      // tail entries: record of each wave's group (bundles consecutive)
     std::vector<DPack> packs;     // gathers into the pack workspace
     std::vector<DTask> pack_tasks;   // 64 x 64 pieces of the gathers (group = gather index)
     int64_t ws_elems = 0;         // pack workspace size (operand elements)
@@ -258,7 +281,7 @@ struct Plan {
     // device binding
     void *dev = nullptr;
     size_t dev_bytes = 0;
-    size_t off_groups = 0, off_runs = 0, off_ap = 0, off_bp = 0, off_cp = 0, off_tasks = 0, off_fast = 0;
+    size_t off_groups = 0, off_runs = 0, off_ap = 0, off_bp = 0, off_cp = 0, off_tasks = 0, off_fast = 0, off_tail = 0;
     size_t off_packs = 0, off_ptasks = 0, off_ws = 0;   // gathers, their tasks, the workspace
     size_t off_cnt = 0, off_part = 0;                    // K-split counters (in the image), partials
     std::vector<unsigned char> image;   // host copy of the device tables

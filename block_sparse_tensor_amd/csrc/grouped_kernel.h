@@ -20,6 +20,7 @@
 #include "kernels_mfma_bf16_wide.h"
 #include "kernels_mfma_f.h"
 #include "kernels_skinny.h"
+#include "kernels_tail.h"
 #include "launch.h"
 
 namespace bsc {
@@ -38,6 +39,7 @@ template <typename TA, typename ACC, int32_t FEAT>
 union TileSmem {
     GenericSmem<ACC> g;
     SkinnySmem<ACC> s;
+    TailSmem<ACC> t;
     typename std::conditional<(FEAT & FEAT_MFMA) != 0, typename MfmaSmemOf<TA>::type, char>::type m;
     typename std::conditional<(FEAT & (FEAT_FAST_N | FEAT_FAST_K)) != 0, FastSmemBf16, char>::type f;
     typename std::conditional<(FEAT & FEAT_WIDE) != 0, WideSmemBf16, char>::type x;
@@ -53,6 +55,10 @@ __device__ __forceinline__ void grouped_body(const KArgs &ka) {
         const int32_t ti = ka.task0 + t;
         const DTask task = ka.tasks[ti];
         if (task.cls == T_NOP) continue;
+        if (task.cls == T_TAIL) {
+            tail_bundle<TA, TC, ACC>(ka, task, sm.t);
+            continue;
+        }
         if (task.cls == T_SKINNY_DENSE_M) {
             skinny_dense<TA, TC, ACC, true>(ka, ka.fast[ti], sm.s);
             continue;

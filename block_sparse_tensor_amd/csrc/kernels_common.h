@@ -18,6 +18,7 @@ struct KArgs {
     const DRun *runs;
     const DView *ap, *bp, *cp;
     const DFast *fast;
+    const DFast *tail;      // tail entries (record of each wave's group in a T_TAIL bundle)
     const void *A, *B;
     void *C;
     const void *W;          // pack workspace (operands of runs flagged R_A_WS / R_B_WS)

@@ -733,6 +733,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         // ---- tasks ------------------------------------------------------------------
         p.tasks.clear();
         p.fast.clear();
+        p.tail.clear();
         p.launches.clear();
         p.n_counters = 0;
         p.part_elems = 0;
@@ -961,9 +962,32 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             const int64_t per = (chunks + S - 1) / S;   // chunks per slice; the last slice takes the rest
             return (int32_t)((chunks + per - 1) / per);
         };
+        // Tail groups: near-zero-flop groups (2 M N K <= TAIL_MAX_FLOPS) that are
+        // one run of single views, so a single wave computes the whole group from
+        // its record (bases and strides) as part of a tail bundle.  Measured on
+        // MI355X: tail bundles for every group of at most 256 outputs (records or
+        // piece walks) made the U(1) update's W stage slower than its skinny
+        // streams (28.0 -> 36.8 us); for near-zero groups the skinny stream's
+        // 256-thread workgroup is mostly idle.
+        std::vector<std::pair<int32_t, DFast>> tail_groups;
+        auto tail_of = [&](const DGroup &g, int32_t gi, DFast &f) -> bool {
+            if (per_sector || g.nrun != 1 || 2 * (int64_t)g.M * g.N * g.K > TAIL_MAX_FLOPS) return false;
+            if ((int64_t)g.M * g.N > TAIL_MAX_OUT || g.K > TAIL_MAX_K || g.M + g.N > TAIL_STAGE) return false;
+            const int32_t mn = g.M * g.N, lanes = tail_lanes_host(mn);
+            const int32_t outs = (mn + 64 / lanes - 1) / (64 / lanes);   // outputs per lane
+            if ((int64_t)outs * ((g.K + lanes - 1) / lanes) > TAIL_LANE_WORK) return false;
+            return dense_record(g, gi, 0, g.M, 0, g.N, f);
+        };
         auto tiles_of = [&](int32_t gi, std::vector<DTask> &out, std::vector<double> *cost) {
             const DGroup &g = p.groups[(size_t)gi];
             const int32_t cls = class_of(g);
+            {
+                DFast f{};
+                if (cls != T_ZERO && tail_of(g, gi, f)) {
+                    tail_groups.push_back({gi, f});
+                    return;
+                }
+            }
             int32_t TM = 0, TN = 0;
             tile_extents(p.dtype, cls, g.M, g.N, TM, TN);
             if ((cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) && half_rows(g)) TM = TILE_MFMA_DENSE_M / 2;
@@ -1048,7 +1072,27 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             for (int32_t gi = 0; gi < (int32_t)p.groups.size(); ++gi) {
                 size_t a = tk.size();
                 tiles_of(gi, tk, &cost);
-                span.push_back({a, tk.size()});
+                if (tk.size() > a) span.push_back({a, tk.size()});
+            }
+            // Tail bundles: tiny groups sorted by work, TAIL_BUNDLE consecutive ones
+            // per workgroup (one per wave), so the waves of a bundle finish together.
+            {
+                auto work = [&](int32_t gi) {
+                    const DGroup &g = p.groups[(size_t)gi];
+                    return 2.0 * g.M * g.N * g.K + 4.0 * g.M * g.N + 2.0e4 * g.nrun;
+                };
+                std::stable_sort(tail_groups.begin(), tail_groups.end(),
+                                 [&](const std::pair<int32_t, DFast> &x, const std::pair<int32_t, DFast> &y) {
+                                     return work(x.first) > work(y.first);
+                                 });
+                for (size_t b = 0; b < tail_groups.size(); b += TAIL_BUNDLE) {
+                    const size_t e = std::min(tail_groups.size(), b + TAIL_BUNDLE);
+                    const size_t a = tk.size();
+                    tk.push_back({T_TAIL, (int32_t)p.tail.size(), (int32_t)(e - b), 0});
+                    cost.push_back(work(tail_groups[b].first));
+                    for (size_t i = b; i < e; ++i) p.tail.push_back(tail_groups[i].second);
+                    span.push_back({a, tk.size()});
+                }
             }
             double total = 0;
             for (double c : cost) total += c;
@@ -1141,6 +1185,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         p.off_cp = off;     off = align(off + p.cpieces.size() * sizeof(DView));
         p.off_tasks = off;  off = align(off + p.tasks.size() * sizeof(DTask));
         p.off_fast = off;   off = align(off + p.fast.size() * sizeof(DFast));
+        p.off_tail = off;   off = align(off + p.tail.size() * sizeof(DFast));
         p.off_packs = off;  off = align(off + p.packs.size() * sizeof(DPack));
         p.off_ptasks = off; off = align(off + p.pack_tasks.size() * sizeof(DTask));
         p.off_cnt = off;    off = align(off + (size_t)p.n_counters * sizeof(int32_t));   // zero in the image
@@ -1156,6 +1201,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         put(p.off_cp, p.cpieces.data(), p.cpieces.size() * sizeof(DView));
         put(p.off_tasks, p.tasks.data(), p.tasks.size() * sizeof(DTask));
         put(p.off_fast, p.fast.data(), p.fast.size() * sizeof(DFast));
+        put(p.off_tail, p.tail.data(), p.tail.size() * sizeof(DFast));
         put(p.off_packs, p.packs.data(), p.packs.size() * sizeof(DPack));
         put(p.off_ptasks, p.pack_tasks.data(), p.pack_tasks.size() * sizeof(DTask));
 

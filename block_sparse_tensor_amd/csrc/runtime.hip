@@ -92,6 +92,7 @@ static bsc_status contract_on(Plan *p, const void *region, int32_t cu_count, con
     ka.cp = reinterpret_cast<const DView *>(base + p->off_cp);
     ka.tasks = reinterpret_cast<const DTask *>(base + p->off_tasks);
     ka.fast = reinterpret_cast<const DFast *>(base + p->off_fast);
+    ka.tail = reinterpret_cast<const DFast *>(base + p->off_tail);
     ka.A = A;
     ka.B = B;
     ka.C = C;

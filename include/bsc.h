@@ -262,6 +262,7 @@ typedef struct {
     int64_t n_launches;      /* launches per contraction */
     int64_t n_counters, off_counters;   /* K-split arrival counters (int32, in the image, zero) */
     int64_t off_partials, partial_elems; /* K-split partial tiles (fp32, after the workspace) */
+    int64_t n_tail, off_tail;            /* tail entries (one dense-tile record per wave of the tail bundles) */
 } bsc_worklist_info;
 
 /* Fill *info and, if image != NULL and bytes >= info->bytes, copy the host

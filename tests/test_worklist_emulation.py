@@ -61,6 +61,18 @@ def decode(plan):
             tab(DFAST, info["n_dense"], info["off_dense"]))
 
 
+def decode_tail(plan):
+    info, img = plan.worklist()
+    return np.frombuffer(img, dtype=DFAST, count=info["n_tail"], offset=info["off_tail"])
+
+
+def tail_lanes(mn):
+    p = 1
+    while 2 * p * mn <= 64:
+        p *= 2
+    return p
+
+
 def decode_packs(plan):
     info, img = plan.worklist()
     tab = lambda dt, n, off: np.frombuffer(img, dtype=dt, count=n, offset=off)
@@ -118,7 +130,44 @@ def replay(plan, con, a, b, c0, accumulate=False):
     a64, b64 = np.asarray(a, np.float64), np.asarray(b, np.float64)
     ws, ws_written = replay_packs(plan, con, a64, b64)
     splits = {}   # K-split tiles by counter: the partials of their slices
+    tail = decode_tail(plan)
+    # a tail bundle: entries group .. group + m0 - 1 of the tail table, one whole group per wave
+    expanded = []
     for t in tasks:
+        if t["cls"] == T_TAIL:
+            assert 1 <= t["m0"] <= 4 and 0 <= t["group"] and t["group"] + t["m0"] <= len(tail)
+            for e in range(int(t["group"]), int(t["group"] + t["m0"])):
+                f = tail[e]
+                mn = int(f["mlen"]) * int(f["nlen"])
+                lanes = tail_lanes(mn)
+                assert mn <= 256 and f["K"] <= 512 and f["mlen"] + f["nlen"] <= 1024
+                assert -(-mn // (64 // lanes)) * -(-int(f["K"]) // lanes) <= 64, "tail lane work"
+                # record-addressed tail group: bases and strides, the whole group at once
+                assert f["nsplit"] == 1 and 2 * mn * int(f["K"]) <= 1024
+                g = groups[f["group"]]
+                assert g["M"] == f["mlen"] and g["N"] == f["nlen"] and g["K"] == f["K"] and g["nrun"] == 1
+                expanded.append(("tail_dense", f))
+        else:
+            expanded.append(t)
+    for t in expanded:
+        if isinstance(t, tuple):
+            f = t[1]
+            i = np.arange(f["mlen"])[:, None]
+            j = np.arange(f["nlen"])[None, :]
+            k = np.arange(f["K"])
+            aad = f["a_base"] + i * f["a_rs"] + k[None, :] * f["a_ks"]
+            bad = f["b_base"] + k[:, None] * f["b_ks"] + j * f["b_ns"]
+            cad = f["c_base"] + i * f["c_rs"] + j * f["c_cs"]
+            abuf = ws if f["flags"] & F_A_WS else a64
+            bbuf = ws if f["flags"] & F_B_WS else b64
+            for ad, n in ((aad, abuf.size), (bad, bbuf.size), (cad, con.C.buffer_elems)):
+                assert ad.min() >= 0 and ad.max() < n
+            acc = abuf[aad] @ bbuf[bad]
+            if f["flags"] & G_ACCUMULATE:
+                acc = acc + c[cad]
+            c[cad] = acc
+            np.add.at(written, cad.ravel(), 1)
+            continue
         if t["cls"] == 6:      # no-op placeholder
             continue
         if t["cls"] in T_DIRECT + (T_MFMA_DENSE,) + T_SKINNY_DENSE:
@@ -164,7 +213,9 @@ def replay(plan, con, a, b, c0, accumulate=False):
             np.add.at(written, cad.ravel(), 1)
             continue
         g = groups[t["group"]]
-        if t["cls"] == T_SKINNY_M:
+        if t["cls"] == T_TAIL:
+            TM, TN = int(g["M"]), int(g["N"])
+        elif t["cls"] == T_SKINNY_M:
             TM, TN = skinny_long(con.dtype, int(g["N"])), max(1, int(g["N"]))
         elif t["cls"] == T_SKINNY_N:
             TM, TN = max(1, int(g["M"])), skinny_long(con.dtype, int(g["M"]))
@@ -503,3 +554,30 @@ def test_replay_wide_single(shape, brow, split_k):
 def test_tile_cols_option_checked():
     with pytest.raises(bst.BscError):
         bst.Plan(_dense_con(64, 64, 64, True), tile_cols=192)
+
+
+@pytest.mark.parametrize("name", ["ragged_batch", "tiny_u1", "small_chain"])
+def test_tail_bundles_cover_tiny_groups(name):
+    """Tiny groups go to tail bundles (one group per wave, at most four per
+    bundle), every one of them exactly once, and the replay matches the oracle."""
+    if name == "small_chain":
+        ch = C.small_chain(seed=3, layout="natural")
+        cases = [(st.con, None) for st in ch.stages]
+        bufs = oracle.run_chain(ch)
+        cases = [(st.con, (bufs[st.a_buf], bufs[st.b_buf])) for st in ch.stages]
+    else:
+        prob = C.ragged_batch() if name == "ragged_batch" else C.tiny_u1()
+        cases = [(prob.con, (prob.a, prob.b))]
+    seen = 0
+    for con, (a, b) in cases:
+        plan = bst.Plan(con)
+        tasks = decode(plan)[6]
+        tail = decode_tail(plan)
+        n_bundles = int(np.sum(tasks["cls"] == T_TAIL))
+        assert plan.stats()["items_by_class"]["tail"] == n_bundles
+        assert len(tail) == len(np.unique(tail["group"])), "a group in two bundles"
+        seen += len(tail)
+        got, written = replay(plan, con, a, b, np.zeros(con.C.buffer_elems))
+        ref = oracle.contract(con, a, b, np.zeros(con.C.buffer_elems), check=False)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    assert seen > 0

@@ -178,6 +178,20 @@ def parity_vs_oracle(stages, bufs, ref, dtype):
     return {"rel_frobenius": worst, "tol": TOL[dtype], "pass": bool(worst <= TOL[dtype])}
 
 
+def _view_mask(con):
+    """Buffer elements that belong to some C block of `con`."""
+    import numpy as np
+    from workloads.layout import view_addresses
+    mask = np.zeros(con.C.buffer_elems, bool)
+    for i in range(con.C.nblocks):
+        r, c = int(con.C.row_key[i]), int(con.C.col_key[i])
+        ri = 1 if con.m.inner is None else int(con.m.inner[r])
+        ci = 1 if con.n.inner is None else int(con.n.inner[c])
+        mask[view_addresses(con.C.offset[i], con.C.row_stride[i], con.C.col_stride[i], int(con.m.dim[r]),
+                            int(con.n.dim[c]), ri, ci).ravel()] = True
+    return mask
+
+
 def load_workload(name, ld_align=1, relayout=False):
     from workloads import configs as C
     if name == "blockdiag_bf16":
@@ -370,6 +384,64 @@ def main():
         graph = {"ms_per_step": round(gms, 6), "value": round(flops / (gms * 1e-3) / 1e9, 3), "unit": "GFLOP/s",
                  "launches_per_step": 1}
 
+    # --- stages 1 and 2 as one fused launch (bsc_fused): the intermediate never written ---
+    fused = None
+    if multi and dtype in ("f64", "f32"):
+        try:
+            fplan = bst.FusedPlan(stages[0][0], stages[1][0]).bind()
+        except bst.BscError as e:
+            fused = {"skipped": str(e)}
+        else:
+            fbuf = {k: v for k, v in bufs.items()}
+            fbuf[stages[1][3]] = torch.zeros_like(bufs[stages[1][3]])
+
+            def fstep(marks=None):
+                fplan.contract(fbuf[stages[0][1]], fbuf[stages[0][2]], fbuf[stages[1][2]], fbuf[stages[1][3]])
+                if marks is not None:
+                    ev = torch.cuda.Event(enable_timing=True)
+                    ev.record()
+                    marks.append(ev)
+                for p, (_, a, b, c, _) in zip(grouped[2:], stages[2:]):
+                    p.contract(fbuf[a], fbuf[b], fbuf[c])
+                    if marks is not None:
+                        ev = torch.cuda.Event(enable_timing=True)
+                        ev.record()
+                        marks.append(ev)
+            for _ in range(args.warmup):
+                fstep()
+            torch.cuda.synchronize()
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            f0.record()
+            for _ in range(args.steps):
+                fstep()
+            f1.record()
+            torch.cuda.synchronize()
+            fms = f0.elapsed_time(f1) / args.steps
+            fm = [torch.cuda.Event(enable_timing=True)]
+            fm[0].record()
+            for _ in range(args.steps):
+                fstep(fm)
+            torch.cuda.synchronize()
+            nl = len(stages) - 1
+            fstage = [statistics.fmean(fm[j].elapsed_time(fm[j + 1]) for j in range(i, len(fm) - 1, nl))
+                      for i in range(nl)]
+            fs = fplan.stats()
+            # parity of the fused intermediate-free path against the two-stage engine result
+            step(grouped)
+            fstep()
+            torch.cuda.synchronize()
+            ad = torch.from_numpy(np.nonzero(_view_mask(stages[1][0]))[0]).cuda()
+            ref_t2 = bufs[stages[1][3]].index_select(0, ad).double()
+            got_t2 = fbuf[stages[1][3]].index_select(0, ad).double()
+            rel = float((got_t2 - ref_t2).norm() / ref_t2.norm().clamp_min(1e-300))
+            fused = {"ms_per_step": round(fms, 6), "value": round(flops / (fms * 1e-3) / 1e9, 3), "unit": "GFLOP/s",
+                     "stage_kernel_ms": [round(x, 6) for x in fstage],
+                     "fused_kernel_ms_vs_stages_1_2": [round(fstage[0], 6), round(stage_ms[0] + stage_ms[1], 6)],
+                     "fused_flops": fs["useful_flops"], "fused_alg_bytes": fs["alg_bytes"],
+                     "fused_tflops": round(fs["useful_flops"] / (fstage[0] * 1e-3) / 1e12, 4),
+                     "items": fs["items"], "products": fs["channels"], "terms": fs["terms"],
+                     "t2_rel_diff_vs_two_stage": rel, "launches_per_step": len(stages) - 1}
+
     # --- host planning of every stage: fresh, and a plan-cache hit (a site revisited in a sweep) ---
     def plan_all(cache=None):
         t0 = time.perf_counter()
@@ -509,6 +581,8 @@ def main():
     if graph is not None:
         # the stages as one captured graph (bsc_chain): no host gaps between launches
         out["graph_chain"] = graph
+    if fused is not None:
+        out["fused_stage_1_2"] = fused
 
     # --- CPU oracle baseline on the host cores ----------------------------------------
     if not args.no_cpu:

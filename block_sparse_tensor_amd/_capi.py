@@ -21,7 +21,8 @@ EXPORTED = ["bsc_options_default", "bsc_plan", "bsc_plan_device_bytes", "bsc_pla
             "bsc_plan_stats", "bsc_plan_export", "bsc_plan_worklist", "bsc_plan_destroy", "bsc_status_string",
             "bsc_last_error", "bsc_chain_create", "bsc_chain_launch", "bsc_chain_destroy", "bsc_plan_cache_create",
             "bsc_plan_cached", "bsc_plan_cache_stats", "bsc_plan_cache_destroy", "bsc_plan_layout",
-            "bsc_contract_noalloc"]
+            "bsc_contract_noalloc", "bsc_fused_plan", "bsc_fused_device_bytes", "bsc_fused_bind",
+            "bsc_fused_contract", "bsc_fused_stats", "bsc_fused_worklist", "bsc_fused_destroy"]
 
 
 class BscIndex(ctypes.Structure):
@@ -60,6 +61,14 @@ class BscWorklistInfo(ctypes.Structure):
                                         "off_packs", "off_pack_tasks", "off_workspace", "workspace_elems",
                                         "bytes", "n_launches", "n_counters", "off_counters",
                                         "off_partials", "partial_elems", "n_tail", "off_tail")]
+
+
+class BscFusedStats(ctypes.Structure):
+    _fields_ = [(n, c_int64) for n in ("groups", "channels", "outputs", "terms", "items", "launches_per_contract",
+                                        "useful_flops", "stage1_flops", "alg_bytes", "device_bytes",
+                                        "launches_issued", "off_groups", "off_chans", "off_outs", "off_widx",
+                                        "off_tasks", "outs_per_task", "off_parts", "n_parts", "off_pchans",
+                                        "n_pchans")]
 
 
 _lib = None
@@ -115,5 +124,20 @@ def lib():
         L.bsc_plan_layout.argtypes = L.bsc_plan.argtypes[:-1] + [c_int32, c_int64, POINTER(c_int64), POINTER(c_int64),
                                                                 POINTER(c_int64), POINTER(c_int64)]
         L.bsc_plan_layout.restype = c_int32
+        L.bsc_fused_plan.argtypes = ([POINTER(BscIndex)] * 3 + [POINTER(BscOperand)] * 3) * 2 + [
+            c_int32, POINTER(BscOptions), POINTER(c_void_p)]
+        L.bsc_fused_plan.restype = c_int32
+        L.bsc_fused_device_bytes.argtypes = [c_void_p, POINTER(c_size_t)]
+        L.bsc_fused_device_bytes.restype = c_int32
+        L.bsc_fused_bind.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p]
+        L.bsc_fused_bind.restype = c_int32
+        L.bsc_fused_contract.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.bsc_fused_contract.restype = c_int32
+        L.bsc_fused_stats.argtypes = [c_void_p, POINTER(BscFusedStats)]
+        L.bsc_fused_stats.restype = c_int32
+        L.bsc_fused_worklist.argtypes = [c_void_p, c_void_p, c_size_t]
+        L.bsc_fused_worklist.restype = c_int32
+        L.bsc_fused_destroy.argtypes = [c_void_p]
+        L.bsc_fused_destroy.restype = None
         _lib = L
     return _lib

@@ -55,3 +55,21 @@ extern "C" bsc_status bsc_chain_launch(bsc_chain_t, void *) {
 }
 
 extern "C" void bsc_chain_destroy(bsc_chain_t) {}
+
+extern "C" bsc_status bsc_fused_bind(bsc_fused_t plan, void *dev, size_t, void *) {
+    if (!plan || !dev) {
+        set_error("bsc_fused_bind: NULL argument");
+        return BSC_ERR_ARG;
+    }
+    set_error("bsc_fused_bind: host-only planner build has no device runtime");
+    return BSC_ERR_UNSUPPORTED;
+}
+
+extern "C" bsc_status bsc_fused_contract(bsc_fused_t plan, const void *, const void *, const void *, void *, void *) {
+    if (!plan) {
+        set_error("bsc_fused_contract: NULL plan");
+        return BSC_ERR_ARG;
+    }
+    set_error("bsc_fused_contract: host-only planner build has no device runtime");
+    return BSC_ERR_UNSUPPORTED;
+}

@@ -267,6 +267,89 @@ class Plan:
             self._h = None
 
 
+class FusedPlan:
+    """Two contractions planned as one launch (bsc_fused_plan): stage 1
+    C1 = A1 B1 (`con1`), then stage 2 C2 (+)= C1 B2 (`con2`), where stage 2's
+    A operand is C1's blocks with their rows and columns fused into one row
+    index and B2 holds 1 x 1 blocks.  C1 is never formed: contract() reads
+    A1, B1, B2 and writes C2 only."""
+
+    def __init__(self, con1, con2, dtype: str = None, accumulate: bool = False, split: int = 0):
+        L = _capi.lib()
+        self.dtype = dtype or con1.dtype
+        if self.dtype not in ("f64", "f32"):
+            raise BscError(-7, "fused plans take f64 or f32")
+        keep = _Keep()
+        a1 = _plan_args(con1, self.dtype, "auto", keep)
+        a2 = _plan_args(con2, self.dtype, "auto", keep)
+        opt = _capi.BscOptions()
+        L.bsc_options_default(byref(opt))
+        opt.accumulate = int(bool(accumulate))
+        opt.split_k = int(split)   # waves per output tile: 0 automatic (up to 4), 1 never split
+        keep.arrays.append(opt)
+        h = c_void_p()
+        _check(L.bsc_fused_plan(*a1[:6], *a2[:6], DTYPES[self.dtype], byref(opt), byref(h)))
+        self._h = h
+        self.elems = {"A1": int(con1.A.buffer_elems), "B1": int(con1.B.buffer_elems),
+                      "B2": int(con2.B.buffer_elems), "C2": int(con2.C.buffer_elems)}
+        self._dev = None
+
+    def device_bytes(self) -> int:
+        n = c_size_t()
+        _check(_capi.lib().bsc_fused_device_bytes(self._h, byref(n)))
+        return int(n.value)
+
+    def stats(self) -> dict:
+        s = _capi.BscFusedStats()
+        _check(_capi.lib().bsc_fused_stats(self._h, byref(s)))
+        return {name: int(getattr(s, name)) for name, _ in s._fields_}
+
+    def worklist(self):
+        """(stats dict, bytes) of the device image, for host replay."""
+        s = self.stats()
+        buf = ctypes.create_string_buffer(max(1, s["device_bytes"]))
+        _check(_capi.lib().bsc_fused_worklist(self._h, ctypes.cast(buf, c_void_p), c_size_t(s["device_bytes"])))
+        return s, bytes(buf.raw[:s["device_bytes"]])
+
+    def bind(self, device=None, stream=None):
+        """Allocate the work-list region (torch memory) and upload it."""
+        torch = _torch()
+        nbytes = self.device_bytes()
+        dev = torch.empty(nbytes + 256, dtype=torch.uint8, device=device or "cuda")
+        ptr = dev.data_ptr()
+        pad = (-ptr) % 256
+        _check(_capi.lib().bsc_fused_bind(self._h, c_void_p(ptr + pad), c_size_t(nbytes), _stream_handle(stream)))
+        self._dev = dev
+        return self
+
+    def contract(self, A1, B1, B2, C2, stream=None):
+        """Enqueue C2 (+)= (A1 B1) B2 on `stream` (default: torch's current stream)."""
+        if self._dev is None:
+            raise BscError(-8, "plan is not bound (call bind())")
+        torch = _torch()
+        dt = torch.float64 if self.dtype == "f64" else torch.float32
+        for name, t in (("A1", A1), ("B1", B1), ("B2", B2), ("C2", C2)):
+            if not isinstance(t, torch.Tensor) or not t.is_cuda:
+                raise TypeError(f"{name} must be a CUDA/HIP torch tensor")
+            if t.dtype != dt:
+                raise TypeError(f"{name} has dtype {t.dtype}, expected {dt}")
+            if not t.is_contiguous() or t.numel() < self.elems[name]:
+                raise ValueError(f"{name} must be contiguous with at least {self.elems[name]} elements")
+        _check(_capi.lib().bsc_fused_contract(self._h, c_void_p(A1.data_ptr()), c_void_p(B1.data_ptr()),
+                                              c_void_p(B2.data_ptr()), c_void_p(C2.data_ptr()),
+                                              _stream_handle(stream)))
+        return C2
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                _capi.lib().bsc_fused_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+
 class Chain:
     """A fixed sequence of contractions [(plan, A, B, C), ...] captured once
     into a HIP graph and replayed with one launch (bsc_chain_*).  The plans

@@ -364,6 +364,70 @@ bsc_status bsc_chain_create(const bsc_plan_t *plans, const void *const *A, const
 bsc_status bsc_chain_launch(bsc_chain_t chain, void *stream);
 void bsc_chain_destroy(bsc_chain_t chain);
 
+/* Fused two-stage plan (uni20 "block coalescing", Open questions: the
+ * "A.Y accumulate" stage of the R/A/B/C update; the memory-wall argument of
+ * the "Sparse Operator Fusion" glossary page): stage 1 is a block-sparse
+ * contraction C1 = A1 B1 (m1, k1, n1, A1, B1, C1 as for bsc_plan); stage 2
+ * contracts C1's blocks with a matrix B2 whose blocks are all 1 x 1
+ * (C2 = A2 B2), where every stage-2 A block is one stage-1 C block read
+ * through the same buffer with its rows and columns fused into one row index
+ * (outer leg = the stage-1 row, inner leg = the stage-1 column; one column).
+ * In the environment update this is T1 = E^T A followed by T2 = T1 W.
+ *
+ * bsc_fused_plan validates both stages as bsc_plan does, matches every stage-2
+ * A block to the stage-1 C block with the same elements, and plans one
+ * launch that computes C2 directly: each output block of stage-2 row key r,
+ * viewed as an M x N matrix (M, N the outer and inner extents of r), receives
+ * the sum over the stage-1 products A1(m1, a) B1(a, n1) that make up the
+ * stage-2 A blocks (r, k) of row r, each weighted by the B2 element (k, n)
+ * of that output (no term where B2 has no block).  C1 is neither read nor
+ * written.  Overwrite or accumulate per opt->accumulate; opt->split_k bounds
+ * how many waves share one output tile's stage-1 blocks (0: automatic, at
+ * most 4; 1: one wave per tile; negative: BSC_ERR_ARG); other options are
+ * ignored.  Requirements (else BSC_ERR_UNSUPPORTED): dtype BSC_F64 or BSC_F32;
+ * every stage-2 B block and output column of dim 1; stage-1 A, B, C blocks and
+ * the stage-2 output blocks single strided views (as M x N for the outputs);
+ * at most 64 stage-1 blocks per stage-2 row key;
+ * C1's buffer length equal to A2's (else BSC_ERR_ARG).  Any error bsc_plan
+ * reports for either stage is reported here.
+ *
+ * bsc_fused_bind uploads the work list into a caller-owned device region of
+ * bsc_fused_device_bytes (256-byte aligned) on `stream` and waits for it.
+ * bsc_fused_contract enqueues the one launch on `stream`: A1, B1 the stage-1
+ * operand buffers, B2 the scalar matrix's buffer, C2 the output buffer.
+ * Repeats are bit-identical (fixed summation order, no atomics). */
+typedef struct bsc_fused_s *bsc_fused_t;
+typedef struct {
+    int64_t groups;                 /* stage-2 output row keys */
+    int64_t channels;               /* stage-1 block products */
+    int64_t outputs;                /* stage-2 output blocks */
+    int64_t terms;                  /* nonzero (stage-1 block, output) weights */
+    int64_t items;                  /* 16 x 16 output tiles */
+    int64_t launches_per_contract;
+    int64_t useful_flops;           /* stage-1 products (2 M N K each) + weighted adds (2 M N per term) */
+    int64_t stage1_flops;
+    int64_t alg_bytes;              /* stage-1 operands and B2 read once, C2 written once */
+    int64_t device_bytes;
+    int64_t launches_issued;
+    /* byte offsets of the record arrays in the device image (bsc_fused_worklist) */
+    int64_t off_groups, off_chans, off_outs, off_widx, off_tasks;
+    int64_t outs_per_task;          /* outputs one task accumulates (4, 8 or 16) */
+    int64_t off_parts, n_parts;     /* per-wave records, four per workgroup */
+    int64_t off_pchans, n_pchans;   /* the parts' product lists */
+} bsc_fused_summary;
+bsc_status bsc_fused_plan(const bsc_index *m1, const bsc_index *k1, const bsc_index *n1, const bsc_operand *A1,
+                          const bsc_operand *B1, const bsc_operand *C1, const bsc_index *m2, const bsc_index *k2,
+                          const bsc_index *n2, const bsc_operand *A2, const bsc_operand *B2, const bsc_operand *C2,
+                          bsc_dtype dtype, const bsc_options *opt, bsc_fused_t *out);
+bsc_status bsc_fused_device_bytes(bsc_fused_t plan, size_t *bytes);
+bsc_status bsc_fused_bind(bsc_fused_t plan, void *dev, size_t bytes, void *stream);
+bsc_status bsc_fused_contract(bsc_fused_t plan, const void *A1, const void *B1, const void *B2, void *C2, void *stream);
+bsc_status bsc_fused_stats(bsc_fused_t plan, bsc_fused_summary *out);
+/* Copy of the device image bsc_fused_bind uploads (for inspection and host
+ * replay): `bytes` must be at least bsc_fused_device_bytes, else BSC_ERR_ARG. */
+bsc_status bsc_fused_worklist(bsc_fused_t plan, void *buf, size_t bytes);
+void bsc_fused_destroy(bsc_fused_t plan);
+
 const char *bsc_status_string(bsc_status s);
 
 /* Thread-local text of the last error raised on this thread ("" if none). */

@@ -14,7 +14,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HOST_TESTS = ["tests/test_capi_host.py", "tests/test_worklist_emulation.py", "tests/test_plan_cache.py",
-              "tests/test_layouts.py"]
+              "tests/test_layouts.py", "tests/test_fused_host.py"]
 
 
 def _runtime(name):

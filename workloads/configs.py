@@ -529,6 +529,20 @@ def small_chain(seed: int = 7, layout: str = "coop", values: str = "normal", dty
     return rabc_chain(bq, bd, local, mpo, pairs, dtype, rng, layout, values, name=f"small-{layout}-{values}")
 
 
+def neutral_chain(seed: int = 9, dims=(3, 37, 17, 40), layout: str = "natural", values: str = "int",
+                  dtype: str = "f64", d: int = 4) -> Chain:
+    """An environment-update chain whose charges are all zero, so every pair of
+    blocks meets: several products per stage-1 block (one per bond sector),
+    stage-2 rows of d x w stage-1 blocks and up to d x w outputs (w = 5, the
+    U(1) MPO pairs), bond dims across several 16-wide tiles and 32-long chunks."""
+    rng = np.random.default_rng(seed)
+    bq = np.zeros((len(dims), 1), np.int64)
+    local = np.zeros((d, 1), np.int64)
+    mpo = np.zeros((5, 1), np.int64)
+    return rabc_chain(bq, list(dims), local, mpo, U1_MPO_PAIRS, dtype, rng, layout, values,
+                      name=f"neutral-{layout}-{values}")
+
+
 # ----------------------------------------------------------------------------
 # random structures for property tests
 # ----------------------------------------------------------------------------

@@ -104,9 +104,10 @@ struct FPart {
 };
 static_assert(sizeof(FPart) == 128, "FPart layout");
 
-// Lane-held tables: a wave keeps the records of its group's first 64 products
-// (one per lane) and up to FUSED_WREG x 64 weights in registers.
-constexpr int FUSED_LANE_RECS = 64;
+// Lane-held tables: a wave keeps the records of 64 of its part's products
+// (one per lane; the next 64 are loaded when the stream reaches them) and up to
+// FUSED_WREG x 64 weights in registers.
+constexpr int FUSED_LANE_RECS = 64;   // a power of two
 constexpr int FUSED_WREG = 4;
 constexpr int FUSED_WCAP = 64 * FUSED_WREG;   // stage-1 blocks x outputs per task
 

@@ -178,7 +178,12 @@ struct FuSlot {
 };
 
 // One part's product stream (record pr) through the matrix cores, weighted
-// into acc.
+// into acc.  The loop body is branch-free where the loads are: every slot
+// refill issues the same loads (offsets beyond the range once the stream has
+// ended, which read zero) and every chunk runs all its matrix-core steps
+// (zeros past K add nothing), so the compiler's wait counts stay exact:
+// computing a slot waits for that slot's loads only, never for the D - 1
+// chunks behind it.
 template <typename T, int NO>
 __device__ __forceinline__ void fused_stream(const FArgs &fa, const FPart &pr, int32_t lane,
                                              typename FuTraits<T>::acc_t (&acc)[NO]) {
@@ -197,84 +202,87 @@ __device__ __forceinline__ void fused_stream(const FArgs &fa, const FPart &pr, i
     // the issue cursor: product ip (operands P), next chunk offset ik
     int32_t ip = 0, ik = 0;
     FuProd P = fu_prod(A, B, pr.first, pr.M, pr.N, ia, jb);
-    auto load_into = [&](FuSlot<T> &sl) {
-        fu_load(P, ik, arow, bcol, q, sl.v);
-        sl.p = ip;
+    FChan myrec{};
+    // the next chunk of the stream into slot sl; past the end the slot is
+    // marked empty and its loads read zero
+    auto issue = [&](FuSlot<T> &sl) {
+        if (ik >= P.K && ip < pr.nchan) {
+            ++ip;
+            ik = 0;
+            if (ip < pr.nchan) {
+                if ((ip & (FUSED_LANE_RECS - 1)) == 0) {
+                    // the next batch of lane-held records (rare: parts of more than 64 products)
+                    myrec = ip + lane < pr.nchan ? chans[ip + lane] : FChan{};
+                    __builtin_amdgcn_s_waitcnt(0);
+                }
+                P = fu_prod(A, B, fu_rl(myrec, ip & (FUSED_LANE_RECS - 1)), pr.M, pr.N, ia, jb);
+            }
+        }
+        const bool live = ip < pr.nchan;
+        fu_load(P, ik, arow && live, bcol && live, q, sl.v);
+        sl.p = live ? ip : -1;
         sl.k0 = ik;
         sl.K = P.K;
         sl.wrow = P.wrow;
         sl.last = P.last;
         ik += FUSED_KC;
     };
-    load_into(ring[0]);
+    issue(ring[0]);   // the first chunk waits on the part record alone
 
-    // product records, one per lane
-    FChan myrec{};
-    if (lane < pr.nchan && lane < FUSED_LANE_RECS) myrec = chans[lane];
+    // product records, one per lane (the first batch of 64)
+    if (lane < pr.nchan) myrec = chans[lane];
     // weights of (block r, output o) at entry r * NO + o, FUSED_WREG per lane
+    // (all index loads first, then all value loads: two round trips in all)
     T wv[FUSED_WREG];
+    int32_t wi[FUSED_WREG];
     const int32_t nw = pr.nblk * NO;
 #pragma unroll
     for (int m = 0; m < FUSED_WREG; ++m) {
         const int32_t e = lane + 64 * m;
         const int32_t r = e / NO, o = e - r * NO;
-        const int32_t wi = (e < nw && o < pr.no) ? fa.widx[pr.wbase + static_cast<int64_t>(r) * pr.wstride + o] : -1;
-        wv[m] = wi >= 0 ? W[wi] : T(0);
+        wi[m] = (e < nw && o < pr.no) ? fa.widx[pr.wbase + static_cast<int64_t>(r) * pr.wstride + o] : -1;
     }
-
-    // the next chunk of the stream into slot sl (or mark it empty)
-    auto issue = [&](FuSlot<T> &sl) {
-        if (ik >= P.K) {
-            ++ip;
-            ik = 0;
-            if (ip < pr.nchan) {
-                const FChan ch = ip < FUSED_LANE_RECS ? fu_rl(myrec, ip) : chans[ip];
-                P = fu_prod(A, B, ch, pr.M, pr.N, ia, jb);
-            }
-        }
-        if (ip < pr.nchan) load_into(sl);
-        else sl.p = -1;
-    };
+#pragma unroll
+    for (int m = 0; m < FUSED_WREG; ++m) wv[m] = wi[m] >= 0 ? W[wi[m]] : T(0);
+    // the lane-held tables complete before the stream starts (together with the
+    // first chunk, issued before them): inside the loop the compiler then knows
+    // they are ready and never waits for outstanding chunk loads to read them
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int u = 1; u < D; ++u) issue(ring[u]);
 
     acc_t t1 = acc_t{0, 0, 0, 0};
-    bool done = false;
-    while (!done) {
+    while (true) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            if (!done) {
-                FuSlot<T> &sl = ring[u];
-                if (sl.p < 0) {
-                    done = true;
-                } else {
-                    const int32_t steps = min(FUSED_STEPS, (sl.K - sl.k0 + 3) / 4);
+            FuSlot<T> &sl = ring[u];
+            // all steps, operands swapped for a transposed tile by selects
 #pragma unroll
-                    for (int s = 0; s < FUSED_STEPS; ++s) {
-                        if (s < steps)
-                            t1 = tr ? FuTraits<T>::mma(sl.v.b[s], sl.v.a[s], t1)
-                                    : FuTraits<T>::mma(sl.v.a[s], sl.v.b[s], t1);
-                    }
-                    if (sl.k0 + FUSED_KC >= sl.K && sl.last) {
-                        // the stage-1 block is complete: weighted into every output of the task
-#pragma unroll
-                        for (int o = 0; o < NO; ++o) {
-                            if (o < pr.no) {
-                                const int32_t e = sl.wrow * NO + o, m = e >> 6, l = e & 63;
-                                T wgt = fu_rl(wv[0], l);
-#pragma unroll
-                                for (int mm = 1; mm < FUSED_WREG; ++mm)
-                                    if (m == mm) wgt = fu_rl(wv[mm], l);
-#pragma unroll
-                                for (int v = 0; v < 4; ++v) acc[o][v] = fma(wgt, t1[v], acc[o][v]);
-                            }
-                        }
-                        t1 = acc_t{0, 0, 0, 0};
-                    }
-                    issue(sl);   // refill the slot
-                }
+            for (int s = 0; s < FUSED_STEPS; ++s) {
+                const T xa = tr ? sl.v.b[s] : sl.v.a[s];
+                const T xb = tr ? sl.v.a[s] : sl.v.b[s];
+                t1 = FuTraits<T>::mma(xa, xb, t1);
             }
+            if (sl.p >= 0 && sl.k0 + FUSED_KC >= sl.K && sl.last) {
+                // the stage-1 block is complete: weighted into every output of the task
+#pragma unroll
+                for (int o = 0; o < NO; ++o) {
+                    if (o < pr.no) {
+                        const int32_t e = sl.wrow * NO + o, m = e >> 6, l = e & 63;
+                        T wgt = fu_rl(wv[0], l);
+#pragma unroll
+                        for (int mm = 1; mm < FUSED_WREG; ++mm)
+                            if (m == mm) wgt = fu_rl(wv[mm], l);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[o][v] = fma(wgt, t1[v], acc[o][v]);
+                    }
+                }
+                t1 = acc_t{0, 0, 0, 0};
+            }
+            issue(sl);   // refill the slot
         }
+        // slots hold consecutive chunks: slot 0 empty means the stream has ended
+        if (ring[0].p < 0) break;
     }
 }
 

@@ -192,6 +192,113 @@ def _view_mask(con):
     return mask
 
 
+def kernel_times(torch, fn, reps=10):
+    """Device time per call (us) and launches per call of every kernel that fn
+    enqueues, from torch.profiler's device activity (HIP kernel records)."""
+    from torch.profiler import ProfilerActivity, profile
+    fn()
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+    out = {}
+    for ev in prof.key_averages():
+        t = getattr(ev, "device_time_total", 0)
+        if t > 0 and ev.device_type.name == "CUDA":
+            out[ev.key] = {"us": round(t / reps, 3), "launches": ev.count / reps}
+    return out
+
+
+def calibrate_pack(torch, bst, np, reps=20):
+    """Measure the pack-cost model's constants on this GPU (uni20 "block
+    coalescing": the crossover uses calibrated constants).  For every stage of
+    the two environment-update chains with operands to gather: the grouped
+    kernel's time without gathers (NEVER_PACK), with every gatherable operand
+    gathered (FORCE_PACK) and as the model decides at the constants in use
+    (AUTO), each gather kernel's time, and the model's terms.  Fits
+      pack_gbps   = 2 x bytes / gather kernel time of the largest gather;
+      t_launch_us = the fixed cost of a plan's extra launch, on the plan with
+                    the smallest gather: its contraction time minus its grouped
+                    kernel's time minus the gather's bandwidth term;
+      t_seg_us    = (measured grouped-kernel saving - modelled padding saving)
+                    / (piece set-ups saved, in units of t_seg_us) on the stage
+                    where the piece term is largest;
+    then re-plans every stage with the fitted constants and reports whether
+    AUTO picks the faster of NEVER_PACK and FORCE_PACK."""
+    cur_seg = 0.05   # t_seg_us the model's gain terms are computed with here
+    rows = []
+    for wl in ("rabc_u1", "rabc_u1u1"):
+        stages, inputs, sizes, dtype = load_workload(wl)
+        cdt = torch.float64 if dtype == "f64" else torch.float32
+        bufs = {k: torch.from_numpy(np.ascontiguousarray(v)).to(cdt).cuda() for k, v in inputs.items()}
+        for k, n in sizes.items():
+            if k not in bufs:
+                bufs[k] = torch.zeros(n, dtype=cdt, device="cuda")
+        for si, (con, a, b, c, ax) in enumerate(stages):
+            r = {"workload": wl, "stage": si}
+            for lay, kw in (("never_pack", {}), ("force_pack", {}), ("auto", {"t_launch_us": 4.0, "pack_gbps": 2500.0})):
+                p = bst.Plan(con, axis=ax, layout=lay, t_seg_us=cur_seg, **kw).bind()
+                st = p.stats()
+                call = lambda: p.contract(bufs[a], bufs[b], bufs[c])
+                for _ in range(5):
+                    call()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
+                kt = kernel_times(torch, call)
+                r[lay] = {"us": round(e0.elapsed_time(e1) / reps * 1e3, 3), "pack_bytes": st["pack_bytes"],
+                          "gather_us": sum(v["us"] for k, v in kt.items() if "pack_gather" in k),
+                          "grouped_us": sum(v["us"] for k, v in kt.items() if "grouped_contract" in k),
+                          "gain_seg_us": st["pack_gain_seg_us"], "gain_pad_us": st["pack_gain_pad_us"],
+                          "cost_us": st["pack_cost_us"], "predicted_us": round(st["predicted_us"], 3)}
+                del p
+            if r["force_pack"]["pack_bytes"] > 0:
+                rows.append(r)
+    gathers = [r[lay] for r in rows for lay in ("force_pack", "auto") if r[lay]["pack_bytes"] > 0]
+    big = max(gathers, key=lambda g: g["pack_bytes"])
+    pack_gbps = 2 * big["pack_bytes"] / (big["gather_us"] * 1e3)
+    tiny = min(gathers, key=lambda g: g["pack_bytes"])
+    t_launch = tiny["us"] - tiny["grouped_us"] - 2 * tiny["pack_bytes"] / (pack_gbps * 1e3)
+    seg = max(rows, key=lambda r: r["force_pack"]["gain_seg_us"])
+    saving = seg["never_pack"]["grouped_us"] - seg["force_pack"]["grouped_us"] - seg["force_pack"]["gain_pad_us"]
+    t_seg = max(0.0, saving / (seg["force_pack"]["gain_seg_us"] / cur_seg))
+    fitted = {"pack_gbps": round(pack_gbps, 1), "t_launch_us": round(t_launch, 3), "t_seg_us": round(t_seg, 6)}
+    # AUTO with the fitted constants against the measured faster arrangement
+    checks = []
+    for r in rows:
+        stages, _, _, _ = load_workload(r["workload"])
+        con, _, _, _, ax = stages[r["stage"]]
+        st = bst.Plan(con, axis=ax, layout="auto", t_launch_us=t_launch, t_seg_us=t_seg, pack_gbps=pack_gbps).stats()
+        picks_pack = st["pack_bytes"] > 0
+        faster_pack = r["force_pack"]["us"] < r["never_pack"]["us"]
+        checks.append({"workload": r["workload"], "stage": r["stage"], "auto_gathers": picks_pack,
+                       "gathering_is_faster": faster_pack, "agrees": picks_pack == faster_pack})
+    return {"stages": rows, "fitted": fitted, "auto_with_fitted": checks}
+
+
+def measured_mfma_peaks(torch, bst):
+    """Matrix-core rates measured on this GPU (bsc_probe_mfma), TFLOP/s, for
+    the instruction each dtype's tiles use: the mean of 5 timed launches of
+    about a millisecond each after one warm-up."""
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    out = {}
+    for dt, iters in (("bf16", 2000), ("f32", 1000), ("f64", 500)):
+        bst.probe_mfma(dt, iters, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = sum(bst.probe_mfma(dt, iters, sink) for _ in range(5))
+        e1.record()
+        torch.cuda.synchronize()
+        out[dt] = round(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 2)
+    return out
+
+
 def load_workload(name, ld_align=1, relayout=False):
     from workloads import configs as C
     if name == "blockdiag_bf16":
@@ -234,6 +341,8 @@ def main():
                          "elements; 8 = 16-byte aligned rows (default), 1 = unpadded contiguous blocks")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (counter calibration) and exit")
+    ap.add_argument("--calibrate-pack", action="store_true",
+                    help="only measure the pack-cost model's constants on the chains' stages and exit")
     ap.add_argument("--layout", default="auto", choices=["auto", "never_pack", "force_pack"],
                     help="operand arrangement policy of the grouped plans (auto = the planner's pack-cost model)")
     ap.add_argument("--relayout", action="store_true",
@@ -271,6 +380,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}), flush=True)
+        return
+    if args.calibrate_pack:
+        print(json.dumps(calibrate_pack(torch, bst, np)), flush=True)
         return
     stages, inputs, sizes, dtype = load_workload(args.workload, args.ld_align, args.relayout)
 
@@ -442,6 +554,25 @@ def main():
                      "items": fs["items"], "products": fs["channels"], "terms": fs["terms"],
                      "t2_rel_diff_vs_two_stage": rel, "launches_per_step": len(stages) - 1}
 
+    # --- the gather (pack) phase against the HBM roofline: every gatherable operand of each
+    # stage gathered (FORCE_PACK), the gather kernel's own time from the profiler ---
+    pack_phase = []
+    if multi:
+        for si, (con, a, b, c, ax) in enumerate(stages):
+            fpl = bst.Plan(con, axis=ax, layout="force_pack").bind()
+            pb = fpl.stats()["pack_bytes"]
+            if pb == 0:
+                continue
+            kt = kernel_times(torch, lambda: fpl.contract(bufs[a], bufs[b], bufs[c]))
+            gus = sum(v["us"] for k, v in kt.items() if "pack_gather" in k)
+            if gus > 0:
+                pack_phase.append({"stage": si, "bytes_gathered": pb, "gather_kernel_us": round(gus, 3),
+                                   "gbps": round(2 * pb / (gus * 1e3), 1),
+                                   "frac_hbm": round(2 * pb / (gus * 1e3) / HBM_PEAK, 4),
+                                   "auto_gathers": st[si]["pack_bytes"] > 0})
+            del fpl
+        step(grouped)   # the timed plans' results back in C for the parity check below
+
     # --- host planning of every stage: fresh, and a plan-cache hit (a site revisited in a sweep) ---
     def plan_all(cache=None):
         t0 = time.perf_counter()
@@ -577,7 +708,18 @@ def main():
             dense_ref, engine_pct_of_it=round(100.0 * value / 1e3 / dense_ref["tflops"], 3)),
         "stage_kernel_ms": [round(x, 6) for x in stage_ms],
         "host_planning": planning,
+        # the pack-cost model's estimate of one step next to the measured time
+        "cost_model": {"predicted_us": round(sum(x["predicted_us"] for x in st), 3),
+                       "measured_us": round(ms * 1e3, 3),
+                       "per_stage": [{"predicted_us": round(x["predicted_us"], 3), "measured_us": round(t * 1e3, 3),
+                                      "pack_bytes": x["pack_bytes"]} for x, t in zip(st, stage_ms)]},
     }
+    mpk = measured_mfma_peaks(torch, bst)
+    out["mfma_peak_measured"] = dict(mpk, unit="TFLOP/s", spec=MFMA_PEAK, kernel="bsc_probe_mfma")
+    if not hbm_bound:
+        out["roofline"]["frac_of_measured_peak"] = round(achieved_tflops / mpk[dtype], 5)
+    if pack_phase:
+        out["pack_phase"] = pack_phase
     if graph is not None:
         # the stages as one captured graph (bsc_chain): no host gaps between launches
         out["graph_chain"] = graph

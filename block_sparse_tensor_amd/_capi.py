@@ -22,7 +22,7 @@ EXPORTED = ["bsc_options_default", "bsc_plan", "bsc_plan_device_bytes", "bsc_pla
             "bsc_last_error", "bsc_chain_create", "bsc_chain_launch", "bsc_chain_destroy", "bsc_plan_cache_create",
             "bsc_plan_cached", "bsc_plan_cache_stats", "bsc_plan_cache_destroy", "bsc_plan_layout",
             "bsc_contract_noalloc", "bsc_fused_plan", "bsc_fused_device_bytes", "bsc_fused_bind",
-            "bsc_fused_contract", "bsc_fused_stats", "bsc_fused_worklist", "bsc_fused_destroy"]
+            "bsc_fused_contract", "bsc_fused_stats", "bsc_fused_worklist", "bsc_fused_destroy", "bsc_probe_mfma"]
 
 
 class BscIndex(ctypes.Structure):
@@ -51,7 +51,8 @@ class BscStats(ctypes.Structure):
                 ("launches_per_sector", c_int64), ("useful_flops", c_int64), ("alg_bytes", c_int64),
                 ("pack_bytes", c_int64), ("device_bytes", c_int64), ("tail_triples", c_int64),
                 ("launches_issued", c_int64), ("grid", c_int32), ("split_tiles", c_int32),
-                ("predicted_us", c_double)]
+                ("predicted_us", c_double), ("pack_gain_seg_us", c_double), ("pack_gain_pad_us", c_double),
+                ("pack_cost_us", c_double)]
 
 
 class BscWorklistInfo(ctypes.Structure):
@@ -137,6 +138,8 @@ def lib():
         L.bsc_fused_stats.restype = c_int32
         L.bsc_fused_worklist.argtypes = [c_void_p, c_void_p, c_size_t]
         L.bsc_fused_worklist.restype = c_int32
+        L.bsc_probe_mfma.argtypes = [c_int32, c_int32, c_void_p, c_void_p, POINTER(c_double)]
+        L.bsc_probe_mfma.restype = c_int32
         L.bsc_fused_destroy.argtypes = [c_void_p]
         L.bsc_fused_destroy.restype = None
         _lib = L

@@ -29,19 +29,24 @@ void bsc_options_default(bsc_options *opt) {
 }
 
 static void fill_cost_defaults(bsc_options &o, bsc_dtype dt) {
-    // MI355X defaults, measured on one MI355X with this library (calibrated
-    // constants may be passed in instead):
-    //   t_launch_us  back-to-back launches of small grouped kernels, 3.6-6 us each;
-    //   pack_gbps    the gather kernel moved 2 x 29.6 MB in 23.5 us (2.5 TB/s)
+    // MI355X defaults, measured on one MI355X with this library by the pack
+    // calibration of the benchmark driver (calibrated constants may be passed
+    // in instead):
+    //   t_launch_us  the fixed cost of a plan's extra (gather) launch: a
+    //                19.7 KB gather adds 5.9 us to the U(1) update's W stage
+    //                beyond its bytes;
+    //   pack_gbps    the gather kernel moved 2 x 33.8 MB in 28.2 us (2.4 TB/s)
     //                on the natural-layout environment update;
     //   tile_gflops  sustained whole-GPU rate of the matrix-core tiles on
     //                mid-sized sector GEMMs (bf16 ~ 250 TFLOP/s, fp32 and fp64
     //                ~ 10 TFLOP/s);
-    //   t_seg_us     per extra piece walked by one tile (record set-up and a
-    //                pipeline restart), an estimate.
-    if (o.t_launch_us <= 0) o.t_launch_us = 4.0;
-    if (o.t_seg_us <= 0) o.t_seg_us = 0.05;
-    if (o.pack_gbps <= 0) o.pack_gbps = 2500.0;
+    //   t_seg_us     per extra piece walked by one tile: gathering every
+    //                operand of the U(1)xU(1) W stage saves 16.7 us of grouped
+    //                kernel time (beyond its padding term) for 35,364 units of
+    //                the piece term, 0.00046 us each.
+    if (o.t_launch_us <= 0) o.t_launch_us = 5.9;
+    if (o.t_seg_us <= 0) o.t_seg_us = 0.00046;
+    if (o.pack_gbps <= 0) o.pack_gbps = 2400.0;
     if (o.tile_gflops <= 0) o.tile_gflops = dt == BSC_BF16_F32 ? 250000.0 : 10000.0;
 }
 

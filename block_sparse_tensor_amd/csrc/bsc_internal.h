@@ -276,6 +276,8 @@ struct Plan {
     int32_t n_counters = 0;       // K-split arrival counters (one per split tile, zero between launches)
     int64_t part_elems = 0;       // K-split partial tiles (fp32 elements)
     int32_t split_tiles = 0;      // output tiles cut along K
+    // pack-cost model terms summed over the gathered operands (microseconds)
+    double gain_seg_us = 0, gain_pad_us = 0, pack_cost_us = 0;
     std::vector<std::array<int32_t, 2>> launches;  // per-sector mode: task ranges, one launch each
 
     // device binding

@@ -543,7 +543,6 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                                const std::vector<int64_t> &segK, bool is_a) -> bool {
             if (p.opt.layout_policy == BSC_LAYOUT_NEVER_PACK) return false;
             if (one_view(seg, segK)) return false;   // already zero-copy and single-view
-            if (p.opt.layout_policy == BSC_LAYOUT_FORCE_PACK) return true;
             const int64_t free = is_a ? dg.M : dg.N;
             const int64_t other = is_a ? dg.N : dg.M;
             const int64_t T = p.dtype == BSC_BF16_F32 ? TILE_MFMA : TILE_MFMA_F;
@@ -555,12 +554,15 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             }
             const int64_t pad_after = ((int64_t)dg.K + kq - 1) / kq * kq - dg.K;
             const double extra = (double)(pieces - 1);
-            const double gain = (double)tiles * extra * p.opt.t_seg_us / concurrent +
-                                2.0 * (double)free * (double)other * (double)std::max<int64_t>(0, pad - pad_after) /
-                                    (p.opt.tile_gflops * 1e3);
+            const double gain_seg = (double)tiles * extra * p.opt.t_seg_us / concurrent;
+            const double gain_pad = 2.0 * (double)free * (double)other *
+                                    (double)std::max<int64_t>(0, pad - pad_after) / (p.opt.tile_gflops * 1e3);
             const double cost = 2.0 * (double)(free * dg.K * esz) / (p.opt.pack_gbps * 1e3);
-            if (gain <= cost) return false;
-            pack_net_us += gain - cost;
+            if (p.opt.layout_policy != BSC_LAYOUT_FORCE_PACK && gain_seg + gain_pad <= cost) return false;
+            pack_net_us += gain_seg + gain_pad - cost;
+            p.gain_seg_us += gain_seg;
+            p.gain_pad_us += gain_pad;
+            p.pack_cost_us += cost;
             return true;
         };
         // Gather an operand into a fresh workspace region with a constant
@@ -1172,6 +1174,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         // a plan with gathers needs one more launch: keep them only if they pay for it
         if (!p.packs.empty() && p.opt.layout_policy == BSC_LAYOUT_AUTO && pack_net_us <= p.opt.t_launch_us) {
             p.opt.layout_policy = BSC_LAYOUT_NEVER_PACK;
+            p.gain_seg_us = p.gain_pad_us = p.pack_cost_us = 0;
             return build_plan(p, m, k, n, A, B, C);
         }
 
@@ -1248,6 +1251,9 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         s.device_bytes = (int64_t)p.dev_bytes;
         s.tail_triples = tail;
         s.split_tiles = p.split_tiles;
+        s.pack_gain_seg_us = p.gain_seg_us;
+        s.pack_gain_pad_us = p.gain_pad_us;
+        s.pack_cost_us = p.pack_cost_us;
         const double rate_gflops = p.dtype == BSC_BF16_F32 ? 2.5e6 : (p.dtype == BSC_F32 ? 157.3e3 : 78.6e3);
         s.predicted_us = s.launches_per_contract * p.opt.t_launch_us +
                          std::max((double)flops / (rate_gflops * 1e3), (double)s.alg_bytes / 8.0e6) +

@@ -73,3 +73,12 @@ extern "C" bsc_status bsc_fused_contract(bsc_fused_t plan, const void *, const v
     set_error("bsc_fused_contract: host-only planner build has no device runtime");
     return BSC_ERR_UNSUPPORTED;
 }
+
+extern "C" bsc_status bsc_probe_mfma(bsc_dtype, int32_t iters, float *sink, void *, double *flops) {
+    if (!sink || !flops || iters < 1) {
+        set_error("bsc_probe_mfma: NULL sink or flops, or iters < 1");
+        return BSC_ERR_ARG;
+    }
+    set_error("bsc_probe_mfma: host-only planner build has no device runtime");
+    return BSC_ERR_UNSUPPORTED;
+}

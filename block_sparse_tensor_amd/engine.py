@@ -267,6 +267,16 @@ class Plan:
             self._h = None
 
 
+def probe_mfma(dtype: str, iters: int, sink, stream=None) -> float:
+    """Enqueue the matrix-core issue-rate probe (bsc_probe_mfma) on `stream`
+    and return its flops; the caller times the launch.  `sink` is a device
+    float32 tensor the kernel never writes."""
+    f = ctypes.c_double()
+    _check(_capi.lib().bsc_probe_mfma(DTYPES[dtype], int(iters), c_void_p(sink.data_ptr()), _stream_handle(stream),
+                                      byref(f)))
+    return f.value
+
+
 class FusedPlan:
     """Two contractions planned as one launch (bsc_fused_plan): stage 1
     C1 = A1 B1 (`con1`), then stage 2 C2 (+)= C1 B2 (`con2`), where stage 2's

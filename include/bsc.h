@@ -193,6 +193,9 @@ typedef struct {
     int32_t grid;                    /* workgroups of the grouped launch */
     int32_t split_tiles;             /* output tiles whose K is cut into slices (see split_k) */
     double predicted_us;             /* cost-model estimate of one contraction */
+    /* the pack-cost model's terms over the gathered operands (0 without gathers):
+     * saved piece set-ups (t_seg_us), saved K-step padding, gather traffic */
+    double pack_gain_seg_us, pack_gain_pad_us, pack_cost_us;
 } bsc_stats;
 
 typedef struct bsc_plan_s *bsc_plan_t;
@@ -427,6 +430,18 @@ bsc_status bsc_fused_stats(bsc_fused_t plan, bsc_fused_summary *out);
  * replay): `bytes` must be at least bsc_fused_device_bytes, else BSC_ERR_ARG. */
 bsc_status bsc_fused_worklist(bsc_fused_t plan, void *buf, size_t bytes);
 void bsc_fused_destroy(bsc_fused_t plan);
+
+/* Matrix-core issue-rate probe (measurement only, not part of a contraction):
+ * enqueues on `stream` one launch of 8 workgroups per CU whose waves run
+ * `iters` rounds of independent back-to-back matrix-core operations of the
+ * kind the tiles of `dtype` use (v_mfma_f32_32x32x16_bf16 for BSC_BF16_F32,
+ * v_mfma_f32_16x16x4_f32 for BSC_F32, v_mfma_f64_16x16x4_f64 for BSC_F64),
+ * operands in registers.  *flops receives the launch's floating-point
+ * operations; the caller times the launch (events on `stream`) to get the
+ * measured peak.  `sink` is a device float the kernel could write but never
+ * does.  Errors: BSC_ERR_ARG (NULL sink or flops, iters < 1, unknown dtype),
+ * BSC_ERR_HIP. */
+bsc_status bsc_probe_mfma(bsc_dtype dtype, int32_t iters, float *sink, void *stream, double *flops);
 
 const char *bsc_status_string(bsc_status s);
 

@@ -206,7 +206,8 @@ def test_chain_views_agree(make):
 
 def test_chain_relayout_removes_gathers_and_segments():
     """The U(1) update in its natural layout walks per-member pieces in stage
-    1 and gathers in stage 2; laid out for the readers, both disappear."""
+    1 and has several views per group in stage 2; laid out for the readers,
+    every group sees its members as one view."""
     _lib_or_skip()
     ch = C.rabc_u1(layout="natural")
     st = _chain_stages(ch)
@@ -214,9 +215,14 @@ def test_chain_relayout_removes_gathers_and_segments():
     m0, s0 = _modes(st[0][0])
     m1, s1 = _modes(new[0])
     assert m0["A"][2] > 0 and m1["A"] == (s1["groups"] - s1["zero_groups"], 0, 0)
-    _, s0 = _modes(st[1][0])
+    # stage 2: in the natural layout many groups' members are several views
+    # (gathering them is possible; the calibrated model finds it does not pay);
+    # laid out for the readers far fewer are, and nothing is gathered
+    before = bst.Plan(st[1][0], layout="force_pack").stats()["pack_bytes"]
+    after = bst.Plan(new[1], layout="force_pack").stats()["pack_bytes"]
+    assert before > 0 and after < before
     _, s1 = _modes(new[1])
-    assert s0["launches_per_contract"] == 2 and s1["launches_per_contract"] == 1 and s1["pack_bytes"] == 0
+    assert s1["launches_per_contract"] == 1 and s1["pack_bytes"] == 0
 
 
 def test_move_blocks_round_trip():

@@ -279,3 +279,15 @@ def test_header_is_plain_c(tmp_path):
     r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
                         "-fsyntax-only", str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_probe_mfma_checks_arguments():
+    """The matrix-core probe refuses bad arguments before touching a device."""
+    from ctypes import byref, c_double, c_void_p
+    L = bst._capi.lib() if hasattr(bst, "_capi") else None
+    if L is None:
+        pytest.skip("library not built")
+    f = c_double()
+    assert L.bsc_probe_mfma(2, 0, c_void_p(1), None, byref(f)) == -1      # iters < 1
+    assert L.bsc_probe_mfma(2, 10, None, None, byref(f)) == -1             # NULL sink
+    assert L.bsc_probe_mfma(2, 10, c_void_p(1), None, None) == -1          # NULL flops

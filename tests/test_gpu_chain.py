@@ -137,3 +137,22 @@ def test_chain_checks_tensors_and_guards_rebind():
     p.bind()                                      # allowed again
     p.contract(g[st.a_buf], g[st.b_buf], g[st.c_buf])
     t.cuda.synchronize()
+
+
+def test_probe_mfma_measures_a_rate():
+    """bsc_probe_mfma: a launch of known flops whose measured rate is positive
+    and below the published peak of its instruction."""
+    t = torch()
+    sink = t.zeros(1, dtype=t.float32, device="cuda")
+    spec = {"bf16": 2516.6e12, "f32": 157.3e12, "f64": 78.6e12}
+    for dt, iters in (("bf16", 200), ("f32", 100), ("f64", 50)):
+        bst.probe_mfma(dt, iters, sink)
+        t.cuda.synchronize()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = bst.probe_mfma(dt, iters, sink)
+        e1.record()
+        t.cuda.synchronize()
+        rate = flops / (e0.elapsed_time(e1) * 1e-3)
+        assert flops > 0 and 0.05 * spec[dt] < rate < 1.05 * spec[dt], (dt, rate)
+        assert sink.item() == 0.0   # never written

@@ -81,6 +81,13 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run `python -m block_sparse_tensor_amd.build`")
+        # torch (which supplies device memory and streams) ships its own HIP
+        # runtime under the same sonames as the system one the library links;
+        # whichever is loaded first serves the whole process.  Importing torch
+        # first makes the library bind to torch's runtime, so both see the
+        # same devices, streams and allocations (loaded the other way round,
+        # the library's calls found no device).
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.bsc_options_default.argtypes = [POINTER(BscOptions)]
         L.bsc_options_default.restype = None

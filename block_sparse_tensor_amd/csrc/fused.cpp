@@ -40,7 +40,7 @@ struct PlanGuard {
 };
 
 void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *m2idx, bool accumulate,
-                 int32_t max_parts) {
+                 int32_t max_parts, int32_t tile_cols) {
     if (s1.c_elems != s2.a_elems)
         ffail(BSC_ERR_ARG, "bsc_fused_plan: stage 2's A buffer must be stage 1's C buffer (lengths differ)");
     // stage 2's B: scalars only (every contracted and output key of stage 2 has dim 1)
@@ -185,13 +185,33 @@ void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *
     if ((int64_t)most_blk * f.outs_per_task > FUSED_WCAP)
         ffail(BSC_ERR_UNSUPPORTED, "bsc_fused_plan: a stage-2 row fuses more than " +
                                        std::to_string(FUSED_WCAP / 4) + " stage-1 blocks");
+    // the wave tile: 32 x 32 (two by two matrix-core blocks) for fp32 plans of
+    // at most 4 outputs per task (fp64 accumulators, or more outputs, would
+    // not fit the registers), when 32 x 32 tiles cover at most a quarter more
+    // padding than 16 x 16 ones and still make at least FUSED_WIDE_TASKS tasks
+    // (fewer, larger tasks leave the chip idle: on a 768-bond chain they were
+    // slower, on a 2048-bond chain 11 % faster); 16 x 16 otherwise.
+    // tile_cols 16 or 32 fixes the choice (32 only where it fits).
+    {
+        int64_t cover16 = 0, cover32 = 0, tasks32 = 0;
+        for (const FGroup &g : f.groups) {
+            const int64_t tiles32 = (int64_t)((g.M + 31) / 32) * ((g.N + 31) / 32);
+            cover16 += (int64_t)((g.M + 15) / 16) * ((g.N + 15) / 16) * 256;
+            cover32 += tiles32 * 1024;
+            tasks32 += tiles32 * ((g.nout + f.outs_per_task - 1) / f.outs_per_task);
+        }
+        const bool fits = f.dtype == BSC_F32 && f.outs_per_task <= 4;
+        const bool pays = cover16 > 0 && cover32 * 4 <= cover16 * 5 && tasks32 >= FUSED_WIDE_TASKS;
+        f.tile_blocks = fits && (tile_cols == 32 || (tile_cols == 0 && pays)) ? 2 : 1;
+    }
+    const int32_t TILE = FUSED_TILE * f.tile_blocks;
     std::vector<int64_t> work(f.groups.size(), 0);   // register chunks of one part
     for (size_t gi = 0; gi < f.groups.size(); ++gi) {
         const FGroup &g = f.groups[gi];
         const int32_t nchunks = std::max(1, (g.nout + f.outs_per_task - 1) / f.outs_per_task);
         for (int32_t oc = 0; oc < nchunks; ++oc)
-            for (int32_t i0 = 0; i0 < g.M; i0 += FUSED_TILE)
-                for (int32_t j0 = 0; j0 < g.N; j0 += FUSED_TILE) f.tasks.push_back({(int32_t)gi, i0, j0, oc});
+            for (int32_t i0 = 0; i0 < g.M; i0 += TILE)
+                for (int32_t j0 = 0; j0 < g.N; j0 += TILE) f.tasks.push_back({(int32_t)gi, i0, j0, oc});
     }
     f.useful_flops += f.stage1_flops;
     // algorithmic bytes: stage-1 operand blocks read once, W read once, outputs written once
@@ -288,8 +308,8 @@ void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *
             FPart pr{};
             pr.i0 = t.i0;
             pr.j0 = t.j0;
-            pr.ml = std::min(FUSED_TILE, g.M - t.i0);
-            pr.nl = std::min(FUSED_TILE, g.N - t.j0);
+            pr.ml = std::min(TILE, g.M - t.i0);
+            pr.nl = std::min(TILE, g.N - t.j0);
             pr.M = g.M;
             pr.N = g.N;
             pr.chan0 = plist[(size_t)t.group][(size_t)p].first;
@@ -359,6 +379,13 @@ extern "C" bsc_status bsc_fused_plan(const bsc_index *m1, const bsc_index *k1, c
         return BSC_ERR_ARG;
     }
     const int32_t max_parts = o.split_k == 0 ? 4 : std::min(4, o.split_k);
+    // tile_cols: the wave tile's edge (0: automatic, 16, or 32 where it fits)
+    if (o.tile_cols != 0 && o.tile_cols != 16 && o.tile_cols != 32) {
+        set_error("bsc_fused_plan: tile_cols must be 0, 16 or 32");
+        return BSC_ERR_ARG;
+    }
+    const int32_t tile_cols = o.tile_cols;
+    o.tile_cols = 0;
     o.accumulate = 0;
     o.split_k = 0;
     o.launch_mode = BSC_LAUNCH_GROUPED;
@@ -380,7 +407,7 @@ extern "C" bsc_status bsc_fused_plan(const bsc_index *m1, const bsc_index *k1, c
     }
     f->dtype = dtype;
     try {
-        build_fused(*f, *reinterpret_cast<Plan *>(g1.p), *reinterpret_cast<Plan *>(g2.p), m2, accumulate, max_parts);
+        build_fused(*f, *reinterpret_cast<Plan *>(g1.p), *reinterpret_cast<Plan *>(g2.p), m2, accumulate, max_parts, tile_cols);
     } catch (const FFail &e) {
         delete f;
         return e.st;
@@ -430,6 +457,7 @@ extern "C" bsc_status bsc_fused_stats(bsc_fused_t plan, bsc_fused_summary *out) 
     out->off_widx = (int64_t)f->off_widx;
     out->off_tasks = (int64_t)f->off_tasks;
     out->outs_per_task = f->outs_per_task;
+    out->tile_blocks = f->tile_blocks;
     out->off_parts = (int64_t)f->off_parts;
     out->n_parts = (int64_t)f->parts.size();
     out->off_pchans = (int64_t)f->off_pchans;

@@ -46,7 +46,12 @@
 
 namespace bsc {
 
-constexpr int FUSED_TILE = 16;      // output tile edge: one 16 x 16 matrix-core tile per wave
+constexpr int FUSED_TILE = 16;      // matrix-core block edge (16 x 16)
+// A wave's output tile is TW x TW matrix-core blocks (TW = 1 or 2): with
+// TW = 2 a wave loads two rows of A and two columns of B per contracted
+// index for four matrix-core operations instead of one of each for one,
+// halving the operand loads per flop.  Chosen per plan (fp32 plans whose
+// accumulators fit, see fused.cpp).
 constexpr int FUSED_MAX_OUT = 16;   // outputs per task (larger groups are split over several tasks)
 constexpr int FUSED_KC = 32;        // contracted indices per register chunk (8 matrix-core steps)
 // Splitting: a task with more register chunks than a share is split into up to
@@ -55,6 +60,7 @@ constexpr int FUSED_KC = 32;        // contracted indices per register chunk (8 
 // compute units, each holding as many workgroups as the kernel instance's
 // register use allows (one wave per SIMD per workgroup).
 constexpr int FUSED_CUS = 256;
+constexpr int64_t FUSED_WIDE_TASKS = 1024;   // 32 x 32 tiles only with at least this many tasks (4 per CU)
 constexpr int FUSED_MIN_PART = 4;
 inline int fused_wgs_per_cu(bsc_dtype dt, int no) {
     if (dt == BSC_F64) return no <= 8 ? 2 : 1;   // about 190-215 VGPRs; 256 at 16 outputs
@@ -129,6 +135,7 @@ struct FusedPlan {
     int64_t useful_flops = 0, alg_bytes = 0, stage1_flops = 0;
     int64_t terms = 0;              // nonzero (stage-1 block, output) weights
     int32_t outs_per_task = FUSED_MAX_OUT;   // 4, 8 or 16: the kernel instance
+    int32_t tile_blocks = 1;                 // TW: the wave's tile is TW x TW blocks of 16 x 16
     // device image
     size_t off_groups = 0, off_chans = 0, off_outs = 0, off_widx = 0, off_tasks = 0, off_parts = 0, off_pchans = 0;
     std::vector<unsigned char> image;

@@ -74,10 +74,11 @@ struct FuTraits<double> {
 
 constexpr int FUSED_STEPS = FUSED_KC / 4;   // matrix-core steps per chunk
 
-// one chunk of a product's operands in registers
-template <typename T>
+// one chunk of a product's operands in registers: for each of the wave's TW
+// row blocks of A and column blocks of B, one value per step
+template <typename T, int TW>
 struct FuChunk {
-    T a[FUSED_STEPS], b[FUSED_STEPS];
+    T a[TW][FUSED_STEPS], b[TW][FUSED_STEPS];
 };
 
 // A product's operands as raw buffers: each block's range in scalar registers
@@ -90,6 +91,7 @@ constexpr int32_t FU_RAW = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor w
 struct FuProd {
     __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t la, lb;        // lane byte offsets at k = 0 (row x of A, column x of B)
+    uint32_t a16, b16;      // bytes from one 16-row (16-column) block of the tile to the next
     uint32_t ka, kb;        // bytes per contracted index
     int32_t K, wrow, last;
 };
@@ -111,6 +113,8 @@ __device__ __forceinline__ FuProd fu_prod(const T *A, const T *B, const FChan &c
     P.rb = fu_rsrc(B + ch.b_off, ((ch.K - 1) * ch.b_ks + (N - 1) * ch.b_ns + 1) * SZ);
     P.la = static_cast<uint32_t>(i * ch.a_rs * SZ);
     P.lb = static_cast<uint32_t>(j * ch.b_ns * SZ);
+    P.a16 = static_cast<uint32_t>(FUSED_TILE * ch.a_rs * SZ);
+    P.b16 = static_cast<uint32_t>(FUSED_TILE * ch.b_ns * SZ);
     P.ka = static_cast<uint32_t>(ch.a_ks * SZ);
     P.kb = static_cast<uint32_t>(ch.b_ks * SZ);
     P.K = ch.K;
@@ -126,16 +130,23 @@ __device__ __forceinline__ double fu_buf(__amdgpu_buffer_rsrc_t r, uint32_t off,
     return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
-// chunk k0 of a product: lane (x, q) takes k = k0 + 4 s + q, s < FUSED_STEPS
-template <typename T>
-__device__ __forceinline__ void fu_load(const FuProd &P, int32_t k0, bool arow, bool bcol, int32_t q, FuChunk<T> &v) {
+// chunk k0 of a product: lane (x, q) takes k = k0 + 4 s + q, s < FUSED_STEPS,
+// for rows x + 16 i of A and columns x + 16 i of B (i < TW).  The offsets of
+// the masked elements (outside the tile, past K) are replaced, never formed
+// by adding to another (so they cannot wrap into the range).
+template <typename T, int TW>
+__device__ __forceinline__ void fu_load(const FuProd &P, int32_t k0, const bool (&arow)[TW], const bool (&bcol)[TW],
+                                        int32_t q, FuChunk<T, TW> &v) {
 #pragma unroll
     for (int s = 0; s < FUSED_STEPS; ++s) {
         const int32_t k = k0 + 4 * s + q;
         const bool ok = k < P.K;
         const uint32_t uk = static_cast<uint32_t>(k);
-        v.a[s] = fu_buf(P.ra, (arow && ok) ? P.la + uk * P.ka : FU_OOB, T(0));
-        v.b[s] = fu_buf(P.rb, (bcol && ok) ? P.lb + uk * P.kb : FU_OOB, T(0));
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            v.a[i][s] = fu_buf(P.ra, (arow[i] && ok) ? P.la + i * P.a16 + uk * P.ka : FU_OOB, T(0));
+            v.b[i][s] = fu_buf(P.rb, (bcol[i] && ok) ? P.lb + i * P.b16 + uk * P.kb : FU_OOB, T(0));
+        }
     }
 }
 
@@ -170,9 +181,9 @@ __device__ __forceinline__ FChan fu_rl(const FChan &c, int32_t l) {
 }
 
 // One ring slot: the chunk and what the compute step needs to know about it.
-template <typename T>
+template <typename T, int TW>
 struct FuSlot {
-    FuChunk<T> v;
+    FuChunk<T, TW> v;
     int32_t p;              // product index, -1: empty (the stream has ended)
     int32_t k0, K, wrow, last;
 };
@@ -184,28 +195,33 @@ struct FuSlot {
 // (zeros past K add nothing), so the compiler's wait counts stay exact:
 // computing a slot waits for that slot's loads only, never for the D - 1
 // chunks behind it.
-template <typename T, int NO>
+template <typename T, int NO, int TW>
 __device__ __forceinline__ void fused_stream(const FArgs &fa, const FPart &pr, int32_t lane,
-                                             typename FuTraits<T>::acc_t (&acc)[NO]) {
+                                             typename FuTraits<T>::acc_t (&acc)[NO][TW][TW]) {
     typedef typename FuTraits<T>::acc_t acc_t;
-    constexpr int D = FuTraits<T>::D;
+    constexpr int D = TW == 1 ? FuTraits<T>::D : 2;   // chunks in the ring (registers: TW^2 more per chunk)
     const T *A = static_cast<const T *>(fa.A);
     const T *B = static_cast<const T *>(fa.B);
     const T *W = static_cast<const T *>(fa.W);
     const bool tr = (pr.flags & G_FTRANS) != 0;
     const int32_t x = lane & 15, q = lane >> 4;
-    const bool arow = x < pr.ml, bcol = x < pr.nl;
+    bool arow[TW], bcol[TW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        arow[i] = x + FUSED_TILE * i < pr.ml;
+        bcol[i] = x + FUSED_TILE * i < pr.nl;
+    }
     const int32_t ia = pr.i0 + x, jb = pr.j0 + x;   // masked where out of the tile
     const FChan *chans = fa.pchans + pr.chan0;
 
-    FuSlot<T> ring[D];
+    FuSlot<T, TW> ring[D];
     // the issue cursor: product ip (operands P), next chunk offset ik
     int32_t ip = 0, ik = 0;
     FuProd P = fu_prod(A, B, pr.first, pr.M, pr.N, ia, jb);
     FChan myrec{};
     // the next chunk of the stream into slot sl; past the end the slot is
     // marked empty and its loads read zero
-    auto issue = [&](FuSlot<T> &sl) {
+    auto issue = [&](FuSlot<T, TW> &sl) {
         if (ik >= P.K && ip < pr.nchan) {
             ++ip;
             ik = 0;
@@ -219,7 +235,13 @@ __device__ __forceinline__ void fused_stream(const FArgs &fa, const FPart &pr, i
             }
         }
         const bool live = ip < pr.nchan;
-        fu_load(P, ik, arow && live, bcol && live, q, sl.v);
+        bool ar[TW], bc[TW];
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            ar[i] = arow[i] && live;
+            bc[i] = bcol[i] && live;
+        }
+        fu_load(P, ik, ar, bc, q, sl.v);
         sl.p = live ? ip : -1;
         sl.k0 = ik;
         sl.K = P.K;
@@ -251,18 +273,26 @@ __device__ __forceinline__ void fused_stream(const FArgs &fa, const FPart &pr, i
 #pragma unroll
     for (int u = 1; u < D; ++u) issue(ring[u]);
 
-    acc_t t1 = acc_t{0, 0, 0, 0};
+    acc_t t1[TW][TW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i)
+#pragma unroll
+        for (int j = 0; j < TW; ++j) t1[i][j] = acc_t{0, 0, 0, 0};
     while (true) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            FuSlot<T> &sl = ring[u];
+            FuSlot<T, TW> &sl = ring[u];
             // all steps, operands swapped for a transposed tile by selects
 #pragma unroll
-            for (int s = 0; s < FUSED_STEPS; ++s) {
-                const T xa = tr ? sl.v.b[s] : sl.v.a[s];
-                const T xb = tr ? sl.v.a[s] : sl.v.b[s];
-                t1 = FuTraits<T>::mma(xa, xb, t1);
-            }
+            for (int s = 0; s < FUSED_STEPS; ++s)
+#pragma unroll
+                for (int i = 0; i < TW; ++i)
+#pragma unroll
+                    for (int j = 0; j < TW; ++j) {
+                        const T xa = tr ? sl.v.b[j][s] : sl.v.a[i][s];
+                        const T xb = tr ? sl.v.a[i][s] : sl.v.b[j][s];
+                        t1[i][j] = FuTraits<T>::mma(xa, xb, t1[i][j]);
+                    }
             if (sl.p >= 0 && sl.k0 + FUSED_KC >= sl.K && sl.last) {
                 // the stage-1 block is complete: weighted into every output of the task
 #pragma unroll
@@ -274,10 +304,17 @@ __device__ __forceinline__ void fused_stream(const FArgs &fa, const FPart &pr, i
                         for (int mm = 1; mm < FUSED_WREG; ++mm)
                             if (m == mm) wgt = fu_rl(wv[mm], l);
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[o][v] = fma(wgt, t1[v], acc[o][v]);
+                        for (int i = 0; i < TW; ++i)
+#pragma unroll
+                            for (int j = 0; j < TW; ++j)
+#pragma unroll
+                                for (int v = 0; v < 4; ++v) acc[o][i][j][v] = fma(wgt, t1[i][j][v], acc[o][i][j][v]);
                     }
                 }
-                t1 = acc_t{0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < TW; ++i)
+#pragma unroll
+                    for (int j = 0; j < TW; ++j) t1[i][j] = acc_t{0, 0, 0, 0};
             }
             issue(sl);   // refill the slot
         }
@@ -286,47 +323,55 @@ __device__ __forceinline__ void fused_stream(const FArgs &fa, const FPart &pr, i
     }
 }
 
-template <typename T>
+template <typename T, int TW>
 struct FusedSmem {
-    T red[4][4][4][64];             // [wave][output of the pass][accumulator element][lane]
+    T red[4][4][4 * TW * TW][64];   // [wave][output of the pass][accumulator element][lane]
 };
 
 // Four slots per workgroup, one per wave: each wave runs its part; the parts
 // of a task are then added in part order by the part-0 wave, four outputs per
 // pass through shared memory, and written through the outputs' views.
-template <typename T, int NO>
+template <typename T, int NO, int TW>
 __global__ __launch_bounds__(256) void fused_contract(FArgs fa) {
     typedef typename FuTraits<T>::acc_t acc_t;
-    __shared__ FusedSmem<T> sm;
+    __shared__ FusedSmem<T, TW> sm;
     const int32_t w = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
     const int32_t lane = tid_x() & 63;
     const FPart pr = fa.parts[static_cast<int64_t>(blockIdx.x) * 4 + w];
-    acc_t acc[NO];
+    acc_t acc[NO][TW][TW];
 #pragma unroll
-    for (int o = 0; o < NO; ++o) acc[o] = acc_t{0, 0, 0, 0};
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int j = 0; j < TW; ++j) acc[o][i][j] = acc_t{0, 0, 0, 0};
     // output views, one per lane (the part-0 wave writes)
     FOut myout{};
     if (pr.nparts > 0 && pr.part == 0 && lane < pr.no) myout = fa.outs[pr.out0 + lane];
-    if (pr.nparts > 0 && pr.nchan > 0) fused_stream<T, NO>(fa, pr, lane, acc);
+    if (pr.nparts > 0 && pr.nchan > 0) fused_stream<T, NO, TW>(fa, pr, lane, acc);
 
     T *Cp = static_cast<T *>(fa.C);
     const bool tr = (pr.flags & G_FTRANS) != 0, accum = (pr.flags & G_ACCUMULATE) != 0;
     const int32_t x = lane & 15;
     // the part-0 wave's outputs (sum: the task's total for output o) through their views
-    auto write_out = [&](int32_t o, const acc_t &sum) {
+    auto write_out = [&](int32_t o, const acc_t (&sum)[TW][TW]) {
         const int64_t c_off = fu_rl(myout.c_off, o), c_rs = fu_rl(myout.c_rs, o), c_cs = fu_rl(myout.c_cs, o);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int32_t r = FuTraits<T>::row(lane, v);
-            const int32_t i = tr ? x : r, j = tr ? r : x;
-            if (i < pr.ml && j < pr.nl) {
-                const int64_t ad =
-                    c_off + static_cast<int64_t>(pr.i0 + i) * c_rs + static_cast<int64_t>(pr.j0 + j) * c_cs;
-                T val = sum[v];
-                if (accum) val += Cp[ad];
-                Cp[ad] = val;
-            }
-        }
+        for (int bi = 0; bi < TW; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < TW; ++bj)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int32_t r = FuTraits<T>::row(lane, v);
+                    const int32_t i = FUSED_TILE * bi + (tr ? x : r), j = FUSED_TILE * bj + (tr ? r : x);
+                    if (i < pr.ml && j < pr.nl) {
+                        const int64_t ad =
+                            c_off + static_cast<int64_t>(pr.i0 + i) * c_rs + static_cast<int64_t>(pr.j0 + j) * c_cs;
+                        T val = sum[bi][bj][v];
+                        if (accum) val += Cp[ad];
+                        Cp[ad] = val;
+                    }
+                }
     };
     if (!pr.reduce) {
         // no task of this workgroup is split (the same for all its waves): no barriers
@@ -345,7 +390,12 @@ __global__ __launch_bounds__(256) void fused_contract(FArgs fa) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) sm.red[w][u][v][lane] = acc[pass * 4 + u][v];
+                    for (int i = 0; i < TW; ++i)
+#pragma unroll
+                        for (int j = 0; j < TW; ++j)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                sm.red[w][u][(i * TW + j) * 4 + v][lane] = acc[pass * 4 + u][i][j][v];
             }
             __syncthreads();
             if (pr.nparts > 0 && pr.part == 0) {
@@ -353,10 +403,18 @@ __global__ __launch_bounds__(256) void fused_contract(FArgs fa) {
                 for (int u = 0; u < 4; ++u) {
                     const int32_t o = pass * 4 + u;
                     if (o < pr.no) {
-                        acc_t sum = acc[pass * 4 + u];
+                        acc_t sum[TW][TW];
+#pragma unroll
+                        for (int i = 0; i < TW; ++i)
+#pragma unroll
+                            for (int j = 0; j < TW; ++j) sum[i][j] = acc[pass * 4 + u][i][j];
                         for (int32_t pp = 1; pp < pr.nparts; ++pp) {
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) sum[v] += sm.red[w + pp][u][v][lane];
+                            for (int i = 0; i < TW; ++i)
+#pragma unroll
+                                for (int j = 0; j < TW; ++j)
+#pragma unroll
+                                    for (int v = 0; v < 4; ++v) sum[i][j][v] += sm.red[w + pp][u][(i * TW + j) * 4 + v][lane];
                         }
                         write_out(o, sum);
                     }

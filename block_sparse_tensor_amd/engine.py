@@ -284,7 +284,8 @@ class FusedPlan:
     index and B2 holds 1 x 1 blocks.  C1 is never formed: contract() reads
     A1, B1, B2 and writes C2 only."""
 
-    def __init__(self, con1, con2, dtype: str = None, accumulate: bool = False, split: int = 0):
+    def __init__(self, con1, con2, dtype: str = None, accumulate: bool = False, split: int = 0,
+                 tile_cols: int = 0):
         L = _capi.lib()
         self.dtype = dtype or con1.dtype
         if self.dtype not in ("f64", "f32"):
@@ -296,6 +297,7 @@ class FusedPlan:
         L.bsc_options_default(byref(opt))
         opt.accumulate = int(bool(accumulate))
         opt.split_k = int(split)   # waves per output tile: 0 automatic (up to 4), 1 never split
+        opt.tile_cols = int(tile_cols)   # a wave's output tile edge: 0 automatic, 16, 32 (fp32, <= 4 outputs)
         keep.arrays.append(opt)
         h = c_void_p()
         _check(L.bsc_fused_plan(*a1[:6], *a2[:6], DTYPES[self.dtype], byref(opt), byref(h)))

@@ -386,8 +386,10 @@ void bsc_chain_destroy(bsc_chain_t chain);
  * of that output (no term where B2 has no block).  C1 is neither read nor
  * written.  Overwrite or accumulate per opt->accumulate; opt->split_k bounds
  * how many waves share one output tile's stage-1 blocks (0: automatic, at
- * most 4; 1: one wave per tile; negative: BSC_ERR_ARG); other options are
- * ignored.  Requirements (else BSC_ERR_UNSUPPORTED): dtype BSC_F64 or BSC_F32;
+ * most 4; 1: one wave per tile; negative: BSC_ERR_ARG); opt->tile_cols sets
+ * a wave's output tile edge (0: automatic; 16; 32, taken for fp32 plans of at
+ * most 4 outputs per task and ignored otherwise; anything else: BSC_ERR_ARG);
+ * other options are ignored.  Requirements (else BSC_ERR_UNSUPPORTED): dtype BSC_F64 or BSC_F32;
  * every stage-2 B block and output column of dim 1; stage-1 A, B, C blocks and
  * the stage-2 output blocks single strided views (as M x N for the outputs);
  * at most 64 stage-1 blocks per stage-2 row key;
@@ -417,6 +419,7 @@ typedef struct {
     int64_t outs_per_task;          /* outputs one task accumulates (4, 8 or 16) */
     int64_t off_parts, n_parts;     /* per-wave records, four per workgroup */
     int64_t off_pchans, n_pchans;   /* the parts' product lists */
+    int64_t tile_blocks;            /* a wave's tile: tile_blocks^2 blocks of 16 x 16 */
 } bsc_fused_summary;
 bsc_status bsc_fused_plan(const bsc_index *m1, const bsc_index *k1, const bsc_index *n1, const bsc_operand *A1,
                           const bsc_operand *B1, const bsc_operand *C1, const bsc_index *m2, const bsc_index *k2,

@@ -62,6 +62,8 @@ def replay(fp, A1, B1, W, C2):
     s, groups, chans, outs, widx, tasks, parts, pchans = decode(fp)
     NO = s["outs_per_task"]
     assert NO in (4, 8, 16) and len(parts) % 4 == 0
+    assert s["tile_blocks"] in (1, 2)
+    TILE = 16 * s["tile_blocks"]
     assert s["groups"] == 0 or max(int(g["nblk"]) for g in groups) * NO <= 256
 
     def part_sum(pr):
@@ -143,26 +145,33 @@ def replay(fp, A1, B1, W, C2):
     return C2
 
 
+def _wide_chain():
+    # fp32, bond 1024 in 4 charges, one-column W: 32 x 32 wave tiles when asked
+    return C.small_chain(seed=3, layout="coop", dtype="f32", total=1024, qmax=4, sigma=2.0, w=1, values="int")
+
+
 CASES = {
-    # name: (chain, split bound)
-    "small-coop": (lambda: C.small_chain(seed=3, layout="coop", values="int"), 0),
-    "small-natural": (lambda: C.small_chain(seed=5, layout="natural", values="int", dtype="f32"), 0),
-    "rabc_u1": (lambda: C.rabc_u1(layout="coop", values="int"), 0),
+    # name: (chain, split bound, wave tile edge)
+    "small-coop": (lambda: C.small_chain(seed=3, layout="coop", values="int"), 0, 0),
+    "small-natural": (lambda: C.small_chain(seed=5, layout="natural", values="int", dtype="f32"), 0, 0),
+    "rabc_u1": (lambda: C.rabc_u1(layout="coop", values="int"), 0, 0),
     # every charge zero: 4 products per stage-1 block, 20 blocks and 20 outputs
     # per stage-2 row (outputs over three tasks), K over two chunks; unsplit,
     # 80 products per wave (past the 64 lane-held records)
-    "neutral-natural-unsplit": (lambda: C.neutral_chain(layout="natural"), 1),
-    "neutral-coop-f32-split": (lambda: C.neutral_chain(seed=4, layout="coop", dtype="f32"), 0),
+    "neutral-natural-unsplit": (lambda: C.neutral_chain(layout="natural"), 1, 0),
+    "neutral-coop-f32-split": (lambda: C.neutral_chain(seed=4, layout="coop", dtype="f32"), 0, 0),
+    "wide-coop-f32-tile32": (_wide_chain, 0, 32),
 }
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
 @pytest.mark.parametrize("accumulate", [False, True])
 def test_fused_replay_equals_two_stage_oracle(name, accumulate):
-    make, split = CASES[name]
+    make, split, tile = CASES[name]
     ch = make()
     s1, s2 = ch.stages[0], ch.stages[1]
-    fp = bst.FusedPlan(s1.con, s2.con, accumulate=accumulate, split=split)
+    fp = bst.FusedPlan(s1.con, s2.con, accumulate=accumulate, split=split, tile_cols=tile)
+    assert fp.stats()["tile_blocks"] == (2 if tile == 32 else 1)
     bufs = {k: np.asarray(v, np.float64) for k, v in ch.buffers.items()}
     rng = np.random.default_rng(11)
     c0 = rng.integers(-3, 4, ch.sizes[s2.c_buf]).astype(np.float64) if accumulate else np.zeros(ch.sizes[s2.c_buf])
@@ -252,3 +261,22 @@ def test_fused_split_bound_is_honoured():
     with pytest.raises(bst.BscError) as e:
         bst.FusedPlan(s1, s2, split=-1)
     assert e.value.name == "BSC_ERR_ARG"
+
+
+def test_fused_wave_tile_choice():
+    """32 x 32 wave tiles: fp32 with at most 4 outputs per task only, chosen
+    automatically when they add little padding and still make enough tasks."""
+    big = C.small_chain(seed=3, layout="coop", dtype="f32", total=2048, qmax=4, sigma=2.0, w=1)
+    wide = _wide_chain()
+    f64 = C.small_chain(seed=3, layout="coop", values="int")
+    tb = lambda ch, t: bst.FusedPlan(ch.stages[0].con, ch.stages[1].con, tile_cols=t).stats()["tile_blocks"]
+    assert tb(big, 0) == 2 and tb(big, 16) == 1
+    assert tb(wide, 0) == 1 and tb(wide, 32) == 2      # too few 32 x 32 tasks to pick by itself
+    assert tb(f64, 32) == 1                            # fp64 accumulators do not fit
+    s_wide = bst.FusedPlan(wide.stages[0].con, wide.stages[1].con, tile_cols=32).stats()
+    s_narrow = bst.FusedPlan(wide.stages[0].con, wide.stages[1].con, tile_cols=16).stats()
+    assert s_wide["items"] < s_narrow["items"]
+    for bad in (-16, 8, 64):
+        with pytest.raises(bst.BscError) as e:
+            bst.FusedPlan(wide.stages[0].con, wide.stages[1].con, tile_cols=bad)
+        assert e.value.name == "BSC_ERR_ARG"

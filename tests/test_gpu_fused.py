@@ -21,17 +21,24 @@ else:
     bst = None
 
 
+def _wide(total):
+    return lambda v: C.small_chain(seed=3, layout="coop", dtype="f32", total=total, qmax=4, sigma=2.0, w=1, values=v)
+
+
 def _cases():
-    # name: chain for a value kind, split bound
+    # name: chain for a value kind, split bound, wave tile edge (0 automatic)
     return {
-        "small-coop-f64": (lambda v: C.small_chain(seed=3, layout="coop", values=v), 0),
-        "small-natural-f32": (lambda v: C.small_chain(seed=5, layout="natural", values=v, dtype="f32"), 0),
-        "rabc_u1": (lambda v: C.rabc_u1(layout="coop", values=v), 0),
-        "rabc_u1u1": (lambda v: C.rabc_u1u1(layout="natural", values=v), 0),
+        "small-coop-f64": (lambda v: C.small_chain(seed=3, layout="coop", values=v), 0, 0),
+        "small-natural-f32": (lambda v: C.small_chain(seed=5, layout="natural", values=v, dtype="f32"), 0, 0),
+        "rabc_u1": (lambda v: C.rabc_u1(layout="coop", values=v), 0, 0),
+        "rabc_u1u1": (lambda v: C.rabc_u1u1(layout="natural", values=v), 0, 0),
         # all charges zero: several products per stage-1 block, 20 outputs per row
         # (three output chunks), K over two chunks; unsplit past 64 records per wave
-        "neutral-natural-unsplit": (lambda v: C.neutral_chain(layout="natural", values=v), 1),
-        "neutral-coop-f32-split": (lambda v: C.neutral_chain(seed=4, layout="coop", dtype="f32", values=v), 0),
+        "neutral-natural-unsplit": (lambda v: C.neutral_chain(layout="natural", values=v), 1, 0),
+        "neutral-coop-f32-split": (lambda v: C.neutral_chain(seed=4, layout="coop", dtype="f32", values=v), 0, 0),
+        # 32 x 32 wave tiles: asked for on a 1024 bond, chosen on a 2048 bond
+        "wide-coop-f32-tile32": (_wide(1024), 0, 32),
+        "big-coop-f32-auto": (_wide(2048), 0, 0),
     }
 
 
@@ -42,10 +49,10 @@ def _two_stage(ch, bufs, c0=None, accumulate=False):
     return oracle.contract(s2.con, t1, bufs[s2.b_buf], base.copy(), accumulate=accumulate)
 
 
-def _run_fused(ch, c_init, accumulate=False, repeats=1, split=0):
+def _run_fused(ch, c_init, accumulate=False, repeats=1, split=0, tile=0):
     t = torch()
     s1, s2 = ch.stages[0], ch.stages[1]
-    fp = bst.FusedPlan(s1.con, s2.con, accumulate=accumulate, split=split).bind()
+    fp = bst.FusedPlan(s1.con, s2.con, accumulate=accumulate, split=split, tile_cols=tile).bind()
     A1 = to_dev(ch.buffers[s1.a_buf], ch.dtype)
     B1 = to_dev(ch.buffers[s1.b_buf], ch.dtype)
     W = to_dev(ch.buffers[s2.b_buf], ch.dtype)
@@ -59,10 +66,11 @@ def _run_fused(ch, c_init, accumulate=False, repeats=1, split=0):
 
 
 @pytest.mark.parametrize("name", ["small-coop-f64", "small-natural-f32", "rabc_u1", "rabc_u1u1",
-                                  "neutral-natural-unsplit", "neutral-coop-f32-split"])
+                                  "neutral-natural-unsplit", "neutral-coop-f32-split", "wide-coop-f32-tile32",
+                                  "big-coop-f32-auto"])
 @pytest.mark.parametrize("accumulate", [False, True])
 def test_fused_int_bit_exact(name, accumulate):
-    make, split = _cases()[name]
+    make, split, tile = _cases()[name]
     ch = make("int")
     if ch.dtype == "f32":
         assert int_chain_bound(ch) < 2 ** 24
@@ -74,16 +82,19 @@ def test_fused_int_bit_exact(name, accumulate):
     bufs = {k: np.asarray(v, np.float64) for k, v in ch.buffers.items()}
     want = _two_stage(ch, bufs, np.nan_to_num(c0), accumulate)
     print(f"[fused] {name} int accumulate={accumulate}", flush=True)
-    fp, (got, again) = _run_fused(ch, c0, accumulate, repeats=2, split=split)
+    fp, (got, again) = _run_fused(ch, c0, accumulate, repeats=2, split=split, tile=tile)
+    if name.endswith("tile32") or name.startswith("big"):
+        assert fp.stats()["tile_blocks"] == 2
     assert np.all(np.isnan(got[~mask])), "a write landed outside the T2 views"
     assert np.array_equal(got[mask].astype(np.float64), want[mask]), name
     assert np.array_equal(got[mask], again[mask]), "repeats differ"
     assert fp.stats()["launches_issued"] == 2
 
 
-@pytest.mark.parametrize("name", ["small-coop-f64", "rabc_u1", "rabc_u1u1", "neutral-coop-f32-split"])
+@pytest.mark.parametrize("name", ["small-coop-f64", "rabc_u1", "rabc_u1u1", "neutral-coop-f32-split",
+                                  "big-coop-f32-auto"])
 def test_fused_normal_values_within_error_bound(name):
-    make, split = _cases()[name]
+    make, split, tile = _cases()[name]
     ch = make("normal")
     s2 = ch.stages[1]
     addr, mask = c_addresses(s2.con)
@@ -93,7 +104,7 @@ def test_fused_normal_values_within_error_bound(name):
     c0 = np.full(ch.sizes[s2.c_buf], np.nan)
     c0[mask] = 0.0
     print(f"[fused] {name} normal", flush=True)
-    _, (got,) = _run_fused(ch, c0, split=split)
+    _, (got,) = _run_fused(ch, c0, split=split, tile=tile)
     assert np.all(np.isnan(got[~mask]))
     errs = block_errors(s2.con, got.astype(np.float64), want, scale)
     worst = int(np.argmax(errs)) if len(errs) else 0

@@ -31,22 +31,22 @@ void bsc_options_default(bsc_options *opt) {
 static void fill_cost_defaults(bsc_options &o, bsc_dtype dt) {
     // MI355X defaults, measured on one MI355X with this library by the pack
     // calibration of the benchmark driver (calibrated constants may be passed
-    // in instead):
-    //   t_launch_us  the fixed cost of a plan's extra (gather) launch: a
-    //                19.7 KB gather adds 5.9 us to the U(1) update's W stage
-    //                beyond its bytes;
-    //   pack_gbps    the gather kernel moved 2 x 33.8 MB in 28.2 us (2.4 TB/s)
-    //                on the natural-layout environment update;
+    // in instead).  Over the eight gathers of the environment-update chains'
+    // stages and the unpadded block-diagonal bf16 workload (19.7 KB to
+    // 33.8 MB), the gather kernel's time fits 6.4 us + 2 x bytes / 4.9 TB/s:
+    //   t_launch_us  a plan's extra (gather) launch: the gather's fixed 6.4 us
+    //                plus the 0.6 us gap the second launch leaves;
+    //   pack_gbps    the gather's bandwidth, read + write bytes;
     //   tile_gflops  sustained whole-GPU rate of the matrix-core tiles on
     //                mid-sized sector GEMMs (bf16 ~ 250 TFLOP/s, fp32 and fp64
     //                ~ 10 TFLOP/s);
     //   t_seg_us     per extra piece walked by one tile: gathering every
-    //                operand of the U(1)xU(1) W stage saves 16.7 us of grouped
+    //                operand of the U(1)xU(1) W stage saves 16.8 us of grouped
     //                kernel time (beyond its padding term) for 35,364 units of
-    //                the piece term, 0.00046 us each.
-    if (o.t_launch_us <= 0) o.t_launch_us = 5.9;
-    if (o.t_seg_us <= 0) o.t_seg_us = 0.00046;
-    if (o.pack_gbps <= 0) o.pack_gbps = 2400.0;
+    //                the piece term, 0.00047 us each.
+    if (o.t_launch_us <= 0) o.t_launch_us = 7.0;
+    if (o.t_seg_us <= 0) o.t_seg_us = 0.00047;
+    if (o.pack_gbps <= 0) o.pack_gbps = 4900.0;
     if (o.tile_gflops <= 0) o.tile_gflops = dt == BSC_BF16_F32 ? 250000.0 : 10000.0;
 }
 

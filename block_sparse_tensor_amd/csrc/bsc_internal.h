@@ -194,6 +194,15 @@ constexpr bool has_record(int32_t cls) {
 }
 constexpr bool is_mfma(int32_t cls) { return cls == T_MFMA || cls == T_MFMA_DENSE || is_direct(cls); }
 constexpr int TILE_SKINNY_SHORT = 16;   // largest short extent of a skinny group
+// Slot time a 32-wide K chunk of the register-staged general bf16 tile costs
+// beyond the direct-to-LDS tile's, for the alignment gathers (microseconds
+// per chunk of a 128 x 128 tile): measured on MI355X on the block-diagonal
+// bf16 workload with every row misaligned (64 sectors, 609 general tiles of
+// 11,622 chunks in all), whose grouped kernel took 79.5 us on the general
+// tile and 30.7 us after gathering every operand into 16-byte rows:
+// 48.8 us x 512 concurrent tiles / 11,622 chunks.
+constexpr double ALIGN_CHUNK_US = 2.15;
+constexpr int32_t ALIGN_CHUNK_K = 32;   // K chunk of the general bf16 tile
 
 // Tail bundles (T_TAIL): up to four whole tiny groups per workgroup, one per
 // wave.  A tail group is one run of single views with near-zero flops
@@ -277,7 +286,7 @@ struct Plan {
     int64_t part_elems = 0;       // K-split partial tiles (fp32 elements)
     int32_t split_tiles = 0;      // output tiles cut along K
     // pack-cost model terms summed over the gathered operands (microseconds)
-    double gain_seg_us = 0, gain_pad_us = 0, pack_cost_us = 0;
+    double gain_seg_us = 0, gain_pad_us = 0, gain_align_us = 0, pack_cost_us = 0;
     std::vector<std::array<int32_t, 2>> launches;  // per-sector mode: task ranges, one launch each
 
     // device binding

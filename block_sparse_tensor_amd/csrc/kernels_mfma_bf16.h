@@ -12,6 +12,10 @@
 //   free-axis-contiguous -> 16-byte loads along M (or N) for two K rows,
 //                          interleaved into K-pairs while storing (transpose);
 //   anything else        -> element loads through the per-row address records.
+// The 16-byte loads need only element alignment: the HSA code object runs in
+// unaligned-access mode, so a row that starts at an odd element still takes
+// one vector load per 8 elements (rows of odd length, as sectors are stored
+// when nothing pads them, made every other row fall back to 8 element loads).
 // LDS rows are padded to 40 elements and skewed by 8 more every 8 rows so the
 // fragment reads and the transposing stores spread over all banks.
 #pragma once
@@ -83,6 +87,13 @@ __device__ __forceinline__ uint4 u4_from(const uint16_t e[8]) {
     return v;
 }
 
+// 8 consecutive bf16 values from any element address (one 16-byte load)
+__device__ __forceinline__ uint4 ld8_bf16(const uint16_t *p) {
+    uint4 v;
+    __builtin_memcpy(&v, p, sizeof(v));
+    return v;
+}
+
 __device__ __forceinline__ void mb_load(const OpCtx &o, int32_t k0, MbStage &st) {
     const int32_t tid = tid_x();
     if (o.mode == LD_KCONTIG) {
@@ -93,8 +104,8 @@ __device__ __forceinline__ void mb_load(const OpCtx &o, int32_t k0, MbStage &st)
             uint4 v = make_uint4(0, 0, 0, 0);
             if (x < o.xlen && k < o.K) {
                 const int64_t ad = o.rec[x].base + k;
-                if (o.vec && k + 8 <= o.K && (ad & 7) == 0) {
-                    v = *reinterpret_cast<const uint4 *>(o.P + ad);
+                if (k + 8 <= o.K) {
+                    v = ld8_bf16(o.P + ad);
                 } else {
                     uint16_t e[8];
 #pragma unroll
@@ -112,8 +123,8 @@ __device__ __forceinline__ void mb_load(const OpCtx &o, int32_t k0, MbStage &st)
             uint4 v = make_uint4(0, 0, 0, 0);
             if (k < o.K && x < o.xlen) {
                 const int64_t ad = o.off + static_cast<int64_t>(o.x0 + x) + static_cast<int64_t>(k) * o.sk;
-                if (o.vec && x + 8 <= o.xlen && (ad & 7) == 0) {
-                    v = *reinterpret_cast<const uint4 *>(o.P + ad);
+                if (x + 8 <= o.xlen) {
+                    v = ld8_bf16(o.P + ad);
                 } else {
                     uint16_t e[8];
 #pragma unroll
@@ -282,9 +293,18 @@ __device__ __forceinline__ void mfma_tile_bf16(const KArgs &ka, const DTask &tas
             if (!cn) {
                 const Rec rc = sm.ra[i];
                 const int64_t ad = along(rc, n0 + c4);
-                if (!accum && sizeof(TC) == 4 && rc.in == 1 && rc.s0 == 1 && c4 + 4 <= nlen && (ad & 3) == 0 &&
-                    (reinterpret_cast<uintptr_t>(Cp) & 15) == 0) {
-                    *reinterpret_cast<float4 *>(Cp + ad) = v;
+                if (sizeof(TC) == 4 && rc.in == 1 && rc.s0 == 1 && c4 + 4 <= nlen) {
+                    // four consecutive fp32 outputs, one 16-byte access at any element address
+                    float4 o = v;
+                    if (accum) {
+                        float4 c;
+                        __builtin_memcpy(&c, Cp + ad, sizeof(c));
+                        o.x += c.x;
+                        o.y += c.y;
+                        o.z += c.z;
+                        o.w += c.w;
+                    }
+                    __builtin_memcpy(Cp + ad, &o, sizeof(o));
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {

@@ -56,11 +56,26 @@ __global__ __launch_bounds__(256) void pack_gather(PArgs pa) {
         const bool s_f = d.ia == 1 && (d.sa0 == 1 || d.rows == 1);
         const bool d_k = d.dmode == 0;
         if ((d_k && s_k) || (!d_k && s_f)) {
-            // same unit axis on both sides: straight copy along it
-            for (int32_t e = tid; e < n; e += 256) {
-                const int32_t x = d_k ? e / cols : e % rows;
-                const int32_t y = d_k ? e % cols : e / rows;
-                W[pack_dst(d, x0 + x, y0 + y)] = S[pack_src(d, x0 + x, y0 + y)];
+            // same unit axis on both sides: straight copy along it, 16 bytes
+            // per lane (any element address: the code object runs in
+            // unaligned-access mode), the line's last partial vector element
+            // by element
+            constexpr int32_t V = 16 / static_cast<int32_t>(sizeof(T));
+            const int32_t len = d_k ? cols : rows;     // extent along the unit axis
+            const int32_t nv = (len + V - 1) / V;      // vectors per line
+            const int32_t units = (d_k ? rows : cols) * nv;
+            for (int32_t e = tid; e < units; e += 256) {
+                const int32_t line = e / nv, u = (e - line * nv) * V;
+                const int32_t x = d_k ? line : u, y = d_k ? u : line;
+                const T *sp = S + pack_src(d, x0 + x, y0 + y);
+                T *dp = W + pack_dst(d, x0 + x, y0 + y);
+                if (u + V <= len) {
+                    uint4 v;
+                    __builtin_memcpy(&v, sp, sizeof(v));
+                    __builtin_memcpy(dp, &v, sizeof(v));
+                } else {
+                    for (int32_t j = 0; u + j < len; ++j) dp[j] = sp[j];
+                }
             }
             continue;
         }

@@ -513,9 +513,11 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         p.ws_elems = 0;
 
         // Whether an operand of a group, as per-k-segment piece lists, is one
-        // strided view over the group's whole free x contracted extent.
-        auto one_view = [&](const std::vector<std::vector<DView>> &seg, const std::vector<int64_t> &segK) {
-            DView v{};
+        // strided view over the group's whole free x contracted extent (the
+        // view in v when it is).
+        auto merged_view = [&](const std::vector<std::vector<DView>> &seg, const std::vector<int64_t> &segK,
+                               DView &v) {
+            v = DView{};
             int64_t kk = 0;
             for (size_t s = 0; s < seg.size(); ++s) {
                 if (seg[s].size() != 1) return false;
@@ -523,7 +525,11 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                 else if (!merge_along_b(v, kk, seg[s][0], segK[s])) return false;
                 kk += segK[s];
             }
-            return true;
+            return !seg.empty();
+        };
+        auto one_view = [&](const std::vector<std::vector<DView>> &seg, const std::vector<int64_t> &segK) {
+            DView v;
+            return merged_view(seg, segK, v);
         };
         // Pack-cost-versus-savings model (uni20 "block coalescing", section
         // "Interleaved vs contiguous — the real tradeoff is a copy", and the
@@ -564,6 +570,42 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             p.gain_pad_us += gain_pad;
             p.pack_cost_us += cost;
             return true;
+        };
+        // Alignment gathers (bf16).  The direct-to-LDS tile copies 16-byte
+        // granules, so it takes a group only when A is one view with K-contiguous
+        // rows and B one view with N- or K-contiguous lines, every line starting
+        // on a 16-byte boundary.  A group that is single views but misaligned
+        // (blocks stored back to back with odd extents, as nothing pads them)
+        // runs on the register-staged general tile (128 x 128) instead, whose
+        // K chunks each hold a tile slot ALIGN_CHUNK_US longer than the direct
+        // tile needs for the same work.  Gathering the misaligned operands into
+        // 16-byte rows costs their traffic and saves that time on every chunk
+        // of every general tile of the group (tiles run CONCURRENT_TILES at a
+        // time).  Decides both operands of the group.
+        auto decide_align = [&](const DGroup &dg, const GroupSpec &g, const std::vector<std::vector<DView>> &sa,
+                                const std::vector<std::vector<DView>> &sb, const std::vector<int64_t> &segK,
+                                bool &pa, bool &pb) {
+            pa = pb = false;
+            if (per_sector || p.dtype != BSC_BF16_F32 || p.opt.layout_policy == BSC_LAYOUT_NEVER_PACK) return;
+            if (std::min(dg.M, dg.N) <= TILE_SKINNY_SHORT || (int64_t)dg.M * dg.N * dg.K < 32 * 32 * 16) return;
+            if (g.rows.size() != 1 || g.cols.size() != 1) return;
+            const Blk &cb = p.C[(size_t)g.cblk[0]];
+            if (cb.ri != 1 || cb.ci != 1) return;   // the dense tile writes a single-leg C view
+            DView va, vb;
+            if (!merged_view(sa, segK, va) || !merged_view(sb, segK, vb) || va.ia != 1 || vb.ia != 1) return;
+            const bool a_ok = vec_kcontig({va}, dg.K);
+            const bool b_ok = vec_ncontig({vb}, dg.K, p.b_elems) || vec_kcontig({vb}, dg.K);
+            if (a_ok && b_ok) return;
+            const double tiles = (double)((dg.M + TILE_MFMA - 1) / TILE_MFMA) * ((dg.N + TILE_MFMA - 1) / TILE_MFMA);
+            const double gain = tiles * (double)((dg.K + ALIGN_CHUNK_K - 1) / ALIGN_CHUNK_K) * ALIGN_CHUNK_US / concurrent;
+            const double cost = 2.0 * (double)((a_ok ? 0 : (int64_t)dg.M * dg.K) + (b_ok ? 0 : (int64_t)dg.N * dg.K)) *
+                                esz / (p.opt.pack_gbps * 1e3);
+            if (p.opt.layout_policy != BSC_LAYOUT_FORCE_PACK && gain <= cost) return;
+            pa = !a_ok;
+            pb = !b_ok;
+            pack_net_us += gain - cost;
+            p.gain_align_us += gain;
+            p.pack_cost_us += cost;
         };
         // Gather an operand into a fresh workspace region with a constant
         // leading dimension (rounded up to 8 elements: 16-byte rows for every
@@ -655,8 +697,10 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                 segK.push_back(p.dk[kk]);
             }
             // operand arrangement: the zero-copy pieces, or one gather into the workspace
-            const bool pack_a = !per_sector && decide_pack(dg, segA, segK, true);
-            const bool pack_b = !per_sector && decide_pack(dg, segB, segK, false);
+            bool align_a = false, align_b = false;
+            decide_align(dg, g, segA, segB, segK, align_a, align_b);
+            const bool pack_a = align_a || (!per_sector && decide_pack(dg, segA, segK, true));
+            const bool pack_b = align_b || (!per_sector && decide_pack(dg, segB, segK, false));
             if (pack_a) segA = pack_operand(segA, segK, dg.M, dg.K, 0);
             if (pack_b) segB = pack_operand(segB, segK, dg.N, dg.K, 1);
             // merge consecutive segments into runs while both operands continue as one view
@@ -1174,7 +1218,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         // a plan with gathers needs one more launch: keep them only if they pay for it
         if (!p.packs.empty() && p.opt.layout_policy == BSC_LAYOUT_AUTO && pack_net_us <= p.opt.t_launch_us) {
             p.opt.layout_policy = BSC_LAYOUT_NEVER_PACK;
-            p.gain_seg_us = p.gain_pad_us = p.pack_cost_us = 0;
+            p.gain_seg_us = p.gain_pad_us = p.gain_align_us = p.pack_cost_us = 0;
             return build_plan(p, m, k, n, A, B, C);
         }
 
@@ -1254,6 +1298,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         s.pack_gain_seg_us = p.gain_seg_us;
         s.pack_gain_pad_us = p.gain_pad_us;
         s.pack_cost_us = p.pack_cost_us;
+        s.pack_gain_align_us = p.gain_align_us;
         const double rate_gflops = p.dtype == BSC_BF16_F32 ? 2.5e6 : (p.dtype == BSC_F32 ? 157.3e3 : 78.6e3);
         s.predicted_us = s.launches_per_contract * p.opt.t_launch_us +
                          std::max((double)flops / (rate_gflops * 1e3), (double)s.alg_bytes / 8.0e6) +

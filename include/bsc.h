@@ -196,6 +196,9 @@ typedef struct {
     /* the pack-cost model's terms over the gathered operands (0 without gathers):
      * saved piece set-ups (t_seg_us), saved K-step padding, gather traffic */
     double pack_gain_seg_us, pack_gain_pad_us, pack_cost_us;
+    /* bf16: time saved by gathering misaligned single-view operands into
+     * 16-byte rows, which moves their groups onto the direct-to-LDS tile */
+    double pack_gain_align_us;
 } bsc_stats;
 
 typedef struct bsc_plan_s *bsc_plan_t;

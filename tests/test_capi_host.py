@@ -86,8 +86,36 @@ def test_per_sector_stats():
 
 def test_blockdiag_bf16_one_launch():
     _lib_or_skip()
-    s = bst.Plan(C.blockdiag_bf16(values=False).con).stats()
-    assert s["launches_per_contract"] == 1 and s["launches_per_sector"] == 64
+    # padded rows: one grouped launch, every large group on the direct-to-LDS tile
+    s = bst.Plan(C.blockdiag_bf16(values=False, ld_align=8, align=8).con).stats()
+    assert s["launches_per_contract"] == 1 and s["launches_per_sector"] == 64 and s["pack_bytes"] == 0
+    # the as-generated layout gathers nothing when told not to
+    s = bst.Plan(C.blockdiag_bf16(values=False).con, layout="never_pack").stats()
+    assert s["launches_per_contract"] == 1 and s["items_by_class"]["mfma_fast"] == 0
+
+
+def test_alignment_gathers():
+    """bf16 groups whose single-view operands have rows off 16-byte boundaries:
+    the planner gathers the misaligned operands of the large groups (the
+    modelled saving at the two tiles' rates exceeds the traffic) into 16-byte
+    rows, which puts those groups on the direct-to-LDS tile; small groups
+    stay where they are."""
+    _lib_or_skip()
+    prob = C.blockdiag_bf16(values=False)
+    con = prob.con
+    s = bst.Plan(con).stats()
+    assert s["launches_per_contract"] == 2 and s["pack_gain_align_us"] > s["pack_cost_us"] > 0
+    assert s["items_by_class"]["mfma_fast"] > 0 and s["items_by_class"]["mfma"] > 0
+    # the gathered operands are the misaligned blocks of the groups above the
+    # modelled break-even (M N / (M + N) > ~150 for square blocks)
+    dims = [int(d) for d in con.m.dim]
+    big = [d for d in dims if d % 8 != 0 and d > 320]
+    assert s["mode_count"]["A"]["pack"] >= len(big) and s["mode_count"]["B"]["pack"] >= len(big)
+    assert s["pack_bytes"] >= sum(2 * 2 * d * d for d in big)
+    # fp32 / fp64 plans have no direct-to-LDS tile: nothing to align
+    p32 = C.blockdiag_bf16(values=False)
+    p32.con.dtype = "f32"
+    assert bst.Plan(p32.con, dtype="f32").stats()["pack_gain_align_us"] == 0
 
 
 def test_zero_blocks_counted():

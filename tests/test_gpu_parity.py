@@ -109,10 +109,25 @@ def test_accumulate(dtype):
 
 
 def test_blockdiag_bf16_full_size():
+    """The as-generated layout (blocks back to back, rows off 16-byte
+    boundaries): the large groups' operands are gathered into 16-byte rows
+    (one gather launch) and run on the direct-to-LDS tile, the rest on the
+    general tile."""
     prob = C.blockdiag_bf16()
     plan, got = _parity(prob, axis="auto")
     s = plan.stats()
-    assert s["launches_per_contract"] == 1 and s["launches_per_sector"] == 64
+    assert s["launches_per_contract"] == 2 and s["launches_per_sector"] == 64
+    assert s["pack_bytes"] > 0 and s["pack_gain_align_us"] > 0
+    assert s["items_by_class"]["mfma_fast"] > 0 and s["items_by_class"]["mfma"] > 0
+
+
+def test_blockdiag_bf16_full_size_no_gathers():
+    """The same layout without gathers: every tile on the general tile, whose
+    16-byte loads and stores start at any element."""
+    prob = C.blockdiag_bf16()
+    plan, got = _parity(prob, axis="auto", layout="never_pack")
+    s = plan.stats()
+    assert s["launches_per_contract"] == 1 and s["items_by_class"]["mfma_fast"] == 0
 
 
 def test_blockdiag_bf16_full_size_aligned():
@@ -123,17 +138,18 @@ def test_blockdiag_bf16_full_size_aligned():
     assert s["items_by_class"]["mfma_fast"] > 0 and s["launches_per_contract"] == 1
 
 
-@pytest.mark.parametrize("ld_align", [8, 1])
-def test_blockdiag_bf16_full_size_int_bit_exact(ld_align):
+@pytest.mark.parametrize("ld_align,layout", [(8, "auto"), (1, "auto"), (1, "never_pack")])
+def test_blockdiag_bf16_full_size_int_bit_exact(ld_align, layout):
     """The bench workload's structure and launch configuration (default plan
     options) on integer values in {-2..2}: every element of every C block,
     the 19 tail sectors of dims 1-4 included, equal to the oracle bit for
-    bit (K <= 1024, so every partial sum is an exact fp32 integer)."""
+    bit (K <= 1024, so every partial sum is an exact fp32 integer).  Unpadded,
+    automatically with alignment gathers and without any."""
     prob = C.blockdiag_bf16(ld_align=ld_align, align=ld_align, int_values=True)
-    plan, got = _parity(prob, axis="auto", exact=True, min_triples=64)
+    plan, got = _parity(prob, axis="auto", exact=True, min_triples=64, layout=layout)
     s = plan.stats()
-    assert s["launches_per_contract"] == 1
-    if ld_align == 8:
+    assert s["launches_per_contract"] == (2 if (ld_align, layout) == (1, "auto") else 1)
+    if layout == "auto":
         assert s["items_by_class"]["mfma_fast"] > 0
 
 

@@ -120,6 +120,30 @@ def test_split_repeat_deterministic_and_accumulate():
     check_float(con, got, ref3, a, b, 2e-2, label="accumulate x3")
 
 
+@pytest.mark.parametrize("split_k", [15, 10, 6])
+def test_split_normal_values_repeat_bit_identical(split_k):
+    """Normal values, two to five slices: the partials are added in slice
+    order whichever slice arrives last (the last slice adds the others around
+    its own partial in that order), so launches repeat bit for bit."""
+    con, a, b = _single(300, 900, 200, True, seed=10, ints=False)
+    addr, mask = c_addresses(con)
+    t = torch()
+    A, B = to_dev(a, "bf16"), to_dev(b, "bf16")
+    plan = bst.Plan(con, split_k=split_k).bind()
+    assert plan.stats()["split_tiles"] >= 4
+    Cd = t.zeros(con.C.buffer_elems, dtype=t.float32, device="cuda")
+    outs = []
+    for i in range(6):
+        print(f"[split] normal repeat split_k={split_k} {i}", flush=True)
+        plan.contract(A, B, Cd)
+        t.cuda.synchronize()
+        outs.append(Cd.cpu().numpy().copy())
+    for o in outs[1:]:
+        assert np.array_equal(o[addr], outs[0][addr])
+    ref = oracle.contract(con, a, b, np.zeros(con.C.buffer_elems), check=False)
+    check_float(con, outs[0], ref, a, b, 2e-2, label=f"normal split_k={split_k}")
+
+
 def test_split_unaligned_fallback():
     """Operand bases off a 16-byte boundary: split tiles run on the general
     matrix-core tile, the first slice computing the whole tile."""

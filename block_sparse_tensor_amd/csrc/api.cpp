@@ -31,9 +31,10 @@ void bsc_options_default(bsc_options *opt) {
 static void fill_cost_defaults(bsc_options &o, bsc_dtype dt) {
     // MI355X defaults, measured on one MI355X with this library by the pack
     // calibration of the benchmark driver (calibrated constants may be passed
-    // in instead).  Over the eight gathers of the environment-update chains'
-    // stages and the unpadded block-diagonal bf16 workload (19.7 KB to
-    // 33.8 MB), the gather kernel's time fits 6.4 us + 2 x bytes / 4.9 TB/s:
+    // in instead).  Over six gathers of the environment-update chains' stages
+    // and the unpadded block-diagonal bf16 workload (4.3 to 33.8 MB), the
+    // gather kernel's time fits 6.4 us + 2 x bytes / 4.9 TB/s (a 19.7 KB
+    // gather took 5.4 us):
     //   t_launch_us  a plan's extra (gather) launch: the gather's fixed 6.4 us
     //                plus the 0.6 us gap the second launch leaves;
     //   pack_gbps    the gather's bandwidth, read + write bytes;

@@ -503,11 +503,22 @@ __device__ __forceinline__ bool split_arrive(const KArgs &ka, const DFast &fd, f
     }
     __syncthreads();
     if (!last) return false;
-    // The sum is p0 + p1 + ... + p(S-1), added left to right.  Loads go out in
-    // batches of SPLIT_BATCH before any of them is used: added one by one, each
-    // load would wait out a full memory round trip.
+    // slice 0 replaces the accumulators, slices 1.. add in order.  Loads go out
+    // in batches of SPLIT_BATCH before any of them is used: added one by one,
+    // each load would wait out a full memory round trip.
     constexpr int SPLIT_BATCH = 16;
-    auto add_slice = [&](int32_t s) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        f32x16_t &a = acc[q / 8][(q / 4) & 1];
+        const int r = 4 * (q & 3);
+        // (the whole vector is reinterpreted at once: extracting single lanes of
+        // the loaded integer vector through bit casts is narrowed to a
+        // one-dword load by this compiler)
+        const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + q * 1024, 0, CPOL_SC1));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[r + e] = x[e];
+    }
+    for (int32_t s = 1; s < nsplit; ++s) {
         const int32_t src = s * SPLIT_BYTES + lane_off;
 #pragma unroll
         for (int h = 0; h < NQ; h += SPLIT_BATCH) {
@@ -525,29 +536,7 @@ __device__ __forceinline__ bool split_arrive(const KArgs &ka, const DFast &fd, f
                 for (int e = 0; e < 4; ++e) a[r + e] += x[e];
             }
         }
-    };
-    // The last slice already holds its own partial.  As slice 0 it adds p1,
-    // p2, ... in order; as slice 1 it adds p0 (a + b and b + a are the same
-    // float) and then p2, ...; a later slice reloads every partial, its own
-    // included, because p0 + p1 must be formed first.
-    const int32_t me = __builtin_amdgcn_readfirstlane(fd.split);
-    if (me <= 1) {
-        for (int32_t s = 0; s < nsplit; ++s)
-            if (s != me) add_slice(s);
-        return true;
     }
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        f32x16_t &a = acc[q / 8][(q / 4) & 1];
-        const int r = 4 * (q & 3);
-        // (the whole vector is reinterpreted at once: extracting single lanes of
-        // the loaded integer vector through bit casts is narrowed to a
-        // one-dword load by this compiler)
-        const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + q * 1024, 0, CPOL_SC1));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[r + e] = x[e];
-    }
-    for (int32_t s = 1; s < nsplit; ++s) add_slice(s);
     return true;
 }
 

@@ -249,11 +249,17 @@ void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *
         }
         return wgs;
     };
-    // a quarter over what fits at once: the longest parts go first and finish last
-    const int64_t cap = (int64_t)FUSED_CUS * fused_wgs_per_cu(f.dtype, f.outs_per_task) * 5 / 4;
+    // Split only a plan whose unsplit workgroups leave CUs idle, and then up
+    // to a quarter over what fits at once (the longest parts go first and
+    // finish last).  Measured on MI355X: U(1)xU(1) (1289 unsplit workgroups,
+    // 1280 resident) 33.2 us unsplit, 36.3 us split to 1489; the U(1) update
+    // (329 unsplit, 512 resident) 30.5 -> 21.2 us split to 549.
+    const int64_t resident = (int64_t)FUSED_CUS * fused_wgs_per_cu(f.dtype, f.outs_per_task, f.tile_blocks);
+    const int64_t cap = resident * 5 / 4;
     int64_t share = INT64_MAX;
+    const bool idle = ((int64_t)f.tasks.size() + 3) / 4 < resident;   // unsplit: four tasks per workgroup
     for (int64_t cand : {4, 5, 6, 8, 10, 12, 16, 24, 32, 48, 64}) {
-        if (max_parts <= 1) break;
+        if (max_parts <= 1 || !idle) break;
         if (cand < FUSED_MIN_PART) continue;
         if (wgs_for(cand) <= cap) {
             share = cand;

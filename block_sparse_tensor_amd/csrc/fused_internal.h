@@ -62,9 +62,12 @@ constexpr int FUSED_KC = 32;        // contracted indices per register chunk (8 
 constexpr int FUSED_CUS = 256;
 constexpr int64_t FUSED_WIDE_TASKS = 1024;   // 32 x 32 tiles only with at least this many tasks (4 per CU)
 constexpr int FUSED_MIN_PART = 4;
-inline int fused_wgs_per_cu(bsc_dtype dt, int no) {
-    if (dt == BSC_F64) return no <= 8 ? 2 : 1;   // about 190-215 VGPRs; 256 at 16 outputs
-    return no <= 8 ? 3 : 2;                       // about 135-150 VGPRs; 240 at 16 outputs
+inline int fused_wgs_per_cu(bsc_dtype dt, int no, int tile_blocks) {
+    // every workgroup puts one wave on each SIMD, so this is the instance's
+    // waves per SIMD as compiled (register counts from the compiler's report)
+    if (dt == BSC_F64) return no <= 4 ? 3 : 2;      // 146 / 176 / 240 VGPRs at 4 / 8 / 16 outputs
+    if (tile_blocks == 2) return 2;                 // 32 x 32 tiles: 185 VGPRs + 24 accumulation registers
+    return no <= 4 ? 5 : (no <= 8 ? 4 : 3);         // 78 / 96 / 129 VGPRs
 }
 
 struct FGroup {

@@ -11,7 +11,10 @@
 //  * Products are walked in order through a ring of D register chunks of
 //    FUSED_KC contracted indices: while one chunk runs on the matrix cores
 //    (v_mfma_f64_16x16x4_f64 / v_mfma_f32_16x16x4_f32), the next D - 1 are in
-//    flight.  Lane l supplies A_p(i0 + (l & 15), k) and B_p(k, j0 + (l & 15))
+//    flight (D = 2 for fp64; for fp32 D = 1, the refill issued after each
+//    chunk, and the latency hidden by the other waves: the smaller ring
+//    leaves room for five waves per SIMD, which measured faster than four
+//    waves with four or two chunks each).  Lane l supplies A_p(i0 + (l & 15), k) and B_p(k, j0 + (l & 15))
 //    for k = k0 + 4 s + (l >> 4), read through raw buffer descriptors over the
 //    product's operand blocks (consecutive lanes read consecutive rows of A_p
 //    and columns of B_p, the operands' contiguous axes in the environment
@@ -55,7 +58,7 @@ struct FuTraits;
 template <>
 struct FuTraits<float> {
     typedef fu_f32x4 acc_t;
-    static constexpr int D = 4;     // register chunks in the ring
+    static constexpr int D = 1;     // register chunks in the ring
     // tile row of accumulator element v of lane l (column l & 15)
     static __device__ __forceinline__ int32_t row(int32_t l, int32_t v) { return (l >> 4) * 4 + v; }
     static __device__ __forceinline__ acc_t mma(float a, float b, acc_t c) {
@@ -65,7 +68,7 @@ struct FuTraits<float> {
 template <>
 struct FuTraits<double> {
     typedef fu_f64x4 acc_t;
-    static constexpr int D = 3;
+    static constexpr int D = 2;
     static __device__ __forceinline__ int32_t row(int32_t l, int32_t v) { return (l >> 4) + 4 * v; }
     static __device__ __forceinline__ acc_t mma(double a, double b, acc_t c) {
         return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);

@@ -315,6 +315,47 @@ def measured_mfma_peaks(torch, bst):
     return out
 
 
+def measured_memory_peaks(torch):
+    """Memory rates and launch cost measured on this GPU, beside the published
+    HBM figure: a device-to-device copy (torch copy_, the runtime's copy
+    kernel) of 2 x 2 GiB buffers, far larger than the 256 MB Infinity Cache
+    (HBM), and of 2 x 32 MiB buffers copied back to back, which stay in the
+    Infinity Cache (MALL); bytes counted as read + write.  Launch cost: the
+    interval between back-to-back launches of a one-element kernel."""
+    def rate(nbytes, reps):
+        n = nbytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        gbps = 2.0 * n * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+        return round(gbps, 1)
+    hbm = rate(2 << 30, 5)
+    mall = rate(32 << 20, 200)
+    x = torch.zeros(1, dtype=torch.float32, device="cuda")
+    x.add_(1.0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(500):
+        x.add_(1.0)
+    e1.record()
+    torch.cuda.synchronize()
+    launch_us = e0.elapsed_time(e1) * 1e3 / 500
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbps": hbm, "mall_copy_gbps": mall, "hbm_spec_gbps": HBM_PEAK,
+            "hbm_frac_of_spec": round(hbm / HBM_PEAK, 4), "launch_interval_us": round(launch_us, 3),
+            "kind": "torch copy_ of 2 x 2 GiB (HBM) and 2 x 32 MiB (Infinity Cache), read + write bytes; "
+                    "back-to-back one-element kernels"}
+
+
 def load_workload(name, ld_align=1, relayout=False):
     from workloads import configs as C
     if name == "blockdiag_bf16":
@@ -732,8 +773,12 @@ def main():
     }
     mpk = measured_mfma_peaks(torch, bst)
     out["mfma_peak_measured"] = dict(mpk, unit="TFLOP/s", spec=MFMA_PEAK, kernel="bsc_probe_mfma")
+    mem = measured_memory_peaks(torch)
+    out["memory_peak_measured"] = mem
     if not hbm_bound:
         out["roofline"]["frac_of_measured_peak"] = round(achieved_tflops / mpk[dtype], 5)
+    else:
+        out["roofline"]["frac_of_measured_peak"] = round(achieved_gbps / mem["hbm_copy_gbps"], 5)
     if pack_phase:
         out["pack_phase"] = pack_phase
     if graph is not None:

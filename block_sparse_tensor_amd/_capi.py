@@ -22,7 +22,8 @@ EXPORTED = ["bsc_options_default", "bsc_plan", "bsc_plan_device_bytes", "bsc_pla
             "bsc_last_error", "bsc_chain_create", "bsc_chain_launch", "bsc_chain_destroy", "bsc_plan_cache_create",
             "bsc_plan_cached", "bsc_plan_cache_stats", "bsc_plan_cache_destroy", "bsc_plan_layout",
             "bsc_contract_noalloc", "bsc_fused_plan", "bsc_fused_device_bytes", "bsc_fused_bind",
-            "bsc_fused_contract", "bsc_fused_stats", "bsc_fused_worklist", "bsc_fused_destroy", "bsc_probe_mfma"]
+            "bsc_fused_contract", "bsc_fused_stats", "bsc_fused_worklist", "bsc_fused_destroy", "bsc_probe_mfma",
+            "bsc_stream_plan"]
 
 
 class BscIndex(ctypes.Structure):
@@ -69,7 +70,7 @@ class BscFusedStats(ctypes.Structure):
                                         "useful_flops", "stage1_flops", "alg_bytes", "device_bytes",
                                         "launches_issued", "off_groups", "off_chans", "off_outs", "off_widx",
                                         "off_tasks", "outs_per_task", "off_parts", "n_parts", "off_pchans",
-                                        "n_pchans", "tile_blocks")]
+                                        "n_pchans", "tile_blocks", "stream", "off_ones")]
 
 
 _lib = None
@@ -135,6 +136,9 @@ def lib():
         L.bsc_fused_plan.argtypes = ([POINTER(BscIndex)] * 3 + [POINTER(BscOperand)] * 3) * 2 + [
             c_int32, POINTER(BscOptions), POINTER(c_void_p)]
         L.bsc_fused_plan.restype = c_int32
+        L.bsc_stream_plan.argtypes = [POINTER(BscIndex)] * 3 + [POINTER(BscOperand)] * 3 + [
+            c_int32, POINTER(BscOptions), POINTER(c_void_p)]
+        L.bsc_stream_plan.restype = c_int32
         L.bsc_fused_device_bytes.argtypes = [c_void_p, POINTER(c_size_t)]
         L.bsc_fused_device_bytes.restype = c_int32
         L.bsc_fused_bind.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p]

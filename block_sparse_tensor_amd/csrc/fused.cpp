@@ -39,6 +39,90 @@ struct PlanGuard {
     ~PlanGuard() { bsc_plan_destroy(p); }
 };
 
+bool single(const Blk &b) { return b.ri == 1 && b.ci == 1; }
+
+// Every stage-1 C block's products (A block, B block), ascending k.
+std::vector<std::vector<std::pair<size_t, size_t>>> stage1_products(const Plan &s1) {
+    std::map<std::pair<int32_t, int32_t>, size_t> a1_at, b1_at, c1_key;
+    for (size_t i = 0; i < s1.A.size(); ++i) a1_at[{s1.A[i].r, s1.A[i].c}] = i;
+    for (size_t i = 0; i < s1.B.size(); ++i) b1_at[{s1.B[i].r, s1.B[i].c}] = i;
+    std::vector<std::vector<std::pair<size_t, size_t>>> prods(s1.C.size());
+    for (size_t i = 0; i < s1.C.size(); ++i) c1_key[{s1.C[i].r, s1.C[i].c}] = i;
+    for (const auto &t : s1.triples) {   // sorted by (m, n, k): ascending k per C block
+        const size_t ci = c1_key.at({t[0], t[2]});
+        prods[ci].push_back({a1_at.at({t[0], t[1]}), b1_at.at({t[1], t[2]})});
+    }
+    return prods;
+}
+
+// The product record of one stage-1 product A1 B1 of an M x N block; wrow is
+// the block's weight row, last marks the block's last product.
+void push_chan(FusedPlan &f, const Plan &s1, const Blk &a1, const Blk &b1, int64_t M, int64_t N, int32_t wrow,
+               bool last, const char *who) {
+    const int64_t esz = s1.dtype == BSC_F64 ? 8 : 4;
+    if (!single(a1) || !single(b1))
+        ffail(BSC_ERR_UNSUPPORTED, std::string(who) + ": the A and B blocks must be single-leg views");
+    FChan ch{};
+    ch.a_off = a1.off;
+    ch.a_rs = a1.rs0;
+    ch.a_ks = a1.cs0;
+    ch.b_off = b1.off;
+    ch.b_ks = b1.rs0;
+    ch.b_ns = b1.cs0;
+    ch.K = (int32_t)s1.dk[(size_t)a1.c];
+    // the kernel reads each operand block as one raw buffer of 32-bit range
+    const int64_t span_a = ((M - 1) * ch.a_rs + (ch.K - 1) * ch.a_ks + 1) * esz;
+    const int64_t span_b = ((int64_t)(ch.K - 1) * ch.b_ks + (N - 1) * ch.b_ns + 1) * esz;
+    if (span_a >= ((int64_t)1 << 31) || span_b >= ((int64_t)1 << 31))
+        ffail(BSC_ERR_UNSUPPORTED, std::string(who) + ": an operand block spans 2 GiB or more");
+    ch.wrow = (int16_t)wrow;
+    ch.last = last ? 1 : 0;
+    f.chans.push_back(ch);
+    f.stage1_flops += 2 * M * N * ch.K;
+}
+
+void finish_fused(FusedPlan &f, const Plan &s1, int32_t max_parts, int32_t tile_cols);
+
+// One contraction through the register stream: every C block is a group of
+// one stage-1 block whose tile is written (weight 1) to the block itself.
+void build_stream(FusedPlan &f, const Plan &s1, bool accumulate, int32_t tile_cols) {
+    const char *who = "bsc_stream_plan";
+    const auto prods = stage1_products(s1);
+    f.stream = true;
+    f.a_elems = s1.a_elems;
+    f.b_elems = s1.b_elems;
+    f.w_elems = 0;
+    f.c_elems = s1.c_elems;
+    const int64_t esz = s1.dtype == BSC_F64 ? 8 : 4;
+    for (size_t ci = 0; ci < s1.C.size(); ++ci) {
+        const Blk &c = s1.C[ci];
+        if (!single(c)) ffail(BSC_ERR_UNSUPPORTED, std::string(who) + ": the C blocks must be single-leg views");
+        const int64_t M = s1.dm[(size_t)c.r], N = s1.dn[(size_t)c.c];
+        FGroup g{};
+        g.M = (int32_t)M;
+        g.N = (int32_t)N;
+        g.out0 = (int32_t)f.outs.size();
+        g.nout = 1;
+        g.chan0 = (int32_t)f.chans.size();
+        g.flags = accumulate ? G_ACCUMULATE : 0;
+        f.outs.push_back({c.off, c.rs0, c.cs0});
+        if (M > 1 && N > 1 && std::llabs(c.rs0) < std::llabs(c.cs0)) g.flags |= G_FTRANS;
+        f.alg_bytes += M * N * esz;
+        const auto &pl = prods[ci];
+        for (size_t pi = 0; pi < pl.size(); ++pi)
+            push_chan(f, s1, s1.A[pl[pi].first], s1.B[pl[pi].second], M, N, 0, pi + 1 == pl.size(), who);
+        g.nchan = (int32_t)f.chans.size() - g.chan0;
+        g.nblk = pl.empty() ? 0 : 1;   // a block without products is written as zero (or left as is)
+        g.wbase = (int32_t)f.widx.size();
+        if (g.nblk) {
+            f.widx.push_back(0);       // the plan's own weight 1
+            f.terms++;
+        }
+        f.groups.push_back(g);
+    }
+    finish_fused(f, s1, 1, tile_cols);
+}
+
 void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *m2idx, bool accumulate,
                  int32_t max_parts, int32_t tile_cols) {
     if (s1.c_elems != s2.a_elems)
@@ -49,23 +133,13 @@ void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *
             ffail(BSC_ERR_UNSUPPORTED, "bsc_fused_plan: stage 2's B blocks must all be 1 x 1");
     for (const Blk &b : s2.C)
         if (s2.dn[(size_t)b.c] != 1) ffail(BSC_ERR_UNSUPPORTED, "bsc_fused_plan: stage 2's output columns must have dim 1");
-    auto single = [](const Blk &b) { return b.ri == 1 && b.ci == 1; };
     // stage-1 C blocks by offset
     std::map<int64_t, size_t> c1_at;
     for (size_t i = 0; i < s1.C.size(); ++i) {
         if (!single(s1.C[i])) ffail(BSC_ERR_UNSUPPORTED, "bsc_fused_plan: stage 1's C blocks must be single-leg views");
         c1_at[s1.C[i].off] = i;
     }
-    // stage-1 products of every C block: (A block, B block), ascending k
-    std::map<std::pair<int32_t, int32_t>, size_t> a1_at, b1_at, c1_key;
-    for (size_t i = 0; i < s1.A.size(); ++i) a1_at[{s1.A[i].r, s1.A[i].c}] = i;
-    for (size_t i = 0; i < s1.B.size(); ++i) b1_at[{s1.B[i].r, s1.B[i].c}] = i;
-    std::vector<std::vector<std::pair<size_t, size_t>>> prods(s1.C.size());
-    for (size_t i = 0; i < s1.C.size(); ++i) c1_key[{s1.C[i].r, s1.C[i].c}] = i;
-    for (const auto &t : s1.triples) {   // sorted by (m, n, k): ascending k per C block
-        const size_t ci = c1_key.at({t[0], t[2]});
-        prods[ci].push_back({a1_at.at({t[0], t[1]}), b1_at.at({t[1], t[2]})});
-    }
+    const auto prods = stage1_products(s1);
     // stage 2: A blocks and outputs by row key, B blocks by (k, n)
     std::map<int32_t, std::vector<size_t>> a2_rows, c2_rows;
     for (size_t i = 0; i < s2.A.size(); ++i) a2_rows[s2.A[i].r].push_back(i);
@@ -127,31 +201,11 @@ void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *
                                                        "in another element order");
                 const auto &pl = prods[hit->second];
                 if (pl.empty()) continue;   // a stage-1 block with no product stays zero: no term
-                for (size_t pi = 0; pi < pl.size(); ++pi) {
-                    const auto &pr = pl[pi];
-                    const Blk &a1 = s1.A[pr.first], &b1 = s1.B[pr.second];
-                    if (!single(a1) || !single(b1))
-                        ffail(BSC_ERR_UNSUPPORTED, "bsc_fused_plan: stage 1's A and B blocks must be single-leg views");
-                    FChan ch{};
-                    ch.a_off = a1.off;
-                    ch.a_rs = a1.rs0;
-                    ch.a_ks = a1.cs0;
-                    ch.b_off = b1.off;
-                    ch.b_ks = b1.rs0;
-                    ch.b_ns = b1.cs0;
-                    ch.K = (int32_t)s1.dk[(size_t)a1.c];
-                    // the kernel reads each operand block as one raw buffer of 32-bit range
-                    const int64_t span_a = ((M - 1) * ch.a_rs + (ch.K - 1) * ch.a_ks + 1) * esz;
-                    const int64_t span_b = ((int64_t)(ch.K - 1) * ch.b_ks + (N - 1) * ch.b_ns + 1) * esz;
-                    if (span_a >= ((int64_t)1 << 31) || span_b >= ((int64_t)1 << 31))
-                        ffail(BSC_ERR_UNSUPPORTED, "bsc_fused_plan: a stage-1 operand block spans 2 GiB or more");
-                    if (blk_k2.size() >= (size_t)INT16_MAX)
-                        ffail(BSC_ERR_UNSUPPORTED, "bsc_fused_plan: a stage-2 row fuses too many stage-1 blocks");
-                    ch.wrow = (int16_t)blk_k2.size();
-                    ch.last = pi + 1 == pl.size() ? 1 : 0;
-                    f.chans.push_back(ch);
-                    f.stage1_flops += 2 * M * N * ch.K;
-                }
+                if (blk_k2.size() >= (size_t)INT16_MAX)
+                    ffail(BSC_ERR_UNSUPPORTED, "bsc_fused_plan: a stage-2 row fuses too many stage-1 blocks");
+                for (size_t pi = 0; pi < pl.size(); ++pi)
+                    push_chan(f, s1, s1.A[pl[pi].first], s1.B[pl[pi].second], M, N, (int32_t)blk_k2.size(),
+                              pi + 1 == pl.size(), "bsc_fused_plan: stage 1");
                 blk_k2.push_back(a2.c);
             }
         }
@@ -171,6 +225,14 @@ void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *
         if (trans) g.flags |= G_FTRANS;
         f.groups.push_back(g);
     }
+    f.alg_bytes += (int64_t)s2.B.size() * (s1.dtype == BSC_F64 ? 8 : 4);   // W read once
+    finish_fused(f, s1, max_parts, tile_cols);
+}
+
+// The part both plans share: kernel instance, wave tile, tasks, splits, the
+// parts of every workgroup and the device image.
+void finish_fused(FusedPlan &f, const Plan &s1, int32_t max_parts, int32_t tile_cols) {
+    const int64_t esz = s1.dtype == BSC_F64 ? 8 : 4;
     // outputs per task: the smallest kernel instance that holds every group's
     // outputs (larger groups are split over tasks, each recomputing the tile),
     // as long as every group's weights (blocks x outputs per task) fit the
@@ -214,10 +276,9 @@ void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *
                 for (int32_t j0 = 0; j0 < g.N; j0 += TILE) f.tasks.push_back({(int32_t)gi, i0, j0, oc});
     }
     f.useful_flops += f.stage1_flops;
-    // algorithmic bytes: stage-1 operand blocks read once, W read once, outputs written once
+    // algorithmic bytes: stage-1 operand blocks read once (W and the outputs are counted above)
     for (const Blk &b : s1.A) f.alg_bytes += s1.dm[(size_t)b.r] * s1.dk[(size_t)b.c] * esz;
     for (const Blk &b : s1.B) f.alg_bytes += s1.dk[(size_t)b.r] * s1.dn[(size_t)b.c] * esz;
-    f.alg_bytes += (int64_t)s2.B.size() * esz;
     // splits: a task's register chunks over S parts (S <= min(4, nblk)) when it
     // holds more than a wave's share of the whole launch; each (group, S) gets
     // its parts' product lists once
@@ -343,6 +404,7 @@ void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *
     f.off_tasks = off;  off = align(off + f.tasks.size() * sizeof(FTask));
     f.off_parts = off;  off = align(off + f.parts.size() * sizeof(FPart));
     f.off_pchans = off; off = align(off + f.pchans.size() * sizeof(FChan));
+    f.off_ones = off;   off = align(off + sizeof(double));   // a stream plan's weight 1 in the plan's type
     f.image.assign(std::max<size_t>(off, 256), 0);
     auto put = [&](size_t o, const void *src, size_t nbytes) { if (nbytes) std::memcpy(f.image.data() + o, src, nbytes); };
     put(f.off_groups, f.groups.data(), f.groups.size() * sizeof(FGroup));
@@ -352,6 +414,13 @@ void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *
     put(f.off_tasks, f.tasks.data(), f.tasks.size() * sizeof(FTask));
     put(f.off_parts, f.parts.data(), f.parts.size() * sizeof(FPart));
     put(f.off_pchans, f.pchans.data(), f.pchans.size() * sizeof(FChan));
+    if (f.dtype == BSC_F64) {
+        const double one = 1.0;
+        put(f.off_ones, &one, sizeof(one));
+    } else {
+        const float one = 1.0f;
+        put(f.off_ones, &one, sizeof(one));
+    }
 }
 
 }  // namespace
@@ -430,6 +499,62 @@ extern "C" bsc_status bsc_fused_plan(const bsc_index *m1, const bsc_index *k1, c
     return BSC_OK;
 }
 
+extern "C" bsc_status bsc_stream_plan(const bsc_index *m, const bsc_index *k, const bsc_index *n,
+                                      const bsc_operand *A, const bsc_operand *B, const bsc_operand *C,
+                                      bsc_dtype dtype, const bsc_options *opt, bsc_fused_t *out) {
+    set_error("");
+    if (!out) {
+        set_error("bsc_stream_plan: out is NULL");
+        return BSC_ERR_ARG;
+    }
+    *out = nullptr;
+    if (dtype != BSC_F64 && dtype != BSC_F32) {
+        set_error("bsc_stream_plan: f64 and f32 only");
+        return BSC_ERR_UNSUPPORTED;
+    }
+    bsc_options o;
+    if (opt) o = *opt;
+    else bsc_options_default(&o);
+    const bool accumulate = o.accumulate != 0;
+    if (o.tile_cols != 0 && o.tile_cols != 16 && o.tile_cols != 32) {
+        set_error("bsc_stream_plan: tile_cols must be 0, 16 or 32");
+        return BSC_ERR_ARG;
+    }
+    const int32_t tile_cols = o.tile_cols;
+    o.tile_cols = 0;
+    o.accumulate = 0;
+    o.split_k = 0;
+    o.launch_mode = BSC_LAUNCH_GROUPED;
+    PlanGuard g1;
+    bsc_status st = bsc_plan(m, k, n, A, B, C, dtype, BSC_AXIS_AUTO, &o, &g1.p);
+    if (st != BSC_OK) {
+        set_error(std::string("bsc_stream_plan: ") + bsc_last_error());
+        return st;
+    }
+    FusedPlan *f = new (std::nothrow) FusedPlan();
+    if (!f) {
+        set_error("bsc_stream_plan: out of host memory");
+        return BSC_ERR_UNSUPPORTED;
+    }
+    f->dtype = dtype;
+    try {
+        build_stream(*f, *reinterpret_cast<Plan *>(g1.p), accumulate, tile_cols);
+    } catch (const FFail &e) {
+        delete f;
+        return e.st;
+    } catch (const std::bad_alloc &) {
+        delete f;
+        set_error("bsc_stream_plan: out of host memory");
+        return BSC_ERR_UNSUPPORTED;
+    } catch (const std::out_of_range &) {
+        delete f;
+        set_error("bsc_stream_plan: inconsistent sector join");
+        return BSC_ERR_ARG;
+    }
+    *out = reinterpret_cast<bsc_fused_t>(f);
+    return BSC_OK;
+}
+
 extern "C" bsc_status bsc_fused_device_bytes(bsc_fused_t plan, size_t *bytes) {
     if (!plan || !bytes) {
         set_error("bsc_fused_device_bytes: NULL argument");
@@ -468,6 +593,8 @@ extern "C" bsc_status bsc_fused_stats(bsc_fused_t plan, bsc_fused_summary *out) 
     out->n_parts = (int64_t)f->parts.size();
     out->off_pchans = (int64_t)f->off_pchans;
     out->n_pchans = (int64_t)f->pchans.size();
+    out->stream = f->stream ? 1 : 0;
+    out->off_ones = (int64_t)f->off_ones;
     return BSC_OK;
 }
 

@@ -59,7 +59,8 @@ extern "C" bsc_status bsc_fused_contract(bsc_fused_t plan, const void *A1, const
         set_error("bsc_fused_contract: plan is not bound to a device region");
         return BSC_ERR_NOT_BOUND;
     }
-    if ((!A1 && f->a_elems > 0) || (!B1 && f->b_elems > 0) || (!B2 && f->w_elems > 0) || (!C2 && f->c_elems > 0)) {
+    if ((!A1 && f->a_elems > 0) || (!B1 && f->b_elems > 0) || (!B2 && !f->stream && f->w_elems > 0) ||
+        (!C2 && f->c_elems > 0)) {
         set_error("bsc_fused_contract: NULL operand buffer");
         return BSC_ERR_ARG;
     }
@@ -74,7 +75,7 @@ extern "C" bsc_status bsc_fused_contract(bsc_fused_t plan, const void *A1, const
     fa.no = f->outs_per_task;
     fa.A = A1;
     fa.B = B1;
-    fa.W = B2;
+    fa.W = f->stream ? static_cast<const void *>(base + f->off_ones) : B2;   // a stream plan's own weight 1
     fa.C = C2;
     // four part records per workgroup (longest parts first)
     dim3 grid((unsigned)fa.nwg), block(256);

@@ -139,8 +139,10 @@ struct FusedPlan {
     int64_t terms = 0;              // nonzero (stage-1 block, output) weights
     int32_t outs_per_task = FUSED_MAX_OUT;   // 4, 8 or 16: the kernel instance
     int32_t tile_blocks = 1;                 // TW: the wave's tile is TW x TW blocks of 16 x 16
+    bool stream = false;                     // one contraction, each C block weighted by the plan's own 1
     // device image
     size_t off_groups = 0, off_chans = 0, off_outs = 0, off_widx = 0, off_tasks = 0, off_parts = 0, off_pchans = 0;
+    size_t off_ones = 0;                     // the weight 1 of a stream plan, in the plan's type
     std::vector<unsigned char> image;
     void *dev = nullptr;
     int32_t cu_count = 0;

@@ -362,6 +362,49 @@ class FusedPlan:
             self._h = None
 
 
+class StreamPlan(FusedPlan):
+    """One contraction C (+)= A B (`con`) planned for the fused launch's
+    register-stream kernel (bsc_stream_plan): every C block computed by waves
+    of 16 x 16 (fp32: possibly 32 x 32) tiles that stream the block's products
+    through registers and write it directly.  f64 and f32 only; bind, stats
+    and worklist as for FusedPlan; contract(A, B, C)."""
+
+    def __init__(self, con, dtype: str = None, accumulate: bool = False, tile_cols: int = 0):
+        L = _capi.lib()
+        self.dtype = dtype or con.dtype
+        if self.dtype not in ("f64", "f32"):
+            raise BscError(-7, "stream plans take f64 or f32")
+        keep = _Keep()
+        a = _plan_args(con, self.dtype, "auto", keep)
+        opt = _capi.BscOptions()
+        L.bsc_options_default(byref(opt))
+        opt.accumulate = int(bool(accumulate))
+        opt.tile_cols = int(tile_cols)
+        keep.arrays.append(opt)
+        h = c_void_p()
+        _check(L.bsc_stream_plan(*a[:6], DTYPES[self.dtype], byref(opt), byref(h)))
+        self._h = h
+        self.elems = {"A": int(con.A.buffer_elems), "B": int(con.B.buffer_elems), "C": int(con.C.buffer_elems)}
+        self._dev = None
+
+    def contract(self, A, B, C, stream=None):
+        """Enqueue C (+)= A B on `stream` (default: torch's current stream)."""
+        if self._dev is None:
+            raise BscError(-8, "plan is not bound (call bind())")
+        torch = _torch()
+        dt = torch.float64 if self.dtype == "f64" else torch.float32
+        for name, t in (("A", A), ("B", B), ("C", C)):
+            if not isinstance(t, torch.Tensor) or not t.is_cuda:
+                raise TypeError(f"{name} must be a CUDA/HIP torch tensor")
+            if t.dtype != dt:
+                raise TypeError(f"{name} has dtype {t.dtype}, expected {dt}")
+            if not t.is_contiguous() or t.numel() < self.elems[name]:
+                raise ValueError(f"{name} must be contiguous with at least {self.elems[name]} elements")
+        _check(_capi.lib().bsc_fused_contract(self._h, c_void_p(A.data_ptr()), c_void_p(B.data_ptr()), None,
+                                              c_void_p(C.data_ptr()), _stream_handle(stream)))
+        return C
+
+
 class Chain:
     """A fixed sequence of contractions [(plan, A, B, C), ...] captured once
     into a HIP graph and replayed with one launch (bsc_chain_*).  The plans

@@ -423,11 +423,31 @@ typedef struct {
     int64_t off_parts, n_parts;     /* per-wave records, four per workgroup */
     int64_t off_pchans, n_pchans;   /* the parts' product lists */
     int64_t tile_blocks;            /* a wave's tile: tile_blocks^2 blocks of 16 x 16 */
+    int64_t stream;                 /* 1: a bsc_stream_plan (one contraction), 0: two stages */
+    int64_t off_ones;               /* byte offset of a stream plan's weight 1 in the device image */
 } bsc_fused_summary;
 bsc_status bsc_fused_plan(const bsc_index *m1, const bsc_index *k1, const bsc_index *n1, const bsc_operand *A1,
                           const bsc_operand *B1, const bsc_operand *C1, const bsc_index *m2, const bsc_index *k2,
                           const bsc_index *n2, const bsc_operand *A2, const bsc_operand *B2, const bsc_operand *C2,
                           bsc_dtype dtype, const bsc_options *opt, bsc_fused_t *out);
+/* One block-sparse contraction C (+)= A B (the operation of bsc_plan, uni20
+ * "block coalescing": every C block the sum over its k sectors of A B block
+ * products) planned for the register-stream kernel of the fused plan instead
+ * of the grouped tiles: every C block is its own group (one stage-1 block,
+ * one output, weight 1) cut into 16 x 16 (or, fp32, 32 x 32) wave tiles, each
+ * wave streaming its tile's products through registers and writing the C
+ * block directly.  Suits many short-K sector GEMMs in fp32 / fp64, where the
+ * grouped tiles wait on their dependent loads.  Arguments as for bsc_plan
+ * (dtype BSC_F64 or BSC_F32 only; every A, B and C block a single strided
+ * view, else BSC_ERR_UNSUPPORTED); opt->accumulate and opt->tile_cols (0, 16
+ * or 32, as for bsc_fused_plan) are used, other options ignored.  C blocks no
+ * product reaches are written as zero (overwrite) or left as they are
+ * (accumulate).  The result is a bsc_fused_t: bind, contract, stats, worklist
+ * and destroy as for a fused plan, with bsc_fused_contract(plan, A, B, NULL,
+ * C, stream) (the B2 argument is ignored).  Repeats are bit-identical. */
+bsc_status bsc_stream_plan(const bsc_index *m, const bsc_index *k, const bsc_index *n, const bsc_operand *A,
+                           const bsc_operand *B, const bsc_operand *C, bsc_dtype dtype, const bsc_options *opt,
+                           bsc_fused_t *out);
 bsc_status bsc_fused_device_bytes(bsc_fused_t plan, size_t *bytes);
 bsc_status bsc_fused_bind(bsc_fused_t plan, void *dev, size_t bytes, void *stream);
 bsc_status bsc_fused_contract(bsc_fused_t plan, const void *A1, const void *B1, const void *B2, void *C2, void *stream);

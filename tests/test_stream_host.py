@@ -1,0 +1,101 @@
+"""Host checks of the stream plan (bsc_stream_plan): one block-sparse
+contraction planned for the fused launch's register-stream kernel, every C
+block its own group of one stage-1 block and one output with the plan's own
+weight 1.
+
+The device image is replayed on the host as the kernel evaluates it (the fused
+plan's replay, tile by tile and product by product, with that weight) and must
+equal the oracle's contraction bit for bit on integer values (every summation
+order is exact).  C blocks no product reaches come out zero, or unchanged under
+accumulation; a planner mistake (a product on the wrong block, a missed tile, a
+transposed view) changes the result."""
+import numpy as np
+import pytest
+
+import oracle
+
+from gpuhelp import c_addresses
+from stream_cases import CASES
+from test_fused_host import decode, replay
+
+bst = pytest.importorskip("block_sparse_tensor_amd")
+
+
+def _lib_ok():
+    try:
+        bst._capi.lib()
+        return True
+    except Exception:
+        return False
+
+
+pytestmark = pytest.mark.skipif(not _lib_ok(), reason="libbsc.so not built")
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_stream_replay_equals_oracle(name, accumulate):
+    make, tile = CASES[name]
+    con, a, b = make()
+    sp = bst.StreamPlan(con, accumulate=accumulate, tile_cols=tile)
+    s = sp.stats()
+    assert s["stream"] == 1 and s["tile_blocks"] == (2 if tile == 32 else 1)
+    rng = np.random.default_rng(5)
+    c0 = rng.integers(-3, 4, con.C.buffer_elems).astype(np.float64)
+    want = oracle.contract(con, a, b, c0.copy(), accumulate=accumulate) if accumulate else \
+        oracle.contract(con, a, b, np.where(c_addresses(con)[1], 0.0, c0))
+    got = replay(sp, a, b, np.ones(1), c0.copy())
+    _, mask = c_addresses(con)
+    assert np.array_equal(got[mask], want[mask])
+    assert np.array_equal(got[~mask], c0[~mask]), "a write outside the C views"
+
+
+def test_stream_stats_and_zero_blocks():
+    con, a, b = CASES["random-f64-sparse"][0]()
+    s = bst.StreamPlan(con).stats()
+    t = oracle.triples(con)
+    reached = {(int(m), int(n)) for m, k, n in t}
+    assert s["groups"] == s["outputs"] == con.C.nblocks
+    assert s["terms"] == len(reached) < con.C.nblocks   # some C blocks no product reaches
+    assert s["channels"] == len(t)
+    assert s["useful_flops"] == s["stage1_flops"] == oracle.useful_flops(con)
+    assert s["alg_bytes"] == oracle.algorithmic_bytes(con)
+    assert s["launches_per_contract"] == 1 and s["launches_issued"] == 0
+    # the plan's own weight 1 in its type
+    st, img = bst.StreamPlan(con).worklist()
+    assert np.frombuffer(img, np.float64, count=1, offset=st["off_ones"])[0] == 1.0
+    groups = decode(bst.StreamPlan(con))[1]
+    assert (groups["nout"] == 1).all() and set(np.unique(groups["nblk"])) <= {0, 1}
+
+
+def test_stream_refuses_what_it_cannot_plan():
+    con, a, b = CASES["small-coop-stage1"][0]()
+    with pytest.raises(bst.BscError) as e:
+        bst.StreamPlan(con, dtype="bf16")
+    assert e.value.name == "BSC_ERR_UNSUPPORTED"
+    with pytest.raises(bst.BscError) as e:
+        bst.StreamPlan(con, tile_cols=8)
+    assert e.value.name == "BSC_ERR_ARG"
+    # the W stage writes C blocks whose columns fuse two legs
+    from workloads import configs as C
+    w = C.rabc_u1(layout="coop").stages[1].con
+    with pytest.raises(bst.BscError) as e:
+        bst.StreamPlan(w)
+    assert e.value.name == "BSC_ERR_UNSUPPORTED"
+    # planning errors of the contraction itself are reported as bsc_plan reports them
+    bad = CASES["small-coop-stage1"][0]()[0]
+    bad.A.offset[0] = -1
+    with pytest.raises(bst.BscError) as e:
+        bst.StreamPlan(bad)
+    assert e.value.name == "BSC_ERR_BOUNDS"
+
+
+def test_stream_device_entry_checks_arguments():
+    from ctypes import c_void_p
+    con, a, b = CASES["small-coop-stage1"][0]()
+    sp = bst.StreamPlan(con)
+    L = bst._capi.lib()
+    # unbound: refused before anything is enqueued (B2 may be NULL for a stream plan)
+    st = L.bsc_fused_contract(sp._h, c_void_p(1), c_void_p(1), None, c_void_p(1), None)
+    assert st in (-8, -7)
+    assert L.bsc_stream_plan(None, None, None, None, None, None, 0, None, None) == -1

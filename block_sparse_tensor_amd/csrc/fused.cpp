@@ -242,7 +242,7 @@ void finish_fused(FusedPlan &f, const Plan &s1, int32_t max_parts, int32_t tile_
         most = std::max(most, g.nout);
         most_blk = std::max(most_blk, g.nblk);
     }
-    f.outs_per_task = most <= 4 ? 4 : most <= 8 ? 8 : FUSED_MAX_OUT;
+    f.outs_per_task = most <= 1 ? 1 : most <= 4 ? 4 : most <= 8 ? 8 : FUSED_MAX_OUT;
     while (f.outs_per_task > 4 && (int64_t)most_blk * f.outs_per_task > FUSED_WCAP) f.outs_per_task /= 2;
     if ((int64_t)most_blk * f.outs_per_task > FUSED_WCAP)
         ffail(BSC_ERR_UNSUPPORTED, "bsc_fused_plan: a stage-2 row fuses more than " +

@@ -81,13 +81,16 @@ extern "C" bsc_status bsc_fused_contract(bsc_fused_t plan, const void *A1, const
     dim3 grid((unsigned)fa.nwg), block(256);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (f->dtype == BSC_F64) {
-        if (fa.no == 4) hipLaunchKernelGGL((fused_contract<double, 4, 1>), grid, block, 0, s, fa);
+        if (fa.no == 1) hipLaunchKernelGGL((fused_contract<double, 1, 1>), grid, block, 0, s, fa);
+        else if (fa.no == 4) hipLaunchKernelGGL((fused_contract<double, 4, 1>), grid, block, 0, s, fa);
         else if (fa.no == 8) hipLaunchKernelGGL((fused_contract<double, 8, 1>), grid, block, 0, s, fa);
         else hipLaunchKernelGGL((fused_contract<double, FUSED_MAX_OUT, 1>), grid, block, 0, s, fa);
     } else if (f->tile_blocks == 2) {
-        hipLaunchKernelGGL((fused_contract<float, 4, 2>), grid, block, 0, s, fa);
+        if (fa.no == 1) hipLaunchKernelGGL((fused_contract<float, 1, 2>), grid, block, 0, s, fa);
+        else hipLaunchKernelGGL((fused_contract<float, 4, 2>), grid, block, 0, s, fa);
     } else {
-        if (fa.no == 4) hipLaunchKernelGGL((fused_contract<float, 4, 1>), grid, block, 0, s, fa);
+        if (fa.no == 1) hipLaunchKernelGGL((fused_contract<float, 1, 1>), grid, block, 0, s, fa);
+        else if (fa.no == 4) hipLaunchKernelGGL((fused_contract<float, 4, 1>), grid, block, 0, s, fa);
         else if (fa.no == 8) hipLaunchKernelGGL((fused_contract<float, 8, 1>), grid, block, 0, s, fa);
         else hipLaunchKernelGGL((fused_contract<float, FUSED_MAX_OUT, 1>), grid, block, 0, s, fa);
     }

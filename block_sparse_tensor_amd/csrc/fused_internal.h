@@ -65,9 +65,9 @@ constexpr int FUSED_MIN_PART = 4;
 inline int fused_wgs_per_cu(bsc_dtype dt, int no, int tile_blocks) {
     // every workgroup puts one wave on each SIMD, so this is the instance's
     // waves per SIMD as compiled (register counts from the compiler's report)
-    if (dt == BSC_F64) return no <= 4 ? 3 : 2;      // 146 / 176 / 240 VGPRs at 4 / 8 / 16 outputs
-    if (tile_blocks == 2) return 2;                 // 32 x 32 tiles: 185 VGPRs + 24 accumulation registers
-    return no <= 4 ? 5 : (no <= 8 ? 4 : 3);         // 78 / 96 / 129 VGPRs
+    if (dt == BSC_F64) return no <= 4 ? 3 : 2;      // 124 / 146 / 176 / 240 VGPRs at 1 / 4 / 8 / 16 outputs
+    if (tile_blocks == 2) return 2;                 // 32 x 32 tiles: 120 / 185 VGPRs + 24 accumulation registers
+    return no <= 1 ? 7 : no <= 4 ? 5 : (no <= 8 ? 4 : 3);   // 61 / 78 / 96 / 129 VGPRs
 }
 
 struct FGroup {

@@ -386,26 +386,27 @@ __global__ __launch_bounds__(256) void fused_contract(FArgs fa) {
         return;
     }
 #pragma unroll
-    for (int pass = 0; pass < NO / 4; ++pass) {
+    for (int pass = 0; pass < (NO + 3) / 4; ++pass) {
         if (pass < pr.npass) {   // the same for every wave of the workgroup: all join both barriers
             const bool reduce = pr.nparts > 1;   // the same for every wave of a task
             if (reduce && pr.part > 0) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
+                    if (pass * 4 + u < NO)   // (a one-output instance has one accumulator set)
 #pragma unroll
-                    for (int i = 0; i < TW; ++i)
+                        for (int i = 0; i < TW; ++i)
 #pragma unroll
-                        for (int j = 0; j < TW; ++j)
+                            for (int j = 0; j < TW; ++j)
 #pragma unroll
-                            for (int v = 0; v < 4; ++v)
-                                sm.red[w][u][(i * TW + j) * 4 + v][lane] = acc[pass * 4 + u][i][j][v];
+                                for (int v = 0; v < 4; ++v)
+                                    sm.red[w][u][(i * TW + j) * 4 + v][lane] = acc[pass * 4 + u][i][j][v];
             }
             __syncthreads();
             if (pr.nparts > 0 && pr.part == 0) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int32_t o = pass * 4 + u;
-                    if (o < pr.no) {
+                    if (pass * 4 + u < NO && o < pr.no) {
                         acc_t sum[TW][TW];
 #pragma unroll
                         for (int i = 0; i < TW; ++i)

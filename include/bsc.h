@@ -419,7 +419,7 @@ typedef struct {
     int64_t launches_issued;
     /* byte offsets of the record arrays in the device image (bsc_fused_worklist) */
     int64_t off_groups, off_chans, off_outs, off_widx, off_tasks;
-    int64_t outs_per_task;          /* outputs one task accumulates (4, 8 or 16) */
+    int64_t outs_per_task;          /* outputs one task accumulates (1, 4, 8 or 16) */
     int64_t off_parts, n_parts;     /* per-wave records, four per workgroup */
     int64_t off_pchans, n_pchans;   /* the parts' product lists */
     int64_t tile_blocks;            /* a wave's tile: tile_blocks^2 blocks of 16 x 16 */

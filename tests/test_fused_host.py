@@ -61,7 +61,7 @@ def replay(fp, A1, B1, W, C2):
     groups, and that the tasks cover every tile and output chunk once."""
     s, groups, chans, outs, widx, tasks, parts, pchans = decode(fp)
     NO = s["outs_per_task"]
-    assert NO in (4, 8, 16) and len(parts) % 4 == 0
+    assert NO in (1, 4, 8, 16) and len(parts) % 4 == 0
     assert s["tile_blocks"] in (1, 2)
     TILE = 16 * s["tile_blocks"]
     assert s["groups"] == 0 or max(int(g["nblk"]) for g in groups) * NO <= 256

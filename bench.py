@@ -610,6 +610,56 @@ def main():
                      "fused_tflops": round(fs["useful_flops"] / (fstage[0] * 1e-3) / 1e12, 4),
                      "items": fs["items"], "products": fs["channels"], "terms": fs["terms"],
                      "t2_rel_diff_vs_two_stage": rel, "launches_per_step": len(stages) - 1}
+            # the same with the later stages through the register stream (bsc_stream_plan)
+            # wherever it takes them, the grouped plan elsewhere
+            tail = []
+            for p, (con, _, _, _, _) in zip(grouped[2:], stages[2:]):
+                try:
+                    tail.append(("stream", bst.StreamPlan(con).bind()))
+                except bst.BscError:
+                    tail.append(("grouped", p))
+            sbuf = {k: v for k, v in fbuf.items()}
+            for _, a, b, c, _ in stages[2:]:
+                sbuf[c] = torch.zeros_like(fbuf[c])
+
+            def sstep(marks=None):
+                fplan.contract(sbuf[stages[0][1]], sbuf[stages[0][2]], sbuf[stages[1][2]], sbuf[stages[1][3]])
+                if marks is not None:
+                    ev = torch.cuda.Event(enable_timing=True)
+                    ev.record()
+                    marks.append(ev)
+                for (_, p), (_, a, b, c, _) in zip(tail, stages[2:]):
+                    p.contract(sbuf[a], sbuf[b], sbuf[c])
+                    if marks is not None:
+                        ev = torch.cuda.Event(enable_timing=True)
+                        ev.record()
+                        marks.append(ev)
+            for _ in range(args.warmup):
+                sstep()
+            torch.cuda.synchronize()
+            f0.record()
+            for _ in range(args.steps):
+                sstep()
+            f1.record()
+            torch.cuda.synchronize()
+            sms = f0.elapsed_time(f1) / args.steps
+            sm = [torch.cuda.Event(enable_timing=True)]
+            sm[0].record()
+            for _ in range(args.steps):
+                sstep(sm)
+            torch.cuda.synchronize()
+            sstage = [statistics.fmean(sm[j].elapsed_time(sm[j + 1]) for j in range(i, len(sm) - 1, nl))
+                      for i in range(nl)]
+            # parity of the last stage's output against the all-grouped step
+            last = stages[-1][3]
+            adl = torch.from_numpy(np.nonzero(_view_mask(stages[-1][0]))[0]).cuda()
+            ref_l = bufs[last].index_select(0, adl).double()
+            got_l = sbuf[last].index_select(0, adl).double()
+            srel = float((got_l - ref_l).norm() / ref_l.norm().clamp_min(1e-300))
+            fused["stream_tail"] = {"ms_per_step": round(sms, 6), "value": round(flops / (sms * 1e-3) / 1e9, 3),
+                                    "unit": "GFLOP/s", "stage_kernel_ms": [round(x, 6) for x in sstage],
+                                    "tail_plans": [k for k, _ in tail],
+                                    "last_output_rel_diff_vs_grouped": srel}
 
     # --- the gather (pack) phase against the HBM roofline: every gatherable operand of each
     # stage gathered (FORCE_PACK), the gather kernel's own time from the profiler ---

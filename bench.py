@@ -610,14 +610,12 @@ def main():
                      "fused_tflops": round(fs["useful_flops"] / (fstage[0] * 1e-3) / 1e12, 4),
                      "items": fs["items"], "products": fs["channels"], "terms": fs["terms"],
                      "t2_rel_diff_vs_two_stage": rel, "launches_per_step": len(stages) - 1}
-            # the same with the later stages through the register stream (bsc_stream_plan)
-            # wherever it takes them, the grouped plan elsewhere
+            # the same with the later stages on the plan the library prefers for them
+            # (best_plan: the register stream where bsc_stream_plan reports it preferred)
             tail = []
-            for p, (con, _, _, _, _) in zip(grouped[2:], stages[2:]):
-                try:
-                    tail.append(("stream", bst.StreamPlan(con).bind()))
-                except bst.BscError:
-                    tail.append(("grouped", p))
+            for p, (con, _, _, _, ax) in zip(grouped[2:], stages[2:]):
+                bp = bst.best_plan(con, dtype=dtype)
+                tail.append(("stream", bp.bind()) if isinstance(bp, bst.StreamPlan) else ("grouped", p))
             sbuf = {k: v for k, v in fbuf.items()}
             for _, a, b, c, _ in stages[2:]:
                 sbuf[c] = torch.zeros_like(fbuf[c])

@@ -70,7 +70,8 @@ class BscFusedStats(ctypes.Structure):
                                         "useful_flops", "stage1_flops", "alg_bytes", "device_bytes",
                                         "launches_issued", "off_groups", "off_chans", "off_outs", "off_widx",
                                         "off_tasks", "outs_per_task", "off_parts", "n_parts", "off_pchans",
-                                        "n_pchans", "tile_blocks", "stream", "off_ones")]
+                                        "n_pchans", "tile_blocks", "stream", "off_ones", "longest_chunks",
+                                        "stream_preferred")]
 
 
 _lib = None

@@ -346,6 +346,7 @@ void finish_fused(FusedPlan &f, const Plan &s1, int32_t max_parts, int32_t tile_
             plist[gi].push_back({start, (int32_t)f.pchans.size() - start});
         }
         work[gi] = (chunks + S - 1) / S;
+        f.longest_chunks = std::max(f.longest_chunks, work[gi]);
     }
     // longest parts first (tiles of one group stay together)
     std::stable_sort(f.tasks.begin(), f.tasks.end(),
@@ -595,6 +596,8 @@ extern "C" bsc_status bsc_fused_stats(bsc_fused_t plan, bsc_fused_summary *out) 
     out->n_pchans = (int64_t)f->pchans.size();
     out->stream = f->stream ? 1 : 0;
     out->off_ones = (int64_t)f->off_ones;
+    out->longest_chunks = f->longest_chunks;
+    out->stream_preferred = f->stream && f->longest_chunks <= STREAM_MAX_CHUNKS ? 1 : 0;
     return BSC_OK;
 }
 

@@ -60,6 +60,12 @@ constexpr int FUSED_KC = 32;        // contracted indices per register chunk (8 
 // compute units, each holding as many workgroups as the kernel instance's
 // register use allows (one wave per SIMD per workgroup).
 constexpr int FUSED_CUS = 256;
+// A stream plan is preferred over the grouped tiles when no wave's product
+// stream is longer than this many register chunks (32 contracted indices
+// each); measured on MI355X over 22 f32 / f64 contractions, longer streams
+// (long K per C block: 43-52 chunks) ran 10-35 % slower than the grouped
+// 64 x 64 tiles, shorter ones up to 4.5x faster.
+constexpr int64_t STREAM_MAX_CHUNKS = 32;
 constexpr int64_t FUSED_WIDE_TASKS = 1024;   // 32 x 32 tiles only with at least this many tasks (4 per CU)
 constexpr int FUSED_MIN_PART = 4;
 inline int fused_wgs_per_cu(bsc_dtype dt, int no, int tile_blocks) {
@@ -140,6 +146,7 @@ struct FusedPlan {
     int32_t outs_per_task = FUSED_MAX_OUT;   // 4, 8 or 16: the kernel instance
     int32_t tile_blocks = 1;                 // TW: the wave's tile is TW x TW blocks of 16 x 16
     bool stream = false;                     // one contraction, each C block weighted by the plan's own 1
+    int64_t longest_chunks = 0;              // register chunks of the longest part
     // device image
     size_t off_groups = 0, off_chans = 0, off_outs = 0, off_widx = 0, off_tasks = 0, off_parts = 0, off_pchans = 0;
     size_t off_ones = 0;                     // the weight 1 of a stream plan, in the plan's type

@@ -405,6 +405,21 @@ class StreamPlan(FusedPlan):
         return C
 
 
+def best_plan(con, dtype: str = None, accumulate: bool = False, **plan_kw):
+    """The plan the library expects to run `con` fastest: a StreamPlan where
+    bsc_stream_plan accepts the contraction and reports it preferred
+    (stream_preferred), else a grouped Plan (bsc_plan).  Both are unbound."""
+    dt = dtype or con.dtype
+    if dt in ("f64", "f32"):
+        try:
+            sp = StreamPlan(con, dtype=dt, accumulate=accumulate)
+        except BscError:
+            sp = None
+        if sp is not None and sp.stats()["stream_preferred"]:
+            return sp
+    return Plan(con, dtype=dt, accumulate=accumulate, **plan_kw)
+
+
 class Chain:
     """A fixed sequence of contractions [(plan, A, B, C), ...] captured once
     into a HIP graph and replayed with one launch (bsc_chain_*).  The plans

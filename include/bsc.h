@@ -425,6 +425,10 @@ typedef struct {
     int64_t tile_blocks;            /* a wave's tile: tile_blocks^2 blocks of 16 x 16 */
     int64_t stream;                 /* 1: a bsc_stream_plan (one contraction), 0: two stages */
     int64_t off_ones;               /* byte offset of a stream plan's weight 1 in the device image */
+    int64_t longest_chunks;         /* 32-index register chunks of the longest wave's product stream */
+    int64_t stream_preferred;       /* stream plan expected faster than bsc_plan's grouped tiles: 1 when
+                                       longest_chunks <= 32 (measured crossover on MI355X; long K per C
+                                       block favours the grouped tiles' operand reuse) */
 } bsc_fused_summary;
 bsc_status bsc_fused_plan(const bsc_index *m1, const bsc_index *k1, const bsc_index *n1, const bsc_operand *A1,
                           const bsc_operand *B1, const bsc_operand *C1, const bsc_index *m2, const bsc_index *k2,

@@ -99,3 +99,24 @@ def test_stream_device_entry_checks_arguments():
     st = L.bsc_fused_contract(sp._h, c_void_p(1), c_void_p(1), None, c_void_p(1), None)
     assert st in (-8, -7)
     assert L.bsc_stream_plan(None, None, None, None, None, None, 0, None, None) == -1
+
+
+def test_stream_preference_follows_the_longest_stream():
+    """stream_preferred: the longest wave's product stream is at most 32
+    register chunks.  A bond-2048 stage 3 (a few C blocks, K up to 1571) runs
+    longer streams and keeps the grouped tiles; its stage 1 (one product per
+    block, K up to 417) does not."""
+    from workloads import configs as C
+    ch = C.small_chain(seed=3, layout="coop", dtype="f32", total=2048, qmax=4, sigma=2.0, w=1)
+    for si, want in ((0, True), (2, False)):
+        con = ch.stages[si].con
+        sp = bst.StreamPlan(con)
+        s = sp.stats()
+        longest = max(sum((int(con.k.dim[k]) + 31) // 32 for m2, k, n2 in oracle.triples(con) if (m2, n2) == mn)
+                      for mn in {(m, n) for m, k, n in oracle.triples(con)})
+        assert s["longest_chunks"] == longest
+        assert bool(s["stream_preferred"]) == want == (longest <= 32)
+        assert isinstance(bst.best_plan(con), bst.StreamPlan if want else bst.Plan)
+    # bf16 has no stream kernel: always the grouped plan
+    bf = C.blockdiag_bf16(values=False).con
+    assert isinstance(bst.best_plan(bf), bst.Plan)

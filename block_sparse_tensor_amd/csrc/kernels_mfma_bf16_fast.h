@@ -460,18 +460,19 @@ __device__ __forceinline__ void frag_step(uint32_t stage, uint32_t bstage, const
 // (lane-contiguous: 16-byte group q of lane l at q * 64 + l within the wave's
 // block), waits until the stores are complete, then counts itself in the
 // tile's counter.  Returns false for every slice but the last; the last resets
-// the counter for the next launch and reloads its accumulators as the sum of
-// all partials taken in slice order, so the result does not depend on which
-// slice finishes last.
+// the counter for the next launch and forms p0 + p1 + ... + p(S-1), added left
+// to right, so the result does not depend on which slice finishes last.
 //
-// Slices run on different CUs, possibly on different chiplets, whose L2
-// caches are not kept coherent with each other.  The partials are therefore
-// written and read with device-coherent buffer accesses (the sc1 cache policy
-// that device-scope atomic loads and stores use, here without their
-// one-at-a-time waits), and the counter is a device-scope atomic; no
-// device-scope fence, whose whole-cache write-back and invalidation would
-// stall every other workgroup on the chiplet.  The buffer descriptor covers
-// exactly the tile's partials, so the hardware drops any access outside them.
+// Slices may run on different chiplets, whose L2 caches are not kept coherent
+// with each other.  The partials are therefore written and read with
+// device-coherent buffer accesses (the sc1 cache policy that device-scope
+// atomic loads and stores use, here without their one-at-a-time waits), and
+// the counter is a device-scope atomic; no device-scope fence, whose
+// whole-cache write-back and invalidation would stall every other workgroup on
+// the chiplet.  A pair's last slice adds the other's partial to the one it
+// holds (a + b and b + a are the same float); more slices reload all partials
+// in slice order.  The buffer descriptor covers exactly the tile's partials,
+// so the hardware drops any access outside them.
 constexpr int32_t CPOL_SC1 = 16;             // device-coherent cache policy
 
 __device__ __forceinline__ bool split_arrive(const KArgs &ka, const DFast &fd, f32x16_t (&acc)[FB_FM][2], int32_t w,
@@ -483,10 +484,11 @@ __device__ __forceinline__ bool split_arrive(const KArgs &ka, const DFast &fd, f
     const uint64_t ubase = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(base >> 32))) << 32) |
                            static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(base)));
     const int32_t nsplit = __builtin_amdgcn_readfirstlane(fd.nsplit);
+    const int32_t me = __builtin_amdgcn_readfirstlane(fd.split);
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(ubase), 0, nsplit * SPLIT_BYTES, BUF_DWORD3);
     const int32_t lane_off = (w * NQ * 64 + lane) * 16;
-    const int32_t mine = fd.split * SPLIT_BYTES + lane_off;
+    const int32_t mine = me * SPLIT_BYTES + lane_off;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const f32x16_t &a = acc[q / 8][(q / 4) & 1];
@@ -503,25 +505,33 @@ __device__ __forceinline__ bool split_arrive(const KArgs &ka, const DFast &fd, f
     }
     __syncthreads();
     if (!last) return false;
-    // slice 0 replaces the accumulators, slices 1.. add in order.  Loads go out
-    // in batches of SPLIT_BATCH before any of them is used: added one by one,
-    // each load would wait out a full memory round trip.
     constexpr int SPLIT_BATCH = 16;
+    // A pair's last slice keeps its own partial and adds the other's; with
+    // more slices, slice 0 replaces the accumulators and slices 1.. are added
+    // in order.  (One add loop serves both: a second copy of it made the
+    // compiler spill the whole kernel to scratch.)
+    const bool pair = nsplit == 2;
+    if (!pair) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        f32x16_t &a = acc[q / 8][(q / 4) & 1];
-        const int r = 4 * (q & 3);
-        // (the whole vector is reinterpreted at once: extracting single lanes of
-        // the loaded integer vector through bit casts is narrowed to a
-        // one-dword load by this compiler)
-        const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + q * 1024, 0, CPOL_SC1));
+        for (int q = 0; q < NQ; ++q) {
+            f32x16_t &a = acc[q / 8][(q / 4) & 1];
+            const int r = 4 * (q & 3);
+            // (the whole vector is reinterpreted at once: extracting single lanes of
+            // the loaded integer vector through bit casts is narrowed to a
+            // one-dword load by this compiler)
+            const f32x4_t x =
+                __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + q * 1024, 0, CPOL_SC1));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[r + e] = x[e];
+            for (int e = 0; e < 4; ++e) a[r + e] = x[e];
+        }
     }
-    for (int32_t s = 1; s < nsplit; ++s) {
+    for (int32_t s = pair ? 0 : 1; s < nsplit; ++s) {
+        if (pair && s == me) continue;
         const int32_t src = s * SPLIT_BYTES + lane_off;
 #pragma unroll
         for (int h = 0; h < NQ; h += SPLIT_BATCH) {
+            // a batch of loads issued before any is added (one by one, each
+            // would wait out a full memory round trip)
             v4i32_t t[SPLIT_BATCH];
 #pragma unroll
             for (int u = 0; u < SPLIT_BATCH; ++u)

@@ -406,13 +406,15 @@ void bsc_chain_destroy(bsc_chain_t chain);
  * Repeats are bit-identical (fixed summation order, no atomics). */
 typedef struct bsc_fused_s *bsc_fused_t;
 typedef struct {
-    int64_t groups;                 /* stage-2 output row keys */
-    int64_t channels;               /* stage-1 block products */
-    int64_t outputs;                /* stage-2 output blocks */
-    int64_t terms;                  /* nonzero (stage-1 block, output) weights */
-    int64_t items;                  /* 16 x 16 output tiles */
+    int64_t groups;                 /* stage-2 output row keys (stream plan: C blocks) */
+    int64_t channels;               /* stage-1 block products (stream plan: sector GEMMs) */
+    int64_t outputs;                /* stage-2 output blocks (stream plan: C blocks) */
+    int64_t terms;                  /* nonzero (stage-1 block, output) weights (stream plan: C blocks
+                                       some product reaches) */
+    int64_t items;                  /* output tiles (16 x 16, or 32 x 32 when tile_blocks is 2) x output chunks */
     int64_t launches_per_contract;
-    int64_t useful_flops;           /* stage-1 products (2 M N K each) + weighted adds (2 M N per term) */
+    int64_t useful_flops;           /* stage-1 products (2 M N K each) + weighted adds (2 M N per term);
+                                       a stream plan counts its products only */
     int64_t stage1_flops;
     int64_t alg_bytes;              /* stage-1 operands and B2 read once, C2 written once */
     int64_t device_bytes;

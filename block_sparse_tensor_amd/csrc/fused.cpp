@@ -108,19 +108,30 @@ void build_stream(FusedPlan &f, const Plan &s1, bool accumulate, int32_t tile_co
         f.outs.push_back({c.off, c.rs0, c.cs0});
         if (M > 1 && N > 1 && std::llabs(c.rs0) < std::llabs(c.cs0)) g.flags |= G_FTRANS;
         f.alg_bytes += M * N * esz;
+        // A C block of many products makes every product a block of its own,
+        // weighted by 1 into the output, so its list can be shared by up to
+        // four waves (the fused plan's split by blocks, taken when the launch
+        // would leave CUs idle), their sums added in part order.  Measured on
+        // MI355X: an all-zero-charge chain's stage 3 (16 products per block)
+        // 23.0 -> 11.8 us; blocks of a few products ran slower that way (a
+        // random structure 10.4 -> 13.4 us), so they stay one block.
         const auto &pl = prods[ci];
+        const bool each = pl.size() >= (size_t)STREAM_SPLIT_PRODUCTS;
+        if (pl.size() > (size_t)FUSED_WCAP)
+            ffail(BSC_ERR_UNSUPPORTED, std::string(who) + ": a C block has more than " + std::to_string(FUSED_WCAP) +
+                                           " products");
         for (size_t pi = 0; pi < pl.size(); ++pi)
-            push_chan(f, s1, s1.A[pl[pi].first], s1.B[pl[pi].second], M, N, 0, pi + 1 == pl.size(), who);
+            push_chan(f, s1, s1.A[pl[pi].first], s1.B[pl[pi].second], M, N, each ? (int32_t)pi : 0,
+                      each || pi + 1 == pl.size(), who);
         g.nchan = (int32_t)f.chans.size() - g.chan0;
-        g.nblk = pl.empty() ? 0 : 1;   // a block without products is written as zero (or left as is)
+        // a C block without products is written as zero (or left as is)
+        g.nblk = pl.empty() ? 0 : (each ? (int32_t)pl.size() : 1);
         g.wbase = (int32_t)f.widx.size();
-        if (g.nblk) {
-            f.widx.push_back(0);       // the plan's own weight 1
-            f.terms++;
-        }
+        for (int32_t b = 0; b < g.nblk; ++b) f.widx.push_back(0);   // the plan's own weight 1
+        if (!pl.empty()) f.terms++;
         f.groups.push_back(g);
     }
-    finish_fused(f, s1, 1, tile_cols);
+    finish_fused(f, s1, 4, tile_cols);
 }
 
 void build_fused(FusedPlan &f, const Plan &s1, const Plan &s2, const bsc_index *m2idx, bool accumulate,

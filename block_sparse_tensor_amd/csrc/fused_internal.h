@@ -66,6 +66,7 @@ constexpr int FUSED_CUS = 256;
 // (long K per C block: 43-52 chunks) ran 10-35 % slower than the grouped
 // 64 x 64 tiles, shorter ones up to 4.5x faster.
 constexpr int64_t STREAM_MAX_CHUNKS = 32;
+constexpr int32_t STREAM_SPLIT_PRODUCTS = 8;   // products from which a stream plan's C block may be split
 constexpr int64_t FUSED_WIDE_TASKS = 1024;   // 32 x 32 tiles only with at least this many tasks (4 per CU)
 constexpr int FUSED_MIN_PART = 4;
 inline int fused_wgs_per_cu(bsc_dtype dt, int no, int tile_blocks) {

@@ -35,4 +35,6 @@ CASES = {
     "random-f32-sparse": (lambda: _random(7102, "f32", 0.5), 0),
     "wide-f32-tile32": (lambda: _stage(C.small_chain(seed=3, layout="coop", dtype="f32", total=1024, qmax=4,
                                                      sigma=2.0, w=1, values="int"), 0, 5), 32),
+    # every charge zero: 16 products per C block, each its own block, split over waves
+    "neutral-f32-stage3-split": (lambda: _stage(C.neutral_chain(seed=4, layout="coop", dtype="f32"), 2, 6), 0),
 }

@@ -120,3 +120,15 @@ def test_stream_preference_follows_the_longest_stream():
     # bf16 has no stream kernel: always the grouped plan
     bf = C.blockdiag_bf16(values=False).con
     assert isinstance(bst.best_plan(bf), bst.Plan)
+
+
+def test_stream_splits_many_product_blocks():
+    """C blocks of at least 8 products make each product a block of its own,
+    so a launch that would leave CUs idle shares them over up to four waves
+    (the replay checks the parts' blocks and their order)."""
+    con, a, b = CASES["neutral-f32-stage3-split"][0]()
+    sp = bst.StreamPlan(con)
+    s, groups, chans, outs, widx, tasks, parts, pchans = decode(sp)
+    assert (groups["nblk"] >= 8).all() and parts["nparts"].max() > 1
+    few = bst.StreamPlan(CASES["small-coop-stage3"][0]()[0])
+    assert decode(few)[6]["nparts"].max() == 1

@@ -116,10 +116,8 @@ void build_stream(FusedPlan &f, const Plan &s1, bool accumulate, int32_t tile_co
         // 23.0 -> 11.8 us; blocks of a few products ran slower that way (a
         // random structure 10.4 -> 13.4 us), so they stay one block.
         const auto &pl = prods[ci];
-        const bool each = pl.size() >= (size_t)STREAM_SPLIT_PRODUCTS;
-        if (pl.size() > (size_t)FUSED_WCAP)
-            ffail(BSC_ERR_UNSUPPORTED, std::string(who) + ": a C block has more than " + std::to_string(FUSED_WCAP) +
-                                           " products");
+        // (at most FUSED_WCAP blocks fit a wave's lane-held weights: longer lists stay one block)
+        const bool each = pl.size() >= (size_t)STREAM_SPLIT_PRODUCTS && pl.size() <= (size_t)FUSED_WCAP;
         for (size_t pi = 0; pi < pl.size(); ++pi)
             push_chan(f, s1, s1.A[pl[pi].first], s1.B[pl[pi].second], M, N, each ? (int32_t)pi : 0,
                       each || pi + 1 == pl.size(), who);

@@ -132,3 +132,26 @@ def test_stream_splits_many_product_blocks():
     assert (groups["nblk"] >= 8).all() and parts["nparts"].max() > 1
     few = bst.StreamPlan(CASES["small-coop-stage3"][0]()[0])
     assert decode(few)[6]["nparts"].max() == 1
+
+
+def test_stream_long_product_list_stays_one_block():
+    """A C block of 300 products (more than a wave's 256 lane-held weights)
+    stays one block and still replays to the oracle's result."""
+    from workloads.model import Contraction, Index, Operand
+    nk = 300
+    m = Index(np.zeros((1, 1), np.int32), [20])
+    n = Index(np.zeros((1, 1), np.int32), [18])
+    k = Index(np.zeros((nk, 1), np.int32), np.full(nk, 3))
+    rng = np.random.default_rng(1)
+    A = Operand(np.zeros(nk), np.arange(nk), np.arange(nk) * 60, np.tile([3, 0], (nk, 1)), np.tile([1, 0], (nk, 1)),
+                [0], nk * 60)
+    B = Operand(np.arange(nk), np.zeros(nk), np.arange(nk) * 54, np.tile([18, 0], (nk, 1)), np.tile([1, 0], (nk, 1)),
+                [0], nk * 54)
+    Cb = Operand([0], [0], [0], [[18, 0]], [[1, 0]], [0], 360)
+    con = Contraction(m, k, n, A, B, Cb, "f64")
+    a = rng.integers(-2, 3, nk * 60).astype(float)
+    b = rng.integers(-2, 3, nk * 54).astype(float)
+    sp = bst.StreamPlan(con)
+    groups = decode(sp)[1]
+    assert groups["nblk"].tolist() == [1] and groups["nchan"].tolist() == [nk]
+    assert np.array_equal(replay(sp, a, b, np.ones(1), np.zeros(360)), oracle.contract(con, a, b, np.zeros(360)))

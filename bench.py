@@ -654,9 +654,14 @@ def main():
             ref_l = bufs[last].index_select(0, adl).double()
             got_l = sbuf[last].index_select(0, adl).double()
             srel = float((got_l - ref_l).norm() / ref_l.norm().clamp_min(1e-300))
+            tail_flops = [bp.stats()["useful_flops"] for _, bp in tail]
             fused["stream_tail"] = {"ms_per_step": round(sms, 6), "value": round(flops / (sms * 1e-3) / 1e9, 3),
                                     "unit": "GFLOP/s", "stage_kernel_ms": [round(x, 6) for x in sstage],
                                     "tail_plans": [k for k, _ in tail],
+                                    # each launch's useful rate against the matrix-core peak of the dtype
+                                    "frac_mfma": [round(fs["useful_flops"] / (sstage[0] * 1e-3) / 1e12 / peak, 5)] +
+                                                 [round(fl / (t * 1e-3) / 1e12 / peak, 5)
+                                                  for fl, t in zip(tail_flops, sstage[1:])],
                                     "last_output_rel_diff_vs_grouped": srel}
 
     # --- the gather (pack) phase against the HBM roofline: every gatherable operand of each

@@ -1152,11 +1152,19 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             std::vector<std::vector<size_t>> q(BSC_XCDS);
             std::vector<double> load(BSC_XCDS, 0.0);
             auto least = [&]() { return (size_t)(std::min_element(load.begin(), load.end()) - load.begin()); };
+            // A group of at most one tile per CU of a chiplet stays on one chiplet
+            // up to twice a chiplet's share: its tiles then run without partners
+            // and share their panels in one L2, and the other chiplets take the
+            // rest (bf16 block-diagonal workload: the 32 tiles of its 1024^3 sector
+            // on one chiplet, 32.8-33.6 -> 31.7-32.0 us).  Larger groups are cut
+            // into contiguous slices of at most half a share.
             for (size_t g : gord) {
                 const size_t a = span[g].first, b = span[g].second;
                 const size_t ntile = b - a;
                 size_t parts = 1;
-                if (gcost[g] > 0.5 * target) parts = std::min<size_t>({(size_t)BSC_XCDS, ntile, (size_t)std::ceil(gcost[g] / (0.5 * target))});
+                const bool whole = ntile <= (size_t)BSC_CUS_PER_XCD && gcost[g] <= 2.0 * target;
+                if (!whole && gcost[g] > 0.5 * target)
+                    parts = std::min<size_t>({(size_t)BSC_XCDS, ntile, (size_t)std::ceil(gcost[g] / (0.5 * target))});
                 for (size_t part = 0; part < parts; ++part) {
                     const size_t lo = a + ntile * part / parts, hi = a + ntile * (part + 1) / parts;
                     const size_t x = least();

@@ -581,3 +581,32 @@ def test_tail_bundles_cover_tiny_groups(name):
         ref = oracle.contract(con, a, b, np.zeros(con.C.buffer_elems), check=False)
         np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
     assert seen > 0
+
+
+def test_chiplet_placement():
+    """Task t runs on chiplet t % 8.  A group of at most 32 tiles (one per CU of
+    a chiplet) costing at most twice a chiplet's share stays on one chiplet; a
+    larger group is cut over several.  The 32 tiles of the bf16 block-diagonal
+    workload's 1024^3 sector share one chiplet and run without a CU partner."""
+    prob = C.blockdiag_bf16(ld_align=8, align=8, values=False)
+    info, groups, runs, ap, bp, cp, tasks, fast = decode(bst.Plan(prob.con))
+    direct = [t for t in range(len(tasks)) if tasks[t]["cls"] in (T_DENSE_N, T_DENSE_K)]
+    by_group = {}
+    for t in direct:
+        by_group.setdefault(int(fast[t]["group"]), []).append(t)
+    assert max(len(v) for v in by_group.values()) == 32
+    for g, ts in by_group.items():
+        if len(ts) <= 32:
+            assert len({t % 8 for t in ts}) == 1, g
+    big = [t for t in direct if fast[t]["K"] == 1024]
+    assert len(big) == 32 and len({t % 8 for t in big}) == 1
+    # slot d of a chiplet's queue is task 8 d + x; slots d and d + 32 share a CU
+    for t in big:
+        d = t // 8
+        assert d < 32
+        partner = t + 8 * 32
+        assert partner >= len(tasks) or tasks[partner]["cls"] == 6   # T_NOP
+    # 4096^3: 512 tiles over all eight chiplets
+    _, _, _, _, _, _, tk, _ = decode(bst.Plan(_dense_con(4096, 4096, 4096, True)))
+    cl = [t % 8 for t in range(len(tk)) if tk[t]["cls"] in T_DIRECT]
+    assert len(cl) == 512 and set(cl) == set(range(8))

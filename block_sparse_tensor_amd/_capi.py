@@ -53,7 +53,8 @@ class BscStats(ctypes.Structure):
                 ("pack_bytes", c_int64), ("device_bytes", c_int64), ("tail_triples", c_int64),
                 ("launches_issued", c_int64), ("grid", c_int32), ("split_tiles", c_int32),
                 ("predicted_us", c_double), ("pack_gain_seg_us", c_double), ("pack_gain_pad_us", c_double),
-                ("pack_cost_us", c_double), ("pack_gain_align_us", c_double)]
+                ("pack_cost_us", c_double), ("pack_gain_align_us", c_double),
+                ("wide_only", c_int64)]
 
 
 class BscWorklistInfo(ctypes.Structure):

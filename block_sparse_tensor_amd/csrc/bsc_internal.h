@@ -299,6 +299,7 @@ struct Plan {
     int32_t cu_count = 0;
     int32_t grid = 0;
     int32_t features = 0;             // FEAT_* bits over all tasks
+    bool only_wide = false;           // every task is a wide tile (or a no-op)
 
     bsc_stats stats{};
 };

@@ -161,7 +161,7 @@ KernelRef kernel_ref() {
     static const hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)once;
-    return {fn, lds};
+    return {fn, lds, 256};
 }
 
 }  // namespace bsc

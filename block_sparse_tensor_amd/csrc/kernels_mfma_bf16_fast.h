@@ -204,13 +204,13 @@ __device__ __forceinline__ void fast_issue(const FastOp<NI> &f, int32_t c, uint1
 
 // Masked fill of a partial chunk (k0 .. K-1 valid) of a K-contiguous operand
 // through registers: ROWS rows of four 16-byte granules.
-template <int ROWS>
+template <int ROWS, int NT = 256>
 __device__ __forceinline__ void dense_fill_kcontig(int64_t base, int64_t xs, int32_t xlen, int32_t k0, int32_t K,
                                                    const uint16_t *P, uint16_t *lds) {
     const int32_t tid = tid_x();
 #pragma unroll 1
-    for (int q = 0; q < ROWS * 4 / 256; ++q) {
-        const int32_t u = tid + 256 * q;         // row u / 4, k-granule u % 4
+    for (int q = 0; q < ROWS * 4 / NT; ++q) {
+        const int32_t u = tid + NT * q;         // row u / 4, k-granule u % 4
         const int32_t r = u >> 2, g = u & 3;
         const int32_t k = k0 + 8 * g;
         uint16_t e[8];

@@ -1,5 +1,6 @@
 // Wide dense matrix-core tile for bf16 inputs / fp32 accumulation: one
-// workgroup per CU.
+// workgroup per CU.  Two forms: four waves (below), and eight waves of
+// 128 x 64 (wide8_tile_bf16, a launch of wide tiles only).
 //
 // Same record-addressed groups as the 256 x 128 direct-to-LDS tile
 // (kernels_mfma_bf16_fast.h: one run of single strided views, 16-byte aligned
@@ -42,17 +43,20 @@ constexpr int WB_BM = 256;   // tile rows
 constexpr int WB_FM = 4;     // row fragments (of 32) per wave: 128 rows
 constexpr int WB_RING_ELEMS = 81920;   // 160 KB: the CU's whole LDS
 
-// Geometry of the wide tile for a wave tile width WN (128 or 64 columns).
-template <int WN>
+// Geometry of the wide tile for a wave tile width WN (128 or 64 columns) and
+// NW waves (4, or 8 with 64-column waves: 256 columns); the copies of a chunk
+// are shared out over the NW waves.
+template <int WN, int NW = 4>
 struct Wide {
-    static constexpr int BN = 2 * WN;                  // tile columns
+    static constexpr int NT = 64 * NW;
+    static constexpr int BN = (NW / 2) * WN;                  // tile columns
     static constexpr int FN = WN / 32;                 // column fragments per wave (4 or 2)
     static constexpr int A_ELEMS = WB_BM * FB_BK;      // A part of a stage
     static constexpr int B_ELEMS = BN * FB_BK;         // B part of a stage
     static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
     static constexpr int STAGES = WB_RING_ELEMS / STAGE_ELEMS < 6 ? WB_RING_ELEMS / STAGE_ELEMS : 6;
-    static constexpr int NIA = A_ELEMS * 2 / 1024 / 4;   // 1 KB copies of A per wave and chunk (4)
-    static constexpr int NIB = B_ELEMS * 2 / 1024 / 4;   // of B (4 or 2)
+    static constexpr int NIA = A_ELEMS * 2 / 1024 / NW;   // 1 KB copies of A per wave and chunk (4)
+    static constexpr int NIB = B_ELEMS * 2 / 1024 / NW;   // of B (4 or 2)
     static constexpr int SLOTS = BN * 2 / 16;            // 16-byte slots per N-contiguous B row (32 or 16)
     static constexpr int ROWS_PER = 64 / SLOTS;          // B k-rows one copy instruction fills (2 or 4)
     static_assert(STAGES * STAGE_ELEMS <= WB_RING_ELEMS, "ring fits the LDS");
@@ -83,10 +87,10 @@ static_assert(4 * (Wide<128>::NIA + Wide<128>::NIB) < 64 && 4 * (Wide<64>::NIA +
 // into BN-wide LDS rows: instruction j fills k rows ROWS_PER (NI w + j) ..;
 // lane l fills row l / SLOTS, 16-byte slot l % SLOTS, i.e. 64-byte position
 // (l % SLOTS) / 4, which holds n-granule position ^ (k & 3).
-template <int WN, int NI>
+template <int WN, int NI, int NW = 4>
 __device__ __forceinline__ FastOp<NI> wide_setup_ncontig(int64_t base, int64_t ks, int32_t nlen, int32_t K,
                                                          const uint16_t *P, int32_t w) {
-    using G = Wide<WN>;
+    using G = Wide<WN, NW>;
     FastOp<NI> f;
     const int32_t lane = tid_x() & 63;
     const int32_t s = lane % G::SLOTS;
@@ -103,14 +107,14 @@ __device__ __forceinline__ FastOp<NI> wide_setup_ncontig(int64_t base, int64_t k
 }
 
 // Masked fill of a partial chunk (k0 .. K-1 valid) of an N-contiguous B into BN-wide rows.
-template <int WN>
+template <int WN, int NW = 4>
 __device__ __forceinline__ void wide_fill_ncontig(int64_t base, int64_t ks, int32_t nlen, int32_t k0, int32_t K,
                                                   const uint16_t *P, uint16_t *lds) {
-    using G = Wide<WN>;
+    using G = Wide<WN, NW>;
     const int32_t tid = tid_x();
 #pragma unroll 1
-    for (int q = 0; q < FB_BK * G::SLOTS / 256; ++q) {
-        const int32_t u = tid + 256 * q;         // k row u / SLOTS, 8-column piece u % SLOTS
+    for (int q = 0; q < FB_BK * G::SLOTS / G::NT; ++q) {
+        const int32_t u = tid + G::NT * q;         // k row u / SLOTS, 8-column piece u % SLOTS
         const int32_t kr = u / G::SLOTS, s = u % G::SLOTS;
         const int32_t n = 8 * s, k = k0 + kr;
         uint16_t e[8];
@@ -134,9 +138,9 @@ struct WideOff {
     uint32_t b[4];   // K-contiguous B: by K-step (b[0], b[1]); N-contiguous B: by column fragment
 };
 
-template <int WN, bool BN>
+template <int WN, bool BN, int NW = 4>
 __device__ __forceinline__ WideOff wide_offsets() {
-    using G = Wide<WN>;
+    using G = Wide<WN, NW>;
     const int32_t lane = tid_x() & 63, w = tid_x() >> 6;
     const int32_t wm = w & 1, wn = w >> 1;
     WideOff o;
@@ -183,10 +187,10 @@ struct WideFrags {
 // plus this wave's A offset for the K-step; vb: K-contiguous B: the stage's B
 // base plus the B offset of the K-step; N-contiguous B: the stage's B base,
 // to which each fragment adds its own lane offset o.b[f].
-template <int WN, bool BN, int KS>
+template <int WN, bool BN, int KS, int NW = 4>
 __device__ __forceinline__ void wide_read_one(int r, uint32_t va, uint32_t vb, const WideOff &o,
                                               WideFrags<WN / 32> &fr) {
-    using G = Wide<WN>;
+    using G = Wide<WN, NW>;
     constexpr int FN = G::FN;
     constexpr int AR = 2 * 32 * FB_BK;               // bytes between row fragments
     if constexpr (BN) {
@@ -218,10 +222,10 @@ __device__ __forceinline__ void wide_read_one(int r, uint32_t va, uint32_t vb, c
 template <int WN, bool BN>
 constexpr int wide_reads() { return (BN ? 2 * (WN / 32) : WN / 32) + WB_FM; }
 
-template <int WN, bool BN, int KS>
+template <int WN, bool BN, int KS, int NW = 4>
 __device__ __forceinline__ void wide_read_all(uint32_t va, uint32_t vb, const WideOff &o, WideFrags<WN / 32> &fr) {
 #pragma unroll
-    for (int r = 0; r < wide_reads<WN, BN>(); ++r) wide_read_one<WN, BN, KS>(r, va, vb, o, fr);
+    for (int r = 0; r < wide_reads<WN, BN>(); ++r) wide_read_one<WN, BN, KS, NW>(r, va, vb, o, fr);
 }
 
 template <int WN, bool BN>
@@ -253,7 +257,7 @@ __device__ __forceinline__ bf16x8_t wide_bfrag(const WideFrags<FN> &fr, int f) {
 // The MFMAs of one K-step (fragments `cur`, FM x FN of them) with the reads of
 // the next K-step's fragments (`nxt`, K-step KS at bases va, vb) issued between
 // them after the first PRE MFMAs; `mid` runs right before MFMA PRE.
-template <int WN, bool BN, int KS, int PRE, typename Mid>
+template <int WN, bool BN, int KS, int PRE, int NW, typename Mid>
 __device__ __forceinline__ void wide_mfma_interleaved(const WideFrags<WN / 32> &cur, WideFrags<WN / 32> &nxt,
                                                       uint32_t va, uint32_t vb, const WideOff &o,
                                                       f32x16_t (&acc)[WB_FM][WN / 32], Mid &&mid) {
@@ -283,7 +287,7 @@ __device__ __forceinline__ void wide_mfma_interleaved(const WideFrags<WN / 32> &
             const int slot = k - PRE;
 #pragma unroll
             for (int r = 0; r < NR; ++r)
-                if (r >= 2 * slot && r < 2 * slot + 2) wide_read_one<WN, BN, KS>(r, va, vb, o, nxt);
+                if (r >= 2 * slot && r < 2 * slot + 2) wide_read_one<WN, BN, KS, NW>(r, va, vb, o, nxt);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -318,11 +322,11 @@ __device__ __forceinline__ void wide_mfma(const WideFrags<WN / 32> &fr, f32x16_t
 // slice's partial tile lane-contiguously, count the slice in the tile's
 // counter, and let the last slice reload the accumulators as the partials'
 // sum in slice order.
-template <int WN>
+template <int WN, int NW>
 __device__ __forceinline__ bool wide_split_arrive(const KArgs &ka, const DFast &fd, f32x16_t (&acc)[WB_FM][WN / 32],
                                                   int32_t w, int32_t lane, int32_t &last) {
     constexpr int FN = WN / 32;
-    constexpr int SPLIT_BYTES = WB_BM * 2 * WN * 4;   // one partial tile
+    constexpr int SPLIT_BYTES = WB_BM * Wide<WN, NW>::BN * 4;   // one partial tile
     constexpr int NQ = WB_FM * FN * 4;                // 16-byte groups per lane
     const uint64_t base = reinterpret_cast<uint64_t>(ka.P + fd.part);
     const uint64_t ubase = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(base >> 32))) << 32) |
@@ -378,9 +382,9 @@ __device__ __forceinline__ bool wide_split_arrive(const KArgs &ka, const DFast &
     return true;
 }
 
-template <typename TC, bool BN, int WN>
+template <typename TC, bool BN, int WN, int NW>
 __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd, WideSmemBf16 &sm) {
-    using G = Wide<WN>;
+    using G = Wide<WN, NW>;
     constexpr int FN = G::FN;
     const uint16_t *A = static_cast<const uint16_t *>((fd.flags & F_A_WS) ? ka.W : ka.A);
     const uint16_t *B = static_cast<const uint16_t *>((fd.flags & F_B_WS) ? ka.W : ka.B);
@@ -402,15 +406,15 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
     // the same barriers.
     const int32_t wm = w & 1, wn = w >> 1;
     const bool compute = wm * (WB_BM / 2) < mlen && wn * WN < nlen;
-    const bool acopy = 64 * w < mlen;
+    const bool acopy = (WB_BM / NW) * w < mlen;
     const FastOp<G::NIA> fa = dense_setup_kcontig<G::NIA>(fd.a_base, fd.a_rs, mlen, K, A, w);
     FastOp<G::NIB> fb;
-    if constexpr (BN) fb = wide_setup_ncontig<WN, G::NIB>(fd.b_base, fd.b_ks, nlen, K, B, w);
+    if constexpr (BN) fb = wide_setup_ncontig<WN, G::NIB, NW>(fd.b_base, fd.b_ks, nlen, K, B, w);
     else fb = dense_setup_kcontig<G::NIB>(fd.b_base, fd.b_ns, nlen, K, B, w);
     const int64_t b_s = BN ? fd.b_ks : fd.b_ns;
     const int32_t nfull = K / FB_BK;
     const int32_t ntot = (K + FB_BK - 1) / FB_BK;
-    const WideOff fo = wide_offsets<WN, BN>();
+    const WideOff fo = wide_offsets<WN, BN, NW>();
     wait_vm<0>();      // nothing else outstanding: the counted waits below see only this tile's copies
     __syncthreads();   // previous users of the LDS ring are done
 
@@ -421,9 +425,9 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
         uint16_t *const ops = sm.op;
         auto fill_partial = [&](int32_t stage) {
             uint16_t *at = ops + stage * G::STAGE_ELEMS;
-            dense_fill_kcontig<WB_BM>(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, at);
-            if constexpr (BN) wide_fill_ncontig<WN>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + G::A_ELEMS);
-            else dense_fill_kcontig<G::BN>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + G::A_ELEMS);
+            dense_fill_kcontig<WB_BM, G::NT>(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, at);
+            if constexpr (BN) wide_fill_ncontig<WN, NW>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + G::A_ELEMS);
+            else dense_fill_kcontig<G::BN, G::NT>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + G::A_ELEMS);
         };
         auto issue = [&](int32_t c, int32_t stage) {
             uint16_t *at = ops + stage * G::STAGE_ELEMS;
@@ -458,10 +462,10 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
         // B base of a stage for K-step ks: N-contiguous B adds per-fragment offsets later
         auto bbase = [&](uint32_t stage, int ks) { return stage + B_OFF + (BN ? 0u : fo.b[ks]); };
         auto reads0 = [&](uint32_t stage, WideFrags<FN> &fr) {
-            if constexpr (COMPUTE) wide_read_all<WN, BN, 0>(stage + fo.a[0], bbase(stage, 0), fo, fr);
+            if constexpr (COMPUTE) wide_read_all<WN, BN, 0, NW>(stage + fo.a[0], bbase(stage, 0), fo, fr);
         };
         auto reads1 = [&](uint32_t stage, WideFrags<FN> &fr) {
-            if constexpr (COMPUTE) wide_read_all<WN, BN, 1>(stage + fo.a[1], bbase(stage, 1), fo, fr);
+            if constexpr (COMPUTE) wide_read_all<WN, BN, 1, NW>(stage + fo.a[1], bbase(stage, 1), fo, fr);
         };
         auto mfmas = [&](const WideFrags<FN> &fr) {
             if constexpr (COMPUTE) {
@@ -483,9 +487,9 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
             const int32_t sn = st == STAGES - 1 ? 0 : st + 1;
             if constexpr (COMPUTE) {
                 const uint32_t here = ring + st * STAGE_BYTES, next = ring + sn * STAGE_BYTES;
-                wide_mfma_interleaved<WN, BN, 1, 2>(s0, s1, here + fo.a[1], bbase(here, 1), fo, acc, [] {});
+                wide_mfma_interleaved<WN, BN, 1, 2, NW>(s0, s1, here + fo.a[1], bbase(here, 1), fo, acc, [] {});
                 settle(s1);
-                wide_mfma_interleaved<WN, BN, 0, 2>(s1, s0, next + fo.a[0], bbase(next, 0), fo, acc, [&] {
+                wide_mfma_interleaved<WN, BN, 0, 2, NW>(s1, s0, next + fo.a[0], bbase(next, 0), fo, acc, [&] {
                     wait_vm<PER * (STAGES - 2)>();
                     lds_barrier();
                     issue(c + STAGES, st);
@@ -523,7 +527,7 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
     }
 
     const int32_t lane = tid_x() & 63;
-    if (fd.nsplit > 1 && !wide_split_arrive<WN>(ka, fd, acc, w, lane, *reinterpret_cast<int32_t *>(sm.op))) return;
+    if (fd.nsplit > 1 && !wide_split_arrive<WN, NW>(ka, fd, acc, w, lane, *reinterpret_cast<int32_t *>(sm.op))) return;
 
     // epilogue: straight from the accumulators, 32 consecutive columns per row
     TC *Cp = static_cast<TC *>(ka.C);
@@ -552,8 +556,19 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
 template <typename TC, bool BN>
 __device__ __forceinline__ void wide_tile_bf16(const KArgs &ka, const DFast &fd_ref, WideSmemBf16 &sm) {
     const DFast fd = fd_ref;   // one read of the record
-    if (fd.nlen > 128) wide_tile_body<TC, BN, 128>(ka, fd, sm);
-    else wide_tile_body<TC, BN, 64>(ka, fd, sm);
+    if (fd.nlen > 128) wide_tile_body<TC, BN, 128, 4>(ka, fd, sm);
+    else wide_tile_body<TC, BN, 64, 4>(ka, fd, sm);
+}
+
+// The same tile on eight waves (a 512-thread workgroup, two waves per SIMD):
+// 2 x 4 waves of 128 x 64, so one wave's fragment reads overlap the other's
+// MFMAs on every SIMD, which four waves of 128 x 128 cannot do.  A tile of at
+// most 128 columns runs the same loop; the waves whose columns lie past its
+// edge copy their share of B (clamped to a valid column) and compute nothing.
+template <typename TC, bool BN>
+__device__ __forceinline__ void wide8_tile_bf16(const KArgs &ka, const DFast &fd_ref, WideSmemBf16 &sm) {
+    const DFast fd = fd_ref;
+    wide_tile_body<TC, BN, 64, 8>(ka, fd, sm);
 }
 
 }  // namespace bsc

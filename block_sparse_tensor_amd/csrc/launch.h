@@ -17,7 +17,8 @@ using KernelFn = void (*)(KArgs);
 
 struct KernelRef {
     KernelFn fn;
-    size_t lds;     // dynamic LDS bytes of the variant
+    size_t lds;         // dynamic LDS bytes of the variant
+    unsigned threads;   // workgroup size it is compiled for
 };
 
 // Grouped-contraction kernel of a plan dtype holding the tile bodies `feat`
@@ -28,6 +29,7 @@ KernelRef grouped_kernel_f32(int32_t feat);
 KernelRef grouped_kernel_bf16_lo(int32_t feat);   // feat 0..3
 KernelRef grouped_kernel_bf16_hi(int32_t feat);   // feat 4..7
 KernelRef grouped_kernel_bf16_wide(int32_t feat); // FEAT_WIDE, with or without FEAT_MFMA
+KernelRef grouped_kernel_bf16_wide8();            // a launch of wide tiles only (512 threads)
 
 // Enqueue the gather kernel of a plan dtype.
 void launch_pack(bsc_dtype dt, dim3 grid, hipStream_t s, const PArgs &pa);

@@ -1276,8 +1276,10 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         s.items = 0;
         for (auto &t : p.tasks) s.items += t.cls != T_NOP;
         p.features = 0;
+        p.only_wide = !p.tasks.empty();
         for (auto &t : p.tasks) {
             if (t.cls == T_NOP) continue;
+            if (!is_wide(t.cls)) p.only_wide = false;
             const int32_t slot = (t.cls == T_MFMA_FAST_K || is_wide(t.cls)) ? T_MFMA_FAST_N
                                  : (t.cls == T_SKINNY_M || t.cls == T_SKINNY_N || t.cls == T_SKINNY_DENSE_M ||
                                     t.cls == T_SKINNY_DENSE_N) ? 5
@@ -1307,6 +1309,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         s.pack_gain_pad_us = p.gain_pad_us;
         s.pack_cost_us = p.pack_cost_us;
         s.pack_gain_align_us = p.gain_align_us;
+        s.wide_only = p.only_wide ? 1 : 0;
         const double rate_gflops = p.dtype == BSC_BF16_F32 ? 2.5e6 : (p.dtype == BSC_F32 ? 157.3e3 : 78.6e3);
         s.predicted_us = s.launches_per_contract * p.opt.t_launch_us +
                          std::max((double)flops / (rate_gflops * 1e3), (double)s.alg_bytes / 8.0e6) +

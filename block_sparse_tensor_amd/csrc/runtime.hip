@@ -21,9 +21,11 @@ static bsc_status hip_fail(hipError_t e, const char *what) {
 // bf16 launches pick the variant that holds exactly the tile bodies the plan uses;
 // when an operand base is not 16-byte aligned the direct-to-LDS tiles fall back
 // to the general matrix-core tile (task class T_MFMA_FAST_* is accepted there).
-static KernelRef pick_bf16(int32_t feat, bool vec) {
+// A plan of wide tiles only runs them on eight waves per workgroup.
+static KernelRef pick_bf16(int32_t feat, bool vec, bool only_wide) {
     constexpr int32_t DIRECT = FEAT_FAST_N | FEAT_FAST_K | FEAT_WIDE;
     if (!vec && (feat & DIRECT)) feat = (feat & ~DIRECT) | FEAT_MFMA;
+    if (feat == FEAT_WIDE && only_wide) return grouped_kernel_bf16_wide8();
     if (feat & FEAT_WIDE) return grouped_kernel_bf16_wide(feat);
     return feat < 4 ? grouped_kernel_bf16_lo(feat) : grouped_kernel_bf16_hi(feat);
 }
@@ -125,24 +127,11 @@ static bsc_status contract_on(Plan *p, const void *region, int32_t cu_count, con
     for (auto &l : p->launches) {
         ka.task0 = l[0];
         ka.ntasks = l[1] - l[0];
-        dim3 grid((unsigned)grid_for(*p, ka.ntasks, cu_count)), block(256);
-        switch (p->dtype) {
-            case BSC_F64: {
-                const KernelRef k = grouped_kernel_f64(p->features);
-                hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
-                break;
-            }
-            case BSC_F32: {
-                const KernelRef k = grouped_kernel_f32(p->features);
-                hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
-                break;
-            }
-            case BSC_BF16_F32: {
-                const KernelRef k = pick_bf16(p->features, ka.vec_a && ka.vec_b);
-                hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
-                break;
-            }
-        }
+        const KernelRef k = p->dtype == BSC_F64   ? grouped_kernel_f64(p->features)
+                            : p->dtype == BSC_F32 ? grouped_kernel_f32(p->features)
+                                                  : pick_bf16(p->features, ka.vec_a && ka.vec_b, p->only_wide);
+        dim3 grid((unsigned)grid_for(*p, ka.ntasks, cu_count)), block(k.threads);
+        hipLaunchKernelGGL(k.fn, grid, block, k.lds, s, ka);
         p->stats.launches_issued++;
     }
     hipError_t e = hipGetLastError();

@@ -199,6 +199,10 @@ typedef struct {
     /* bf16: time saved by gathering misaligned single-view operands into
      * 16-byte rows, which moves their groups onto the direct-to-LDS tile */
     double pack_gain_align_us;
+    /* 1 when every task is a wide tile (tile_cols = 256): with both operand
+     * bases 16-byte aligned the launch then runs eight-wave workgroups of
+     * 512 threads instead of four-wave ones */
+    int64_t wide_only;
 } bsc_stats;
 
 typedef struct bsc_plan_s *bsc_plan_t;

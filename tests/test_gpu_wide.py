@@ -1,8 +1,10 @@
-"""GPU parity of the wide bf16 tile (one workgroup per CU: 256 x 256 output,
-four waves of 128 x 128; 128 x 64 waves for tiles of at most 128 columns):
-integer-valued inputs compare bit for bit with the oracle (every summation
-order is exact), both B orientations, ragged edges, partial last K chunks,
-K-slices, accumulation, and the bench workload's structure at full size."""
+"""GPU parity of the wide bf16 tile (one workgroup per CU: 256 x 256 output).
+A plan of wide tiles only runs eight waves of 128 x 64 per workgroup; a plan
+that also holds other tiles runs four waves of 128 x 128 (128 x 64 for tiles
+of at most 128 columns).  Integer-valued inputs compare bit for bit with the
+oracle (every summation order is exact), both B orientations, ragged edges,
+partial last K chunks, K-slices, accumulation, several tiles per workgroup,
+and the bench workload's structure at full size (four-wave form)."""
 import numpy as np
 import pytest
 
@@ -11,6 +13,8 @@ from workloads import configs as C
 
 from gpuhelp import c_addresses, canary, check_canary, check_float, have_gpu, run_engine, to_dev, torch
 from test_gpu_split import _single
+from workloads.layout import write_block
+from workloads.model import Contraction, Index, Operand
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +35,56 @@ def test_wide_single_integer_bit_exact(shape, brow, split_k):
     con, a, b = _single(M, K, N, brow, seed=M + 3 * K + 7 * N, ints=True)
     plan = bst.Plan(con, tile_cols=256, split_k=split_k).bind()
     print(f"[wide] {M}x{K}x{N} brow={brow} split_k={split_k} items={plan.stats()['items']} "
-          f"split_tiles={plan.stats()['split_tiles']}", flush=True)
+          f"split_tiles={plan.stats()['split_tiles']} wide_only={plan.stats()['wide_only']}", flush=True)
+    addr, mask = c_addresses(con)
+    got = run_engine(plan, a, b, canary(con, "bf16"), "bf16")
+    check_canary(got, mask)
+    ref = oracle.contract(con, a, b, np.zeros(con.C.buffer_elems), check=False)
+    assert np.array_equal(got[addr], ref[addr].astype(np.float32))
+
+
+def _blocks(dims, brow, seed):
+    """Block-diagonal bf16 contraction: sector i is an M_i x K_i by K_i x N_i
+    GEMM with 16-byte aligned rows, small integer values."""
+    rng = np.random.default_rng(seed)
+    nb = len(dims)
+    lda = [(k + 7) // 8 * 8 for _, k, _ in dims]
+    ldb = [(n + 7) // 8 * 8 for _, _, n in dims] if brow else [(k + 7) // 8 * 8 for _, k, _ in dims]
+    aoff, boff, coff = [], [], []
+    a_n = b_n = c_n = 0
+    for (m, k, n), la, lb in zip(dims, lda, ldb):
+        aoff.append(a_n); boff.append(b_n); coff.append(c_n)
+        a_n += m * la
+        b_n += k * lb if brow else n * lb
+        c_n += m * n
+    abuf, bbuf = np.zeros(a_n + 8, np.float32), np.zeros(b_n + 8, np.float32)
+    brs = [((lb, 0), (1, 0)) if brow else ((1, 0), (lb, 0)) for lb in ldb]
+    for i, (m, k, n) in enumerate(dims):
+        write_block(abuf, aoff[i], (lda[i], 0), (1, 0), rng.integers(-2, 3, (m, k)).astype(np.float32))
+        write_block(bbuf, boff[i], brs[i][0], brs[i][1], rng.integers(-2, 3, (k, n)).astype(np.float32))
+    keys = [[i] for i in range(nb)]
+    r = list(range(nb))
+    con = Contraction(Index(keys, [d[0] for d in dims]), Index(keys, [d[1] for d in dims]),
+                      Index(keys, [d[2] for d in dims]),
+                      Operand(r, r, aoff, [(l, 0) for l in lda], [(1, 0)] * nb, [0], abuf.size),
+                      Operand(r, r, boff, [b[0] for b in brs], [b[1] for b in brs], [0], bbuf.size),
+                      Operand(r, r, coff, [(d[2], 0) for d in dims], [(1, 0)] * nb, [0], c_n), "bf16")
+    return con, abuf, bbuf
+
+
+@pytest.mark.parametrize("brow", [True, False])
+@pytest.mark.parametrize("grid", [0, 8])
+def test_wide_only_blocks_integer_bit_exact(brow, grid):
+    """Several sectors, all on wide tiles (eight-wave workgroups), ragged
+    edges and one K-split sector; grid 8 makes every workgroup loop over
+    several tiles of the persistent task list."""
+    dims = [(512, 512, 512), (300, 700, 260), (256, 96, 100), (700, 1200, 520), (64, 40, 300), (520, 256, 256)]
+    con, a, b = _blocks(dims, brow, seed=31 + brow)
+    plan = bst.Plan(con, tile_cols=256, split_k=12, grid_limit=grid).bind()
+    s = plan.stats()
+    print(f"[wide] blocks brow={brow} grid={grid} items={s['items']} split_tiles={s['split_tiles']} "
+          f"wide_only={s['wide_only']}", flush=True)
+    assert s["wide_only"] == 1 and s["split_tiles"] > 0
     addr, mask = c_addresses(con)
     got = run_engine(plan, a, b, canary(con, "bf16"), "bf16")
     check_canary(got, mask)

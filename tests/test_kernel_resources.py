@@ -2,8 +2,9 @@
 it for the last build (kernel-resource-usage remarks recorded by
 block_sparse_tensor_amd.build).  A kernel that spills to scratch memory pays
 a private-memory round trip in its inner loop, so no kernel may use scratch
-beyond the two known cases: the wide bf16 tile (an option, 256 x 256 output
-per workgroup with all accumulators in registers) and the fp32 general-tile
+beyond the two known cases: the four-wave wide bf16 tile (an option, 256 x 256
+output per workgroup with all accumulators in registers; its eight-wave form
+has none) and the fp32 general-tile
 instance compiled for four waves per SIMD (12 bytes per lane; compiled for
 three it was measured slower)."""
 import json
@@ -38,7 +39,7 @@ def test_every_kernel_reported():
     k = _load()
     for name in ("pack_gather<unsigned short>", "fused_contract<float, 4, 2>", "fused_contract<double, 16, 1>",
                  "grouped_contract<unsigned short, float, float, 2>", "grouped_contract<double, double, double, 1>",
-                 "grouped_contract_narrow<float, float, float, 0>", "probe_bf16"):
+                 "grouped_contract_narrow<float, float, float, 0>", "probe_bf16", "grouped_contract_wide8"):
         assert any(name in d for d in k), name
     assert len(k) >= 27
 
@@ -56,5 +57,5 @@ def test_bench_kernel_keeps_two_waves_per_simd():
     SIMD) to overlap one wave's copies with the other's matrix-core work."""
     k = _load()
     for d, r in k.items():
-        if "grouped_contract<unsigned short, float, float," in d:
+        if "grouped_contract<unsigned short, float, float," in d or "grouped_contract_wide8" in d:
             assert r["occupancy"] >= 2, (d, r)

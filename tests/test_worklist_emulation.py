@@ -37,9 +37,13 @@ T_WIDE_N, T_WIDE_K = 12, 13       # wide tile (one workgroup per CU): 256 x 256,
 T_DIRECT = (T_DENSE_N, T_DENSE_K, T_WIDE_N, T_WIDE_K)
 
 
-def split_tile_elems(cls, nlen):
-    """fp32 elements the kernel strides per K-slice partial tile."""
-    return 256 * 256 if cls in (T_WIDE_N, T_WIDE_K) and nlen > 128 else SPLIT_TILE
+def split_tile_elems(cls, nlen, wide_only=False):
+    """fp32 elements the kernel strides per K-slice partial tile: the 256 x 128
+    tile's, a wide tile's 256 x 256 (four waves of 128 x 64 at <= 128 columns:
+    256 x 128), and always 256 x 256 on eight waves (a plan of wide tiles only)."""
+    if cls in (T_WIDE_N, T_WIDE_K) and (nlen > 128 or wide_only):
+        return 256 * 256
+    return SPLIT_TILE
 T_MFMA_DENSE = 9                  # fp32 / fp64 record-addressed matrix-core tile
 T_SKINNY_DENSE = (10, 11)         # record-addressed skinny items (long axis M / N)
 T_SKINNY_M, T_SKINNY_N = 7, 8    # long axis M (at most 16 columns) / long axis N (at most 16 rows)
@@ -130,6 +134,9 @@ def replay(plan, con, a, b, c0, accumulate=False):
     a64, b64 = np.asarray(a, np.float64), np.asarray(b, np.float64)
     ws, ws_written = replay_packs(plan, con, a64, b64)
     splits = {}   # K-split tiles by counter: the partials of their slices
+    # a plan of wide tiles only: the task list is all wide tiles and no-ops
+    wide_only = plan.stats()["wide_only"] == 1
+    assert wide_only == (len(tasks) > 0 and bool(np.isin(tasks["cls"], (T_WIDE_N, T_WIDE_K, 6)).all()))
     tail = decode_tail(plan)
     # a tail bundle: entries group .. group + m0 - 1 of the tail table, one whole group per wave
     expanded = []
@@ -199,7 +206,7 @@ def replay(plan, con, a, b, c0, accumulate=False):
                 # K-slice of a split tile: its partial waits for the other slices
                 assert t["cls"] in T_DIRECT and 0 <= f["split"] < f["nsplit"]
                 assert 0 <= f["counter"] < info["n_counters"]
-                pt = split_tile_elems(int(t["cls"]), int(f["nlen"]))
+                pt = split_tile_elems(int(t["cls"]), int(f["nlen"]), wide_only)
                 assert 0 <= f["part"] and f["part"] + f["nsplit"] * pt <= info["partial_elems"]
                 slot = splits.setdefault(int(f["counter"]), {"n": int(f["nsplit"]), "part": int(f["part"]),
                                                              "cad": cad, "f": f, "p": {}, "pt": pt})
@@ -549,6 +556,18 @@ def test_replay_wide_single(shape, brow, split_k):
     got, written = replay(plan, con, a, b, c0)
     ref = oracle.contract(con, a, b, c0)
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_wide_only_plans():
+    """Plans whose every task is a wide tile say so (their launch runs
+    eight-wave workgroups); a wide plan with other tiles, and every plan on the
+    256 x 128 tile, does not."""
+    con, _, _ = _dense_single(3, 1024, 1024, 1024, True)
+    assert bst.Plan(con, tile_cols=256).stats()["wide_only"] == 1
+    assert bst.Plan(con, tile_cols=256, split_k=3).stats()["wide_only"] == 1
+    assert bst.Plan(con).stats()["wide_only"] == 0
+    prob = C.blockdiag_bf16(ld_align=8, align=8, values=False)
+    assert bst.Plan(prob.con, tile_cols=256).stats()["wide_only"] == 0   # tail bundles share the launch
 
 
 def test_tile_cols_option_checked():

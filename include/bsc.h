@@ -161,10 +161,10 @@ typedef struct {
     int32_t tile_rows;
     /* Columns of the bf16 direct-to-LDS tiles: 0 = automatic, 128 = the
      * 256 x 128 tile (two workgroups per CU), 256 = the wide tile (one
-     * workgroup per CU holding the whole LDS: 256 x 256 output, four waves of
-     * 128 x 128, five K chunks of copies in flight; groups of at most 128
-     * columns run it with 128 x 64 per wave).  tile_rows applies to the
-     * 256 x 128 tile only. */
+     * workgroup per CU holding the whole LDS: 256 x 256 output, four chunks of
+     * copies in flight; eight waves of 128 x 64 when every task of the plan is
+     * a wide tile, else four waves of 128 x 128, or 128 x 64 for groups of at
+     * most 128 columns).  tile_rows applies to the 256 x 128 tile only. */
     int32_t tile_cols;
 } bsc_options;
 

@@ -47,6 +47,16 @@ union TileSmem {
 
 extern __shared__ __align__(16) unsigned char bsc_dyn_smem[];
 
+// A 256 x 128 direct-to-LDS task: a tile of at most 128 rows runs as a
+// 128 x 128 tile of four 64 x 64 waves (every SIMD busy, four chunks of
+// copies in flight in the same 80 KB ring), a taller one on the 256 x 128 tile.
+template <typename TC, bool BN>
+__device__ __forceinline__ void direct_tile_bf16(const KArgs &ka, const DFast &fd_ref, FastSmemBf16 &sm) {
+    const DFast fd = fd_ref;   // one read of the record
+    if (fd.mlen <= HalfTile::TM) wide_tile_body<TC, BN, HalfTile>(ka, fd, sm.op);
+    else fast_tile_bf16<TC, BN>(ka, fd, sm);
+}
+
 template <typename TA, typename TC, typename ACC, int32_t FEAT>
 __device__ __forceinline__ void grouped_body(const KArgs &ka) {
     TileSmem<TA, ACC, FEAT> &sm = *reinterpret_cast<TileSmem<TA, ACC, FEAT> *>(bsc_dyn_smem);
@@ -77,13 +87,13 @@ __device__ __forceinline__ void grouped_body(const KArgs &ka) {
         }
         if constexpr ((FEAT & FEAT_FAST_N) != 0) {
             if (task.cls == T_MFMA_FAST_N) {
-                fast_tile_bf16<TC, true>(ka, ka.fast[ti], sm.f);
+                direct_tile_bf16<TC, true>(ka, ka.fast[ti], sm.f);
                 continue;
             }
         }
         if constexpr ((FEAT & FEAT_FAST_K) != 0) {
             if (task.cls == T_MFMA_FAST_K) {
-                fast_tile_bf16<TC, false>(ka, ka.fast[ti], sm.f);
+                direct_tile_bf16<TC, false>(ka, ka.fast[ti], sm.f);
                 continue;
             }
         }

@@ -57,19 +57,16 @@ static_assert(FB_BM == TILE_MFMA_DENSE_M && FB_BN == TILE_MFMA, "tile shape the 
 
 #define BSC_LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 
-// The LDS ring.  A full tile (more than 128 rows) uses three 24 KB stages
-// (A 256 x 32, then B 32 x 128); a tile of at most 128 rows needs half the A
-// rows, so the same 80 KB hold five 16 KB stages and four chunks are in flight
-// instead of two (what bounds a tile under load is the latency of its copies).
-template <bool HALF>
+// The LDS ring: three 24 KB stages (A 256 x 32, then B 32 x 128).  A task of
+// at most 128 rows runs in the same 80 KB as a 128 x 128 tile of four 64 x 64
+// waves with five 16 KB stages (HalfTile, kernels_mfma_bf16_wide.h).
 struct Ring {
-    static constexpr int STAGES = HALF ? 5 : 3;
-    static constexpr int A_ELEMS = (HALF ? FB_BM / 2 : FB_BM) * FB_BK;   // A part of a stage
+    static constexpr int STAGES = 3;
+    static constexpr int A_ELEMS = FB_BM * FB_BK;   // A part of a stage
     static constexpr int STAGE_ELEMS = A_ELEMS + FB_B_STAGE;
 };
 constexpr int FB_RING_ELEMS = 40960;   // 80 KB: two workgroups per CU
-static_assert(Ring<false>::STAGES * Ring<false>::STAGE_ELEMS <= FB_RING_ELEMS, "full ring");
-static_assert(Ring<true>::STAGES * Ring<true>::STAGE_ELEMS <= FB_RING_ELEMS, "half ring");
+static_assert(Ring::STAGES * Ring::STAGE_ELEMS <= FB_RING_ELEMS, "full ring");
 
 struct FastSmemBf16 {
     uint16_t op[FB_RING_ELEMS];
@@ -94,7 +91,7 @@ __device__ __forceinline__ void wait_vm_chunks(int32_t chunks_after) {
         default: wait_vm<3 * PER>(); break;
     }
 }
-static_assert(Ring<true>::STAGES - 2 <= 3 && 3 * (FB_NIA + FB_NIB) < 64, "wait table: at most three newer chunks");
+static_assert(Ring::STAGES - 2 <= 3 && 3 * (FB_NIA + FB_NIB) < 64, "wait table: at most three newer chunks");
 
 // Workgroup barrier for handing LDS stages between waves.  Each wave first
 // waits for its own LDS writes (lgkmcnt) — its direct-to-LDS copies were
@@ -570,8 +567,8 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
     // Wave roles.  Wave (wm, wn) computes rows wm*128 .. +128 and columns
     // wn*64 .. +64 of the tile and copies A rows wm*128 + wn*64 .. +64; a wave
     // whose rows (or columns) lie wholly past the tile edge computes nothing,
-    // and one whose A rows do copies no A (tiles of at most 128 rows, as the
-    // planner cuts for long-K groups, run on half the matrix cores).  Every
+    // and one whose A rows do copies no A (only tiles of more than 128 rows
+    // come here, so every wave computes unless the tile is narrow).  Every
     // wave copies its share of B.  The roles are wave-uniform, so each wave
     // runs one instantiation of the K loop below; all of them meet at the same
     // barriers.
@@ -587,16 +584,15 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
     wait_vm<0>();      // nothing else outstanding: the counted waits below see only this tile's copies
     __syncthreads();   // previous users of the LDS ring are done
 
-    auto kloop = [&](auto half_c, auto compute_c, auto acopy_c) {
-        constexpr bool HALF = decltype(half_c)::value;
+    auto kloop = [&](auto compute_c, auto acopy_c) {
         constexpr bool COMPUTE = decltype(compute_c)::value, ACOPY = decltype(acopy_c)::value;
-        using R = Ring<HALF>;
+        using R = Ring;
         constexpr int STAGES = R::STAGES;
         constexpr int PER = (ACOPY ? FB_NIA : 0) + FB_NIB;   // copies per chunk and wave
         uint16_t *const ops = sm.op;
         auto fill_partial = [&](int32_t stage) {
             uint16_t *at = ops + stage * R::STAGE_ELEMS;
-            dense_fill_kcontig<HALF ? FB_BM / 2 : FB_BM>(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, at);
+            dense_fill_kcontig<FB_BM>(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, at);
             if constexpr (BN) dense_fill_ncontig(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + R::A_ELEMS);
             else dense_fill_kcontig<FB_BN>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + R::A_ELEMS);
         };
@@ -700,17 +696,13 @@ __device__ __forceinline__ void fast_tile_bf16(const KArgs &ka, const DFast &fd_
     };
     using T = std::true_type;
     using F = std::false_type;
-    auto roles = [&](auto half_c) {
-        if (compute) {
-            if (acopy) kloop(half_c, T(), T());
-            else kloop(half_c, T(), F());
-        } else {
-            if (acopy) kloop(half_c, F(), T());
-            else kloop(half_c, F(), F());
-        }
-    };
-    if (mlen <= FB_BM / 2) roles(T());
-    else roles(F());
+    if (compute) {
+        if (acopy) kloop(T(), T());
+        else kloop(T(), F());
+    } else {
+        if (acopy) kloop(F(), T());
+        else kloop(F(), F());
+    }
 
     const int32_t lane = tid_x() & 63;
     // (the ring is idle from here on: the K-split flag may alias its first word)

@@ -39,30 +39,41 @@
 
 namespace bsc {
 
-constexpr int WB_BM = 256;   // tile rows
-constexpr int WB_FM = 4;     // row fragments (of 32) per wave: 128 rows
 constexpr int WB_RING_ELEMS = 81920;   // 160 KB: the CU's whole LDS
 
-// Geometry of the wide tile for a wave tile width WN (128 or 64 columns) and
-// NW waves (4, or 8 with 64-column waves: 256 columns); the copies of a chunk
+// Geometry of a direct-to-LDS tile computed by NW waves in a 2 x (NW / 2)
+// arrangement, each wave 32 FM rows by WN columns (FM row and WN / 32 column
+// fragments of 32 x 32), with a ring of RING bf16 elements.  The wide tile:
+// FM = 4 (256 rows), WN = 128 or 64, NW = 4 or 8, the CU's whole LDS.  The
+// 128 x 128 tile of four 64 x 64 waves: FM = 2, in the 80 KB ring of the
+// 256 x 128 tile's launch (kernels_mfma_bf16_fast.h).  The copies of a chunk
 // are shared out over the NW waves.
-template <int WN, int NW = 4>
+template <int WN, int NW = 4, int FM = 4, int RING = WB_RING_ELEMS>
 struct Wide {
-    static constexpr int NT = 64 * NW;
-    static constexpr int BN = (NW / 2) * WN;                  // tile columns
-    static constexpr int FN = WN / 32;                 // column fragments per wave (4 or 2)
-    static constexpr int A_ELEMS = WB_BM * FB_BK;      // A part of a stage
-    static constexpr int B_ELEMS = BN * FB_BK;         // B part of a stage
+    static constexpr int WC = WN;                       // columns per wave
+    static constexpr int NWV = NW;                      // waves
+    static constexpr int FR = FM;                       // row fragments per wave
+    static constexpr int TM = 2 * 32 * FM;              // tile rows
+    static constexpr int NT = 64 * NW;                  // threads
+    static constexpr int BN = (NW / 2) * WN;            // tile columns
+    static constexpr int FN = WN / 32;                  // column fragments per wave
+    static constexpr int A_ELEMS = TM * FB_BK;          // A part of a stage
+    static constexpr int B_ELEMS = BN * FB_BK;          // B part of a stage
     static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
-    static constexpr int STAGES = WB_RING_ELEMS / STAGE_ELEMS < 6 ? WB_RING_ELEMS / STAGE_ELEMS : 6;
-    static constexpr int NIA = A_ELEMS * 2 / 1024 / NW;   // 1 KB copies of A per wave and chunk (4)
-    static constexpr int NIB = B_ELEMS * 2 / 1024 / NW;   // of B (4 or 2)
-    static constexpr int SLOTS = BN * 2 / 16;            // 16-byte slots per N-contiguous B row (32 or 16)
-    static constexpr int ROWS_PER = 64 / SLOTS;          // B k-rows one copy instruction fills (2 or 4)
-    static_assert(STAGES * STAGE_ELEMS <= WB_RING_ELEMS, "ring fits the LDS");
+    static constexpr int STAGES = RING / STAGE_ELEMS < 6 ? RING / STAGE_ELEMS : 6;
+    static constexpr int NIA = A_ELEMS * 2 / 1024 / NW;   // 1 KB copies of A per wave and chunk
+    static constexpr int NIB = B_ELEMS * 2 / 1024 / NW;   // of B
+    static constexpr int SLOTS = BN * 2 / 16;            // 16-byte slots per N-contiguous B row
+    static constexpr int ROWS_PER = 64 / SLOTS;          // B k-rows one copy instruction fills
+    // the first MFMAs of a K-step before its reads of the next one go out
+    static constexpr int PRE = FM * (WN / 32) >= 8 ? 2 : 1;
+    static_assert(STAGES * STAGE_ELEMS <= RING && STAGES >= 3, "ring fits the LDS");
     static_assert(FN * 32 == WN && (WN == 128 || WN == 64), "wave tile width");
+    static_assert((FM == 4 || FM == 2) && NIA >= 1 && NIB >= 1, "tile shape");
 };
 static_assert(Wide<128>::STAGES == 5 && Wide<64>::STAGES == 6, "ring depths");
+using HalfTile = Wide<64, 4, 2, FB_RING_ELEMS>;   // 128 x 128, four 64 x 64 waves, 80 KB ring
+static_assert(HalfTile::STAGES == 5, "four chunks of copies in flight");
 
 struct WideSmemBf16 {
     uint16_t op[WB_RING_ELEMS];
@@ -87,10 +98,9 @@ static_assert(4 * (Wide<128>::NIA + Wide<128>::NIB) < 64 && 4 * (Wide<64>::NIA +
 // into BN-wide LDS rows: instruction j fills k rows ROWS_PER (NI w + j) ..;
 // lane l fills row l / SLOTS, 16-byte slot l % SLOTS, i.e. 64-byte position
 // (l % SLOTS) / 4, which holds n-granule position ^ (k & 3).
-template <int WN, int NI, int NW = 4>
+template <typename G, int NI>
 __device__ __forceinline__ FastOp<NI> wide_setup_ncontig(int64_t base, int64_t ks, int32_t nlen, int32_t K,
                                                          const uint16_t *P, int32_t w) {
-    using G = Wide<WN, NW>;
     FastOp<NI> f;
     const int32_t lane = tid_x() & 63;
     const int32_t s = lane % G::SLOTS;
@@ -107,10 +117,9 @@ __device__ __forceinline__ FastOp<NI> wide_setup_ncontig(int64_t base, int64_t k
 }
 
 // Masked fill of a partial chunk (k0 .. K-1 valid) of an N-contiguous B into BN-wide rows.
-template <int WN, int NW = 4>
+template <typename G>
 __device__ __forceinline__ void wide_fill_ncontig(int64_t base, int64_t ks, int32_t nlen, int32_t k0, int32_t K,
                                                   const uint16_t *P, uint16_t *lds) {
-    using G = Wide<WN, NW>;
     const int32_t tid = tid_x();
 #pragma unroll 1
     for (int q = 0; q < FB_BK * G::SLOTS / G::NT; ++q) {
@@ -138,13 +147,13 @@ struct WideOff {
     uint32_t b[4];   // K-contiguous B: by K-step (b[0], b[1]); N-contiguous B: by column fragment
 };
 
-template <int WN, bool BN, int NW = 4>
+template <typename G, bool BN>
 __device__ __forceinline__ WideOff wide_offsets() {
-    using G = Wide<WN, NW>;
+    constexpr int WN = G::WC;
     const int32_t lane = tid_x() & 63, w = tid_x() >> 6;
     const int32_t wm = w & 1, wn = w >> 1;
     WideOff o;
-    const int32_t ra = wm * (WB_BM / 2) + (lane & 31);
+    const int32_t ra = wm * (G::TM / 2) + (lane & 31);
     o.a[0] = 2 * (ra * FB_BK + 8 * fa_slot(ra, lane >> 5));
     o.a[1] = o.a[0] ^ 32;
     if constexpr (BN) {
@@ -176,21 +185,19 @@ __device__ __forceinline__ void lds_read_b128_at(int i, uint32_t ad, v4i32_t &r)
     }
 }
 
-template <int FN>
+template <typename G>
 struct WideFrags {
-    v4i32_t a[WB_FM];
-    v4i32_t b[FN];        // K-contiguous B
-    v4i16_t t[2 * FN];    // N-contiguous B: transposed halves
+    v4i32_t a[G::FR];
+    v4i32_t b[G::FN];        // K-contiguous B
+    v4i16_t t[2 * G::FN];    // N-contiguous B: transposed halves
 };
 
 // Fragment read r of a K-step (B reads first, then A).  va: the stage's A base
 // plus this wave's A offset for the K-step; vb: K-contiguous B: the stage's B
 // base plus the B offset of the K-step; N-contiguous B: the stage's B base,
 // to which each fragment adds its own lane offset o.b[f].
-template <int WN, bool BN, int KS, int NW = 4>
-__device__ __forceinline__ void wide_read_one(int r, uint32_t va, uint32_t vb, const WideOff &o,
-                                              WideFrags<WN / 32> &fr) {
-    using G = Wide<WN, NW>;
+template <typename G, bool BN, int KS>
+__device__ __forceinline__ void wide_read_one(int r, uint32_t va, uint32_t vb, const WideOff &o, WideFrags<G> &fr) {
     constexpr int FN = G::FN;
     constexpr int AR = 2 * 32 * FB_BK;               // bytes between row fragments
     if constexpr (BN) {
@@ -215,36 +222,36 @@ __device__ __forceinline__ void wide_read_one(int r, uint32_t va, uint32_t vb, c
     }
     const int ra = r - (BN ? 2 * FN : FN);
 #pragma unroll
-    for (int fi = 0; fi < WB_FM; ++fi)
+    for (int fi = 0; fi < G::FR; ++fi)
         if (fi == ra) lds_read_b128_at<AR>(fi, va, fr.a[fi]);
 }
 
-template <int WN, bool BN>
-constexpr int wide_reads() { return (BN ? 2 * (WN / 32) : WN / 32) + WB_FM; }
+template <typename G, bool BN>
+constexpr int wide_reads() { return (BN ? 2 * G::FN : G::FN) + G::FR; }
 
-template <int WN, bool BN, int KS, int NW = 4>
-__device__ __forceinline__ void wide_read_all(uint32_t va, uint32_t vb, const WideOff &o, WideFrags<WN / 32> &fr) {
+template <typename G, bool BN, int KS>
+__device__ __forceinline__ void wide_read_all(uint32_t va, uint32_t vb, const WideOff &o, WideFrags<G> &fr) {
 #pragma unroll
-    for (int r = 0; r < wide_reads<WN, BN>(); ++r) wide_read_one<WN, BN, KS, NW>(r, va, vb, o, fr);
+    for (int r = 0; r < wide_reads<G, BN>(); ++r) wide_read_one<G, BN, KS>(r, va, vb, o, fr);
 }
 
-template <int WN, bool BN>
-__device__ __forceinline__ void wide_wait(WideFrags<WN / 32> &fr) {
+template <typename G, bool BN>
+__device__ __forceinline__ void wide_wait(WideFrags<G> &fr) {
     // every fragment register is an output, so no use moves above the wait
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int f = 0; f < WB_FM; ++f) asm volatile("" : "+v"(fr.a[f]));
+    for (int f = 0; f < G::FR; ++f) asm volatile("" : "+v"(fr.a[f]));
     if constexpr (BN) {
 #pragma unroll
-        for (int f = 0; f < 2 * (WN / 32); ++f) asm volatile("" : "+v"(fr.t[f]));
+        for (int f = 0; f < 2 * G::FN; ++f) asm volatile("" : "+v"(fr.t[f]));
     } else {
 #pragma unroll
-        for (int f = 0; f < WN / 32; ++f) asm volatile("" : "+v"(fr.b[f]));
+        for (int f = 0; f < G::FN; ++f) asm volatile("" : "+v"(fr.b[f]));
     }
 }
 
-template <int FN, bool BN>
-__device__ __forceinline__ bf16x8_t wide_bfrag(const WideFrags<FN> &fr, int f) {
+template <typename G, bool BN>
+__device__ __forceinline__ bf16x8_t wide_bfrag(const WideFrags<G> &fr, int f) {
     if constexpr (BN) {
         const v4i16_t lo = fr.t[2 * f], hi = fr.t[2 * f + 1];
         short e8 __attribute__((ext_vector_type(8))) = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -257,19 +264,19 @@ __device__ __forceinline__ bf16x8_t wide_bfrag(const WideFrags<FN> &fr, int f) {
 // The MFMAs of one K-step (fragments `cur`, FM x FN of them) with the reads of
 // the next K-step's fragments (`nxt`, K-step KS at bases va, vb) issued between
 // them after the first PRE MFMAs; `mid` runs right before MFMA PRE.
-template <int WN, bool BN, int KS, int PRE, int NW, typename Mid>
-__device__ __forceinline__ void wide_mfma_interleaved(const WideFrags<WN / 32> &cur, WideFrags<WN / 32> &nxt,
+template <typename G, bool BN, int KS, int PRE, typename Mid>
+__device__ __forceinline__ void wide_mfma_interleaved(const WideFrags<G> &cur, WideFrags<G> &nxt,
                                                       uint32_t va, uint32_t vb, const WideOff &o,
-                                                      f32x16_t (&acc)[WB_FM][WN / 32], Mid &&mid) {
-    constexpr int FN = WN / 32;
-    constexpr int NM = WB_FM * FN;                 // MFMAs per K-step
-    constexpr int NR = wide_reads<WN, BN>();       // reads per K-step
+                                                      f32x16_t (&acc)[G::FR][G::FN], Mid &&mid) {
+    constexpr int FN = G::FN, FM = G::FR;
+    constexpr int NM = FM * FN;                    // MFMAs per K-step
+    constexpr int NR = wide_reads<G, BN>();        // reads per K-step
     static_assert(PRE + (NR + 1) / 2 <= NM, "every read issued within the K-step");
-    bf16x8_t fa[WB_FM], fb[FN];
+    bf16x8_t fa[FM], fb[FN];
 #pragma unroll
-    for (int f = 0; f < WB_FM; ++f) fa[f] = __builtin_bit_cast(bf16x8_t, cur.a[f]);
+    for (int f = 0; f < FM; ++f) fa[f] = __builtin_bit_cast(bf16x8_t, cur.a[f]);
 #pragma unroll
-    for (int f = 0; f < FN; ++f) fb[f] = wide_bfrag<FN, BN>(cur, f);
+    for (int f = 0; f < FN; ++f) fb[f] = wide_bfrag<G, BN>(cur, f);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < NM; ++k) {
@@ -287,13 +294,13 @@ __device__ __forceinline__ void wide_mfma_interleaved(const WideFrags<WN / 32> &
             const int slot = k - PRE;
 #pragma unroll
             for (int r = 0; r < NR; ++r)
-                if (r >= 2 * slot && r < 2 * slot + 2) wide_read_one<WN, BN, KS, NW>(r, va, vb, o, nxt);
+                if (r >= 2 * slot && r < 2 * slot + 2) wide_read_one<G, BN, KS>(r, va, vb, o, nxt);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
     // keep `cur` allocated until every read into `nxt` is issued
 #pragma unroll
-    for (int f = 0; f < WB_FM; ++f) asm volatile("" ::"v"(cur.a[f]));
+    for (int f = 0; f < FM; ++f) asm volatile("" ::"v"(cur.a[f]));
     if constexpr (BN) {
 #pragma unroll
         for (int f = 0; f < 2 * FN; ++f) asm volatile("" ::"v"(cur.t[f]));
@@ -304,16 +311,16 @@ __device__ __forceinline__ void wide_mfma_interleaved(const WideFrags<WN / 32> &
 }
 
 // MFMAs of one K-step without interleaved reads.
-template <int WN, bool BN>
-__device__ __forceinline__ void wide_mfma(const WideFrags<WN / 32> &fr, f32x16_t (&acc)[WB_FM][WN / 32]) {
-    constexpr int FN = WN / 32;
-    bf16x8_t fa[WB_FM], fb[FN];
+template <typename G, bool BN>
+__device__ __forceinline__ void wide_mfma(const WideFrags<G> &fr, f32x16_t (&acc)[G::FR][G::FN]) {
+    constexpr int FN = G::FN, FM = G::FR;
+    bf16x8_t fa[FM], fb[FN];
 #pragma unroll
-    for (int f = 0; f < WB_FM; ++f) fa[f] = __builtin_bit_cast(bf16x8_t, fr.a[f]);
+    for (int f = 0; f < FM; ++f) fa[f] = __builtin_bit_cast(bf16x8_t, fr.a[f]);
 #pragma unroll
-    for (int f = 0; f < FN; ++f) fb[f] = wide_bfrag<FN, BN>(fr, f);
+    for (int f = 0; f < FN; ++f) fb[f] = wide_bfrag<G, BN>(fr, f);
 #pragma unroll
-    for (int i = 0; i < WB_FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
@@ -322,12 +329,12 @@ __device__ __forceinline__ void wide_mfma(const WideFrags<WN / 32> &fr, f32x16_t
 // slice's partial tile lane-contiguously, count the slice in the tile's
 // counter, and let the last slice reload the accumulators as the partials'
 // sum in slice order.
-template <int WN, int NW>
-__device__ __forceinline__ bool wide_split_arrive(const KArgs &ka, const DFast &fd, f32x16_t (&acc)[WB_FM][WN / 32],
+template <typename G>
+__device__ __forceinline__ bool wide_split_arrive(const KArgs &ka, const DFast &fd, f32x16_t (&acc)[G::FR][G::FN],
                                                   int32_t w, int32_t lane, int32_t &last) {
-    constexpr int FN = WN / 32;
-    constexpr int SPLIT_BYTES = WB_BM * Wide<WN, NW>::BN * 4;   // one partial tile
-    constexpr int NQ = WB_FM * FN * 4;                // 16-byte groups per lane
+    constexpr int FN = G::FN;
+    constexpr int SPLIT_BYTES = G::TM * G::BN * 4;    // one partial tile
+    constexpr int NQ = G::FR * FN * 4;                // 16-byte groups per lane
     const uint64_t base = reinterpret_cast<uint64_t>(ka.P + fd.part);
     const uint64_t ubase = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(base >> 32))) << 32) |
                            static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(base)));
@@ -382,39 +389,39 @@ __device__ __forceinline__ bool wide_split_arrive(const KArgs &ka, const DFast &
     return true;
 }
 
-template <typename TC, bool BN, int WN, int NW>
-__device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd, WideSmemBf16 &sm) {
-    using G = Wide<WN, NW>;
-    constexpr int FN = G::FN;
+// ring_lds: the LDS ring (G::STAGES stages of G::STAGE_ELEMS elements)
+template <typename TC, bool BN, typename G>
+__device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd, uint16_t *ring_lds) {
+    constexpr int FN = G::FN, FM = G::FR, WN = G::WC, NW = G::NWV;
     const uint16_t *A = static_cast<const uint16_t *>((fd.flags & F_A_WS) ? ka.W : ka.A);
     const uint16_t *B = static_cast<const uint16_t *>((fd.flags & F_B_WS) ? ka.W : ka.B);
     const int32_t mlen = fd.mlen, nlen = fd.nlen, K = fd.K;
     const int32_t w = __builtin_amdgcn_readfirstlane(tid_x() >> 6);
 
-    f32x16_t acc[WB_FM][FN];
+    f32x16_t acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < WB_FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Wave (wm, wn) computes rows wm*128 .. +128 and columns wn*WN .. +WN and
-    // copies A rows 64 w .. +64; a wave whose rows (or columns) lie wholly past
+    // Wave (wm, wn) computes rows wm*TM/2 .. +TM/2 and columns wn*WN .. +WN and
+    // copies A rows TM/NW w .. +TM/NW; a wave whose rows (or columns) lie wholly past
     // the tile edge computes nothing, one whose A rows do copies no A.  Every
     // wave copies its share of B.  Roles are wave-uniform; all waves meet at
     // the same barriers.
     const int32_t wm = w & 1, wn = w >> 1;
-    const bool compute = wm * (WB_BM / 2) < mlen && wn * WN < nlen;
-    const bool acopy = (WB_BM / NW) * w < mlen;
+    const bool compute = wm * (G::TM / 2) < mlen && wn * WN < nlen;
+    const bool acopy = (G::TM / NW) * w < mlen;
     const FastOp<G::NIA> fa = dense_setup_kcontig<G::NIA>(fd.a_base, fd.a_rs, mlen, K, A, w);
     FastOp<G::NIB> fb;
-    if constexpr (BN) fb = wide_setup_ncontig<WN, G::NIB, NW>(fd.b_base, fd.b_ks, nlen, K, B, w);
+    if constexpr (BN) fb = wide_setup_ncontig<G, G::NIB>(fd.b_base, fd.b_ks, nlen, K, B, w);
     else fb = dense_setup_kcontig<G::NIB>(fd.b_base, fd.b_ns, nlen, K, B, w);
     const int64_t b_s = BN ? fd.b_ks : fd.b_ns;
     const int32_t nfull = K / FB_BK;
     const int32_t ntot = (K + FB_BK - 1) / FB_BK;
-    const WideOff fo = wide_offsets<WN, BN, NW>();
+    const WideOff fo = wide_offsets<G, BN>();
     wait_vm<0>();      // nothing else outstanding: the counted waits below see only this tile's copies
     __syncthreads();   // previous users of the LDS ring are done
 
@@ -422,11 +429,11 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
         constexpr bool COMPUTE = decltype(compute_c)::value, ACOPY = decltype(acopy_c)::value;
         constexpr int STAGES = G::STAGES;
         constexpr int PER = (ACOPY ? G::NIA : 0) + G::NIB;   // copies per chunk and wave
-        uint16_t *const ops = sm.op;
+        uint16_t *const ops = ring_lds;
         auto fill_partial = [&](int32_t stage) {
             uint16_t *at = ops + stage * G::STAGE_ELEMS;
-            dense_fill_kcontig<WB_BM, G::NT>(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, at);
-            if constexpr (BN) wide_fill_ncontig<WN, NW>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + G::A_ELEMS);
+            dense_fill_kcontig<G::TM, G::NT>(fd.a_base, fd.a_rs, mlen, nfull * FB_BK, K, A, at);
+            if constexpr (BN) wide_fill_ncontig<G>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + G::A_ELEMS);
             else dense_fill_kcontig<G::BN, G::NT>(fd.b_base, b_s, nlen, nfull * FB_BK, K, B, at + G::A_ELEMS);
         };
         auto issue = [&](int32_t c, int32_t stage) {
@@ -458,24 +465,24 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
         const uint32_t ring = lds_addr(ops);
         constexpr uint32_t STAGE_BYTES = G::STAGE_ELEMS * 2, B_OFF = G::A_ELEMS * 2;
         auto stage_addr = [&](int32_t c) { return ring + (c % STAGES) * STAGE_BYTES; };
-        WideFrags<FN> s0, s1;
+        WideFrags<G> s0, s1;
         // B base of a stage for K-step ks: N-contiguous B adds per-fragment offsets later
         auto bbase = [&](uint32_t stage, int ks) { return stage + B_OFF + (BN ? 0u : fo.b[ks]); };
-        auto reads0 = [&](uint32_t stage, WideFrags<FN> &fr) {
-            if constexpr (COMPUTE) wide_read_all<WN, BN, 0, NW>(stage + fo.a[0], bbase(stage, 0), fo, fr);
+        auto reads0 = [&](uint32_t stage, WideFrags<G> &fr) {
+            if constexpr (COMPUTE) wide_read_all<G, BN, 0>(stage + fo.a[0], bbase(stage, 0), fo, fr);
         };
-        auto reads1 = [&](uint32_t stage, WideFrags<FN> &fr) {
-            if constexpr (COMPUTE) wide_read_all<WN, BN, 1, NW>(stage + fo.a[1], bbase(stage, 1), fo, fr);
+        auto reads1 = [&](uint32_t stage, WideFrags<G> &fr) {
+            if constexpr (COMPUTE) wide_read_all<G, BN, 1>(stage + fo.a[1], bbase(stage, 1), fo, fr);
         };
-        auto mfmas = [&](const WideFrags<FN> &fr) {
+        auto mfmas = [&](const WideFrags<G> &fr) {
             if constexpr (COMPUTE) {
                 __builtin_amdgcn_sched_barrier(0);
-                wide_mfma<WN, BN>(fr, acc);
+                wide_mfma<G, BN>(fr, acc);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        auto settle = [&](WideFrags<FN> &fr) {
-            if constexpr (COMPUTE) wide_wait<WN, BN>(fr);
+        auto settle = [&](WideFrags<G> &fr) {
+            if constexpr (COMPUTE) wide_wait<G, BN>(fr);
         };
         advance(0);
         reads0(stage_addr(0), s0);
@@ -487,9 +494,9 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
             const int32_t sn = st == STAGES - 1 ? 0 : st + 1;
             if constexpr (COMPUTE) {
                 const uint32_t here = ring + st * STAGE_BYTES, next = ring + sn * STAGE_BYTES;
-                wide_mfma_interleaved<WN, BN, 1, 2, NW>(s0, s1, here + fo.a[1], bbase(here, 1), fo, acc, [] {});
+                wide_mfma_interleaved<G, BN, 1, G::PRE>(s0, s1, here + fo.a[1], bbase(here, 1), fo, acc, [] {});
                 settle(s1);
-                wide_mfma_interleaved<WN, BN, 0, 2, NW>(s1, s0, next + fo.a[0], bbase(next, 0), fo, acc, [&] {
+                wide_mfma_interleaved<G, BN, 0, G::PRE>(s1, s0, next + fo.a[0], bbase(next, 0), fo, acc, [&] {
                     wait_vm<PER * (STAGES - 2)>();
                     lds_barrier();
                     issue(c + STAGES, st);
@@ -527,7 +534,7 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
     }
 
     const int32_t lane = tid_x() & 63;
-    if (fd.nsplit > 1 && !wide_split_arrive<WN, NW>(ka, fd, acc, w, lane, *reinterpret_cast<int32_t *>(sm.op))) return;
+    if (fd.nsplit > 1 && !wide_split_arrive<G>(ka, fd, acc, w, lane, *reinterpret_cast<int32_t *>(ring_lds))) return;
 
     // epilogue: straight from the accumulators, 32 consecutive columns per row
     TC *Cp = static_cast<TC *>(ka.C);
@@ -538,10 +545,10 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
         if (j >= nlen) continue;
         TC *col = Cp + fd.c_base + static_cast<int64_t>(j) * fd.c_cs;
 #pragma unroll
-        for (int fi = 0; fi < WB_FM; ++fi)
+        for (int fi = 0; fi < FM; ++fi)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int32_t i = wm * (WB_BM / 2) + fi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int32_t i = wm * (G::TM / 2) + fi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 if (i >= mlen) continue;
                 TC *dst = col + static_cast<int64_t>(i) * fd.c_rs;
                 float v = acc[fi][fj][r];
@@ -556,8 +563,8 @@ __device__ __forceinline__ void wide_tile_body(const KArgs &ka, const DFast &fd,
 template <typename TC, bool BN>
 __device__ __forceinline__ void wide_tile_bf16(const KArgs &ka, const DFast &fd_ref, WideSmemBf16 &sm) {
     const DFast fd = fd_ref;   // one read of the record
-    if (fd.nlen > 128) wide_tile_body<TC, BN, 128, 4>(ka, fd, sm);
-    else wide_tile_body<TC, BN, 64, 4>(ka, fd, sm);
+    if (fd.nlen > 128) wide_tile_body<TC, BN, Wide<128>>(ka, fd, sm.op);
+    else wide_tile_body<TC, BN, Wide<64>>(ka, fd, sm.op);
 }
 
 // The same tile on eight waves (a 512-thread workgroup, two waves per SIMD):
@@ -568,7 +575,7 @@ __device__ __forceinline__ void wide_tile_bf16(const KArgs &ka, const DFast &fd_
 template <typename TC, bool BN>
 __device__ __forceinline__ void wide8_tile_bf16(const KArgs &ka, const DFast &fd_ref, WideSmemBf16 &sm) {
     const DFast fd = fd_ref;
-    wide_tile_body<TC, BN, 64, 8>(ka, fd, sm);
+    wide_tile_body<TC, BN, Wide<64, 8>>(ka, fd, sm.op);
 }
 
 }  // namespace bsc

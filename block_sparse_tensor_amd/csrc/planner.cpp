@@ -988,10 +988,11 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         // 128-row tiles: when the plan's 256 x 128 tiles would leave CUs with at
         // most one tile each, a group whose K chain is long (at least 16
         // chunks) and above one slot's share is cut into 128-row tiles: twice
-        // the tiles (two per CU), each with four chunks of copies in flight.
-        // Measured on MI355X: eight 1024^3 blocks 39 -> 33.6 us; with more
-        // tiles than CUs the extra tiles only add load (bench workload
-        // 34 -> 46 us), so they stay 256 rows.
+        // the tiles (two per CU), each computed by four 64 x 64 waves with four
+        // chunks of copies in flight.  Measured on MI355X: one 1024^3 block
+        // 23.7 -> 16.7 us, eight 32.6 -> 29.2 us; with more tiles than CUs the
+        // extra tiles only add load (bench workload 31.5 -> 40.3 us), so they
+        // stay 256 rows.
         auto half_rows = [&](const DGroup &g) {
             if (p.opt.tile_rows != 0) return p.opt.tile_rows == TILE_MFMA_DENSE_M / 2;
             const int64_t chunks = (g.K + SPLIT_CHUNK - 1) / SPLIT_CHUNK;

@@ -37,13 +37,14 @@ T_WIDE_N, T_WIDE_K = 12, 13       # wide tile (one workgroup per CU): 256 x 256,
 T_DIRECT = (T_DENSE_N, T_DENSE_K, T_WIDE_N, T_WIDE_K)
 
 
-def split_tile_elems(cls, nlen, wide_only=False):
+def split_tile_elems(cls, mlen, nlen, wide_only=False):
     """fp32 elements the kernel strides per K-slice partial tile: the 256 x 128
-    tile's, a wide tile's 256 x 256 (four waves of 128 x 64 at <= 128 columns:
+    tile's (128 x 128 for a tile of at most 128 rows, which runs as four 64 x 64
+    waves), a wide tile's 256 x 256 (four waves of 128 x 64 at <= 128 columns:
     256 x 128), and always 256 x 256 on eight waves (a plan of wide tiles only)."""
-    if cls in (T_WIDE_N, T_WIDE_K) and (nlen > 128 or wide_only):
-        return 256 * 256
-    return SPLIT_TILE
+    if cls in (T_WIDE_N, T_WIDE_K):
+        return 256 * 256 if (nlen > 128 or wide_only) else SPLIT_TILE
+    return 128 * 128 if mlen <= 128 else SPLIT_TILE
 T_MFMA_DENSE = 9                  # fp32 / fp64 record-addressed matrix-core tile
 T_SKINNY_DENSE = (10, 11)         # record-addressed skinny items (long axis M / N)
 T_SKINNY_M, T_SKINNY_N = 7, 8    # long axis M (at most 16 columns) / long axis N (at most 16 rows)
@@ -206,7 +207,7 @@ def replay(plan, con, a, b, c0, accumulate=False):
                 # K-slice of a split tile: its partial waits for the other slices
                 assert t["cls"] in T_DIRECT and 0 <= f["split"] < f["nsplit"]
                 assert 0 <= f["counter"] < info["n_counters"]
-                pt = split_tile_elems(int(t["cls"]), int(f["nlen"]), wide_only)
+                pt = split_tile_elems(int(t["cls"]), int(f["mlen"]), int(f["nlen"]), wide_only)
                 assert 0 <= f["part"] and f["part"] + f["nsplit"] * pt <= info["partial_elems"]
                 slot = splits.setdefault(int(f["counter"]), {"n": int(f["nsplit"]), "part": int(f["part"]),
                                                              "cad": cad, "f": f, "p": {}, "pt": pt})

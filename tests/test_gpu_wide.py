@@ -154,3 +154,26 @@ def test_wide_blockdiag_full_size_float():
     check_canary(got, mask)
     ref = oracle.contract(con, prob.a, prob.b, np.zeros(con.C.buffer_elems), check=False)
     check_float(con, got, ref, prob.a, prob.b, 2e-2, label="wide blockdiag")
+
+
+def test_wide_only_unaligned_bases_fall_back():
+    """A plan of wide tiles only whose operand bases are off a 16-byte
+    boundary runs on the general matrix-core tile (256-thread launch), K-split
+    tiles included: integer values bit for bit."""
+    con, a, b = _single(300, 700, 200, True, seed=41, ints=True)
+    plan = bst.Plan(con, tile_cols=256, split_k=3).bind()
+    s = plan.stats()
+    assert s["wide_only"] == 1 and s["split_tiles"] > 0
+    t = torch()
+    A = to_dev(np.concatenate([[0.0], a]), "bf16")[1:]
+    B = to_dev(np.concatenate([[0.0], b]), "bf16")[1:]
+    assert A.data_ptr() % 16 != 0 and B.data_ptr() % 16 != 0
+    addr, mask = c_addresses(con)
+    Cd = t.tensor(canary(con, "bf16"), dtype=t.float32, device="cuda")
+    print("[wide] wide-only plan, unaligned operand bases", flush=True)
+    plan.contract(A, B, Cd)
+    t.cuda.synchronize()
+    got = Cd.cpu().numpy()
+    check_canary(got, mask)
+    ref = oracle.contract(con, a, b, np.zeros(con.C.buffer_elems), check=False)
+    assert np.array_equal(got[addr], ref[addr].astype(np.float32))

@@ -156,8 +156,8 @@ typedef struct {
      * independent work to fill the machine): 0 = automatic (when the plan has
      * at most one 256 x 128 tile per CU, 128 for a group whose K chain is at
      * least 16 x 32 and above 1.5x one slot's share of the plan's work; 256
-     * otherwise); 128 or 256 to force.  A tile of at most 128 rows keeps four
-     * K chunks in flight instead of two. */
+     * otherwise); 128 or 256 to force.  A tile of at most 128 rows runs as
+     * four 64 x 64 waves with four K chunks in flight instead of two. */
     int32_t tile_rows;
     /* Columns of the bf16 direct-to-LDS tiles: 0 = automatic, 128 = the
      * 256 x 128 tile (two workgroups per CU), 256 = the wide tile (one

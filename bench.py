@@ -17,6 +17,7 @@ Alongside the engine (grouped launches) the same run times:
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -48,14 +49,23 @@ NOT_GROUPED = ("fused.cpp", "fused.hip", "fused_internal.h", "kernels_fused.h", 
                "runtime_host_stub.cpp")
 
 
+def _code_only(text):
+    """C++ source without its comments and blank lines: what the counters
+    depend on is the compiled code, so a comment edit keeps a record valid."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_source_hash():
-    """Hash of the sources that make up the grouped launch: its kernels and
-    launch code and the host planner that writes its work list."""
+    """Hash of the code that makes up the grouped launch: its kernels and
+    launch code and the host planner that writes its work list (comments
+    excluded)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_tensor_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")) and f not in NOT_GROUPED:
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(_code_only(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

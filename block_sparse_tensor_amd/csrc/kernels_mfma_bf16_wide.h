@@ -1,6 +1,8 @@
 // Wide dense matrix-core tile for bf16 inputs / fp32 accumulation: one
 // workgroup per CU.  Two forms: four waves (below), and eight waves of
-// 128 x 64 (wide8_tile_bf16, a launch of wide tiles only).
+// 128 x 64 (wide8_tile_bf16, a launch of wide tiles only).  The same loop,
+// with two row fragments per wave, also computes the 256 x 128 tile's tasks of
+// at most 128 rows as 128 x 128 tiles of four 64 x 64 waves (HalfTile).
 //
 // Same record-addressed groups as the 256 x 128 direct-to-LDS tile
 // (kernels_mfma_bf16_fast.h: one run of single strided views, 16-byte aligned

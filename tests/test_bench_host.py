@@ -38,3 +38,10 @@ def test_traffic_record_matches_sources():
     b = bench.measured_traffic("blockdiag_bf16", 8, 0)
     assert b is not None, "counter record is from other sources: retake the profiles"
     assert 65_000_000 <= b <= 200_000_000
+
+
+def test_record_hash_ignores_comments():
+    a = "int a; // one\n// two\n/* three\nfour */ int b;\n"
+    b = "int a; // changed\n\n/* x */ int b;\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only("int a = 1;") != bench._code_only("int a = 2;")

@@ -47,7 +47,9 @@ __global__ __launch_bounds__(256) void pack_gather(PArgs pa) {
         const DPack d = pa.packs[task.group];
         const T *S = static_cast<const T *>(d.src == 0 ? pa.A : pa.B);
         int32_t tr = 0, tc = 0;
-        pack_tile(d.cols, tr, tc);
+        const int32_t mode = pack_mode(d);
+        constexpr int32_t ESZ = static_cast<int32_t>(sizeof(T));
+        pack_tile(d.rows, d.cols, mode, pack_big(ESZ, mode), tr, tc);
         const int32_t x0 = task.m0, y0 = task.n0;
         const int32_t rows = min(tr, d.rows - x0), cols = min(tc, d.cols - y0);
         const int32_t n = rows * cols;
@@ -55,6 +57,55 @@ __global__ __launch_bounds__(256) void pack_gather(PArgs pa) {
         const bool s_k = d.ib == 1 && (d.sb0 == 1 || d.cols == 1);
         const bool s_f = d.ia == 1 && (d.sa0 == 1 || d.rows == 1);
         const bool d_k = d.dmode == 0;
+        if constexpr (ESZ == 2) {
+            if (pack_big(ESZ, mode)) {
+                // a large bf16 piece: straight along the unit axis, PACK_BATCH
+                // 16-byte vectors per lane loaded before any is stored, a
+                // line's last partial vector element by element
+                constexpr int32_t V = 8;
+                constexpr int32_t PACK_BATCH = 4;
+                const int32_t len = d_k ? cols : rows;     // extent along the unit axis
+                const int32_t nv = (len + V - 1) / V;      // vectors per line
+                const int32_t units = (d_k ? rows : cols) * nv;
+                for (int32_t e0 = tid; e0 < units; e0 += 256 * PACK_BATCH) {
+                    const T *sp[PACK_BATCH];
+                    T *dp[PACK_BATCH];
+                    int32_t left[PACK_BATCH];   // elements of the vector inside the line (0: past the piece)
+                    uint4 v[PACK_BATCH];
+#pragma unroll
+                    for (int32_t b = 0; b < PACK_BATCH; ++b) {
+                        const int32_t e = e0 + 256 * b;
+                        left[b] = 0;
+                        sp[b] = S;
+                        dp[b] = W;
+                        if (e < units) {
+                            const int32_t line = e / nv, u = (e - line * nv) * V;
+                            const int32_t x = d_k ? line : u, y = d_k ? u : line;
+                            sp[b] = S + pack_src(d, x0 + x, y0 + y);
+                            dp[b] = W + pack_dst(d, x0 + x, y0 + y);
+                            left[b] = min(V, len - u);
+                        }
+                        if (left[b] == V) {
+                            // (through a scalar temporary: a copy into the array
+                            // element kept the whole array in private memory)
+                            uint4 t;
+                            __builtin_memcpy(&t, sp[b], sizeof(t));
+                            v[b] = t;
+                        }
+                    }
+#pragma unroll
+                    for (int32_t b = 0; b < PACK_BATCH; ++b) {
+                        if (left[b] == V) {
+                            const uint4 t = v[b];
+                            __builtin_memcpy(dp[b], &t, sizeof(t));
+                        } else {
+                            for (int32_t j = 0; j < left[b]; ++j) dp[b][j] = sp[b][j];
+                        }
+                    }
+                }
+                continue;
+            }
+        }
         if ((d_k && s_k) || (!d_k && s_f)) {
             // same unit axis on both sides: straight copy along it, 16 bytes
             // per lane (any element address: the code object runs in

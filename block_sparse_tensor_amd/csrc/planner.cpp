@@ -644,7 +644,8 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
                     const int32_t gi = (int32_t)p.packs.size();
                     p.packs.push_back(d);
                     int32_t tr = 0, tc = 0;
-                    pack_tile(d.cols, tr, tc);
+                    const int32_t mode = pack_mode(d);
+                    pack_tile(d.rows, d.cols, mode, pack_big(p.dtype == BSC_BF16_F32 ? 2 : 4, mode), tr, tc);
                     for (int32_t x0 = 0; x0 < d.rows; x0 += tr)
                         for (int32_t y0 = 0; y0 < d.cols; y0 += tc) p.pack_tasks.push_back({0, gi, x0, y0});
                 }

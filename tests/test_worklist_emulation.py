@@ -84,6 +84,31 @@ def decode_packs(plan):
     return info, tab(DPACK, info["n_packs"], info["off_packs"]), tab(DTASK, info["n_pack_tasks"], info["off_pack_tasks"])
 
 
+def pack_piece(d, bf16):
+    """The kernel's piece shape (tr rows by tc columns) for a gather: up to
+    4096 elements of at most 64 columns; a straight bf16 gather (both sides
+    unit-stride along the same axis) takes up to 16384 elements with lines of
+    up to 1024 along that axis."""
+    s_k = d["ib"] == 1 and (d["sb0"] == 1 or d["cols"] == 1)
+    s_f = d["ia"] == 1 and (d["sa0"] == 1 or d["rows"] == 1)
+    mode = (1 if s_k else 0) if d["dmode"] == 0 else (2 if s_f else 0)
+    tc = 1
+    if bf16 and mode == 1:
+        while tc < d["cols"] and tc < 1024:
+            tc *= 2
+        return 16384 // tc, tc
+    if bf16 and mode == 2:
+        lr = 1
+        while lr < d["rows"] and lr < 1024:
+            lr *= 2
+        while tc < d["cols"] and tc * lr < 16384:
+            tc *= 2
+        return min(16384 // tc, 4096), tc
+    while tc < d["cols"] and tc < 64:
+        tc *= 2
+    return min(4096 // tc, 1024), tc
+
+
 def replay_packs(plan, con, a64, b64):
     """The gather launch: every pack task copies its 64 x 64 piece of a gather
     from A or B into the workspace.  Every workspace element is written at most
@@ -91,12 +116,10 @@ def replay_packs(plan, con, a64, b64):
     info, packs, ptasks = decode_packs(plan)
     ws = np.full(info["workspace_elems"], np.nan)
     hit = np.zeros(info["workspace_elems"], np.int64)
+    bf16 = plan.stats()["dtype"] == 2
     for t in ptasks:
         d = packs[t["group"]]
-        tc = 1
-        while tc < d["cols"] and tc < 64:
-            tc *= 2
-        tr = min(4096 // tc, 1024)                      # the kernel's piece shape
+        tr, tc = pack_piece(d, bf16)
         assert t["m0"] % tr == 0 and t["n0"] % tc == 0
         x = np.arange(t["m0"], min(t["m0"] + tr, d["rows"]))
         y = np.arange(t["n0"], min(t["n0"] + tc, d["cols"]))

@@ -197,6 +197,9 @@ constexpr void pack_tile(int32_t rows, int32_t cols, int32_t mode, bool big, int
 // Output tiles in flight at once on MI355X (256 CUs x two resident 256-thread
 // workgroups); the planner's cost model divides per-tile costs by it.
 constexpr double CONCURRENT_TILES = 512.0;
+// Wide tiles: a group whose K chain exceeds this many times one CU's share of
+// the launch's chunks is cut into 128-row wide tiles.
+constexpr double WIDE_HALF_SHARE = 2.0;
 
 struct DTask {
     int32_t cls;
@@ -327,7 +330,7 @@ struct Plan {
     int32_t cu_count = 0;
     int32_t grid = 0;
     int32_t features = 0;             // FEAT_* bits over all tasks
-    bool only_wide = false;           // every task is a wide tile (or a no-op)
+    bool only_wide = false;           // every task is a wide tile, a tail bundle or a no-op
 
     bsc_stats stats{};
 };

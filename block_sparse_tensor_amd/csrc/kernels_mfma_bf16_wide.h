@@ -574,10 +574,13 @@ __device__ __forceinline__ void wide_tile_bf16(const KArgs &ka, const DFast &fd_
 // MFMAs on every SIMD, which four waves of 128 x 128 cannot do.  A tile of at
 // most 128 columns runs the same loop; the waves whose columns lie past its
 // edge copy their share of B (clamped to a valid column) and compute nothing.
+// A tile of at most 128 rows (the planner's cut of long-K groups) runs as
+// 128 x 256 with 2 x 4 waves of 64 x 64: half the K chain's work per chunk.
 template <typename TC, bool BN>
 __device__ __forceinline__ void wide8_tile_bf16(const KArgs &ka, const DFast &fd_ref, WideSmemBf16 &sm) {
     const DFast fd = fd_ref;
-    wide_tile_body<TC, BN, Wide<64, 8>>(ka, fd, sm.op);
+    if (fd.mlen <= 128) wide_tile_body<TC, BN, Wide<64, 8, 2>>(ka, fd, sm.op);
+    else wide_tile_body<TC, BN, Wide<64, 8>>(ka, fd, sm.op);
 }
 
 }  // namespace bsc

@@ -1000,6 +1000,14 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             return fast_share > 0 && fast_tiles <= BSC_XCDS * BSC_CUS_PER_XCD && chunks >= 16 &&
                    (double)chunks > 1.5 * fast_share;
         };
+        // Wide tiles of at most 128 rows (128 x 256 on eight 64 x 64 waves):
+        // the groups whose K chain is far above one CU's share of the launch
+        // (the chains that would end last), or every group with tile_rows = 128.
+        auto wide_half_rows = [&](const DGroup &g) {
+            if (p.opt.tile_rows != 0) return p.opt.tile_rows == TILE_MFMA_DENSE_M / 2;
+            const int64_t chunks = (g.K + SPLIT_CHUNK - 1) / SPLIT_CHUNK;
+            return fast_share > 0 && chunks >= 16 && (double)chunks > WIDE_HALF_SHARE * fast_share;
+        };
         // slices of a tile with K contracted indices (1: no split)
         auto slices_of = [&](int32_t K) -> int32_t {
             if (split_target <= 0) return 1;
@@ -1039,6 +1047,7 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
             int32_t TM = 0, TN = 0;
             tile_extents(p.dtype, cls, g.M, g.N, TM, TN);
             if ((cls == T_MFMA_FAST_N || cls == T_MFMA_FAST_K) && half_rows(g)) TM = TILE_MFMA_DENSE_M / 2;
+            if (is_wide(cls) && wide_half_rows(g)) TM = TILE_WIDE / 2;
             if ((cls == T_SKINNY_M || cls == T_SKINNY_N) && skinny_records(g, gi, cls == T_SKINNY_M, out, cost)) return;
             for (int32_t m0 = 0; m0 < g.M; m0 += TM)
                 for (int32_t n0 = 0; n0 < g.N; n0 += TN) {
@@ -1278,10 +1287,15 @@ bsc_status build_plan(Plan &p, const bsc_index *m, const bsc_index *k, const bsc
         s.items = 0;
         for (auto &t : p.tasks) s.items += t.cls != T_NOP;
         p.features = 0;
-        p.only_wide = !p.tasks.empty();
+        p.only_wide = false;
+        bool other = false;
+        for (auto &t : p.tasks) {
+            if (is_wide(t.cls)) p.only_wide = true;
+            else if (t.cls != T_TAIL && t.cls != T_NOP) other = true;
+        }
+        if (other) p.only_wide = false;
         for (auto &t : p.tasks) {
             if (t.cls == T_NOP) continue;
-            if (!is_wide(t.cls)) p.only_wide = false;
             const int32_t slot = (t.cls == T_MFMA_FAST_K || is_wide(t.cls)) ? T_MFMA_FAST_N
                                  : (t.cls == T_SKINNY_M || t.cls == T_SKINNY_N || t.cls == T_SKINNY_DENSE_M ||
                                     t.cls == T_SKINNY_DENSE_N) ? 5

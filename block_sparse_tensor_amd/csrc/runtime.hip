@@ -25,7 +25,7 @@ static bsc_status hip_fail(hipError_t e, const char *what) {
 static KernelRef pick_bf16(int32_t feat, bool vec, bool only_wide) {
     constexpr int32_t DIRECT = FEAT_FAST_N | FEAT_FAST_K | FEAT_WIDE;
     if (!vec && (feat & DIRECT)) feat = (feat & ~DIRECT) | FEAT_MFMA;
-    if (feat == FEAT_WIDE && only_wide) return grouped_kernel_bf16_wide8();
+    if (feat == FEAT_WIDE && only_wide) return grouped_kernel_bf16_wide8();   // (tail bundles hold no FEAT bit)
     if (feat & FEAT_WIDE) return grouped_kernel_bf16_wide(feat);
     return feat < 4 ? grouped_kernel_bf16_lo(feat) : grouped_kernel_bf16_hi(feat);
 }

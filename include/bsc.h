@@ -162,9 +162,11 @@ typedef struct {
     /* Columns of the bf16 direct-to-LDS tiles: 0 = automatic, 128 = the
      * 256 x 128 tile (two workgroups per CU), 256 = the wide tile (one
      * workgroup per CU holding the whole LDS: 256 x 256 output, four chunks of
-     * copies in flight; eight waves of 128 x 64 when every task of the plan is
-     * a wide tile, else four waves of 128 x 128, or 128 x 64 for groups of at
-     * most 128 columns).  tile_rows applies to the 256 x 128 tile only. */
+     * copies in flight; eight waves of 128 x 64 when the plan's tasks are wide
+     * tiles and tail bundles only, else four waves of 128 x 128, or 128 x 64
+     * for groups of at most 128 columns).  tile_rows = 128, or a K chain far
+     * above one CU's share of the launch, cuts wide tiles to 128 rows
+     * (128 x 256 on eight 64 x 64 waves). */
     int32_t tile_cols;
 } bsc_options;
 
@@ -199,9 +201,9 @@ typedef struct {
     /* bf16: time saved by gathering misaligned single-view operands into
      * 16-byte rows, which moves their groups onto the direct-to-LDS tile */
     double pack_gain_align_us;
-    /* 1 when every task is a wide tile (tile_cols = 256): with both operand
-     * bases 16-byte aligned the launch then runs eight-wave workgroups of
-     * 512 threads instead of four-wave ones */
+    /* 1 when the tasks are wide tiles (tile_cols = 256), tail bundles and
+     * nothing else: with both operand bases 16-byte aligned the launch then
+     * runs eight-wave workgroups of 512 threads instead of four-wave ones */
     int64_t wide_only;
 } bsc_stats;
 

@@ -1,10 +1,13 @@
 """GPU parity of the wide bf16 tile (one workgroup per CU: 256 x 256 output).
-A plan of wide tiles only runs eight waves of 128 x 64 per workgroup; a plan
-that also holds other tiles runs four waves of 128 x 128 (128 x 64 for tiles
-of at most 128 columns).  Integer-valued inputs compare bit for bit with the
-oracle (every summation order is exact), both B orientations, ragged edges,
-partial last K chunks, K-slices, accumulation, several tiles per workgroup,
-and the bench workload's structure at full size (four-wave form)."""
+A plan of wide tiles and tail bundles only runs eight waves of 128 x 64 per
+workgroup (128 x 256 tiles of 64 x 64 waves for tiles of at most 128 rows,
+the tail bundles on waves 0-3); a plan that also holds other tiles runs four
+waves of 128 x 128 (128 x 64 for tiles of at most 128 columns).
+Integer-valued inputs compare bit for bit with the oracle (every summation
+order is exact), both B orientations, ragged edges, partial last K chunks,
+K-slices, accumulation, several tiles per workgroup, unaligned operand bases,
+and the bench workload's structure at full size (eight-wave form, its 1024^3
+sector in 128-row tiles, tail bundles in the same launch)."""
 import numpy as np
 import pytest
 
@@ -137,6 +140,7 @@ def test_wide_blockdiag_full_size_int_bit_exact(split_k):
     print(f"[wide] blockdiag_bf16 int split_k={split_k} items={s['items']} split_tiles={s['split_tiles']}",
           flush=True)
     assert s["launches_per_contract"] == 1 and s["items_by_class"]["mfma_fast"] > 0
+    assert s["wide_only"] == 1 and s["items_by_class"]["tail"] > 0
     addr, mask = c_addresses(con)
     got = run_engine(plan, prob.a, prob.b, canary(con, "bf16"), "bf16")
     check_canary(got, mask)

@@ -41,9 +41,12 @@ def split_tile_elems(cls, mlen, nlen, wide_only=False):
     """fp32 elements the kernel strides per K-slice partial tile: the 256 x 128
     tile's (128 x 128 for a tile of at most 128 rows, which runs as four 64 x 64
     waves), a wide tile's 256 x 256 (four waves of 128 x 64 at <= 128 columns:
-    256 x 128), and always 256 x 256 on eight waves (a plan of wide tiles only)."""
+    256 x 128), and on eight waves (a plan of wide tiles and tail bundles only)
+    256 x 256, or 128 x 256 for a tile of at most 128 rows."""
     if cls in (T_WIDE_N, T_WIDE_K):
-        return 256 * 256 if (nlen > 128 or wide_only) else SPLIT_TILE
+        if wide_only:
+            return (128 if mlen <= 128 else 256) * 256
+        return 256 * 256 if nlen > 128 else SPLIT_TILE
     return 128 * 128 if mlen <= 128 else SPLIT_TILE
 T_MFMA_DENSE = 9                  # fp32 / fp64 record-addressed matrix-core tile
 T_SKINNY_DENSE = (10, 11)         # record-addressed skinny items (long axis M / N)
@@ -158,9 +161,10 @@ def replay(plan, con, a, b, c0, accumulate=False):
     a64, b64 = np.asarray(a, np.float64), np.asarray(b, np.float64)
     ws, ws_written = replay_packs(plan, con, a64, b64)
     splits = {}   # K-split tiles by counter: the partials of their slices
-    # a plan of wide tiles only: the task list is all wide tiles and no-ops
+    # a plan of wide tiles, tail bundles and no-ops (at least one wide tile)
     wide_only = plan.stats()["wide_only"] == 1
-    assert wide_only == (len(tasks) > 0 and bool(np.isin(tasks["cls"], (T_WIDE_N, T_WIDE_K, 6)).all()))
+    assert wide_only == (bool(np.isin(tasks["cls"], (T_WIDE_N, T_WIDE_K)).any()) and
+                         bool(np.isin(tasks["cls"], (T_WIDE_N, T_WIDE_K, T_TAIL, 6)).all()))
     tail = decode_tail(plan)
     # a tail bundle: entries group .. group + m0 - 1 of the tail table, one whole group per wave
     expanded = []
@@ -583,7 +587,7 @@ def test_replay_wide_single(shape, brow, split_k):
 
 
 def test_wide_only_plans():
-    """Plans whose every task is a wide tile say so (their launch runs
+    """Plans of wide tiles, tail bundles and no-ops say so (their launch runs
     eight-wave workgroups); a wide plan with other tiles, and every plan on the
     256 x 128 tile, does not."""
     con, _, _ = _dense_single(3, 1024, 1024, 1024, True)
@@ -591,7 +595,25 @@ def test_wide_only_plans():
     assert bst.Plan(con, tile_cols=256, split_k=3).stats()["wide_only"] == 1
     assert bst.Plan(con).stats()["wide_only"] == 0
     prob = C.blockdiag_bf16(ld_align=8, align=8, values=False)
-    assert bst.Plan(prob.con, tile_cols=256).stats()["wide_only"] == 0   # tail bundles share the launch
+    assert bst.Plan(prob.con, tile_cols=256).stats()["wide_only"] == 1   # wide tiles and tail bundles
+    assert bst.Plan(prob.con).stats()["wide_only"] == 0
+    prob = C.blockdiag_bf16(values=False)                                 # unpadded: four general tiles too
+    assert bst.Plan(prob.con, tile_cols=256).stats()["wide_only"] == 0
+
+
+def test_wide_half_rows_policy():
+    """Wide plans cut the groups whose K chain is far above one CU's share
+    into 128-row wide tiles: on the bf16 block-diagonal workload only the
+    1024^3 sector (32 tiles of 128 x 256); tile_rows forces either height."""
+    prob = C.blockdiag_bf16(ld_align=8, align=8, values=False)
+    _, _, _, _, _, _, tk, fa = decode(bst.Plan(prob.con, tile_cols=256))
+    w = [t for t in range(len(tk)) if tk[t]["cls"] in (T_WIDE_N, T_WIDE_K)]
+    cut = [t for t in w if fa[t]["K"] == 1024]
+    assert len(cut) == 32 and all(fa[t]["mlen"] == 128 for t in cut)
+    assert all(fa[t]["mlen"] > 128 or fa[t]["K"] < 1024 for t in w if t not in cut)
+    _, _, _, _, _, _, tk2, fa2 = decode(bst.Plan(prob.con, tile_cols=256, tile_rows=256))
+    assert all(fa2[t]["mlen"] > 128 for t in range(len(tk2)) if tk2[t]["cls"] in (T_WIDE_N, T_WIDE_K)
+               and fa2[t]["K"] == 1024)
 
 
 def test_tile_cols_option_checked():

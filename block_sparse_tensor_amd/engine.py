@@ -79,9 +79,27 @@ def _torch():
     return torch
 
 
+_raw_stream = None
+
+
+def _current_stream_raw():
+    """Raw handle of torch's current stream on the current device.  torch's
+    raw-stream query (the one its own extensions use) takes about 0.3 us;
+    building a Stream object through current_stream() about 2.8 us, which
+    is a third of a whole small contraction's time, so the former is used
+    where this torch has it."""
+    global _raw_stream
+    torch = _torch()
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_stream:
+        return _raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
+
+
 def _stream_handle(stream):
     if stream is None:
-        return c_void_p(_torch().cuda.current_stream().cuda_stream)
+        return c_void_p(_current_stream_raw())
     if isinstance(stream, int):
         return c_void_p(stream)
     return c_void_p(stream.cuda_stream)

@@ -251,3 +251,15 @@ def test_launch_counter():
     before = plan.stats()["launches_issued"]
     run_engine(plan, prob.a, prob.b, np.zeros(prob.con.C.buffer_elems, np.float32), "f32", repeats=3)
     assert plan.stats()["launches_issued"] - before == 3
+
+
+def test_current_stream_handle():
+    """The binding enqueues on torch's current stream, also inside a stream
+    context (its raw-stream query against the Stream object's handle)."""
+    from block_sparse_tensor_amd import engine
+    t = torch()
+    assert engine._current_stream_raw() == t.cuda.current_stream().cuda_stream
+    s = t.cuda.Stream()
+    with t.cuda.stream(s):
+        assert engine._current_stream_raw() == s.cuda_stream
+    assert engine._current_stream_raw() == t.cuda.current_stream().cuda_stream

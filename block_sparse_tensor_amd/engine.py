@@ -231,8 +231,8 @@ class Plan:
         self._dev = dev
         return self
 
-    def _check_tensor(self, t, name, need, dtypes):
-        torch = _torch()
+    @staticmethod
+    def _check_tensor(torch, t, name, need, dtypes):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError(f"{name} must be a CUDA/HIP torch tensor")
         if t.dtype not in dtypes:
@@ -250,11 +250,16 @@ class Plan:
         return (torch.bfloat16, torch.int16, torch.uint16), (torch.float32,)
 
     def check_operands(self, A, B, C):
-        """Device, dtype, contiguity and size of A, B, C (raises on a mismatch)."""
-        ab, cd = self._operand_dtypes()
-        self._check_tensor(A, "A", self.a_elems, ab)
-        self._check_tensor(B, "B", self.b_elems, ab)
-        self._check_tensor(C, "C", self.c_elems, cd)
+        """Device, dtype, contiguity and size of A, B, C (raises on a mismatch).
+        Runs on every contraction, so the accepted dtypes are looked up once."""
+        torch = _torch()
+        dts = getattr(self, "_dtypes", None)
+        if dts is None:
+            dts = self._dtypes = self._operand_dtypes()
+        ab, cd = dts
+        self._check_tensor(torch, A, "A", self.a_elems, ab)
+        self._check_tensor(torch, B, "B", self.b_elems, ab)
+        self._check_tensor(torch, C, "C", self.c_elems, cd)
 
     def contract(self, A, B, C, stream=None):
         """Enqueue C (+)= A B on `stream` (default: torch's current stream)."""
